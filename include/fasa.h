@@ -1,0 +1,178 @@
+/*
+ * fasa.h -- C ABI of libfasa.so: the decode-time hot path of FASA
+ * (Frequency-Aware Sparse Attention) for AMD Instinct MI355X (gfx950).
+ *
+ * One decode step, for every sequence b and kv head g (a "unit"):
+ *   TIP  : S[j] = sum over the group's query heads h and the dominant FCs f of
+ *          q_h[2 I_g[f]] k_j[2 I_g[f]] + q_h[2 I_g[f]+1] k_j[2 I_g[f]+1]
+ *          for every cached token j < t_b  (paper-graph-ui review of FASA,
+ *          section 3.4 "Online Stage 1: Token Importance Predictor (TIP)",
+ *          score equation; FC i is the dimension pair (2i, 2i+1), section 3.4
+ *          "RoPE from a Frequency-Chunk Perspective").
+ *   TOP-B: sel = forced tokens  U  the B candidates with the largest S, where
+ *          the forced tokens are j < n_sink and j >= t_b - n_recent, equal
+ *          scores go to the lower index, and -0.0 equals +0.0 (section 3.4,
+ *          token-selection equation T_t = TopK-I(S_t, N_fac)).
+ *   FAC  : out_h = softmax(q_h K_sel^T * scale) V_sel for every query head of
+ *          the group, over the selected rows at their original positions
+ *          (section 3.4 "Online Stage 2: Focused Attention Computation",
+ *          gather and attention equations).
+ * Query head h belongs to kv head h / (n_q_heads / n_kv_heads).
+ *
+ * Memory layout (all element offsets are in units of the cache dtype):
+ *   q         [batch][n_q_heads][head_dim]            post-RoPE query, kv dtype
+ *   k_pool,   element (p, g, s, c) of physical block p, kv head g, slot s,
+ *   v_pool      channel c at p*kv_block_stride + g*kv_head_stride + s*head_dim + c
+ *               (a paged pool [n_blocks][H_kv][256][d] has strides
+ *               (H_kv*256*d, 256*d); a dense [batch][H_kv][T][d] cache has
+ *               strides (256*d, T*d) with block_table[b][k] = b*H_kv*T/256 + k)
+ *   block_table [batch][max_blocks_per_seq] int32: token j of sequence b lives
+ *               in physical block block_table[b][j/256], slot j%256
+ *   seq_lens  [batch] int32, t_b: cached tokens 0..t_b-1 (the query is at t_b)
+ *   fc_idx    [n_kv_heads][n_fc] int32: dominant FC indices I_g, distinct,
+ *               each in [0, head_dim/2)
+ *   slab      the dominant-key cache (FC-major side copy of the dominant key
+ *               columns): element (p, g, f, s, c) = K(p, g, s, 2*fc_idx[g][f]+c)
+ *               at p*slab_block_stride + g*slab_head_stride + f*512 + s*2 + c
+ *   scores    [batch][n_kv_heads][max_t] fp32, S of token j at column j
+ *   sel_idx   [batch][n_kv_heads][cap] int32, cap = fasa_selection_capacity():
+ *               the selected token indices ascending, then -1 padding
+ *   sel_count [batch][n_kv_heads] int32, number of valid entries of sel_idx
+ *   out       [batch][n_q_heads][head_dim] fp32
+ *
+ * Ownership and threading: the caller owns every buffer; every pointer is a
+ * device pointer except the fasa_shape and fc_idx_host arguments, which are
+ * read during the call only.  The library allocates nothing, frees nothing,
+ * never synchronises, and keeps no mutable global state, so calls are
+ * thread-safe and may be captured into a HIP graph.  Work is enqueued on the
+ * given stream (0 = the null stream).
+ *
+ * Errors: every argument is validated on the host before anything is enqueued;
+ * on any error nothing is enqueued or written.  FASA_ERR_HIP reports a failed
+ * kernel launch.  Faults inside kernels surface at the caller's next
+ * synchronisation.  The *contents* of device arrays are preconditions:
+ * seq_lens[b] <= min(max_t, 256*max_blocks_per_seq), block_table entries name
+ * allocated blocks, fc_idx rows are distinct and in range (check them with
+ * fasa_check_fc_idx), and scores are finite (non-finite scores give an
+ * unspecified selection).  Kernels clamp t_b into range instead of faulting.
+ * A sequence with t_b = 0 selects nothing and its output rows are zero.
+ */
+#ifndef FASA_H
+#define FASA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fasa_status {
+  FASA_OK = 0,
+  FASA_ERR_INVALID_ARG = 1,  /* null pointer, size or stride out of range */
+  FASA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head_dim != 128, ...) */
+  FASA_ERR_WORKSPACE = 3,    /* workspace too small or misaligned */
+  FASA_ERR_HIP = 4           /* a kernel launch failed */
+} fasa_status;
+
+typedef enum fasa_dtype { FASA_F32 = 0, FASA_BF16 = 1 } fasa_dtype;
+
+/* Problem description, read on the host at call time only. */
+typedef struct fasa_shape {
+  int32_t batch;              /* sequences, >= 1 */
+  int32_t n_q_heads;          /* H_q, a multiple of n_kv_heads */
+  int32_t n_kv_heads;         /* H_kv >= 1; group size G = H_q/H_kv <= 16 */
+  int32_t head_dim;           /* d, must be 128 */
+  int32_t n_fc;               /* F dominant FCs per kv head, 1..head_dim/2 */
+  int32_t budget;             /* B >= 1; B >= candidates keeps them all */
+  int32_t n_sink;             /* always-kept first tokens, >= 0 */
+  int32_t n_recent;           /* always-kept last tokens, >= 0 */
+  int32_t block_size;         /* tokens per cache block, must be 256 */
+  int32_t max_blocks_per_seq; /* columns of block_table, >= 1 */
+  int64_t kv_block_stride;    /* elements, multiple of 8, >= 256*head_dim */
+  int64_t kv_head_stride;     /* elements, multiple of 8, >= 256*head_dim */
+  int64_t slab_block_stride;  /* elements, multiple of 8 */
+  int64_t slab_head_stride;   /* elements, multiple of 8, >= 512*n_fc */
+  int32_t kv_dtype;           /* fasa_dtype of q, k_pool, v_pool and slab */
+  float scale;                /* softmax scale; 0 means 1/sqrt(head_dim) */
+} fasa_shape;
+
+/* Text for a status code (static storage). */
+const char* fasa_status_str(fasa_status s);
+
+/* Host-side check of every field of *shape (no device work). */
+fasa_status fasa_validate_shape(const fasa_shape* shape);
+
+/* cap = min(max_t, budget + n_sink + n_recent): the row length of sel_idx. */
+fasa_status fasa_selection_capacity(const fasa_shape* shape, int32_t max_t, int32_t* cap);
+
+/* Bytes of workspace fasa_decode (and fasa_fac) need for contexts up to max_t.
+ * The workspace must be 256-byte aligned; its contents are scratch. */
+fasa_status fasa_workspace_size(const fasa_shape* shape, int32_t max_t, size_t* bytes);
+
+/* Host check of a HOST copy of fc_idx [n_kv_heads][n_fc]: every entry in
+ * [0, head_dim/2) and no duplicate within a row (an FC is an indivisible unit
+ * and is counted once: section 3.4, "FCs Are Indivisible Units"). */
+fasa_status fasa_check_fc_idx(const fasa_shape* shape, const int32_t* fc_idx_host);
+
+/* Build the dominant-key cache for tokens 0..t_b-1 of every sequence from the
+ * post-RoPE key pool (the GPU-resident dominant key cache of section 3.4,
+ * "Hardware-Aware Variants": only the dominant dimensions of every key).
+ * Writes whole blocks: slots past t_b in a sequence's last block are copied
+ * as they are. */
+fasa_status fasa_slab_build(const fasa_shape* shape, const void* k_pool,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* fc_idx, void* slab, hipStream_t stream);
+
+/* After the caller has written the post-RoPE key of token positions[b] of every
+ * sequence into k_pool, copy its dominant columns into the slab.  positions[b]
+ * < 0 skips sequence b; positions must be < 256*max_blocks_per_seq. */
+fasa_status fasa_slab_append(const fasa_shape* shape, const void* k_pool,
+                             const int32_t* block_table, const int32_t* positions,
+                             const int32_t* fc_idx, void* slab, hipStream_t stream);
+
+/* TIP: scores[b][g][j] for j < t_b (columns past t_b are left untouched).
+ * Reads the slab when slab != NULL; with slab == NULL it gathers the dominant
+ * columns straight from k_pool (same arithmetic, same bits, more bytes).
+ * Scores accumulate in fp32: the query heads of the group are first summed per
+ * dominant column (fp32), then each token's 2*n_fc products are added in FC
+ * order with fused multiply-adds. */
+fasa_status fasa_tip(const fasa_shape* shape, const void* q, const void* slab,
+                     const void* k_pool, const int32_t* block_table,
+                     const int32_t* seq_lens, const int32_t* fc_idx, float* scores,
+                     int32_t max_t, hipStream_t stream);
+
+/* TOP-B over given scores: sel_idx / sel_count as described above.  Exact:
+ * the selection is a function of the fp32 score bits only.  The workspace is
+ * sized by fasa_workspace_size (it may be shared with the other calls of one
+ * step, which run in stream order). */
+fasa_status fasa_topk(const fasa_shape* shape, const float* scores,
+                      const int32_t* seq_lens, int32_t max_t, int32_t* sel_idx,
+                      int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* FAC over a given selection (sel_idx / sel_count laid out for max_t).
+ * bf16 caches compute in fp32; fp32 caches compute logits, softmax and the
+ * weighted sum in fp64 and round the result to fp32 once. */
+fasa_status fasa_fac(const fasa_shape* shape, const void* q, const void* k_pool,
+                     const void* v_pool, const int32_t* block_table,
+                     const int32_t* sel_idx, const int32_t* sel_count, int32_t max_t,
+                     float* out, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* The whole step: TIP -> TOP-B -> FAC, enqueued on one stream.  slab == NULL
+ * makes TIP read the dominant columns from k_pool.  sel_idx and sel_count are
+ * outputs (the selection used). */
+fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_pool,
+                        const void* v_pool, const void* slab, const int32_t* block_table,
+                        const int32_t* seq_lens, int32_t max_t, const int32_t* fc_idx,
+                        float* out, int32_t* sel_idx, int32_t* sel_count,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FASA_H */

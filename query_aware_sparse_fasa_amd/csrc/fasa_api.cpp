@@ -1,0 +1,249 @@
+// C ABI of libfasa.so (declared in include/fasa.h): host-side validation, then
+// kernel launches on the caller's stream.  Nothing here allocates, synchronises
+// or keeps state between calls.
+#include <stdint.h>
+#include <string.h>
+
+#include <limits>
+
+#include "fasa.h"
+#include "fasa_internal.hpp"
+
+using fasa::Common;
+using fasa::FacPlan;
+
+namespace {
+
+constexpr int64_t kMaxGrid = 65535;   // limit of gridDim.y / gridDim.z
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+fasa_status check_shape(const fasa_shape* s) {
+  if (!s) return FASA_ERR_INVALID_ARG;
+  if (s->kv_dtype != FASA_F32 && s->kv_dtype != FASA_BF16) return FASA_ERR_INVALID_ARG;
+  if (s->batch < 1 || s->batch > kMaxGrid) return FASA_ERR_INVALID_ARG;
+  if (s->n_kv_heads < 1 || s->n_q_heads < 1) return FASA_ERR_INVALID_ARG;
+  if (s->n_q_heads % s->n_kv_heads != 0) return FASA_ERR_INVALID_ARG;
+  if (s->head_dim < 2 || (s->head_dim & 1)) return FASA_ERR_INVALID_ARG;
+  if (s->head_dim != fasa::kHeadDim) return FASA_ERR_UNSUPPORTED;
+  if (s->block_size != fasa::kBlock) return FASA_ERR_UNSUPPORTED;
+  const int group = s->n_q_heads / s->n_kv_heads;
+  if (group > 16) return FASA_ERR_UNSUPPORTED;
+  if (int64_t(s->n_kv_heads) * ((group + 7) / 8) > kMaxGrid) return FASA_ERR_UNSUPPORTED;
+  if (s->n_q_heads > kMaxGrid) return FASA_ERR_UNSUPPORTED;
+  if (s->n_fc < 1 || s->n_fc > s->head_dim / 2) return FASA_ERR_INVALID_ARG;
+  if (s->budget < 1) return FASA_ERR_INVALID_ARG;
+  if (s->n_sink < 0 || s->n_recent < 0) return FASA_ERR_INVALID_ARG;
+  if (s->max_blocks_per_seq < 1 || s->max_blocks_per_seq > (std::numeric_limits<int32_t>::max() / 256))
+    return FASA_ERR_INVALID_ARG;
+  const int64_t row = int64_t(fasa::kBlock) * s->head_dim;
+  if (s->kv_head_stride < row || (s->kv_head_stride & 7)) return FASA_ERR_INVALID_ARG;
+  if (s->kv_block_stride < row || (s->kv_block_stride & 7)) return FASA_ERR_INVALID_ARG;
+  if (s->slab_head_stride < int64_t(fasa::kSlabFcStride) * s->n_fc || (s->slab_head_stride & 7))
+    return FASA_ERR_INVALID_ARG;
+  if (s->slab_block_stride < int64_t(fasa::kSlabFcStride) * s->n_fc || (s->slab_block_stride & 7))
+    return FASA_ERR_INVALID_ARG;
+  if (!(s->scale >= 0.f) || s->scale == std::numeric_limits<float>::infinity()) return FASA_ERR_INVALID_ARG;
+  return FASA_OK;
+}
+
+fasa_status check_max_t(const fasa_shape* s, int32_t max_t) {
+  if (max_t < 0) return FASA_ERR_INVALID_ARG;
+  // The last block of a sequence is read whole; scores rows must fit an int.
+  if (int64_t(max_t) > int64_t(s->max_blocks_per_seq) * fasa::kBlock) return FASA_ERR_INVALID_ARG;
+  return FASA_OK;
+}
+
+int32_t capacity(const fasa_shape* s, int32_t max_t) {
+  const int64_t want = int64_t(s->budget) + s->n_sink + s->n_recent;
+  return int32_t(want < max_t ? want : max_t);
+}
+
+Common make_common(const fasa_shape* s, int32_t max_t) {
+  Common c;
+  c.batch = s->batch;
+  c.n_q_heads = s->n_q_heads;
+  c.n_kv_heads = s->n_kv_heads;
+  c.group = s->n_q_heads / s->n_kv_heads;
+  c.n_fc = s->n_fc;
+  c.budget = s->budget;
+  c.n_sink = s->n_sink;
+  c.n_recent = s->n_recent;
+  c.max_blocks = s->max_blocks_per_seq;
+  c.max_t = max_t;
+  c.cap = capacity(s, max_t);
+  c.kv_block_stride = s->kv_block_stride;
+  c.kv_head_stride = s->kv_head_stride;
+  c.slab_block_stride = s->slab_block_stride;
+  c.slab_head_stride = s->slab_head_stride;
+  c.bf16 = s->kv_dtype == FASA_BF16 ? 1 : 0;
+  c.scale = s->scale > 0.f ? s->scale : 1.0f / 11.313708498984761f;   // 1/sqrt(128)
+  return c;
+}
+
+size_t decode_workspace(const Common& c, const FacPlan& p) {
+  return fasa::scores_bytes(c) + fasa::fac_workspace_bytes(c, p);
+}
+
+fasa_status hip_status(hipError_t e) { return e == hipSuccess ? FASA_OK : FASA_ERR_HIP; }
+
+// Largest block-table / slab / pool pointers are only checked for null and
+// alignment; their extents are preconditions.
+size_t elem_align(const fasa_shape*) { return 16; }   // 16-byte vector loads
+
+}  // namespace
+
+extern "C" {
+
+const char* fasa_status_str(fasa_status s) {
+  switch (s) {
+    case FASA_OK: return "FASA_OK";
+    case FASA_ERR_INVALID_ARG: return "FASA_ERR_INVALID_ARG: null pointer, size, stride or alignment out of range";
+    case FASA_ERR_UNSUPPORTED: return "FASA_ERR_UNSUPPORTED: shape not implemented (head_dim must be 128, block_size 256, group <= 16)";
+    case FASA_ERR_WORKSPACE: return "FASA_ERR_WORKSPACE: workspace missing, too small or not 256-byte aligned";
+    case FASA_ERR_HIP: return "FASA_ERR_HIP: a kernel launch failed";
+  }
+  return "FASA: unknown status";
+}
+
+fasa_status fasa_validate_shape(const fasa_shape* shape) { return check_shape(shape); }
+
+fasa_status fasa_selection_capacity(const fasa_shape* shape, int32_t max_t, int32_t* cap) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
+  if (!cap) return FASA_ERR_INVALID_ARG;
+  *cap = capacity(shape, max_t);
+  return FASA_OK;
+}
+
+fasa_status fasa_workspace_size(const fasa_shape* shape, int32_t max_t, size_t* bytes) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
+  if (!bytes) return FASA_ERR_INVALID_ARG;
+  const Common c = make_common(shape, max_t);
+  *bytes = decode_workspace(c, fasa::fac_plan(c));
+  return FASA_OK;
+}
+
+fasa_status fasa_check_fc_idx(const fasa_shape* shape, const int32_t* fc_idx_host) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if (!fc_idx_host) return FASA_ERR_INVALID_ARG;
+  const int nfc_all = shape->head_dim / 2;
+  for (int g = 0; g < shape->n_kv_heads; ++g) {
+    uint64_t seen[2] = {0, 0};   // head_dim/2 <= 64 when head_dim == 128
+    for (int f = 0; f < shape->n_fc; ++f) {
+      const int32_t i = fc_idx_host[int64_t(g) * shape->n_fc + f];
+      if (i < 0 || i >= nfc_all) return FASA_ERR_INVALID_ARG;
+      uint64_t& w = seen[i >> 6];
+      const uint64_t bit = uint64_t(1) << (i & 63);
+      if (w & bit) return FASA_ERR_INVALID_ARG;
+      w |= bit;
+    }
+  }
+  return FASA_OK;
+}
+
+fasa_status fasa_slab_build(const fasa_shape* shape, const void* k_pool, const int32_t* block_table,
+                            const int32_t* seq_lens, const int32_t* fc_idx, void* slab,
+                            hipStream_t stream) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if (!k_pool || !block_table || !seq_lens || !fc_idx || !slab) return FASA_ERR_INVALID_ARG;
+  if (!aligned(k_pool, elem_align(shape)) || !aligned(slab, elem_align(shape))) return FASA_ERR_INVALID_ARG;
+  if (shape->max_blocks_per_seq > std::numeric_limits<int32_t>::max() / 256) return FASA_ERR_INVALID_ARG;
+  Common c = make_common(shape, shape->max_blocks_per_seq * fasa::kBlock);
+  return hip_status(fasa::launch_slab_build(c, k_pool, block_table, seq_lens, fc_idx, slab, stream));
+}
+
+fasa_status fasa_slab_append(const fasa_shape* shape, const void* k_pool, const int32_t* block_table,
+                             const int32_t* positions, const int32_t* fc_idx, void* slab,
+                             hipStream_t stream) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if (!k_pool || !block_table || !positions || !fc_idx || !slab) return FASA_ERR_INVALID_ARG;
+  if (!aligned(k_pool, elem_align(shape)) || !aligned(slab, elem_align(shape))) return FASA_ERR_INVALID_ARG;
+  Common c = make_common(shape, shape->max_blocks_per_seq * fasa::kBlock);
+  return hip_status(fasa::launch_slab_append(c, k_pool, block_table, positions, fc_idx, slab, stream));
+}
+
+fasa_status fasa_tip(const fasa_shape* shape, const void* q, const void* slab, const void* k_pool,
+                     const int32_t* block_table, const int32_t* seq_lens, const int32_t* fc_idx,
+                     float* scores, int32_t max_t, hipStream_t stream) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
+  if (!q || !block_table || !seq_lens || !fc_idx || !scores) return FASA_ERR_INVALID_ARG;
+  if (!slab && !k_pool) return FASA_ERR_INVALID_ARG;
+  const void* src = slab ? slab : k_pool;
+  if (!aligned(src, elem_align(shape)) || !aligned(scores, 16)) return FASA_ERR_INVALID_ARG;
+  if (max_t == 0) return FASA_OK;
+  Common c = make_common(shape, max_t);
+  return hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores, stream));
+}
+
+fasa_status fasa_topk(const fasa_shape* shape, const float* scores, const int32_t* seq_lens,
+                      int32_t max_t, int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;   // the select keeps its state on chip
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
+  if (!scores || !seq_lens || !sel_count) return FASA_ERR_INVALID_ARG;
+  if (!sel_idx && capacity(shape, max_t) > 0) return FASA_ERR_INVALID_ARG;
+  Common c = make_common(shape, max_t);
+  return hip_status(fasa::launch_topk(c, scores, seq_lens, sel_idx, sel_count, stream));
+}
+
+fasa_status fasa_fac(const fasa_shape* shape, const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_table, const int32_t* sel_idx, const int32_t* sel_count,
+                     int32_t max_t, float* out, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
+  if (!q || !k_pool || !v_pool || !block_table || !sel_count || !out) return FASA_ERR_INVALID_ARG;
+  if (!sel_idx && capacity(shape, max_t) > 0) return FASA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16)) return FASA_ERR_INVALID_ARG;
+  Common c = make_common(shape, max_t);
+  const FacPlan p = fasa::fac_plan(c);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < fasa::fac_workspace_bytes(c, p))
+    return FASA_ERR_WORKSPACE;
+  return hip_status(fasa::launch_fac(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out,
+                                     workspace, stream));
+}
+
+fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_pool, const void* v_pool,
+                        const void* slab, const int32_t* block_table, const int32_t* seq_lens,
+                        int32_t max_t, const int32_t* fc_idx, float* out, int32_t* sel_idx,
+                        int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !fc_idx || !out || !sel_count)
+    return FASA_ERR_INVALID_ARG;
+  if (!sel_idx && capacity(shape, max_t) > 0) return FASA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16)) return FASA_ERR_INVALID_ARG;
+  if (slab && !aligned(slab, 16)) return FASA_ERR_INVALID_ARG;
+  Common c = make_common(shape, max_t);
+  const FacPlan p = fasa::fac_plan(c);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < decode_workspace(c, p))
+    return FASA_ERR_WORKSPACE;
+  float* scores = static_cast<float*>(workspace);
+  void* fac_ws = static_cast<char*>(workspace) + fasa::scores_bytes(c);
+  if (max_t > 0) {
+    if ((st = hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores,
+                                          stream))) != FASA_OK)
+      return st;
+  }
+  if ((st = hip_status(fasa::launch_topk(c, scores, seq_lens, sel_idx, sel_count, stream))) != FASA_OK)
+    return st;
+  return hip_status(fasa::launch_fac(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out,
+                                     fac_ws, stream));
+}
+
+}  // extern "C"

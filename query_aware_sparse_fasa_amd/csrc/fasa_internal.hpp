@@ -1,0 +1,58 @@
+// Internal interface between the C-ABI layer (fasa_api.cpp) and the kernel
+// translation units.  Every launcher enqueues on the given stream and returns
+// the launch status; the API layer has validated all arguments before.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fasa {
+
+constexpr int kHeadDim = 128;
+constexpr int kBlock = 256;            // tokens per cache block
+constexpr int kSlabFcStride = 512;     // elements between FCs inside a slab block (256 tokens x 2)
+
+// Top-B kernel: candidates staged in LDS up to this many keys per unit.
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkLdsKeys = 32768;
+
+// FAC: 4 waves per workgroup, each wave produces one partial (m, l, acc[128]).
+constexpr int kFacWaves = 4;
+
+struct Common {
+  int batch, n_q_heads, n_kv_heads, group, n_fc, budget, n_sink, n_recent;
+  int max_blocks, max_t, cap;
+  int64_t kv_block_stride, kv_head_stride, slab_block_stride, slab_head_stride;
+  int bf16;     // 1: bf16 storage, 0: fp32 storage
+  float scale;
+};
+
+// FAC work split, derived on the host from the shape (workspace size depends on it).
+struct FacPlan {
+  int rows_per_wave;   // multiple of 4
+  int n_split;         // workgroups per (sequence, kv head, head chunk)
+  int n_partials;      // n_split * kFacWaves
+  int heads_per_pass;  // 1, 2, 4 or 8 (>= min(group, 8)), a power of two
+  int head_chunks;     // ceil(group / heads_per_pass)
+};
+
+FacPlan fac_plan(const Common& c);
+size_t fac_workspace_bytes(const Common& c, const FacPlan& p);
+size_t scores_bytes(const Common& c);
+
+hipError_t launch_slab_build(const Common& c, const void* k_pool, const int32_t* block_table,
+                             const int32_t* seq_lens, const int32_t* fc_idx, void* slab,
+                             hipStream_t s);
+hipError_t launch_slab_append(const Common& c, const void* k_pool, const int32_t* block_table,
+                              const int32_t* positions, const int32_t* fc_idx, void* slab,
+                              hipStream_t s);
+hipError_t launch_tip(const Common& c, const void* q, const void* slab, const void* k_pool,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      const int32_t* fc_idx, float* scores, hipStream_t s);
+hipError_t launch_topk(const Common& c, const float* scores, const int32_t* seq_lens,
+                       int32_t* sel_idx, int32_t* sel_count, hipStream_t s);
+hipError_t launch_fac(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_table, const int32_t* sel_idx,
+                      const int32_t* sel_count, float* out, void* ws, hipStream_t s);
+
+}  // namespace fasa

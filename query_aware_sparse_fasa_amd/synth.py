@@ -274,6 +274,8 @@ def unit_rows(inp: Inputs, b: int, g: int, pool: torch.Tensor) -> torch.Tensor:
     """The first t_b cached rows [t_b][d] of kv head g of sequence b (plain indexing)."""
     t = int(inp.seq_lens[b])
     n = (t + BLOCK - 1) // BLOCK
+    if n == 0:
+        return pool.new_empty((0, pool.shape[-1]))
     idx = torch.as_tensor(inp.block_table[b, :n].astype(np.int64), device=pool.device)
     rows = pool[idx, g]                               # [n][256][d]
     return rows.reshape(n * BLOCK, -1)[:t]

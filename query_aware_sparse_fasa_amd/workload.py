@@ -1,0 +1,80 @@
+"""Device buffers for one decode layer, and calls of the C ABI on them.
+
+Plumbing only: torch allocates device memory, the binding passes pointers.
+Used by the tests, the benchmark and the smoke check.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import fasa
+from .synth import Inputs
+
+
+class DeviceLayer:
+    """One decode layer's inputs and outputs resident on the GPU."""
+
+    def __init__(self, inp: Inputs, device="cuda", with_slab: bool = True, build_slab: bool = True):
+        cfg = inp.cfg
+        dev = torch.device(device)
+        self.inp = inp
+        self.cfg = cfg
+        self.max_t = inp.max_t
+        self.shape = fasa.make_shape(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.n_fc, cfg.budget,
+                                     inp.max_blocks, cfg.torch_dtype, cfg.n_sink, cfg.n_recent)
+        fasa.fasa_check_fc_idx(self.shape, inp.fc_idx)
+        self.q = inp.q.to(dev).contiguous()
+        self.k_pool = inp.k_pool.to(dev).contiguous()
+        self.v_pool = inp.v_pool.to(dev).contiguous()
+        self.block_table = torch.from_numpy(inp.block_table).to(dev)
+        self.seq_lens = torch.from_numpy(inp.seq_lens).to(dev)
+        self.fc_idx = torch.from_numpy(inp.fc_idx).to(dev)
+        self.cap = fasa.fasa_selection_capacity(self.shape, self.max_t)
+        B, H, Hq = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads
+        self.out = torch.zeros(B, Hq, 128, dtype=torch.float32, device=dev)
+        self.sel_idx = torch.full((B, H, max(self.cap, 1)), -7, dtype=torch.int32, device=dev)
+        self.sel_count = torch.full((B, H), -7, dtype=torch.int32, device=dev)
+        self.scores = torch.full((B, H, max(self.max_t, 4)), float("nan"), dtype=torch.float32, device=dev)
+        self.workspace = fasa.alloc_workspace(self.shape, self.max_t, device=dev)
+        self.slab = None
+        if with_slab:
+            self.slab = fasa.alloc_slab(self.shape, inp.n_blocks, device=dev)
+            if build_slab:
+                self.build_slab()
+
+    # -- the C ABI on these buffers ---------------------------------------------------
+    def build_slab(self, stream=None):
+        fasa.fasa_slab_build(self.shape, self.k_pool, self.block_table, self.seq_lens, self.fc_idx,
+                             self.slab, stream)
+
+    def tip(self, use_slab=True, stream=None):
+        fasa.fasa_tip(self.shape, self.q, self.slab if use_slab else None, self.k_pool, self.block_table,
+                      self.seq_lens, self.fc_idx, self.scores, self.max_t, stream)
+
+    def topk(self, scores=None, stream=None):
+        fasa.fasa_topk(self.shape, self.scores if scores is None else scores, self.seq_lens, self.max_t,
+                       self.sel_idx, self.sel_count, self.workspace, stream)
+
+    def fac(self, stream=None):
+        fasa.fasa_fac(self.shape, self.q, self.k_pool, self.v_pool, self.block_table, self.sel_idx,
+                      self.sel_count, self.max_t, self.out, self.workspace, stream)
+
+    def decode(self, use_slab=True, stream=None):
+        fasa.fasa_decode(self.shape, self.q, self.k_pool, self.v_pool, self.slab if use_slab else None,
+                         self.block_table, self.seq_lens, self.max_t, self.fc_idx, self.out,
+                         self.sel_idx, self.sel_count, self.workspace, stream)
+
+    # -- host copies ----------------------------------------------------------------
+    def selection(self, b: int, g: int) -> np.ndarray:
+        n = int(self.sel_count[b, g].item())
+        return self.sel_idx[b, g, :n].cpu().numpy().astype(np.int64)
+
+    def unit_host(self, b: int, g: int):
+        """(q_group, K, V) of one unit as fp64 host arrays (from the generated inputs)."""
+        from .synth import unit_rows
+        G = self.cfg.group
+        q = self.inp.q[b, g * G:(g + 1) * G].double().cpu().numpy()
+        K = unit_rows(self.inp, b, g, self.inp.k_pool).double().cpu().numpy()
+        V = unit_rows(self.inp, b, g, self.inp.v_pool).double().cpu().numpy()
+        return q, K, V

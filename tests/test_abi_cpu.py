@@ -1,0 +1,164 @@
+"""The C ABI without a GPU: the library loads, exports what include/fasa.h
+declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from query_aware_sparse_fasa_amd import fasa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fasa.h")
+FAKE = 0x10000   # never dereferenced: validation fails before any launch
+
+
+def header_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\*|fasa_status)\s+(fasa_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    L = fasa.lib()
+    names = header_functions()
+    assert len(names) == 11, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(fasa.EXPORTS) == names
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(fasa.fasa_shape) == 80
+    assert fasa.fasa_shape.kv_block_stride.offset == 40
+    assert fasa.fasa_shape.kv_dtype.offset == 72
+
+
+def test_status_strings():
+    for s in range(5):
+        assert fasa.status_str(s).startswith("FASA_")
+    assert "unknown" in fasa.status_str(99)
+
+
+def good(**kw):
+    base = dict(batch=2, n_q_heads=32, n_kv_heads=8, n_fc=16, budget=256, max_blocks_per_seq=16,
+                kv_dtype=torch.bfloat16)
+    base.update(kw)
+    return fasa.make_shape(**base)
+
+
+def test_valid_shape_and_sizes():
+    s = good()
+    fasa.fasa_validate_shape(s)
+    assert fasa.fasa_selection_capacity(s, 4096) == 256
+    assert fasa.fasa_selection_capacity(s, 100) == 100
+    s2 = good(n_sink=4, n_recent=64, budget=512)
+    assert fasa.fasa_selection_capacity(s2, 4096) == 580
+    assert fasa.fasa_selection_capacity(s, 0) == 0
+    ws = fasa.fasa_workspace_size(s, 4096)
+    assert ws >= 2 * 8 * 4096 * 4 and ws % 256 == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, fasa.FASA_ERR_UNSUPPORTED),
+    ("head_dim", 127, fasa.FASA_ERR_INVALID_ARG),
+    ("block_size", 128, fasa.FASA_ERR_UNSUPPORTED),
+    ("n_q_heads", 36, fasa.FASA_ERR_UNSUPPORTED),       # group 36/8 not integral -> invalid first
+    ("n_fc", 0, fasa.FASA_ERR_INVALID_ARG),
+    ("n_fc", 65, fasa.FASA_ERR_INVALID_ARG),
+    ("budget", 0, fasa.FASA_ERR_INVALID_ARG),
+    ("n_sink", -1, fasa.FASA_ERR_INVALID_ARG),
+    ("n_recent", -5, fasa.FASA_ERR_INVALID_ARG),
+    ("batch", 0, fasa.FASA_ERR_INVALID_ARG),
+    ("batch", 70000, fasa.FASA_ERR_INVALID_ARG),
+    ("n_kv_heads", 0, fasa.FASA_ERR_INVALID_ARG),
+    ("kv_dtype", 7, fasa.FASA_ERR_INVALID_ARG),
+    ("max_blocks_per_seq", 0, fasa.FASA_ERR_INVALID_ARG),
+    ("kv_head_stride", 256 * 128 - 8, fasa.FASA_ERR_INVALID_ARG),
+    ("kv_block_stride", 8 * 256 * 128 + 3, fasa.FASA_ERR_INVALID_ARG),
+    ("slab_head_stride", 16 * 512 - 8, fasa.FASA_ERR_INVALID_ARG),
+    ("slab_block_stride", 5, fasa.FASA_ERR_INVALID_ARG),
+    ("scale", -1.0, fasa.FASA_ERR_INVALID_ARG),
+    ("scale", float("nan"), fasa.FASA_ERR_INVALID_ARG),
+])
+def test_shape_rejections(field, value, status):
+    s = good()
+    setattr(s, field, value)
+    if field == "n_q_heads":
+        status = fasa.FASA_ERR_INVALID_ARG
+    with pytest.raises(fasa.FasaError) as e:
+        fasa.fasa_validate_shape(s)
+    assert e.value.status == status
+
+
+def test_group_limit():
+    with pytest.raises(fasa.FasaError) as e:
+        fasa.fasa_validate_shape(good(n_q_heads=64, n_kv_heads=2))
+    assert e.value.status == fasa.FASA_ERR_UNSUPPORTED
+    fasa.fasa_validate_shape(good(n_q_heads=32, n_kv_heads=2))
+
+
+def test_fc_idx_check():
+    s = good(n_kv_heads=2, n_q_heads=4, n_fc=3)
+    fasa.fasa_check_fc_idx(s, [[0, 5, 63], [1, 2, 3]])
+    for bad in ([[0, 5, 64], [1, 2, 3]], [[0, 5, 5], [1, 2, 3]], [[0, 5, 6], [1, -1, 3]]):
+        with pytest.raises(fasa.FasaError) as e:
+            fasa.fasa_check_fc_idx(s, bad)
+        assert e.value.status == fasa.FASA_ERR_INVALID_ARG
+
+
+def raw(name, *args):
+    return getattr(fasa.lib(), name)(*args)
+
+
+def test_entry_points_reject_before_launch():
+    s = good()
+    sp = ctypes.byref(s)
+    ws = fasa.fasa_workspace_size(s, 4096)
+    E = fasa.FASA_ERR_INVALID_ARG
+    # null pointers
+    assert raw("fasa_tip", sp, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, None) == E
+    assert raw("fasa_tip", sp, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, 4096, None) == E
+    assert raw("fasa_topk", sp, None, FAKE, 4096, FAKE, FAKE, None, 0, None) == E
+    assert raw("fasa_fac", sp, FAKE, FAKE, FAKE, FAKE, FAKE, None, 4096, FAKE, FAKE, ws, None) == E
+    assert raw("fasa_slab_build", sp, FAKE, FAKE, FAKE, FAKE, None, None) == E
+    assert raw("fasa_slab_append", sp, FAKE, FAKE, None, FAKE, FAKE, None) == E
+    assert raw("fasa_decode", sp, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4096, FAKE, None, FAKE, FAKE,
+               FAKE, ws, None) == E
+    # misaligned device pointers
+    assert raw("fasa_tip", sp, FAKE, FAKE + 2, None, FAKE, FAKE, FAKE, FAKE, 4096, None) == E
+    assert raw("fasa_tip", sp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE + 4, 4096, None) == E
+    # max_t out of range: negative, or more tokens than the block table can hold
+    assert raw("fasa_tip", sp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, -1, None) == E
+    assert raw("fasa_tip", sp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 16 * 256 + 1, None) == E
+    # workspace missing, too small, misaligned
+    W = fasa.FASA_ERR_WORKSPACE
+    args = (sp, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, FAKE)
+    assert raw("fasa_decode", *args, None, ws, None) == W
+    assert raw("fasa_decode", *args, FAKE, ws - 1, None) == W
+    assert raw("fasa_decode", *args, FAKE + 16, ws, None) == W
+    assert raw("fasa_fac", sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, 1024, None) == W
+    # sel_idx may be NULL only when the capacity is 0
+    assert raw("fasa_topk", sp, FAKE, FAKE, 4096, None, FAKE, None, 0, None) == E
+    # bad shape propagates
+    s.head_dim = 64
+    assert raw("fasa_decode", sp, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, FAKE,
+               FAKE, ws, None) == fasa.FASA_ERR_UNSUPPORTED
+    assert raw("fasa_workspace_size", sp, 4096, None) == fasa.FASA_ERR_UNSUPPORTED
+
+
+def test_workspace_grows_with_context_and_batch():
+    a = fasa.fasa_workspace_size(good(), 4096)
+    b = fasa.fasa_workspace_size(good(max_blocks_per_seq=32), 8192)
+    c = fasa.fasa_workspace_size(good(batch=4), 4096)
+    assert b > a and c > a
+    f32 = fasa.fasa_workspace_size(good(kv_dtype=torch.float32), 4096)
+    assert f32 > a     # fp64 partials for fp32 caches
+
+
+def test_binding_refuses_host_tensors():
+    s = good()
+    x = torch.zeros(4)
+    with pytest.raises(ValueError):
+        fasa.fasa_tip(s, x, x, None, x, x, x, x, 4)

@@ -1,0 +1,349 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.  Needs a GPU.
+
+Every case prints its name before touching the GPU so that a failing run names it.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import parity as PR
+from oracle import fasa_oracle as O
+from query_aware_sparse_fasa_amd import fasa, synth
+from query_aware_sparse_fasa_amd.synth import unit_rows
+from query_aware_sparse_fasa_amd.workload import DeviceLayer
+
+pytestmark = pytest.mark.gpu
+
+C = synth.CONFIGS
+SMALL = {
+    "c1": C["c1"],
+    "c2-ragged": C["c2"].replace(batch=3, t=None, t_range=(1000, 5000)),
+    "c3-shape": C["c3"].replace(batch=2, t=None, t_range=(7000, 9000)),
+    "c4-ragged": C["c4"].replace(batch=2, t=None, t_range=(3000, 9000)),
+    "c5-ragged": C["c5"].replace(batch=4, t_range=(300, 3000)),
+    "fp32-gqa4": C["c2"].replace(dtype="fp32", batch=2, t=None, t_range=(700, 2600), budget=100),
+    "g16-f5": C["c2"].replace(n_q_heads=32, n_kv_heads=2, n_fc=5, batch=2, t=None,
+                              t_range=(1500, 2500), budget=64),
+    "g2-f1-sink": C["c2"].replace(n_q_heads=4, n_kv_heads=2, n_fc=1, batch=2, t=None,
+                                  t_range=(600, 900), budget=33, n_sink=3, n_recent=5),
+    "f32-fc32": C["c2"].replace(n_q_heads=6, n_kv_heads=3, n_fc=32, batch=1, t=None,
+                                t_range=(2000, 2000), budget=300),
+    "fp32-g7-f64": C["c4"].replace(dtype="fp32", batch=1, t=None, t_range=(1200, 1300), n_fc=64,
+                                   budget=77),
+}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+_cache = {}
+
+
+def layer_for(name, seed=0, device="cuda"):
+    key = (name, seed)
+    if key not in _cache:
+        cfg = SMALL[name]
+        inp = synth.make_inputs(cfg, seed=seed, device="cpu")
+        _cache[key] = (inp, DeviceLayer(inp, device=device))
+    return _cache[key]
+
+
+def oracle_units(inp, units=None):
+    cfg = inp.cfg
+    res = {}
+    for b in range(cfg.batch):
+        for g in range(cfg.n_kv_heads):
+            if units is not None and (b, g) not in units:
+                continue
+            G = cfg.group
+            q = inp.q[b, g * G:(g + 1) * G].double().cpu().numpy()
+            K = unit_rows(inp, b, g, inp.k_pool).double().cpu().numpy()
+            V = unit_rows(inp, b, g, inp.v_pool).double().cpu().numpy()
+            r = O.decode_unit(q, K, V, inp.fc_idx[g], cfg.budget, cfg.n_sink, cfg.n_recent)
+            res[(b, g)] = (q, K, V, r)
+    return res
+
+
+# ------------------------------------------------------------------------ slab
+@pytest.mark.parametrize("name", list(SMALL))
+def test_slab_build_bit_exact(name):
+    say(f"[slab_build] {name}")
+    inp, L = layer_for(name)
+    torch.cuda.synchronize()
+    slab = L.slab.cpu()
+    cfg = inp.cfg
+    for b in range(cfg.batch):
+        t = int(inp.seq_lens[b])
+        for g in range(cfg.n_kv_heads):
+            K = synth.unit_rows(inp, b, g, inp.k_pool)             # cast values, no widening
+            ref = O.slab_rows(K.float().numpy(), inp.fc_idx[g])   # [F][t][2]
+            n = (t + 255) // 256
+            got = slab[torch.as_tensor(inp.block_table[b, :n].astype(np.int64)), g]  # [n][F][256][2]
+            got = got.permute(1, 0, 2, 3).reshape(cfg.n_fc, n * 256, 2)[:, :t].float().numpy()
+            np.testing.assert_array_equal(got, ref, err_msg=f"{name} b={b} g={g}")
+
+
+def test_slab_append_writes_one_slot():
+    name = "c5-ragged"
+    say(f"[slab_append] {name}")
+    inp, L = layer_for(name)
+    cfg = inp.cfg
+    L2 = DeviceLayer(inp, with_slab=True, build_slab=False)
+    L2.slab.fill_(float("nan"))
+    pos = np.array([int(t) - 1 for t in inp.seq_lens], dtype=np.int32)
+    pos[0] = min(257, int(inp.seq_lens[0]) - 1)       # a slot inside a block
+    pos[1] = -1                                      # skipped
+    fasa.fasa_slab_append(L2.shape, L2.k_pool, L2.block_table, torch.from_numpy(pos).cuda(),
+                          L2.fc_idx, L2.slab)
+    torch.cuda.synchronize()
+    a, ref = L2.slab.cpu(), L.slab.cpu()
+    written = np.zeros(a.shape[0] * 256, dtype=bool)
+    for b in range(cfg.batch):
+        if pos[b] < 0:
+            continue
+        p, s = int(inp.block_table[b, pos[b] // 256]), int(pos[b]) % 256
+        assert torch.equal(a[p, :, :, s], ref[p, :, :, s]), b
+        written[p * 256 + s] = True
+    rest = a.permute(0, 3, 1, 2, 4).reshape(a.shape[0] * 256, -1)[~torch.from_numpy(written)]
+    assert torch.isnan(rest.float()).all()
+
+
+# ------------------------------------------------------------------------ TIP
+@pytest.mark.parametrize("name", list(SMALL))
+def test_tip_scores(name):
+    say(f"[tip] {name}")
+    inp, L = layer_for(name)
+    cfg = inp.cfg
+    L.scores.fill_(float("nan"))
+    L.tip(use_slab=True)
+    s_slab = L.scores.clone()
+    L.scores.fill_(float("nan"))
+    L.tip(use_slab=False)
+    s_rows = L.scores.clone()
+    torch.cuda.synchronize()
+    s_slab, s_rows = s_slab.cpu().numpy(), s_rows.cpu().numpy()
+    for (b, g), (q, K, V, r) in oracle_units(inp).items():
+        t = int(inp.seq_lens[b])
+        got = s_slab[b, g, :t].astype(np.float64)
+        # reading the slab or gathering from the key rows: same arithmetic, same bits
+        np.testing.assert_array_equal(s_slab[b, g, :t], s_rows[b, g, :t])
+        bound = PR.tip_bound(q, K, inp.fc_idx[g])
+        err = np.abs(got - r["S"])
+        assert (err <= bound).all(), f"{name} b={b} g={g}: max err/bound {np.max(err / bound):.3f}"
+        # columns past t_b are untouched
+        assert np.isnan(s_slab[b, g, t:]).all()
+
+
+# ------------------------------------------------------------------------ top-B
+TOPK_CASES = [
+    # (kind, batch, H, max_t, lens, budget, n_sink, n_recent)
+    ("normal", 2, 3, 5000, [5000, 4097], 256, 0, 0),
+    ("normal", 1, 2, 32768, [32768], 256, 0, 0),
+    ("normal", 1, 1, 40000, [39999], 1024, 0, 0),        # past the LDS-staged size
+    ("ties", 2, 2, 3000, [3000, 2999], 100, 0, 0),
+    ("ties", 1, 1, 45000, [45000], 5000, 4, 64),
+    ("const", 2, 1, 2000, [2000, 1500], 37, 0, 0),
+    ("const", 1, 1, 33000, [33000], 999, 0, 0),
+    ("signed_zero", 1, 2, 4096, [4096], 300, 0, 0),
+    ("wide", 2, 2, 8192, [8192, 8000], 512, 4, 64),
+    ("sorted_asc", 1, 2, 1024, [1024], 10, 0, 0),
+    ("sorted_desc", 1, 2, 1024, [1000], 10, 0, 0),
+    ("normal", 3, 2, 700, [700, 68, 0], 512, 4, 64),     # B >= candidates, t < forced, t = 0
+    ("normal", 2, 1, 300, [1, 300], 1, 0, 0),
+    ("normal", 1, 1, 6193 * 5, [6193 * 5], 6193, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", TOPK_CASES, ids=lambda c: f"{c[0]}-t{c[3]}-B{c[5]}")
+def test_topk_exact_on_given_scores(case):
+    kind, batch, H, max_t, lens, budget, ns, nr = case
+    say(f"[topk] {case}")
+    scores = synth.random_scores(batch * H, max_t, kind, seed=max_t + budget).reshape(batch, H, max_t)
+    shape = fasa.make_shape(batch, H, H, 16, budget, (max_t + 255) // 256, torch.bfloat16, ns, nr)
+    cap = fasa.fasa_selection_capacity(shape, max_t)
+    dev = torch.device("cuda")
+    sc = torch.from_numpy(scores).to(dev)
+    lens_t = torch.tensor(lens, dtype=torch.int32, device=dev)
+    sel = torch.full((batch, H, max(cap, 1)), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((batch, H), -7, dtype=torch.int32, device=dev)
+    fasa.fasa_topk(shape, sc, lens_t, max_t, sel, cnt)
+    torch.cuda.synchronize()
+    sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(batch):
+        for g in range(H):
+            t = lens[b]
+            ref, _ = O.select(scores[b, g, :t].astype(np.float64), budget, ns, nr)
+            n = int(cnt[b, g])
+            assert n == len(ref), (b, g, n, len(ref))
+            np.testing.assert_array_equal(sel[b, g, :n], ref, err_msg=f"{case} b={b} g={g}")
+            assert (sel[b, g, n:cap] == -1).all()
+
+
+# ------------------------------------------------------------------------ FAC
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fac_on_oracle_selection(name):
+    say(f"[fac] {name}")
+    inp, L = layer_for(name)
+    cfg = inp.cfg
+    units = oracle_units(inp)
+    sel = np.full((cfg.batch, cfg.n_kv_heads, max(L.cap, 1)), -1, dtype=np.int32)
+    cnt = np.zeros((cfg.batch, cfg.n_kv_heads), dtype=np.int32)
+    for (b, g), (_, _, _, r) in units.items():
+        cnt[b, g] = len(r["sel"])
+        sel[b, g, :len(r["sel"])] = r["sel"]
+    L.sel_idx.copy_(torch.from_numpy(sel))
+    L.sel_count.copy_(torch.from_numpy(cnt))
+    L.out.fill_(float("nan"))
+    L.fac()
+    torch.cuda.synchronize()
+    out = L.out.cpu().numpy()
+    G = cfg.group
+    for (b, g), (q, K, V, r) in units.items():
+        err = np.abs(out[b, g * G:(g + 1) * G] - r["out"]).max()
+        assert err <= PR.OUT_ATOL[cfg.dtype], f"{name} b={b} g={g}: {err:.3e}"
+
+
+# ------------------------------------------------------------------------ whole step
+def _check_decode(inp, L, units, label):
+    cfg = inp.cfg
+    torch.cuda.synchronize()
+    out = L.out.cpu().numpy()
+    sel = L.sel_idx.cpu().numpy()
+    cnt = L.sel_count.cpu().numpy()
+    G = cfg.group
+    same = 0
+    for (b, g), (q, K, V, r) in units.items():
+        t = int(inp.seq_lens[b])
+        gs = sel[b, g, :cnt[b, g]].astype(np.int64)
+        assert (sel[b, g, cnt[b, g]:L.cap] == -1).all()
+        ok = PR.check_selection(gs, r, t, cfg.n_sink, cfg.n_recent, f"{label} b={b} g={g}")
+        same += ok
+        PR.check_output(out[b, g * G:(g + 1) * G], q, K, V, gs, r, ok, cfg.dtype,
+                        1 / np.sqrt(128), f"{label} b={b} g={g}")
+    return same
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_decode_end_to_end(name):
+    say(f"[decode] {name}")
+    inp, L = layer_for(name)
+    L.out.fill_(float("nan"))
+    L.decode()
+    _check_decode(inp, L, oracle_units(inp), name)
+
+
+def test_decode_without_slab_is_identical():
+    name = "c2-ragged"
+    say(f"[decode no-slab] {name}")
+    inp, L = layer_for(name)
+    L.decode(use_slab=True)
+    a = (L.out.clone(), L.sel_idx.clone(), L.sel_count.clone())
+    L.decode(use_slab=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], L.out) and torch.equal(a[1], L.sel_idx) and torch.equal(a[2], L.sel_count)
+
+
+def test_determinism():
+    name = "c5-ragged"
+    say(f"[determinism] {name}")
+    inp, L = layer_for(name)
+    L.decode()
+    a = (L.out.clone(), L.sel_idx.clone())
+    for _ in range(3):
+        L.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], L.out) and torch.equal(a[1], L.sel_idx)
+
+
+def test_all_fcs_and_full_budget_is_dense_attention():
+    """With every FC dominant and B >= t the step is full attention (library SDPA in fp64)."""
+    cfg = C["c2"].replace(n_fc=64, budget=100000, batch=2, t=None, t_range=(500, 1500))
+    say("[dense special case]")
+    inp = synth.make_inputs(cfg, seed=5)
+    L = DeviceLayer(inp)
+    L.decode()
+    torch.cuda.synchronize()
+    out = L.out.cpu().numpy()
+    G = cfg.group
+    for b in range(cfg.batch):
+        t = int(inp.seq_lens[b])
+        assert (L.sel_count[b].cpu().numpy() == t).all()
+        for g in range(cfg.n_kv_heads):
+            q = inp.q[b, g * G:(g + 1) * G].double()
+            K = synth.unit_rows(inp, b, g, inp.k_pool).double()
+            V = synth.unit_rows(inp, b, g, inp.v_pool).double()
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q[None, :, None, :], K[None, None].expand(1, G, t, 128),
+                V[None, None].expand(1, G, t, 128))[0, :, 0, :].numpy()
+            assert np.abs(out[b, g * G:(g + 1) * G] - ref).max() <= 2e-3
+
+
+def test_empty_and_tiny_sequences():
+    cfg = C["c5"].replace(batch=5, budget=16, n_sink=4, n_recent=8)
+    say("[edge lengths]")
+    inp = synth.make_inputs(cfg, seed=9, seq_lens=[0, 1, 13, 29, 300])
+    L = DeviceLayer(inp)
+    L.out.fill_(float("nan"))
+    L.decode()
+    torch.cuda.synchronize()
+    assert (L.out[0] == 0).all()
+    assert (L.sel_count[0] == 0).all()
+    _check_decode(inp, L, {k: v for k, v in oracle_units(inp).items() if k[0] > 0}, "edge")
+
+
+def test_graph_capture_replays():
+    name = "c2-ragged"
+    say(f"[graph] {name}")
+    inp, L = layer_for(name)
+    L.decode()
+    torch.cuda.synchronize()
+    ref = (L.out.clone(), L.sel_idx.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        L.out.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            L.decode()
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(3):
+        L.out.fill_(float("nan"))
+        L.sel_idx.fill_(-5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(L.out, ref[0]) and torch.equal(L.sel_idx, ref[1]), f"replay {i}"
+
+
+# ------------------------------------------------------------------------ full sizes
+FULL_SAMPLES = {
+    "c2": None,                                  # every unit
+    "c3": [(0, 0), (5, 3), (15, 7)],
+    "c4": [(0, 0), (1, 2), (3, 3)],
+    "c5": "extremes",
+}
+
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5"])
+def test_full_size_configs(key):
+    """The workloads at their full sizes, in the launch configuration the benchmark
+    times; the oracle checks sampled (sequence, kv head) units."""
+    cfg = C[key]
+    say(f"[full] {key} {cfg.name}")
+    inp = synth.make_inputs(cfg, seed=0, device="cuda")
+    L = DeviceLayer(inp)
+    L.decode()
+    torch.cuda.synchronize()
+    pick = FULL_SAMPLES.get(key)
+    if pick == "extremes":
+        order = np.argsort(inp.seq_lens)
+        pick = [(int(order[0]), 0), (int(order[-1]), 7), (int(order[len(order) // 2]), 3)]
+    units = oracle_units(inp, set(pick) if pick else None)
+    _check_decode(inp, L, units, key)
+    del L, inp
+    torch.cuda.empty_cache()
