@@ -52,11 +52,12 @@ def time_graph(torch, stream, graphs, reps):
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(reps):
-        for g in graphs:
-            g.replay()
-    end.record(stream)
+    with torch.cuda.stream(stream):        # replay() launches on the current stream
+        start.record(stream)
+        for _ in range(reps):
+            for g in graphs:
+                g.replay()
+        end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / 1e3
 
@@ -138,7 +139,7 @@ def main():
         lay.sel_idx = torch.zeros_like(base.sel_idx)
         lay.sel_count = torch.zeros_like(base.sel_count)
         lay.scores = torch.zeros_like(base.scores)
-        lay.workspace = torch.empty_like(base.workspace)
+        lay.workspace = torch.zeros_like(base.workspace)
         layers.append(lay)
     torch.cuda.synchronize()
     use_slab = not args.no_slab
@@ -169,17 +170,21 @@ def main():
     wall0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps // L):
-        g_full.replay()
-    if g_rem is not None:
-        g_rem.replay()
-    end.record(stream)
+    with torch.cuda.stream(stream):        # replay() launches on the current stream
+        start.record(stream)
+        for _ in range(args.steps // L):
+            g_full.replay()
+        if g_rem is not None:
+            g_rem.replay()
+        end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     el = start.elapsed_time(end) / 1e3
     steps_per_s = args.steps / el
-    log(f"[bench] {steps_per_s:,.0f} steps/s ({el / args.steps * 1e6:.2f} us/step, wall {wall:.3f} s)")
+    log(f"[bench] {steps_per_s:,.0f} steps/s ({el / args.steps * 1e6:.2f} us/step; events {el:.4f} s, "
+        f"host wall {wall:.4f} s)")
+    if not (0.8 * wall <= el <= 1.05 * wall + 1e-3):
+        raise RuntimeError(f"event time {el:.4f} s disagrees with the host clock {wall:.4f} s")
 
     # Per-kernel-group times (each group alone, same rotation over the L layers).
     reps = max(1, min(50, 2000 // L))

@@ -108,8 +108,13 @@ fasa_status fasa_validate_shape(const fasa_shape* shape);
 /* cap = min(max_t, budget + n_sink + n_recent): the row length of sel_idx. */
 fasa_status fasa_selection_capacity(const fasa_shape* shape, int32_t max_t, int32_t* cap);
 
-/* Bytes of workspace fasa_decode (and fasa_fac) need for contexts up to max_t.
- * The workspace must be 256-byte aligned; its contents are scratch. */
+/* Bytes of workspace that fasa_decode, fasa_topk and fasa_fac need for contexts
+ * up to max_t (one size for all three).  The workspace must be 256-byte aligned.
+ * It carries one small per-unit histogram from call to call: the select leaves
+ * it zero, and a workspace that starts zero-filled takes the fast path from the
+ * first call.  Its contents never change any result (a non-zero histogram only
+ * sends the select to its slower full-row path once).  Calls that share a
+ * workspace must be ordered on one stream. */
 fasa_status fasa_workspace_size(const fasa_shape* shape, int32_t max_t, size_t* bytes);
 
 /* Host check of a HOST copy of fc_idx [n_kv_heads][n_fc]: every entry in
@@ -146,8 +151,7 @@ fasa_status fasa_tip(const fasa_shape* shape, const void* q, const void* slab,
 
 /* TOP-B over given scores: sel_idx / sel_count as described above.  Exact:
  * the selection is a function of the fp32 score bits only.  The workspace is
- * sized by fasa_workspace_size (it may be shared with the other calls of one
- * step, which run in stream order). */
+ * sized by fasa_workspace_size. */
 fasa_status fasa_topk(const fasa_shape* shape, const float* scores,
                       const int32_t* seq_lens, int32_t max_t, int32_t* sel_idx,
                       int32_t* sel_count, void* workspace, size_t workspace_bytes,

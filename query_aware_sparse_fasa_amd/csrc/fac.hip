@@ -61,6 +61,15 @@ __device__ __forceinline__ double neg_inf<double>() { return -(double)INFINITY; 
 __device__ __forceinline__ float shfl_xor_acc(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ double shfl_xor_acc(double v, int m) { return __shfl_xor(v, m, 64); }
 
+// Sum over the 16 lanes of a row group, in every lane of it: DPP rotations for
+// fp32, cross-lane shuffles for fp64.
+__device__ __forceinline__ float row_sum(float v) { return row16_sum(v); }
+__device__ __forceinline__ double row_sum(double v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
 template <typename T, typename Acc, int HG>
 __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   const Common& c = a.c;
@@ -72,13 +81,32 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rg = lane >> 4, sub = lane & 15;
   const int64_t unit = int64_t(b) * c.n_kv_heads + g;
-  int count = a.sel_count[unit];
-  count = count < 0 ? 0 : (count > c.cap ? c.cap : count);   // contents are preconditions; stay in bounds
-  const int pidx = blockIdx.x * kFacWaves + wave;
-  const int r0 = pidx * p.rows_per_wave;
-  const int r1 = min(r0 + p.rows_per_wave, count);
+  const int r0 = (blockIdx.x * kFacWaves + wave) * p.rows_per_wave;
   const int32_t* sel = a.sel_idx + unit * c.cap;
   const int32_t* btab = a.block_table + int64_t(b) * c.max_blocks;
+
+  // Three memory round trips: (count, query slices, this wave's selected
+  // indices) are independent; the block-table entries depend on the indices;
+  // the K/V rows depend on those.  Every load is unconditional with clamped
+  // indices -- validity is applied afterwards -- so nothing serialises them.
+  int count = a.sel_count[unit];
+  Raw8<T> qr[HG];
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh) {
+    const int h = g * c.group + h0 + min(hh, nh - 1);
+    qr[hh].load(static_cast<const T*>(a.q) + (int64_t(b) * c.n_q_heads + h) * kHeadDim + 8 * sub);
+  }
+  const int cap1 = c.cap > 0 ? c.cap - 1 : 0;
+  const int j_first = c.cap > 0 ? sel[min(r0 + lane, cap1)] : -1;
+  count = count < 0 ? 0 : (count > c.cap ? c.cap : count);   // contents are preconditions; stay in bounds
+  const int r1 = min(r0 + p.rows_per_wave, count);
+
+  // Byte offset of the row selected at position r (held by lane r - base), or -1.
+  auto row_offset = [&](int r, int j) -> int64_t {
+    const bool ok = r < r1 && j >= 0 && j < c.max_blocks * kBlock;
+    const int64_t pb = btab[ok ? (j >> 8) : 0];
+    return ok ? pb * c.kv_block_stride + int64_t(j & (kBlock - 1)) * kHeadDim : -1;
+  };
 
   // Query slices of this pass's heads, pre-scaled (by scale*log2(e) for exp2 in fp32).
   const Acc qscale = sizeof(Acc) == 4 ? Acc(c.scale) * Acc(1.4426950408889634) : Acc(c.scale);
@@ -88,58 +116,66 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   for (int hh = 0; hh < HG; ++hh) {
     m[hh] = neg_inf<Acc>();
     l[hh] = Acc(0);
+    float x[8];
+    qr[hh].unpack(x);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = Acc(0);
-    if (hh < nh) {
-      const int h = g * c.group + h0 + hh;
-      float x[8];
-      load8(static_cast<const T*>(a.q) + (int64_t(b) * c.n_q_heads + h) * kHeadDim + 8 * sub, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[hh][e] = Acc(x[e]) * qscale;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[hh][e] = Acc(0);
+    for (int e = 0; e < 8; ++e) {
+      acc[hh][e] = Acc(0);
+      qv[hh][e] = (hh < nh) ? Acc(x[e]) * qscale : Acc(0);
     }
   }
 
   const T* kbase = static_cast<const T*>(a.k_pool) + int64_t(g) * c.kv_head_stride + 8 * sub;
   const T* vbase = static_cast<const T*>(a.v_pool) + int64_t(g) * c.kv_head_stride + 8 * sub;
-  for (int r4 = r0; r4 < r1; r4 += 4) {                  // wave-uniform trip count
-    const int r = r4 + rg;
-    const int j = r < r1 ? sel[r] : -1;
-    const bool valid = j >= 0 && j < c.max_blocks * kBlock;
-    float kx[8], vx[8];
-    if (valid) {
-      const int64_t off = int64_t(btab[j >> 8]) * c.kv_block_stride + int64_t(j & (kBlock - 1)) * kHeadDim;
-      load8(kbase + off, kx);
-      load8(vbase + off, vx);
-    } else {
+  constexpr int U = 2;                                     // row quads whose loads are in flight together
+  for (int base = r0; base < r1; base += 64) {             // wave-uniform
+    const int j = base == r0 ? j_first : sel[min(base + lane, cap1)];
+    const int64_t my_off = row_offset(base + lane, j);
+    const uint64_t ok = __ballot(my_off >= 0);
+    if (ok == 0) continue;
+    // Rows that are not valid load a valid row of this wave instead (and are then
+    // ignored), so the loads need no branch and all go out together.
+    const int64_t dummy = __shfl(my_off, __ffsll((unsigned long long)ok) - 1, 64);
+    const int nrows = min(64, r1 - base);
+    for (int q4 = 0; q4 < nrows; q4 += 4 * U) {
+      Raw8<T> kr[U], vr[U];
+      bool valid[U];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kx[e] = vx[e] = 0.f;
-    }
-    Acc z[HG];
+      for (int u = 0; u < U; ++u) {
+        const int src = q4 + 4 * u + rg;                   // lane holding this row's offset
+        const int64_t off = __shfl(my_off, src < 64 ? src : 0, 64);
+        valid[u] = (src < nrows) && off >= 0;
+        const int64_t o = valid[u] ? off : dummy;
+        kr[u].load(kbase + o);
+        vr[u].load(vbase + o);
+      }
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      Acc s = Acc(0);
+      for (int u = 0; u < U; ++u) {
+        float kx[8], vx[8];
+        kr[u].unpack(kx);
+        vr[u].unpack(vx);
+        Acc z[HG];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s = fma(qv[hh][e], Acc(kx[e]), s);
-      z[hh] = s;
-    }
+        for (int hh = 0; hh < HG; ++hh) {
+          Acc sacc = Acc(0);
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) {
+          for (int e = 0; e < 8; ++e) sacc = fma(qv[hh][e], Acc(kx[e]), sacc);
+          z[hh] = sacc;
+        }
 #pragma unroll
-      for (int hh = 0; hh < HG; ++hh) z[hh] += shfl_xor_acc(z[hh], o);
-    }
-    if (valid) {
+        for (int hh = 0; hh < HG; ++hh) z[hh] = row_sum(z[hh]);
+        if (valid[u]) {
 #pragma unroll
-      for (int hh = 0; hh < HG; ++hh) {
-        const Acc mn = fmax(m[hh], z[hh]);
-        const Acc corr = fexp<Acc>(m[hh] - mn);
-        const Acc pz = fexp<Acc>(z[hh] - mn);
-        m[hh] = mn;
-        l[hh] = fma(l[hh], corr, pz);
+          for (int hh = 0; hh < HG; ++hh) {
+            const Acc mn = fmax(m[hh], z[hh]);
+            const Acc corr = fexp<Acc>(m[hh] - mn);
+            const Acc pz = fexp<Acc>(z[hh] - mn);
+            m[hh] = mn;
+            l[hh] = fma(l[hh], corr, pz);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] = fma(acc[hh][e], corr, pz * Acc(vx[e]));
+            for (int e = 0; e < 8; ++e) acc[hh][e] = fma(acc[hh][e], corr, pz * Acc(vx[e]));
+          }
+        }
       }
     }
   }
@@ -164,43 +200,91 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
     }
   }
 
+  // Fold the 4 waves through LDS; the workgroup writes one partial per head.
+  __shared__ Acc s_acc[kFacWaves][HG][kHeadDim];
+  __shared__ Acc s_m[kFacWaves][HG], s_l[kFacWaves][HG];
   if (rg == 0) {
-    Acc* pacc = static_cast<Acc*>(a.part_acc);
-    Acc* pml = static_cast<Acc*>(a.part_ml);
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
-      if (hh < nh) {
-        const int64_t h = int64_t(b) * c.n_q_heads + g * c.group + h0 + hh;
-        const int64_t slot = h * p.n_partials + pidx;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pacc[slot * kHeadDim + 8 * sub + e] = acc[hh][e];
-        if (sub == 0) {
-          pml[slot * 2 + 0] = m[hh];
-          pml[slot * 2 + 1] = l[hh];
-        }
+      for (int e = 0; e < 8; ++e) s_acc[wave][hh][8 * sub + e] = acc[hh][e];
+      if (sub == 0) {
+        s_m[wave][hh] = m[hh];
+        s_l[wave][hh] = l[hh];
       }
+    }
+  }
+  __syncthreads();
+  Acc* pacc = static_cast<Acc*>(a.part_acc);
+  Acc* pml = static_cast<Acc*>(a.part_ml);
+  for (int idx = threadIdx.x; idx < nh * kHeadDim; idx += 256) {
+    const int hh = idx / kHeadDim, ch = idx % kHeadDim;
+    Acc M = neg_inf<Acc>();
+#pragma unroll
+    for (int w = 0; w < kFacWaves; ++w) M = fmax(M, s_m[w][hh]);
+    Acc L = Acc(0), O = Acc(0);
+    if (M != neg_inf<Acc>()) {
+#pragma unroll
+      for (int w = 0; w < kFacWaves; ++w) {
+        const Acc mw = s_m[w][hh];
+        const Acc wgt = (mw == neg_inf<Acc>()) ? Acc(0) : fexp<Acc>(mw - M);
+        L = fma(s_l[w][hh], wgt, L);
+        O = fma(s_acc[w][hh][ch], wgt, O);
+      }
+    }
+    const int64_t h = int64_t(b) * c.n_q_heads + g * c.group + h0 + hh;
+    const int64_t slot = h * p.n_partials + blockIdx.x;
+    pacc[slot * kHeadDim + ch] = O;
+    if (ch == 0) {
+      pml[slot * 2 + 0] = M;
+      pml[slot * 2 + 1] = L;
     }
   }
 }
 
+// One workgroup per (sequence, query head): log-sum-exp merge of the partials.
+// The weights e^(m_i - M) and l_i e^(m_i - M) go through LDS; each thread then
+// streams its channel of every partial with 8 loads in flight.
 template <typename Acc>
 __global__ __launch_bounds__(kHeadDim) void fac_merge_kernel(FacArgs a) {
+  constexpr int MAXP = 512;
+  __shared__ Acc s_w[MAXP], s_lw[MAXP];
+  __shared__ Acc s_red[2];
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int P = a.p.n_partials;
   const int64_t base = (int64_t(b) * a.c.n_q_heads + h) * P;
   const Acc* pacc = static_cast<const Acc*>(a.part_acc) + base * kHeadDim + d;
   const Acc* pml = static_cast<const Acc*>(a.part_ml) + base * 2;
   Acc M = neg_inf<Acc>();
-  for (int i = 0; i < P; ++i) M = fmax(M, pml[2 * i]);
+  for (int i = d; i < P; i += kHeadDim) M = fmax(M, pml[2 * i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmax(M, shfl_xor_acc(M, o));
+  if ((d & 63) == 0) s_red[d >> 6] = M;
+  __syncthreads();
+  M = fmax(s_red[0], s_red[1]);
   float res = 0.f;
   if (M != neg_inf<Acc>()) {
     Acc L = Acc(0), O = Acc(0);
-    for (int i = 0; i < P; ++i) {
-      const Acc mi = pml[2 * i];
-      if (mi == neg_inf<Acc>()) continue;
-      const Acc w = fexp<Acc>(mi - M);
-      L = fma(pml[2 * i + 1], w, L);
-      O = fma(pacc[int64_t(i) * kHeadDim], w, O);
+    for (int p0 = 0; p0 < P; p0 += MAXP) {
+      const int n = min(MAXP, P - p0);
+      __syncthreads();
+      for (int i = d; i < n; i += kHeadDim) {
+        const Acc mi = pml[2 * (p0 + i)];
+        const Acc w = (mi == neg_inf<Acc>()) ? Acc(0) : fexp<Acc>(mi - M);
+        s_w[i] = w;
+        s_lw[i] = pml[2 * (p0 + i) + 1] * w;
+      }
+      __syncthreads();
+      int i = 0;
+      for (; i + 8 <= n; i += 8) {
+        Acc v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = pacc[int64_t(p0 + i + u) * kHeadDim];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) O = fma(v[u], s_w[i + u], O);
+      }
+      for (; i < n; ++i) O = fma(pacc[int64_t(p0 + i) * kHeadDim], s_w[i], O);
+      for (int k = 0; k < n; ++k) L += s_lw[k];
     }
     res = float(O / L);
   }
@@ -244,7 +328,7 @@ FacPlan fac_plan(const Common& c) {
   p.rows_per_wave = int(rpw);
   const int per_wg = kFacWaves * p.rows_per_wave;
   p.n_split = c.cap > 0 ? (c.cap + per_wg - 1) / per_wg : 1;
-  p.n_partials = p.n_split * kFacWaves;
+  p.n_partials = p.n_split;
   return p;
 }
 

@@ -81,9 +81,23 @@ Common make_common(const fasa_shape* s, int32_t max_t) {
   return c;
 }
 
-size_t decode_workspace(const Common& c, const FacPlan& p) {
-  return fasa::scores_bytes(c) + fasa::fac_workspace_bytes(c, p);
+// Workspace layout shared by every entry point:
+//   [unit histograms | scores | FAC partials]
+// The histograms come first so that no other entry point ever writes over them:
+// the select leaves them zero for the next call (a workspace that starts zeroed
+// takes the fast path from the first call; other contents only slow it down).
+struct Layout {
+  size_t hist, scores, fac, total;
+};
+Layout layout(const Common& c, const FacPlan& p) {
+  Layout l;
+  l.hist = 0;
+  l.scores = fasa::hist_bytes(c);
+  l.fac = l.scores + fasa::scores_bytes(c);
+  l.total = l.fac + fasa::fac_workspace_bytes(c, p);
+  return l;
 }
+size_t decode_workspace(const Common& c, const FacPlan& p) { return layout(c, p).total; }
 
 fasa_status hip_status(hipError_t e) { return e == hipSuccess ? FASA_OK : FASA_ERR_HIP; }
 
@@ -181,21 +195,24 @@ fasa_status fasa_tip(const fasa_shape* shape, const void* q, const void* slab, c
   if (!aligned(src, elem_align(shape)) || !aligned(scores, 16)) return FASA_ERR_INVALID_ARG;
   if (max_t == 0) return FASA_OK;
   Common c = make_common(shape, max_t);
-  return hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores, stream));
+  return hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores, nullptr,
+                                     stream));
 }
 
 fasa_status fasa_topk(const fasa_shape* shape, const float* scores, const int32_t* seq_lens,
                       int32_t max_t, int32_t* sel_idx, int32_t* sel_count, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;   // the select keeps its state on chip
   fasa_status st = check_shape(shape);
   if (st != FASA_OK) return st;
   if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
   if (!scores || !seq_lens || !sel_count) return FASA_ERR_INVALID_ARG;
   if (!sel_idx && capacity(shape, max_t) > 0) return FASA_ERR_INVALID_ARG;
+  if (!aligned(scores, 16)) return FASA_ERR_INVALID_ARG;
   Common c = make_common(shape, max_t);
-  return hip_status(fasa::launch_topk(c, scores, seq_lens, sel_idx, sel_count, stream));
+  const Layout l = layout(c, fasa::fac_plan(c));
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < l.total) return FASA_ERR_WORKSPACE;
+  uint32_t* hist = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + l.hist);
+  return hip_status(fasa::launch_topk(c, scores, seq_lens, sel_idx, sel_count, hist, false, stream));
 }
 
 fasa_status fasa_fac(const fasa_shape* shape, const void* q, const void* k_pool, const void* v_pool,
@@ -210,10 +227,10 @@ fasa_status fasa_fac(const fasa_shape* shape, const void* q, const void* k_pool,
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16)) return FASA_ERR_INVALID_ARG;
   Common c = make_common(shape, max_t);
   const FacPlan p = fasa::fac_plan(c);
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < fasa::fac_workspace_bytes(c, p))
-    return FASA_ERR_WORKSPACE;
+  const Layout l = layout(c, p);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < l.total) return FASA_ERR_WORKSPACE;
   return hip_status(fasa::launch_fac(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out,
-                                     workspace, stream));
+                                     static_cast<char*>(workspace) + l.fac, stream));
 }
 
 fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_pool, const void* v_pool,
@@ -231,16 +248,19 @@ fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_po
   if (slab && !aligned(slab, 16)) return FASA_ERR_INVALID_ARG;
   Common c = make_common(shape, max_t);
   const FacPlan p = fasa::fac_plan(c);
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < decode_workspace(c, p))
-    return FASA_ERR_WORKSPACE;
-  float* scores = static_cast<float*>(workspace);
-  void* fac_ws = static_cast<char*>(workspace) + fasa::scores_bytes(c);
+  const Layout l = layout(c, p);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < l.total) return FASA_ERR_WORKSPACE;
+  char* w = static_cast<char*>(workspace);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(w + l.hist);
+  float* scores = reinterpret_cast<float*>(w + l.scores);
+  void* fac_ws = w + l.fac;
   if (max_t > 0) {
     if ((st = hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores,
-                                          stream))) != FASA_OK)
+                                          hist, stream))) != FASA_OK)
       return st;
   }
-  if ((st = hip_status(fasa::launch_topk(c, scores, seq_lens, sel_idx, sel_count, stream))) != FASA_OK)
+  if ((st = hip_status(fasa::launch_topk(c, scores, seq_lens, sel_idx, sel_count, hist, max_t > 0,
+                                         stream))) != FASA_OK)
     return st;
   return hip_status(fasa::launch_fac(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out,
                                      fac_ws, stream));

@@ -26,6 +26,34 @@ __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
+// Eight cache elements as loaded (before widening): one 16-byte vector for bf16,
+// two for fp32.  Keeping loads raw halves the registers held while they are in flight.
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void unpack(float (&x)[8]) const {
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+    x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+  }
+};
+template <>
+struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void unpack(float (&x)[8]) const {
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+};
+
 __device__ __forceinline__ float to_f32(uint16_t h) { return bf16_to_f32(h); }
 __device__ __forceinline__ float to_f32(float f) { return f; }
 
@@ -52,14 +80,38 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0));
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// DPP (data-parallel primitive) lane moves: a VALU operand modifier, no LDS
+// round trip.  update_dpp(old, src, ctrl, row_mask, bank_mask, bound_ctrl)
+// returns old in lanes whose source lane is out of range or masked off.
+constexpr int kDppRowShr = 0x110;      // + n: lane i reads lane i-n of its 16-lane row
+constexpr int kDppRowRor = 0x120;      // + n: rotate right by n inside the row
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row feeds the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 feeds rows 2 and 3
+
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele inside each
+// 16-lane row (shifts 1, 2, 4, 8), then row totals carried across rows.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t n = __shfl_up(v, o, 64);
-    if (lane >= o) v += n;
-  }
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr + 1, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr + 2, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr + 4, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr + 8, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast15, 0xA, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast31, 0xC, 0xF, false);
+  return v;
+}
+
+// Value of lane 63 (the wave total after an inclusive scan), as a scalar.
+__device__ __forceinline__ uint32_t wave_last(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Sum over the 16 lanes of each row, returned in every lane of the row
+// (rotations by 8, 4, 2, 1 inside the row).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowRor + 8, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowRor + 4, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowRor + 2, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowRor + 1, 0xF, 0xF, false));
   return v;
 }
 

@@ -12,11 +12,16 @@ constexpr int kHeadDim = 128;
 constexpr int kBlock = 256;            // tokens per cache block
 constexpr int kSlabFcStride = 512;     // elements between FCs inside a slab block (256 tokens x 2)
 
-// Top-B kernel: candidates staged in LDS up to this many keys per unit.
+// Top-B: one 1024-thread workgroup per unit; rows of up to 32768 tokens stay in
+// registers (32 per thread).  The coarse histogram has one bin per value of key
+// bits 31..21; up to kCandLds candidates are selected from LDS.
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkLdsKeys = 32768;
+constexpr int kHistBins = 2048;
+constexpr int kHistShift = 21;
+constexpr int kCandLds = 12288;
 
-// FAC: 4 waves per workgroup, each wave produces one partial (m, l, acc[128]).
+// FAC: 4 waves per workgroup; the waves' states are folded in LDS into one partial.
 constexpr int kFacWaves = 4;
 
 struct Common {
@@ -31,7 +36,7 @@ struct Common {
 struct FacPlan {
   int rows_per_wave;   // multiple of 4
   int n_split;         // workgroups per (sequence, kv head, head chunk)
-  int n_partials;      // n_split * kFacWaves
+  int n_partials;      // one partial (m, l, acc[128]) per workgroup: n_split
   int heads_per_pass;  // 1, 2, 4 or 8 (>= min(group, 8)), a power of two
   int head_chunks;     // ceil(group / heads_per_pass)
 };
@@ -46,11 +51,18 @@ hipError_t launch_slab_build(const Common& c, const void* k_pool, const int32_t*
 hipError_t launch_slab_append(const Common& c, const void* k_pool, const int32_t* block_table,
                               const int32_t* positions, const int32_t* fc_idx, void* slab,
                               hipStream_t s);
+size_t hist_bytes(const Common& c);
+
+// hist == nullptr: scores only.  Otherwise also accumulate the unit histograms
+// (which must hold the counts of nothing else: the select leaves them zero).
 hipError_t launch_tip(const Common& c, const void* q, const void* slab, const void* k_pool,
                       const int32_t* block_table, const int32_t* seq_lens,
-                      const int32_t* fc_idx, float* scores, hipStream_t s);
+                      const int32_t* fc_idx, float* scores, uint32_t* hist, hipStream_t s);
+// have_hist: the histograms already hold this step's counts (filled by TIP);
+// otherwise they are built first from the scores.  Either way they are zero on exit.
 hipError_t launch_topk(const Common& c, const float* scores, const int32_t* seq_lens,
-                       int32_t* sel_idx, int32_t* sel_count, hipStream_t s);
+                       int32_t* sel_idx, int32_t* sel_count, uint32_t* hist, bool have_hist,
+                       hipStream_t s);
 hipError_t launch_fac(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
                       const void* v_pool, const int32_t* block_table, const int32_t* sel_idx,
                       const int32_t* sel_count, float* out, void* ws, hipStream_t s);

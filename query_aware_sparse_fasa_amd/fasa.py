@@ -223,5 +223,6 @@ def alloc_slab(shape: fasa_shape, n_blocks: int, device="cuda") -> torch.Tensor:
 
 
 def alloc_workspace(shape: fasa_shape, max_t: int, device="cuda") -> torch.Tensor:
+    """Zero-filled, so the select takes its fast path from the first call."""
     n = fasa_workspace_size(shape, max_t)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)

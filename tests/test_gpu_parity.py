@@ -168,19 +168,25 @@ def test_topk_exact_on_given_scores(case):
     dev = torch.device("cuda")
     sc = torch.from_numpy(scores).to(dev)
     lens_t = torch.tensor(lens, dtype=torch.int32, device=dev)
-    sel = torch.full((batch, H, max(cap, 1)), -7, dtype=torch.int32, device=dev)
-    cnt = torch.full((batch, H), -7, dtype=torch.int32, device=dev)
-    fasa.fasa_topk(shape, sc, lens_t, max_t, sel, cnt)
-    torch.cuda.synchronize()
-    sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
-    for b in range(batch):
-        for g in range(H):
-            t = lens[b]
-            ref, _ = O.select(scores[b, g, :t].astype(np.float64), budget, ns, nr)
-            n = int(cnt[b, g])
-            assert n == len(ref), (b, g, n, len(ref))
-            np.testing.assert_array_equal(sel[b, g, :n], ref, err_msg=f"{case} b={b} g={g}")
-            assert (sel[b, g, n:cap] == -1).all()
+    ws = fasa.alloc_workspace(shape, max_t)
+    # First call on a workspace full of garbage (the select must fall back to its
+    # full-row path and still be exact), then two calls on the workspace the
+    # select left behind (the fast path).
+    ws.fill_(0xA5)
+    for attempt in range(3):
+        sel = torch.full((batch, H, max(cap, 1)), -7, dtype=torch.int32, device=dev)
+        cnt = torch.full((batch, H), -7, dtype=torch.int32, device=dev)
+        fasa.fasa_topk(shape, sc, lens_t, max_t, sel, cnt, ws)
+        torch.cuda.synchronize()
+        sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
+        for b in range(batch):
+            for g in range(H):
+                t = lens[b]
+                ref, _ = O.select(scores[b, g, :t].astype(np.float64), budget, ns, nr)
+                n = int(cnt_h[b, g])
+                assert n == len(ref), (attempt, b, g, n, len(ref))
+                np.testing.assert_array_equal(sel_h[b, g, :n], ref, err_msg=f"{case} b={b} g={g} call {attempt}")
+                assert (sel_h[b, g, n:cap] == -1).all()
 
 
 # ------------------------------------------------------------------------ FAC
@@ -234,6 +240,24 @@ def test_decode_end_to_end(name):
     L.out.fill_(float("nan"))
     L.decode()
     _check_decode(inp, L, oracle_units(inp), name)
+
+
+def test_decode_with_garbage_workspace_is_identical():
+    """The workspace carries a histogram between calls; garbage there may only
+    cost speed, never change a result."""
+    name = "c4-ragged"
+    say(f"[decode garbage ws] {name}")
+    inp, L = layer_for(name)
+    L.decode()
+    a = (L.out.clone(), L.sel_idx.clone(), L.sel_count.clone())
+    L.workspace.fill_(0x5A)
+    L.decode()
+    b = (L.out.clone(), L.sel_idx.clone(), L.sel_count.clone())
+    L.decode()
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    assert torch.equal(a[0], L.out) and torch.equal(a[1], L.sel_idx)
 
 
 def test_decode_without_slab_is_identical():
