@@ -62,6 +62,32 @@ def time_graph(torch, stream, graphs, reps):
     return start.elapsed_time(end) / 1e3
 
 
+COUNTERS = os.path.join(ROOT, "profiles", "tip_kernel_llama3-8b-t32768_hbm_counters.txt")
+TIP_SOURCES = ("tip.hip", "fasa_device.hpp", "fasa_internal.hpp")
+
+
+def measured_traffic(cfg_key: str, use_slab: bool):
+    """HBM bytes per TIP launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a 1 GiB reference copy), or None
+    when the summary is for another workload or the TIP sources changed since."""
+    import hashlib
+    if cfg_key != "c2" or not use_slab or not os.path.exists(COUNTERS):
+        return None
+    kv = {}
+    for line in open(COUNTERS):
+        if line.startswith("#") or ":" not in line:
+            continue
+        k, v = line.split(":", 1)
+        kv[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in TIP_SOURCES:
+        with open(os.path.join(ROOT, "query_aware_sparse_fasa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if kv.get("source_sha256") != h.hexdigest():
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
 def cpu_oracle_baseline(layer, cfg, seconds: float):
     """The fp64 oracle (as it stands) on the host: one step = every unit of the layer.
     Runs single-threaded (BLAS limited to 1 thread); returns steps/s and what was sampled."""
@@ -100,6 +126,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-slab", action="store_true", help="TIP gathers from the key rows instead")
+    ap.add_argument("--mode", choices=["step", "tip"], default="step",
+                    help="step: the benchmark; tip: only --steps TIP launches and one 1 GiB "
+                         "reference copy (for hardware-counter runs)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -146,6 +175,23 @@ def main():
 
     stream = torch.cuda.Stream(device=dev)
     stream.wait_stream(torch.cuda.current_stream())
+    if args.mode == "tip":
+        # Counter runs: exactly `steps` TIP launches over the rotated layers, then
+        # a plain device copy of 1 GiB whose bytes are known (read 1 GiB, write
+        # 1 GiB) to scale the counters.
+        with torch.cuda.stream(stream):
+            for i in range(args.steps):
+                layers[i % L].tip(use_slab=use_slab)
+            src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        tip_bytes = sb["slab"] if use_slab else int(inp.seq_lens.sum()) * cfg.n_kv_heads * 128 * cfg.elem_bytes
+        print(json.dumps({"mode": "tip", "tip_launches": args.steps, "tip_algorithmic_bytes": tip_bytes,
+                          "tip_score_bytes_written": int(inp.seq_lens.sum()) * cfg.n_kv_heads * 4,
+                          "copy_bytes_each_way": 1 << 30, "layers": L}), flush=True)
+        return
+
     with torch.cuda.stream(stream):
         for lay in layers:          # eager warm-up of every entry point
             lay.decode(use_slab=use_slab)
@@ -230,7 +276,8 @@ def main():
         "breakdown_us": {"tip": t_tip * 1e6, "topk": t_topk * 1e6, "fac_split_merge": t_fac * 1e6,
                          "decode_step": el / args.steps * 1e6},
         "roofline": {"kernel": "tip_kernel", "bound": "hbm", "achieved": tip_gbps, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": tip_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": tip_gbps / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(args.config, use_slab),
                      "algorithmic_bytes_per_launch": int(tip_bytes),
                      "avg_launch_us": t_tip * 1e6},
         "cpu_baseline": cpu,
