@@ -24,6 +24,7 @@
 // ~2e-6 absolute error, enough to move a fp32 output by more than 1e-5).
 #include <math.h>
 
+#include "fac_core.hpp"
 #include "fasa_device.hpp"
 #include "fasa_internal.hpp"
 
@@ -44,32 +45,6 @@ struct FacArgs {
   float* out;
 };
 
-template <typename Acc>
-__device__ __forceinline__ Acc fexp(Acc x);
-template <>
-__device__ __forceinline__ float fexp<float>(float x) { return exp2f(x); }
-template <>
-__device__ __forceinline__ double fexp<double>(double x) { return exp(x); }
-
-template <typename Acc>
-__device__ __forceinline__ Acc neg_inf();
-template <>
-__device__ __forceinline__ float neg_inf<float>() { return -INFINITY; }
-template <>
-__device__ __forceinline__ double neg_inf<double>() { return -(double)INFINITY; }
-
-__device__ __forceinline__ float shfl_xor_acc(float v, int m) { return __shfl_xor(v, m, 64); }
-__device__ __forceinline__ double shfl_xor_acc(double v, int m) { return __shfl_xor(v, m, 64); }
-
-// Sum over the 16 lanes of a row group, in every lane of it: DPP rotations for
-// fp32, cross-lane shuffles for fp64.
-__device__ __forceinline__ float row_sum(float v) { return row16_sum(v); }
-__device__ __forceinline__ double row_sum(double v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 template <typename T, typename Acc, int HG>
 __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   const Common& c = a.c;
@@ -78,139 +53,46 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   const int g = blockIdx.y / p.head_chunks;
   const int h0 = (blockIdx.y % p.head_chunks) * HG;      // first head of this pass, within the group
   const int nh = min(HG, c.group - h0);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rg = lane >> 4, sub = lane & 15;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, sub = lane & 15;
   const int64_t unit = int64_t(b) * c.n_kv_heads + g;
   const int r0 = (blockIdx.x * kFacWaves + wave) * p.rows_per_wave;
   const int32_t* sel = a.sel_idx + unit * c.cap;
   const int32_t* btab = a.block_table + int64_t(b) * c.max_blocks;
 
-  // Three memory round trips: (count, query slices, this wave's selected
-  // indices) are independent; the block-table entries depend on the indices;
-  // the K/V rows depend on those.  Every load is unconditional with clamped
+  // Three memory round trips: (count, query slices, this wave's first 64
+  // selected indices) are independent; the block-table entries depend on the
+  // indices; the K/V rows depend on those.  Loads are unconditional with clamped
   // indices -- validity is applied afterwards -- so nothing serialises them.
   int count = a.sel_count[unit];
-  Raw8<T> qr[HG];
-#pragma unroll
-  for (int hh = 0; hh < HG; ++hh) {
-    const int h = g * c.group + h0 + min(hh, nh - 1);
-    qr[hh].load(static_cast<const T*>(a.q) + (int64_t(b) * c.n_q_heads + h) * kHeadDim + 8 * sub);
-  }
   const int cap1 = c.cap > 0 ? c.cap - 1 : 0;
   const int j_first = c.cap > 0 ? sel[min(r0 + lane, cap1)] : -1;
+  FacWave<T, Acc, HG> w;
+  w.init(static_cast<const T*>(a.q) + (int64_t(b) * c.n_q_heads + g * c.group + h0) * kHeadDim, nh,
+         c.scale);
   count = count < 0 ? 0 : (count > c.cap ? c.cap : count);   // contents are preconditions; stay in bounds
   const int r1 = min(r0 + p.rows_per_wave, count);
-
-  // Byte offset of the row selected at position r (held by lane r - base), or -1.
-  auto row_offset = [&](int r, int j) -> int64_t {
+  auto lane_offset = [&](int r) -> int64_t {
+    const int j = (r - lane == r0) ? j_first : sel[min(r, cap1)];
     const bool ok = r < r1 && j >= 0 && j < c.max_blocks * kBlock;
     const int64_t pb = btab[ok ? (j >> 8) : 0];
     return ok ? pb * c.kv_block_stride + int64_t(j & (kBlock - 1)) * kHeadDim : -1;
   };
-
-  // Query slices of this pass's heads, pre-scaled (by scale*log2(e) for exp2 in fp32).
-  const Acc qscale = sizeof(Acc) == 4 ? Acc(c.scale) * Acc(1.4426950408889634) : Acc(c.scale);
-  Acc qv[HG][8];
-  Acc m[HG], l[HG], acc[HG][8];
-#pragma unroll
-  for (int hh = 0; hh < HG; ++hh) {
-    m[hh] = neg_inf<Acc>();
-    l[hh] = Acc(0);
-    float x[8];
-    qr[hh].unpack(x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc[hh][e] = Acc(0);
-      qv[hh][e] = (hh < nh) ? Acc(x[e]) * qscale : Acc(0);
-    }
-  }
-
-  const T* kbase = static_cast<const T*>(a.k_pool) + int64_t(g) * c.kv_head_stride + 8 * sub;
-  const T* vbase = static_cast<const T*>(a.v_pool) + int64_t(g) * c.kv_head_stride + 8 * sub;
-  constexpr int U = 2;                                     // row quads whose loads are in flight together
-  for (int base = r0; base < r1; base += 64) {             // wave-uniform
-    const int j = base == r0 ? j_first : sel[min(base + lane, cap1)];
-    const int64_t my_off = row_offset(base + lane, j);
-    const uint64_t ok = __ballot(my_off >= 0);
-    if (ok == 0) continue;
-    // Rows that are not valid load a valid row of this wave instead (and are then
-    // ignored), so the loads need no branch and all go out together.
-    const int64_t dummy = __shfl(my_off, __ffsll((unsigned long long)ok) - 1, 64);
-    const int nrows = min(64, r1 - base);
-    for (int q4 = 0; q4 < nrows; q4 += 4 * U) {
-      Raw8<T> kr[U], vr[U];
-      bool valid[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int src = q4 + 4 * u + rg;                   // lane holding this row's offset
-        const int64_t off = __shfl(my_off, src < 64 ? src : 0, 64);
-        valid[u] = (src < nrows) && off >= 0;
-        const int64_t o = valid[u] ? off : dummy;
-        kr[u].load(kbase + o);
-        vr[u].load(vbase + o);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float kx[8], vx[8];
-        kr[u].unpack(kx);
-        vr[u].unpack(vx);
-        Acc z[HG];
-#pragma unroll
-        for (int hh = 0; hh < HG; ++hh) {
-          Acc sacc = Acc(0);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sacc = fma(qv[hh][e], Acc(kx[e]), sacc);
-          z[hh] = sacc;
-        }
-#pragma unroll
-        for (int hh = 0; hh < HG; ++hh) z[hh] = row_sum(z[hh]);
-        if (valid[u]) {
-#pragma unroll
-          for (int hh = 0; hh < HG; ++hh) {
-            const Acc mn = fmax(m[hh], z[hh]);
-            const Acc corr = fexp<Acc>(m[hh] - mn);
-            const Acc pz = fexp<Acc>(z[hh] - mn);
-            m[hh] = mn;
-            l[hh] = fma(l[hh], corr, pz);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[hh][e] = fma(acc[hh][e], corr, pz * Acc(vx[e]));
-          }
-        }
-      }
-    }
-  }
-
-  // Fold the four row groups (lanes sub, sub+16, sub+32, sub+48 own the same channels).
-#pragma unroll
-  for (int o = 16; o <= 32; o <<= 1) {
-#pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      const Acc mo = shfl_xor_acc(m[hh], o);
-      const Acc lo = shfl_xor_acc(l[hh], o);
-      const Acc mn = fmax(m[hh], mo);
-      const Acc ca = (m[hh] == neg_inf<Acc>()) ? Acc(0) : fexp<Acc>(m[hh] - mn);
-      const Acc cb = (mo == neg_inf<Acc>()) ? Acc(0) : fexp<Acc>(mo - mn);
-      l[hh] = l[hh] * ca + lo * cb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const Acc ao = shfl_xor_acc(acc[hh][e], o);
-        acc[hh][e] = acc[hh][e] * ca + ao * cb;
-      }
-      m[hh] = mn;
-    }
-  }
+  const T* kbase = static_cast<const T*>(a.k_pool) + int64_t(g) * c.kv_head_stride;
+  const T* vbase = static_cast<const T*>(a.v_pool) + int64_t(g) * c.kv_head_stride;
+  w.run(r0, r1, lane_offset, kbase, vbase);
+  w.fold_row_groups();
 
   // Fold the 4 waves through LDS; the workgroup writes one partial per head.
   __shared__ Acc s_acc[kFacWaves][HG][kHeadDim];
   __shared__ Acc s_m[kFacWaves][HG], s_l[kFacWaves][HG];
-  if (rg == 0) {
+  if (lane < 16) {
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_acc[wave][hh][8 * sub + e] = acc[hh][e];
+      for (int e = 0; e < 8; ++e) s_acc[wave][hh][8 * sub + e] = w.acc[hh][e];
       if (sub == 0) {
-        s_m[wave][hh] = m[hh];
-        s_l[wave][hh] = l[hh];
+        s_m[wave][hh] = w.m[hh];
+        s_l[wave][hh] = w.l[hh];
       }
     }
   }
@@ -221,15 +103,14 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
     const int hh = idx / kHeadDim, ch = idx % kHeadDim;
     Acc M = neg_inf<Acc>();
 #pragma unroll
-    for (int w = 0; w < kFacWaves; ++w) M = fmax(M, s_m[w][hh]);
+    for (int v = 0; v < kFacWaves; ++v) M = fmax(M, s_m[v][hh]);
     Acc L = Acc(0), O = Acc(0);
     if (M != neg_inf<Acc>()) {
 #pragma unroll
-      for (int w = 0; w < kFacWaves; ++w) {
-        const Acc mw = s_m[w][hh];
-        const Acc wgt = (mw == neg_inf<Acc>()) ? Acc(0) : fexp<Acc>(mw - M);
-        L = fma(s_l[w][hh], wgt, L);
-        O = fma(s_acc[w][hh][ch], wgt, O);
+      for (int v = 0; v < kFacWaves; ++v) {
+        const Acc wgt = merge_weight(s_m[v][hh], M);
+        L = fma(s_l[v][hh], wgt, L);
+        O = fma(s_acc[v][hh][ch], wgt, O);
       }
     }
     const int64_t h = int64_t(b) * c.n_q_heads + g * c.group + h0 + hh;
