@@ -13,8 +13,10 @@
 // softmax.  Every K/V row is loaded once per kv head and reused by all query
 // heads of the group (GQA).  A wave's logits need a 16-lane reduction; the four
 // row groups of a wave are folded together with cross-lane shuffles at the end
-// and the wave writes one partial.  A second kernel merges the partials of a
-// head with the log-sum-exp rule.  With at most 8 query heads per pass the q.K
+// and the workgroup folds its waves into one partial.  The partials of a head
+// are merged with the log-sum-exp rule, in a decode step by the last workgroup
+// of the head's split to finish (an arrival counter decides which), otherwise
+// by a second launch.  With at most 8 query heads per pass the q.K
 // product is an 8 x 128 by 128 x rows contraction at a few flops per loaded
 // byte -- HBM/latency bound, so it runs on the vector ALUs, not MFMA.
 //
@@ -43,9 +45,58 @@ struct FacArgs {
   void* part_acc;   // [b][H_q][P][128] Acc
   void* part_ml;    // [b][H_q][P][2]   Acc (running max, running sum)
   float* out;
+  uint32_t* arrive; // [b][H_kv][head_chunks] arrival counters (zeroed by the preceding kernel), MERGE only
 };
 
-template <typename T, typename Acc, int HG>
+// Log-sum-exp merge of the P partials of query heads head0 .. head0+nh-1 by one
+// 256-thread workgroup: wave w reduces the (max, sum) pairs of heads w, w+4, ...
+// across its lanes (one partial per lane, P <= 64) into weights e^(m_i - M) in
+// LDS; then every output channel is the weighted sum of its P partials over L.
+template <typename Acc, int HG>
+__device__ void merge_heads(const FacArgs& a, int64_t head0, int nh) {
+  __shared__ Acc s_w[HG][kFacMergeMax];
+  __shared__ Acc s_l[HG];
+  const int P = a.p.n_partials;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const Acc* pml = static_cast<const Acc*>(a.part_ml);
+  const Acc* pacc = static_cast<const Acc*>(a.part_acc);
+  for (int hh = wave; hh < nh; hh += 4) {
+    const int64_t slot = (head0 + hh) * P + min(lane, P - 1);
+    const Acc mi = lane < P ? pml[slot * 2 + 0] : neg_inf<Acc>();
+    const Acc li = lane < P ? pml[slot * 2 + 1] : Acc(0);
+    Acc M = mi;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmax(M, shfl_xor_acc(M, o));
+    const Acc w = (M == neg_inf<Acc>()) ? Acc(0) : merge_weight(mi, M);
+    Acc L = li * w;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L += shfl_xor_acc(L, o);
+    if (lane < P) s_w[hh][lane] = w;
+    if (lane == 0) s_l[hh] = L;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nh * kHeadDim; idx += 256) {
+    const int hh = idx / kHeadDim, ch = idx % kHeadDim;
+    const Acc* src = pacc + (head0 + hh) * P * kHeadDim + ch;
+    Acc O = Acc(0);
+    int i = 0;
+    for (; i + 8 <= P; i += 8) {
+      Acc v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = src[int64_t(i + u) * kHeadDim];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) O = fma(v[u], s_w[hh][i + u], O);
+    }
+    for (; i < P; ++i) O = fma(src[int64_t(i) * kHeadDim], s_w[hh][i], O);
+    const Acc L = s_l[hh];
+    a.out[(head0 + hh) * kHeadDim + ch] = L > Acc(0) ? float(O / L) : 0.f;
+  }
+}
+
+// MERGE: the last workgroup of a (sequence, kv head, head chunk) to finish --
+// counted on an arrival counter -- merges the partials of its heads, so no
+// second launch is needed (used when n_split <= kFacMergeMax).
+template <typename T, typename Acc, int HG, bool MERGE>
 __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   const Common& c = a.c;
   const FacPlan& p = a.p;
@@ -121,6 +172,13 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
       pml[slot * 2 + 1] = L;
     }
   }
+  if constexpr (MERGE) {
+    // The workgroup that completes the head chunk's split merges it.
+    __shared__ uint32_t s_last;
+    if (!arrive_last(&a.arrive[int64_t(blockIdx.z) * gridDim.y + blockIdx.y], uint32_t(p.n_split), &s_last))
+      return;
+    merge_heads<Acc, HG>(a, int64_t(b) * c.n_q_heads + g * c.group + h0, nh);
+  }
 }
 
 // One workgroup per (sequence, query head): log-sum-exp merge of the partials.
@@ -172,16 +230,25 @@ __global__ __launch_bounds__(kHeadDim) void fac_merge_kernel(FacArgs a) {
   a.out[(int64_t(b) * a.c.n_q_heads + h) * kHeadDim + d] = res;
 }
 
+template <typename T, typename Acc, bool MERGE>
+void launch_split(const FacArgs& a, const dim3& grid, hipStream_t s) {
+  switch (a.p.heads_per_pass) {
+    case 1: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 1, MERGE>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 2, MERGE>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 4, MERGE>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 8, MERGE>), grid, dim3(256), 0, s, a); break;
+  }
+}
+
 template <typename T, typename Acc>
 hipError_t launch_fac_t(FacArgs& a, hipStream_t s) {
   const FacPlan& p = a.p;
   const dim3 grid(p.n_split, a.c.n_kv_heads * p.head_chunks, a.c.batch);
-  switch (p.heads_per_pass) {
-    case 1: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 4>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 8>), grid, dim3(256), 0, s, a); break;
+  if (a.arrive != nullptr && p.n_split <= kFacMergeMax) {
+    launch_split<T, Acc, true>(a, grid, s);
+    return hipGetLastError();
   }
+  launch_split<T, Acc, false>(a, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fac_merge_kernel<Acc>, dim3(a.c.n_q_heads, a.c.batch), dim3(kHeadDim), 0, s, a);
@@ -225,12 +292,12 @@ size_t scores_bytes(const Common& c) {
 
 hipError_t launch_fac(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
                       const void* v_pool, const int32_t* block_table, const int32_t* sel_idx,
-                      const int32_t* sel_count, float* out, void* ws, hipStream_t s) {
+                      const int32_t* sel_count, float* out, void* ws, uint32_t* arrive, hipStream_t s) {
   const size_t acc_sz = c.bf16 ? sizeof(float) : sizeof(double);
   const size_t slots = size_t(c.batch) * c.n_q_heads * p.n_partials;
   char* w = static_cast<char*>(ws);
   FacArgs a{c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count,
-            w, w + align256(slots * kHeadDim * acc_sz), out};
+            w, w + align256(slots * kHeadDim * acc_sz), out, arrive};
   if (c.bf16) return launch_fac_t<uint16_t, float>(a, s);
   return launch_fac_t<float, double>(a, s);
 }

@@ -82,20 +82,33 @@ Common make_common(const fasa_shape* s, int32_t max_t) {
 }
 
 // Workspace layout shared by every entry point:
-//   [unit histograms | scores | FAC partials]
+//   [unit histograms | arrival counters | scores | kept pairs | kept counts | FAC partials]
 // The histograms come first so that no other entry point ever writes over them:
 // the select leaves them zero for the next call (a workspace that starts zeroed
 // takes the fast path from the first call; other contents only slow it down).
+// The arrival counters (one per unit for the filter, one per unit and head
+// chunk for FAC) are zeroed by the launch before the one that counts on them.
 struct Layout {
-  size_t hist, scores, fac, total;
+  size_t hist, arrive, fac_arrive, scores, slots, counts, fac, total;
 };
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 Layout layout(const Common& c, const FacPlan& p) {
+  const size_t units = size_t(c.batch) * c.n_kv_heads;
   Layout l;
   l.hist = 0;
-  l.scores = fasa::hist_bytes(c);
-  l.fac = l.scores + fasa::scores_bytes(c);
+  l.arrive = fasa::hist_bytes(c);
+  l.fac_arrive = l.arrive + align256(units * sizeof(uint32_t));
+  l.scores = l.fac_arrive + align256(units * p.head_chunks * sizeof(uint32_t));
+  l.slots = l.scores + fasa::scores_bytes(c);
+  l.counts = l.slots + fasa::slots_bytes(c);
+  l.fac = l.counts + fasa::counts_bytes(c);
   l.total = l.fac + fasa::fac_workspace_bytes(c, p);
   return l;
+}
+fasa::SelectBuffers select_buffers(void* workspace, const Layout& l) {
+  char* w = static_cast<char*>(workspace);
+  return {reinterpret_cast<uint32_t*>(w + l.hist), reinterpret_cast<uint32_t*>(w + l.arrive), w + l.slots,
+          reinterpret_cast<int32_t*>(w + l.counts)};
 }
 size_t decode_workspace(const Common& c, const FacPlan& p) { return layout(c, p).total; }
 
@@ -196,7 +209,7 @@ fasa_status fasa_tip(const fasa_shape* shape, const void* q, const void* slab, c
   if (max_t == 0) return FASA_OK;
   Common c = make_common(shape, max_t);
   return hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores, nullptr,
-                                     stream));
+                                     nullptr, stream));
 }
 
 fasa_status fasa_topk(const fasa_shape* shape, const float* scores, const int32_t* seq_lens,
@@ -211,8 +224,8 @@ fasa_status fasa_topk(const fasa_shape* shape, const float* scores, const int32_
   Common c = make_common(shape, max_t);
   const Layout l = layout(c, fasa::fac_plan(c));
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < l.total) return FASA_ERR_WORKSPACE;
-  uint32_t* hist = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + l.hist);
-  return hip_status(fasa::launch_topk(c, scores, seq_lens, sel_idx, sel_count, hist, false, stream));
+  return hip_status(fasa::launch_topk(c, scores, seq_lens, sel_idx, sel_count, select_buffers(workspace, l),
+                                      false, nullptr, 0, stream));
 }
 
 fasa_status fasa_fac(const fasa_shape* shape, const void* q, const void* k_pool, const void* v_pool,
@@ -230,7 +243,7 @@ fasa_status fasa_fac(const fasa_shape* shape, const void* q, const void* k_pool,
   const Layout l = layout(c, p);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < l.total) return FASA_ERR_WORKSPACE;
   return hip_status(fasa::launch_fac(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out,
-                                     static_cast<char*>(workspace) + l.fac, stream));
+                                     static_cast<char*>(workspace) + l.fac, nullptr, stream));
 }
 
 fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_pool, const void* v_pool,
@@ -250,20 +263,22 @@ fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_po
   const FacPlan p = fasa::fac_plan(c);
   const Layout l = layout(c, p);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < l.total) return FASA_ERR_WORKSPACE;
+  // TIP (+ unit histograms, filter counters zeroed) -> top-B (+ FAC counters
+  // zeroed) -> FAC (merged by its last workgroups).
   char* w = static_cast<char*>(workspace);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(w + l.hist);
+  const fasa::SelectBuffers sb = select_buffers(workspace, l);
   float* scores = reinterpret_cast<float*>(w + l.scores);
-  void* fac_ws = w + l.fac;
+  uint32_t* fac_arrive = reinterpret_cast<uint32_t*>(w + l.fac_arrive);
   if (max_t > 0) {
     if ((st = hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores,
-                                          hist, stream))) != FASA_OK)
+                                          sb.hist, sb.arrive, stream))) != FASA_OK)
       return st;
   }
-  if ((st = hip_status(fasa::launch_topk(c, scores, seq_lens, sel_idx, sel_count, hist, max_t > 0,
-                                         stream))) != FASA_OK)
+  if ((st = hip_status(fasa::launch_topk(c, scores, seq_lens, sel_idx, sel_count, sb, max_t > 0, fac_arrive,
+                                         p.head_chunks, stream))) != FASA_OK)
     return st;
   return hip_status(fasa::launch_fac(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out,
-                                     fac_ws, stream));
+                                     w + l.fac, fac_arrive, stream));
 }
 
 }  // extern "C"

@@ -115,4 +115,27 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Hand-off between the workgroups of one launch: the last one to arrive on
+// `counter` (which must start at zero) sees everything the others stored before
+// arriving.  Every wave waits until its own stores are acknowledged, the
+// workgroup meets at a barrier, then one thread writes the XCD's L2 back
+// (agent-scope release), waits for that, and moves the counter; the thread that
+// moves it to n invalidates its stale cached lines (agent-scope acquire) before
+// the barrier that hands the verdict to the rest of the workgroup.  One L2
+// write-back per workgroup, and one invalidate per hand-off.  Returns true in
+// every thread of the last workgroup.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t n, uint32_t* lds_flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);
+    const bool last = atomicAdd(counter, 1u) == n - 1u;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *lds_flag = last ? 1u : 0u;
+  }
+  __syncthreads();
+  return *lds_flag != 0u;
+}
+
 }  // namespace fasa

@@ -12,17 +12,25 @@ constexpr int kHeadDim = 128;
 constexpr int kBlock = 256;            // tokens per cache block
 constexpr int kSlabFcStride = 512;     // elements between FCs inside a slab block (256 tokens x 2)
 
-// Top-B: one 1024-thread workgroup per unit; rows of up to 32768 tokens stay in
-// registers (32 per thread).  The coarse histogram has one bin per value of key
-// bits 31..21; up to kCandLds candidates are selected from LDS.
+// Top-B: a filter workgroup per 2048 tokens keeps the keys at or above the
+// coarse-histogram bin of the B-th largest (one bin per value of key bits
+// 31..21); then one 1024-thread workgroup per unit selects exactly among up to
+// kCandLds kept keys in LDS.  Its whole-row fallback walks tiles of 16384 tokens.
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkLdsKeys = 32768;
 constexpr int kHistBins = 2048;
 constexpr int kHistShift = 21;
 constexpr int kCandLds = 12288;
+constexpr int kFilterChunk = 2048;
+// Budgets up to kSmallBudget: the last filter workgroup of a unit selects among
+// up to kSmallCand kept keys in its own LDS; larger budgets use finish_kernel.
+constexpr int kSmallBudget = 1024;
+constexpr int kSmallCand = 4096;
 
-// FAC: 4 waves per workgroup; the waves' states are folded in LDS into one partial.
+// FAC: 4 waves per workgroup; the waves' states are folded in LDS into one
+// partial.  Up to kFacMergeMax partials per head are merged by the last
+// workgroup of the split launch; beyond that a separate merge launch runs.
 constexpr int kFacWaves = 4;
+constexpr int kFacMergeMax = 64;
 
 struct Common {
   int batch, n_q_heads, n_kv_heads, group, n_fc, budget, n_sink, n_recent;
@@ -52,19 +60,36 @@ hipError_t launch_slab_append(const Common& c, const void* k_pool, const int32_t
                               const int32_t* positions, const int32_t* fc_idx, void* slab,
                               hipStream_t s);
 size_t hist_bytes(const Common& c);
+size_t slots_bytes(const Common& c);    // kept (key, token) pairs: 8 bytes per token of max_t
+size_t counts_bytes(const Common& c);
+
+// Select state inside the workspace: unit histograms (zero between calls),
+// arrival counters of the filter, per-chunk kept pairs and their counts.
+struct SelectBuffers {
+  uint32_t* hist;
+  uint32_t* arrive;
+  void* slots;
+  int32_t* counts;
+};
 
 // hist == nullptr: scores only.  Otherwise also accumulate the unit histograms
-// (which must hold the counts of nothing else: the select leaves them zero).
+// (which must hold the counts of nothing else: the select leaves them zero) and
+// zero the filter arrival counters `arrive`.
 hipError_t launch_tip(const Common& c, const void* q, const void* slab, const void* k_pool,
                       const int32_t* block_table, const int32_t* seq_lens,
-                      const int32_t* fc_idx, float* scores, uint32_t* hist, hipStream_t s);
-// have_hist: the histograms already hold this step's counts (filled by TIP);
-// otherwise they are built first from the scores.  Either way they are zero on exit.
+                      const int32_t* fc_idx, float* scores, uint32_t* hist, uint32_t* arrive,
+                      hipStream_t s);
+// have_hist: the histograms already hold this step's counts and the arrival
+// counters are zero (both done by TIP); otherwise they are built first from the
+// scores.  Either way the histograms are zero on exit.  fac_arrive (nullable):
+// FAC arrival counters, [units][head_chunks], zeroed for a launch_fac that follows.
 hipError_t launch_topk(const Common& c, const float* scores, const int32_t* seq_lens,
-                       int32_t* sel_idx, int32_t* sel_count, uint32_t* hist, bool have_hist,
-                       hipStream_t s);
+                       int32_t* sel_idx, int32_t* sel_count, const SelectBuffers& w, bool have_hist,
+                       uint32_t* fac_arrive, int head_chunks, hipStream_t s);
+// arrive (nullable): zeroed FAC arrival counters; the merge then runs in the
+// split launch when the plan allows it.
 hipError_t launch_fac(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
                       const void* v_pool, const int32_t* block_table, const int32_t* sel_idx,
-                      const int32_t* sel_count, float* out, void* ws, hipStream_t s);
+                      const int32_t* sel_count, float* out, void* ws, uint32_t* arrive, hipStream_t s);
 
 }  // namespace fasa
