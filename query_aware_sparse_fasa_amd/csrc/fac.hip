@@ -29,6 +29,7 @@
 #include "fac_core.hpp"
 #include "fasa_device.hpp"
 #include "fasa_internal.hpp"
+#include "select_core.hpp"
 
 namespace fasa {
 namespace {
@@ -40,56 +41,102 @@ struct FacArgs {
   const void* k_pool;
   const void* v_pool;
   const int32_t* block_table;
-  const int32_t* sel_idx;
-  const int32_t* sel_count;
+  int32_t* sel_idx;       // read by the split launch; written by the selecting launch
+  int32_t* sel_count;
   void* part_acc;   // [b][H_q][P][128] Acc
   void* part_ml;    // [b][H_q][P][2]   Acc (running max, running sum)
   float* out;
-  uint32_t* arrive; // [b][H_kv][head_chunks] arrival counters (zeroed by the preceding kernel), MERGE only
+  uint32_t* arrive; // [b][H_kv][head_chunks] arrival counters (zeroed by the preceding launch), merge in split
+  // Selecting launch only: the filter's output and the scores behind it.
+  const float* scores;
+  const int32_t* seq_lens;
+  SelectBuffers w;
 };
 
 // Log-sum-exp merge of the P partials of query heads head0 .. head0+nh-1 by one
-// 256-thread workgroup: wave w reduces the (max, sum) pairs of heads w, w+4, ...
-// across its lanes (one partial per lane, P <= 64) into weights e^(m_i - M) in
-// LDS; then every output channel is the weighted sum of its P partials over L.
+// 256-thread workgroup: every output channel is owned by one thread, which
+// streams the (max, sum, acc) of all P partials -- 8 partials' loads in flight
+// at a time, all independent -- and folds them with a running maximum.
 template <typename Acc, int HG>
 __device__ void merge_heads(const FacArgs& a, int64_t head0, int nh) {
-  __shared__ Acc s_w[HG][kFacMergeMax];
-  __shared__ Acc s_l[HG];
   const int P = a.p.n_partials;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const Acc* pml = static_cast<const Acc*>(a.part_ml);
   const Acc* pacc = static_cast<const Acc*>(a.part_acc);
-  for (int hh = wave; hh < nh; hh += 4) {
-    const int64_t slot = (head0 + hh) * P + min(lane, P - 1);
-    const Acc mi = lane < P ? pml[slot * 2 + 0] : neg_inf<Acc>();
-    const Acc li = lane < P ? pml[slot * 2 + 1] : Acc(0);
-    Acc M = mi;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmax(M, shfl_xor_acc(M, o));
-    const Acc w = (M == neg_inf<Acc>()) ? Acc(0) : merge_weight(mi, M);
-    Acc L = li * w;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) L += shfl_xor_acc(L, o);
-    if (lane < P) s_w[hh][lane] = w;
-    if (lane == 0) s_l[hh] = L;
-  }
-  __syncthreads();
   for (int idx = threadIdx.x; idx < nh * kHeadDim; idx += 256) {
     const int hh = idx / kHeadDim, ch = idx % kHeadDim;
-    const Acc* src = pacc + (head0 + hh) * P * kHeadDim + ch;
-    Acc O = Acc(0);
-    int i = 0;
-    for (; i + 8 <= P; i += 8) {
-      Acc v[8];
+    const int64_t base = (head0 + hh) * P;
+    Acc M = neg_inf<Acc>(), L = Acc(0), O = Acc(0);
+    for (int p0 = 0; p0 < P; p0 += 8) {
+      Acc m[8], l[8], o[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = src[int64_t(i + u) * kHeadDim];
+      for (int u = 0; u < 8; ++u) {
+        const int64_t sl = base + min(p0 + u, P - 1);
+        m[u] = pml[sl * 2 + 0];
+        l[u] = pml[sl * 2 + 1];
+        o[u] = pacc[sl * kHeadDim + ch];
+      }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) O = fma(v[u], s_w[hh][i + u], O);
+      for (int u = 0; u < 8; ++u) {
+        const Acc mu = (p0 + u < P) ? m[u] : neg_inf<Acc>();
+        const Acc mn = fmax(M, mu);
+        const Acc cs = merge_weight(M, mn), cu = merge_weight(mu, mn);
+        L = L * cs + l[u] * cu;
+        O = O * cs + o[u] * cu;
+        M = mn;
+      }
     }
-    for (; i < P; ++i) O = fma(src[int64_t(i) * kHeadDim], s_w[hh][i], O);
-    const Acc L = s_l[hh];
     a.out[(head0 + hh) * kHeadDim + ch] = L > Acc(0) ? float(O / L) : 0.f;
+  }
+}
+
+// LDS area in which the 4 waves of a workgroup fold their states.
+template <typename Acc, int HG>
+struct WaveFold {
+  Acc acc[kFacWaves][HG][kHeadDim];
+  Acc m[kFacWaves][HG], l[kFacWaves][HG];
+};
+
+// Fold the 4 wave states of heads head0 .. head0+nh-1 (after fold_row_groups)
+// through LDS into one partial (m, l, acc[128]) per head, stored in slot
+// blockIdx.x of the head's partials.
+template <typename Acc, int HG, typename W>
+__device__ __forceinline__ void store_partial(const FacArgs& a, const W& w, WaveFold<Acc, HG>& f, int64_t head0,
+                                              int nh) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, sub = lane & 15;
+  if (lane < 16) {
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f.acc[wave][hh][8 * sub + e] = w.acc[hh][e];
+      if (sub == 0) {
+        f.m[wave][hh] = w.m[hh];
+        f.l[wave][hh] = w.l[hh];
+      }
+    }
+  }
+  __syncthreads();
+  Acc* pacc = static_cast<Acc*>(a.part_acc);
+  Acc* pml = static_cast<Acc*>(a.part_ml);
+  for (int idx = threadIdx.x; idx < nh * kHeadDim; idx += 256) {
+    const int hh = idx / kHeadDim, ch = idx % kHeadDim;
+    Acc M = neg_inf<Acc>();
+#pragma unroll
+    for (int v = 0; v < kFacWaves; ++v) M = fmax(M, f.m[v][hh]);
+    Acc L = Acc(0), O = Acc(0);
+    if (M != neg_inf<Acc>()) {
+#pragma unroll
+      for (int v = 0; v < kFacWaves; ++v) {
+        const Acc wgt = merge_weight(f.m[v][hh], M);
+        L = fma(f.l[v][hh], wgt, L);
+        O = fma(f.acc[v][hh][ch], wgt, O);
+      }
+    }
+    const int64_t slot = (head0 + hh) * a.p.n_partials + blockIdx.x;
+    pacc[slot * kHeadDim + ch] = O;
+    if (ch == 0) {
+      pml[slot * 2 + 0] = M;
+      pml[slot * 2 + 1] = L;
+    }
   }
 }
 
@@ -133,45 +180,8 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   w.run(r0, r1, lane_offset, kbase, vbase);
   w.fold_row_groups();
 
-  // Fold the 4 waves through LDS; the workgroup writes one partial per head.
-  __shared__ Acc s_acc[kFacWaves][HG][kHeadDim];
-  __shared__ Acc s_m[kFacWaves][HG], s_l[kFacWaves][HG];
-  if (lane < 16) {
-#pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_acc[wave][hh][8 * sub + e] = w.acc[hh][e];
-      if (sub == 0) {
-        s_m[wave][hh] = w.m[hh];
-        s_l[wave][hh] = w.l[hh];
-      }
-    }
-  }
-  __syncthreads();
-  Acc* pacc = static_cast<Acc*>(a.part_acc);
-  Acc* pml = static_cast<Acc*>(a.part_ml);
-  for (int idx = threadIdx.x; idx < nh * kHeadDim; idx += 256) {
-    const int hh = idx / kHeadDim, ch = idx % kHeadDim;
-    Acc M = neg_inf<Acc>();
-#pragma unroll
-    for (int v = 0; v < kFacWaves; ++v) M = fmax(M, s_m[v][hh]);
-    Acc L = Acc(0), O = Acc(0);
-    if (M != neg_inf<Acc>()) {
-#pragma unroll
-      for (int v = 0; v < kFacWaves; ++v) {
-        const Acc wgt = merge_weight(s_m[v][hh], M);
-        L = fma(s_l[v][hh], wgt, L);
-        O = fma(s_acc[v][hh][ch], wgt, O);
-      }
-    }
-    const int64_t h = int64_t(b) * c.n_q_heads + g * c.group + h0 + hh;
-    const int64_t slot = h * p.n_partials + blockIdx.x;
-    pacc[slot * kHeadDim + ch] = O;
-    if (ch == 0) {
-      pml[slot * 2 + 0] = M;
-      pml[slot * 2 + 1] = L;
-    }
-  }
+  __shared__ WaveFold<Acc, HG> fold;
+  store_partial<Acc, HG>(a, w, fold, int64_t(b) * c.n_q_heads + g * c.group + h0, nh);
   if constexpr (MERGE) {
     // The workgroup that completes the head chunk's split merges it.
     __shared__ uint32_t s_last;
@@ -179,6 +189,95 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
       return;
     merge_heads<Acc, HG>(a, int64_t(b) * c.n_q_heads + g * c.group + h0, nh);
   }
+}
+
+// The selecting launch of a decode step (budgets up to kSmallBudget): every
+// workgroup first makes its unit's exact top-B selection itself, from the
+// filter's kept pairs (select_core.hpp), into LDS -- redundantly across the
+// split, since a unit keeps only a few hundred pairs -- and then runs the
+// split-K FAC above over its rows of the list, reading the row indices from
+// LDS.  Workgroup 0 of each unit publishes the list and its count and clears
+// the unit's histogram for the next step; the last workgroup of each head
+// chunk merges the partials.  Grid and plan as fac_split_kernel.
+template <typename Acc, int HG>
+struct FacSelShared {
+  union {
+    struct {
+      sel::SelState<256> st;
+      int32_t chunk_off[sel::CPT * 256 + 1];
+      uint32_t key[kSmallCand];
+      int32_t idx[kSmallCand];
+    } s;
+    WaveFold<Acc, HG> fold;
+  } u;
+  int32_t chosen[kSmallBudget];
+  uint32_t last;
+};
+
+template <typename T, typename Acc, int HG>
+__global__ __launch_bounds__(256) void fac_select_kernel(FacArgs a) {
+  const Common& c = a.c;
+  const FacPlan& p = a.p;
+  const int b = blockIdx.z;
+  const int g = blockIdx.y / p.head_chunks, hc = blockIdx.y % p.head_chunks;
+  const int h0 = hc * HG, nh = min(HG, c.group - h0);
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int64_t unit = int64_t(b) * c.n_kv_heads + g;
+  const int nfa = sel::filter_chunks(c);
+  const uint2* unit_slots = static_cast<const uint2*>(a.w.slots) + unit * nfa * int64_t(sel::FCH);
+  __shared__ FacSelShared<Acc, HG> sm;
+
+  // Independent loads first: the first kept pairs of every chunk (up to 16
+  // chunks), the chunk counts, b1, the length and the query slices.
+  uint2 pre[4];
+  sel::prefetch_kept<256, 4>(unit_slots, nfa, pre);
+  int cnt[sel::CPT];
+  sel::load_counts(a.w.counts + unit * nfa, nfa, cnt);
+  const int b1 = a.w.b1[unit];
+  const int64_t head0 = int64_t(b) * c.n_q_heads + g * c.group + h0;
+  FacWave<T, Acc, HG> w;
+  w.init(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, c.scale);
+  int t, c_lo, c_hi;
+  sel::unit_range(c, a.seq_lens[b], t, c_lo, c_hi);
+  const int nC = c_hi - c_lo;
+  const int Bc = min(c.budget, nC);
+  const int count = (t - nC) + Bc;          // forced + chosen, <= cap
+  const bool keep_all = Bc == nC;
+
+  if (!keep_all)
+    sel::select_from_kept<256, 4>(sm.u.s.st, sm.u.s.chunk_off, sm.u.s.key, sm.u.s.idx, kSmallCand, unit_slots,
+                                  a.scores + unit * c.max_t, c.max_t, nfa, cnt, pre, c_lo, c_hi, Bc, b1, sm.chosen);
+  __syncthreads();                          // the list is complete; the select area is free
+
+  // Row r of the list: the forced prefix, the chosen, then the forced suffix.
+  auto token = [&](int r) -> int {
+    const int ch = sm.chosen[min(max(r - c_lo, 0), kSmallBudget - 1)];
+    return (keep_all || r < c_lo) ? r : (r < c_lo + Bc ? ch : c_hi + (r - c_lo - Bc));
+  };
+  const int r0 = (blockIdx.x * kFacWaves + wave) * p.rows_per_wave;
+  const int r1 = min(r0 + p.rows_per_wave, count);
+  const int32_t* btab = a.block_table + int64_t(b) * c.max_blocks;
+  auto lane_offset = [&](int r) -> int64_t {
+    const int j = token(r);
+    const bool ok = r < r1 && j >= 0 && j < c.max_blocks * kBlock;
+    const int64_t pb = btab[ok ? (j >> 8) : 0];
+    return ok ? pb * c.kv_block_stride + int64_t(j & (kBlock - 1)) * kHeadDim : -1;
+  };
+  const T* kbase = static_cast<const T*>(a.k_pool) + int64_t(g) * c.kv_head_stride;
+  const T* vbase = static_cast<const T*>(a.v_pool) + int64_t(g) * c.kv_head_stride;
+  w.run(r0, r1, lane_offset, kbase, vbase);
+  w.fold_row_groups();
+  store_partial<Acc, HG>(a, w, sm.u.fold, head0, nh);
+
+  if (blockIdx.x == 0 && hc == 0) {
+    int32_t* list = a.sel_idx + unit * c.cap;
+    for (int i = tid; i < c.cap; i += 256) list[i] = i < count ? token(i) : -1;
+    if (tid == 0) a.sel_count[unit] = count;
+    uint4* hg = reinterpret_cast<uint4*>(a.w.hist + unit * sel::HB);
+    for (int i = tid; i < sel::HB / 4; i += 256) hg[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (!arrive_last(&a.arrive[int64_t(blockIdx.z) * gridDim.y + blockIdx.y], uint32_t(p.n_split), &sm.last)) return;
+  merge_heads<Acc, HG>(a, head0, nh);
 }
 
 // One workgroup per (sequence, query head): log-sum-exp merge of the partials.
@@ -255,9 +354,37 @@ hipError_t launch_fac_t(FacArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, typename Acc>
+hipError_t launch_fac_select_t(const FacArgs& a, hipStream_t s) {
+  const FacPlan& p = a.p;
+  const dim3 grid(p.n_split, a.c.n_kv_heads * p.head_chunks, a.c.batch);
+  switch (p.heads_per_pass) {
+    case 1: hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((fac_select_kernel<T, Acc, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((fac_select_kernel<T, Acc, 4>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((fac_select_kernel<T, Acc, 8>), grid, dim3(256), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+FacArgs make_args(const Common& c, const FacPlan& p, const void* q, const void* k_pool, const void* v_pool,
+                  const int32_t* block_table, int32_t* sel_idx, int32_t* sel_count, float* out, void* ws,
+                  uint32_t* arrive) {
+  const size_t acc_sz = c.bf16 ? sizeof(float) : sizeof(double);
+  const size_t slots = size_t(c.batch) * c.n_q_heads * p.n_partials;
+  char* w = static_cast<char*>(ws);
+  FacArgs a{c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count,
+            w, w + align256(slots * kHeadDim * acc_sz), out, arrive, nullptr, nullptr, {}};
+  return a;
+}
+
 }  // namespace
+
+bool fac_selects(const Common& c, const FacPlan& p) {
+  return c.max_t > 0 && c.budget <= kSmallBudget && p.n_split <= kFacMergeMax;
+}
 
 FacPlan fac_plan(const Common& c) {
   FacPlan p;
@@ -293,13 +420,22 @@ size_t scores_bytes(const Common& c) {
 hipError_t launch_fac(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
                       const void* v_pool, const int32_t* block_table, const int32_t* sel_idx,
                       const int32_t* sel_count, float* out, void* ws, uint32_t* arrive, hipStream_t s) {
-  const size_t acc_sz = c.bf16 ? sizeof(float) : sizeof(double);
-  const size_t slots = size_t(c.batch) * c.n_q_heads * p.n_partials;
-  char* w = static_cast<char*>(ws);
-  FacArgs a{c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count,
-            w, w + align256(slots * kHeadDim * acc_sz), out, arrive};
+  FacArgs a = make_args(c, p, q, k_pool, v_pool, block_table, const_cast<int32_t*>(sel_idx),
+                        const_cast<int32_t*>(sel_count), out, ws, arrive);
   if (c.bf16) return launch_fac_t<uint16_t, float>(a, s);
   return launch_fac_t<float, double>(a, s);
+}
+
+hipError_t launch_fac_select(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* block_table, const float* scores,
+                             const int32_t* seq_lens, const SelectBuffers& sb, int32_t* sel_idx,
+                             int32_t* sel_count, float* out, void* ws, uint32_t* arrive, hipStream_t s) {
+  FacArgs a = make_args(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out, ws, arrive);
+  a.scores = scores;
+  a.seq_lens = seq_lens;
+  a.w = sb;
+  if (c.bf16) return launch_fac_select_t<uint16_t, float>(a, s);
+  return launch_fac_select_t<float, double>(a, s);
 }
 
 }  // namespace fasa

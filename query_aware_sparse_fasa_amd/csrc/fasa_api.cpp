@@ -82,23 +82,23 @@ Common make_common(const fasa_shape* s, int32_t max_t) {
 }
 
 // Workspace layout shared by every entry point:
-//   [unit histograms | arrival counters | scores | kept pairs | kept counts | FAC partials]
+//   [unit histograms | FAC arrival counters | unit b1 | scores | kept pairs | kept counts | FAC partials]
 // The histograms come first so that no other entry point ever writes over them:
 // the select leaves them zero for the next call (a workspace that starts zeroed
 // takes the fast path from the first call; other contents only slow it down).
-// The arrival counters (one per unit for the filter, one per unit and head
-// chunk for FAC) are zeroed by the launch before the one that counts on them.
+// The FAC arrival counters (one per unit and head chunk) are zeroed by the
+// launch before the FAC launch that counts on them.
 struct Layout {
-  size_t hist, arrive, fac_arrive, scores, slots, counts, fac, total;
+  size_t hist, fac_arrive, b1, scores, slots, counts, fac, total;
 };
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 Layout layout(const Common& c, const FacPlan& p) {
   const size_t units = size_t(c.batch) * c.n_kv_heads;
   Layout l;
   l.hist = 0;
-  l.arrive = fasa::hist_bytes(c);
-  l.fac_arrive = l.arrive + align256(units * sizeof(uint32_t));
-  l.scores = l.fac_arrive + align256(units * p.head_chunks * sizeof(uint32_t));
+  l.fac_arrive = fasa::hist_bytes(c);
+  l.b1 = l.fac_arrive + align256(units * p.head_chunks * sizeof(uint32_t));
+  l.scores = l.b1 + align256(units * sizeof(int32_t));
   l.slots = l.scores + fasa::scores_bytes(c);
   l.counts = l.slots + fasa::slots_bytes(c);
   l.fac = l.counts + fasa::counts_bytes(c);
@@ -107,8 +107,8 @@ Layout layout(const Common& c, const FacPlan& p) {
 }
 fasa::SelectBuffers select_buffers(void* workspace, const Layout& l) {
   char* w = static_cast<char*>(workspace);
-  return {reinterpret_cast<uint32_t*>(w + l.hist), reinterpret_cast<uint32_t*>(w + l.arrive), w + l.slots,
-          reinterpret_cast<int32_t*>(w + l.counts)};
+  return {reinterpret_cast<uint32_t*>(w + l.hist), w + l.slots, reinterpret_cast<int32_t*>(w + l.counts),
+          reinterpret_cast<int32_t*>(w + l.b1)};
 }
 size_t decode_workspace(const Common& c, const FacPlan& p) { return layout(c, p).total; }
 
@@ -209,7 +209,7 @@ fasa_status fasa_tip(const fasa_shape* shape, const void* q, const void* slab, c
   if (max_t == 0) return FASA_OK;
   Common c = make_common(shape, max_t);
   return hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores, nullptr,
-                                     nullptr, stream));
+                                     stream));
 }
 
 fasa_status fasa_topk(const fasa_shape* shape, const float* scores, const int32_t* seq_lens,
@@ -224,8 +224,9 @@ fasa_status fasa_topk(const fasa_shape* shape, const float* scores, const int32_
   Common c = make_common(shape, max_t);
   const Layout l = layout(c, fasa::fac_plan(c));
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < l.total) return FASA_ERR_WORKSPACE;
-  return hip_status(fasa::launch_topk(c, scores, seq_lens, sel_idx, sel_count, select_buffers(workspace, l),
-                                      false, nullptr, 0, stream));
+  const fasa::SelectBuffers sb = select_buffers(workspace, l);
+  if ((st = hip_status(fasa::launch_filter(c, scores, seq_lens, sb, false, nullptr, 0, stream))) != FASA_OK) return st;
+  return hip_status(fasa::launch_finish(c, scores, seq_lens, sel_idx, sel_count, sb, nullptr, 0, stream));
 }
 
 fasa_status fasa_fac(const fasa_shape* shape, const void* q, const void* k_pool, const void* v_pool,
@@ -263,19 +264,26 @@ fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_po
   const FacPlan p = fasa::fac_plan(c);
   const Layout l = layout(c, p);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < l.total) return FASA_ERR_WORKSPACE;
-  // TIP (+ unit histograms, filter counters zeroed) -> top-B (+ FAC counters
-  // zeroed) -> FAC (merged by its last workgroups).
+  // TIP (+ unit histograms) -> filter (+ FAC counters zeroed) -> FAC that
+  // selects its own rows and merges in its last workgroups; for large budgets
+  // the exact select is a launch of its own before the FAC.
   char* w = static_cast<char*>(workspace);
   const fasa::SelectBuffers sb = select_buffers(workspace, l);
   float* scores = reinterpret_cast<float*>(w + l.scores);
   uint32_t* fac_arrive = reinterpret_cast<uint32_t*>(w + l.fac_arrive);
   if (max_t > 0) {
-    if ((st = hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores,
-                                          sb.hist, sb.arrive, stream))) != FASA_OK)
+    if ((st = hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores, sb.hist,
+                                          stream))) != FASA_OK)
       return st;
   }
-  if ((st = hip_status(fasa::launch_topk(c, scores, seq_lens, sel_idx, sel_count, sb, max_t > 0, fac_arrive,
-                                         p.head_chunks, stream))) != FASA_OK)
+  if ((st = hip_status(fasa::launch_filter(c, scores, seq_lens, sb, true, fac_arrive, p.head_chunks, stream))) !=
+      FASA_OK)
+    return st;
+  if (fasa::fac_selects(c, p))
+    return hip_status(fasa::launch_fac_select(c, p, q, k_pool, v_pool, block_table, scores, seq_lens, sb, sel_idx,
+                                              sel_count, out, w + l.fac, fac_arrive, stream));
+  if ((st = hip_status(fasa::launch_finish(c, scores, seq_lens, sel_idx, sel_count, sb, fac_arrive, p.head_chunks,
+                                           stream))) != FASA_OK)
     return st;
   return hip_status(fasa::launch_fac(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out,
                                      w + l.fac, fac_arrive, stream));

@@ -14,15 +14,15 @@ constexpr int kSlabFcStride = 512;     // elements between FCs inside a slab blo
 
 // Top-B: a filter workgroup per 2048 tokens keeps the keys at or above the
 // coarse-histogram bin of the B-th largest (one bin per value of key bits
-// 31..21); then one 1024-thread workgroup per unit selects exactly among up to
-// kCandLds kept keys in LDS.  Its whole-row fallback walks tiles of 16384 tokens.
+// 31..21); then one workgroup per unit selects exactly among the kept keys in
+// LDS: a 1024-thread finish workgroup (up to kCandLds keys), or, in a decode
+// step with a budget up to kSmallBudget, each FAC workgroup itself (up to
+// kSmallCand keys).
 constexpr int kTopkThreads = 1024;
 constexpr int kHistBins = 2048;
 constexpr int kHistShift = 21;
 constexpr int kCandLds = 12288;
 constexpr int kFilterChunk = 2048;
-// Budgets up to kSmallBudget: the last filter workgroup of a unit selects among
-// up to kSmallCand kept keys in its own LDS; larger budgets use finish_kernel.
 constexpr int kSmallBudget = 1024;
 constexpr int kSmallCand = 4096;
 
@@ -64,32 +64,43 @@ size_t slots_bytes(const Common& c);    // kept (key, token) pairs: 8 bytes per 
 size_t counts_bytes(const Common& c);
 
 // Select state inside the workspace: unit histograms (zero between calls),
-// arrival counters of the filter, per-chunk kept pairs and their counts.
+// per-chunk kept pairs and their counts, and the coarse bin b1 of every unit.
 struct SelectBuffers {
   uint32_t* hist;
-  uint32_t* arrive;
   void* slots;
   int32_t* counts;
+  int32_t* b1;
 };
 
 // hist == nullptr: scores only.  Otherwise also accumulate the unit histograms
-// (which must hold the counts of nothing else: the select leaves them zero) and
-// zero the filter arrival counters `arrive`.
+// (which must hold the counts of nothing else: the select leaves them zero).
 hipError_t launch_tip(const Common& c, const void* q, const void* slab, const void* k_pool,
                       const int32_t* block_table, const int32_t* seq_lens,
-                      const int32_t* fc_idx, float* scores, uint32_t* hist, uint32_t* arrive,
-                      hipStream_t s);
-// have_hist: the histograms already hold this step's counts and the arrival
-// counters are zero (both done by TIP); otherwise they are built first from the
-// scores.  Either way the histograms are zero on exit.  fac_arrive (nullable):
-// FAC arrival counters, [units][head_chunks], zeroed for a launch_fac that follows.
-hipError_t launch_topk(const Common& c, const float* scores, const int32_t* seq_lens,
-                       int32_t* sel_idx, int32_t* sel_count, const SelectBuffers& w, bool have_hist,
-                       uint32_t* fac_arrive, int head_chunks, hipStream_t s);
-// arrive (nullable): zeroed FAC arrival counters; the merge then runs in the
-// split launch when the plan allows it.
+                      const int32_t* fc_idx, float* scores, uint32_t* hist, hipStream_t s);
+// Top-B stages 1-2: the unit histograms (unless have_hist: TIP filled them) and
+// the filter's kept pairs, counts and b1.  Nothing when max_t == 0.
+// fac_arrive (nullable): FAC arrival counters, [units][head_chunks], zeroed here
+// for the FAC launch that follows.
+hipError_t launch_filter(const Common& c, const float* scores, const int32_t* seq_lens, const SelectBuffers& w,
+                         bool have_hist, uint32_t* fac_arrive, int head_chunks, hipStream_t s);
+// Top-B stage 3 as its own launch: the selection lists and counts; zeroes the
+// histograms (and fac_arrive when given).
+hipError_t launch_finish(const Common& c, const float* scores, const int32_t* seq_lens, int32_t* sel_idx,
+                         int32_t* sel_count, const SelectBuffers& w, uint32_t* fac_arrive, int head_chunks,
+                         hipStream_t s);
+// FAC over given selections.  arrive (nullable): zeroed FAC arrival counters;
+// the merge then runs in the split launch when the plan allows it.
 hipError_t launch_fac(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
                       const void* v_pool, const int32_t* block_table, const int32_t* sel_idx,
                       const int32_t* sel_count, float* out, void* ws, uint32_t* arrive, hipStream_t s);
+// Whether a decode step may use launch_fac_select (small budget, merge in the split).
+bool fac_selects(const Common& c, const FacPlan& p);
+// Top-B stage 3 and FAC in one launch, after launch_filter: writes the
+// selection lists and counts, zeroes the histograms, and computes out.
+// arrive: FAC arrival counters zeroed by launch_filter.
+hipError_t launch_fac_select(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* block_table, const float* scores,
+                             const int32_t* seq_lens, const SelectBuffers& sb, int32_t* sel_idx,
+                             int32_t* sel_count, float* out, void* ws, uint32_t* arrive, hipStream_t s);
 
 }  // namespace fasa

@@ -1,0 +1,487 @@
+// Exact top-B selection machinery shared by the select launches (topk.hip)
+// and the FAC launch that selects its own rows (fac.hip): block-wide scans,
+// radix digit search over LDS histograms, the gather of the filter's kept
+// (key, token) pairs into LDS, the exact select over them, and the whole-row
+// fallback.  NTH is the workgroup size (a multiple of 64).
+//
+// Keys are the order-preserving 32-bit images of fp32 scores (score_key);
+// digits are bits 31..21, 20..10 and 9..0 (11, 11, 10 bits).  The selection
+// rule (paper-graph-ui review of FASA, section 3.4, TopK-I over the TIP
+// scores): the Bc largest keys, equal keys going to the lower token index,
+// written as ascending token indices.
+#pragma once
+
+#include "fasa_device.hpp"
+#include "fasa_internal.hpp"
+
+namespace fasa {
+namespace sel {
+
+constexpr int HB = kHistBins;               // 2048
+constexpr int FCH = kFilterChunk;           // 2048 tokens per filter chunk
+constexpr int KPT = 16;                     // fallback slots per thread per tile
+constexpr int CPT = 4;                      // chunk counts summed per thread in the gather
+
+// Filter chunks of a row (at least one, so that slot and count arrays are never
+// empty and clamped loads from them stay in bounds).
+__host__ __device__ __forceinline__ int filter_chunks(const Common& c) {
+  const int n = (c.max_t + FCH - 1) / FCH;
+  return n > 0 ? n : 1;
+}
+
+template <int NTH>
+struct SelState {
+  alignas(16) uint32_t hist[HB];
+  uint32_t wave_sum[NTH / 64];
+  uint32_t digit, rem, full;
+};
+
+// Block-wide exclusive scan of one value per thread; returns the exclusive
+// prefix and writes the block total.
+template <int NTH>
+__device__ __forceinline__ uint32_t block_excl_scan(SelState<NTH>& s, uint32_t v, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_inclusive_scan(v);
+  if (lane == 63) s.wave_sum[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NTH / 64; ++w) {
+    const uint32_t x = s.wave_sum[w];
+    base += (w < wave) ? x : 0u;
+    tot += x;
+  }
+  __syncthreads();
+  total = tot;
+  return base + incl - v;
+}
+
+// Exclusive prefix over the waves of a per-wave value (the same in every lane
+// of a wave); also returns the block total.
+template <int NTH>
+__device__ __forceinline__ uint32_t wave_base(SelState<NTH>& s, uint32_t wave_val, uint32_t& total) {
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) s.wave_sum[wave] = wave_val;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NTH / 64; ++w) {
+    const uint32_t x = s.wave_sum[w];
+    base += (w < wave) ? x : 0u;
+    tot += x;
+  }
+  __syncthreads();
+  total = tot;
+  return base;
+}
+
+// Find the digit d of a histogram with NB bins (1024 or 2048) such that fewer
+// than rem keys lie in bins above d and at least rem in bins >= d.  Thread t
+// owns the BPT bins below NB - BPT t (read as 16-byte vectors when BPT >= 4);
+// an exclusive scan over threads counts the keys above them, and the thread
+// whose bins hold the crossing walks them in registers.  Leaves s.digit
+// untouched when there are fewer than rem keys in total.
+template <int NTH, int NB>
+__device__ __forceinline__ void find_digit(SelState<NTH>& s, uint32_t rem) {
+  constexpr int BPT = NB > NTH ? NB / NTH : 1;
+  const int lo = NB - BPT * (int(threadIdx.x) + 1);     // lowest owned bin
+  uint32_t h[BPT];
+  if constexpr (BPT >= 4) {
+#pragma unroll
+    for (int v = 0; v < BPT / 4; ++v) {
+      const uint4 x = reinterpret_cast<const uint4*>(s.hist + lo)[v];
+      h[4 * v + 0] = x.x; h[4 * v + 1] = x.y; h[4 * v + 2] = x.z; h[4 * v + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) h[i] = lo + i >= 0 ? s.hist[lo + i] : 0u;
+  }
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) sum += h[i];
+  uint32_t total;
+  const uint32_t above = block_excl_scan(s, sum, total);    // keys in bins above the owned ones
+  if (above < rem && rem <= above + sum) {
+    uint32_t cum = above;
+#pragma unroll
+    for (int i = BPT - 1; i >= 0; --i) {
+      if (cum < rem && rem <= cum + h[i]) {
+        s.digit = uint32_t(lo + i);
+        s.rem = rem - cum;
+        s.full = (h[i] == rem - cum) ? 1u : 0u;
+      }
+      cum += h[i];
+    }
+  }
+  __syncthreads();
+}
+
+template <int NTH, int NB>
+__device__ __forceinline__ void zero_bins(SelState<NTH>& s) {
+  for (int i = threadIdx.x; i < NB / 4; i += NTH) reinterpret_cast<uint4*>(s.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Run-length histogram of one lane's slots: consecutive active slots in the same
+// bin are counted in a register and added once, so tied or skewed scores do not
+// serialise on one LDS address.
+struct RunHist {
+  uint32_t bin = 0u, cnt = 0u;
+  __device__ __forceinline__ void add(uint32_t* hist, bool active, uint32_t b) {
+    const bool brk = active && b != bin;
+    if (brk && cnt != 0u) atomicAdd(&hist[bin], cnt);
+    cnt = brk ? 1u : cnt + (active ? 1u : 0u);
+    bin = brk ? b : bin;
+  }
+  __device__ __forceinline__ void flush(uint32_t* hist) {
+    if (cnt != 0u) atomicAdd(&hist[bin], cnt);
+  }
+};
+
+// Keeps the scheduler from hoisting the per-slot comparisons of the unrolled
+// slot loops above each other (each is a 64-bit lane mask in scalar registers).
+__device__ __forceinline__ void slot_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Token index of slot (q, r) of this lane in the fallback tile that starts at `base`.
+__device__ __forceinline__ int tile_index(int base, int q, int r) {
+  return base + (threadIdx.x >> 6) * (64 * KPT) + q * 256 + (threadIdx.x & 63) * 4 + r;
+}
+
+// Raw scores of this lane's KPT slots of the tile at `base`, loaded without
+// branches (indices clamped into the row).
+__device__ __forceinline__ void load_tile(const float* row, int max_t, int base, float (&v)[KPT]) {
+#pragma unroll
+  for (int q = 0; q < KPT / 4; ++q) {
+    const int j = tile_index(base, q, 0);
+    if ((max_t & 3) == 0) {
+      // A clamped vector only ever covers slots >= max_t, which are never used.
+      const float4 x = *reinterpret_cast<const float4*>(row + min(j, max_t - 4));
+      v[4 * q + 0] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[4 * q + r] = row[min(j + r, max_t - 1)];
+    }
+  }
+}
+
+// Index-order placement of flagged slots of a tile.  For each step q, lane l's
+// offset of its first flagged slot among the wave's flagged slots, and the
+// wave's total.  Uses one 64-lane scan per step.
+template <typename Flag>
+__device__ __forceinline__ uint32_t tile_offsets(Flag flag, uint32_t (&qoff)[KPT / 4]) {
+  uint32_t run = 0;
+#pragma unroll
+  for (int q = 0; q < KPT / 4; ++q) {
+    uint32_t cq = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cq += flag(4 * q + r) ? 1u : 0u;
+    const uint32_t incl = wave_inclusive_scan(cq);
+    qoff[q] = run + incl - cq;
+    run += wave_last(incl);
+  }
+  return run;
+}
+
+__device__ __forceinline__ void unit_range(const Common& c, int t_raw, int& t, int& c_lo, int& c_hi) {
+  t = clamp_len(t_raw, c.max_t, c.max_blocks);
+  c_lo = min(c.n_sink, t);
+  c_hi = max(c_lo, t - c.n_recent);
+}
+
+// Gather the kept pairs of the nfc chunks into LDS, in index order.  cnt_raw[k]
+// is the count of chunk CPT t + k (loaded by the caller, clamped); wave w
+// copies chunks w, w + waves, ...; pre[p] holds the first 64 pairs of chunk
+// w + p * waves (loaded early by the caller, unconditionally).  Returns the
+// number of kept pairs, or -1 when they do not fit (then nothing is gathered).
+template <int NTH, int PRE>
+__device__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off, const uint2* slots, int nfc, int cap_lds,
+                           const int (&cnt_raw)[CPT], const uint2 (&pre)[PRE], uint32_t* key, int32_t* idx) {
+  constexpr int NW = NTH / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (nfc > CPT * NTH) return -1;           // uniform
+  int cnt[CPT];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    cnt[k] = (CPT * tid + k < nfc) ? cnt_raw[k] : 0;
+    sum += uint32_t(cnt[k]);
+  }
+  uint32_t N;
+  uint32_t off = block_excl_scan(s, sum, N);
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int ch = CPT * tid + k;
+    if (ch < nfc) chunk_off[ch] = int32_t(off);
+    off += uint32_t(cnt[k]);
+  }
+  if (tid == 0) chunk_off[nfc] = int32_t(N);
+  if (N > uint32_t(cap_lds)) return -1;     // uniform
+  __syncthreads();
+  // The prefetched pairs first (no memory access), then whatever is beyond them.
+  bool more = false;
+#pragma unroll
+  for (int p = 0; p < PRE; ++p) {
+    const int ch = wave + p * NW;
+    if (ch < nfc) {
+      const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
+      if (lane < n) {
+        key[o + lane] = pre[p].x;
+        idx[o + lane] = int32_t(pre[p].y);
+      }
+      more = more || n > 64;
+    }
+  }
+  more = more || nfc > PRE * NW;
+  if (__builtin_amdgcn_readfirstlane(int(more)) != 0) {
+    for (int ch = wave; ch < nfc; ch += NW) {
+      const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
+      const int k0 = (ch < PRE * NW) ? 64 : 0;
+      for (int k = k0 + lane; k < n; k += 64) {
+        const uint2 e = slots[int64_t(ch) * FCH + k];
+        key[o + k] = e.x;
+        idx[o + k] = int32_t(e.y);
+      }
+    }
+  }
+  __syncthreads();
+  return int(N);
+}
+
+// Exact select of the Bc largest of the N keys key[0..N) (index order, with token
+// indices idx) held in LDS; writes the chosen tokens ascending to out[0..Bc).
+// Thread t owns a contiguous run of the keys.  With b1 >= 0 every key is known
+// to lie in a coarse bin >= b1 (the filter kept exactly those): the first digit
+// is then b1 itself unless more than Bc keys lie above it, and only the keys
+// above b1 are counted instead of a first histogram pass.
+template <int NTH>
+__device__ void lds_select(SelState<NTH>& s, const uint32_t* key, const int32_t* idx, int N, int Bc, int b1,
+                           int32_t* out) {
+  const int tid = threadIdx.x;
+  const int per = (N + NTH - 1) / NTH;
+  const int i0 = min(N, tid * per), i1 = min(N, i0 + per);
+  uint32_t prefix = 0, pmask = 0, rem = uint32_t(Bc);
+  int pass = 0;
+  if (b1 >= 0) {
+    // Second-digit histogram of the keys in bin b1, and the count above b1.
+    zero_bins<NTH, HB>(s);
+    __syncthreads();
+    RunHist rh;
+    uint32_t n_above = 0;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t k = key[i];
+      const uint32_t bin = k >> kHistShift;
+      n_above += bin > uint32_t(b1) ? 1u : 0u;
+      rh.add(s.hist, bin == uint32_t(b1), (k >> 10) & 2047u);
+    }
+    rh.flush(s.hist);
+    uint32_t above;
+    (void)block_excl_scan(s, n_above, above);   // block total of the keys above b1
+    if (above < rem) {               // uniform; otherwise start from the first digit
+      rem -= above;
+      prefix = uint32_t(b1) << 21;
+      pmask = 0x7ffu << 21;
+      find_digit<NTH, 2048>(s, rem);
+      const uint32_t d = s.digit, full = s.full;
+      rem = s.rem;
+      prefix |= d << 10;
+      pmask |= 0x7ffu << 10;
+      pass = full ? 3 : 2;
+    }
+  }
+#pragma unroll 1
+  for (; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+    if (pass == 2) zero_bins<NTH, 1024>(s);
+    else zero_bins<NTH, 2048>(s);
+    __syncthreads();
+    RunHist rh;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t k = key[i];
+      rh.add(s.hist, (k & pmask) == prefix, (k >> shift) & dmask);
+    }
+    rh.flush(s.hist);
+    __syncthreads();
+    if (pass == 2) find_digit<NTH, 1024>(s, rem);
+    else find_digit<NTH, 2048>(s, rem);
+    const uint32_t d = s.digit, full = s.full;
+    rem = s.rem;
+    prefix |= d << shift;
+    pmask |= dmask << shift;
+    if (full) break;
+  }
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t m = key[i] & pmask;
+    n_gt += m > prefix ? 1u : 0u;
+    n_eq += m == prefix ? 1u : 0u;
+  }
+  uint32_t eq_tot, sel_tot;
+  const uint32_t eq_base = block_excl_scan(s, n_eq, eq_tot);
+  const uint32_t take_eq = (rem > eq_base) ? min(rem - eq_base, n_eq) : 0u;
+  int pos = int(block_excl_scan(s, n_gt + take_eq, sel_tot));
+  uint32_t eq_seen = eq_base;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t m = key[i] & pmask;
+    const bool eq = m == prefix;
+    const bool take = m > prefix || (eq && eq_seen < rem);
+    eq_seen += eq ? 1u : 0u;
+    if (take && pos < Bc) out[pos] = idx[i];   // the guard never fails when the counts agree
+    pos += take ? 1 : 0;
+  }
+}
+
+// Fallback: radix select over the whole candidate range [c_lo, c_hi) of a row,
+// streamed from memory in tiles.  A bound from group maxima prunes the first
+// pass: the Bc-th largest of the maxima of >= Bc disjoint slot groups is <= the
+// Bc-th largest key.
+template <int NTH>
+__device__ void row_select(SelState<NTH>& s, const float* row, int max_t, int c_lo, int c_hi, int Bc,
+                           int32_t* out) {
+  constexpr int TILE = NTH * KPT;
+  const int tid = threadIdx.x;
+  const int ntiles = (max_t + TILE - 1) / TILE;
+  uint32_t k[KPT];
+  auto keys_of = [&](int ch) {
+    float v[KPT];
+    load_tile(row, max_t, ch * TILE, v);
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+      const int j = tile_index(ch * TILE, e >> 2, e & 3);
+      k[e] = (j >= c_lo && j < c_hi) ? score_key(v[e]) : 0u;
+    }
+  };
+  uint32_t prefix = 0, pmask = 0, rem = uint32_t(Bc);
+  uint32_t b_lo = 0;
+  {
+    const int64_t groups_needed = (int64_t(Bc) + int64_t(NTH) * ntiles - 1) / (int64_t(NTH) * ntiles);
+    int gpt = 1;                               // groups per thread per tile, a power of two
+    while (gpt < KPT && gpt < groups_needed) gpt <<= 1;
+    const int G = KPT / gpt;
+    zero_bins<NTH, HB>(s);
+    if (tid == 0) s.digit = 0u;
+    __syncthreads();
+    RunHist rh;
+    for (int ch = 0; ch < ntiles; ++ch) {
+      keys_of(ch);
+      uint32_t gmax = 0;
+#pragma unroll
+      for (int e = 0; e < KPT; ++e) {
+        gmax = max(gmax, k[e]);
+        const bool end = ((e + 1) & (G - 1)) == 0;
+        rh.add(s.hist, end, gmax >> kHistShift);
+        gmax = end ? 0u : gmax;
+        slot_fence();
+      }
+    }
+    rh.flush(s.hist);
+    __syncthreads();
+    find_digit<NTH, HB>(s, uint32_t(Bc));     // digit stays 0 with fewer than Bc groups
+    b_lo = s.digit;
+  }
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+    const uint32_t lo_bin = pass == 0 ? b_lo : 0u;
+    if (pass == 2) zero_bins<NTH, 1024>(s);
+    else zero_bins<NTH, 2048>(s);
+    __syncthreads();
+    RunHist rh;
+    for (int ch = 0; ch < ntiles; ++ch) {
+      keys_of(ch);
+#pragma unroll
+      for (int e = 0; e < KPT; ++e) {
+        const uint32_t key = k[e];
+        const bool act = key != 0u && (key & pmask) == prefix && (key >> kHistShift) >= lo_bin;
+        rh.add(s.hist, act, (key >> shift) & dmask);
+        slot_fence();
+      }
+    }
+    rh.flush(s.hist);
+    __syncthreads();
+    if (pass == 2) find_digit<NTH, 1024>(s, rem);
+    else find_digit<NTH, 2048>(s, rem);
+    const uint32_t d = s.digit, full = s.full;
+    rem = s.rem;
+    prefix |= d << shift;
+    pmask |= dmask << shift;
+    if (full) break;
+  }
+  // Index-order compaction.  First the rank of every key equal to the prefix
+  // among the equal keys (the first rem of them are taken), then the output
+  // position of every taken key.
+  uint32_t eq_run = 0, sel_run = 0;
+  for (int ch = 0; ch < ntiles; ++ch) {
+    keys_of(ch);
+    auto is_gt = [&](int e) { return k[e] != 0u && (k[e] & pmask) > prefix; };
+    auto is_eq = [&](int e) { return k[e] != 0u && (k[e] & pmask) == prefix; };
+    uint32_t eoff[KPT / 4];
+    const uint32_t ewt = tile_offsets(is_eq, eoff);
+    uint32_t eq_tot;
+    const uint32_t ebase = eq_run + wave_base(s, ewt, eq_tot);
+    // take(e): above the prefix, or equal with an equal-rank below rem
+    uint32_t take_bits = 0;
+#pragma unroll
+    for (int q = 0; q < KPT / 4; ++q) {
+      uint32_t er = ebase + eoff[q];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = 4 * q + r;
+        const bool eq = is_eq(e);
+        const bool take = is_gt(e) || (eq && er < rem);
+        er += eq ? 1u : 0u;
+        take_bits |= take ? (1u << e) : 0u;
+      }
+      slot_fence();
+    }
+    auto taken = [&](int e) { return ((take_bits >> e) & 1u) != 0u; };
+    uint32_t toff[KPT / 4];
+    const uint32_t twt = tile_offsets(taken, toff);
+    uint32_t sel_tot;
+    const uint32_t tbase = sel_run + wave_base(s, twt, sel_tot);
+#pragma unroll
+    for (int q = 0; q < KPT / 4; ++q) {
+      int pos = int(tbase + toff[q]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool tk = taken(4 * q + r);
+        if (tk && pos < Bc) out[pos] = tile_index(ch * TILE, q, r);   // the guard never fails when the counts agree
+        pos += tk ? 1 : 0;
+      }
+      slot_fence();
+    }
+    eq_run += eq_tot;
+    sel_run += sel_tot;
+  }
+}
+
+// First 64 kept pairs of chunks wave, wave + waves, ... of a unit's slots
+// (clamped to the unit's nfa chunks; loaded unconditionally).
+template <int NTH, int PRE>
+__device__ __forceinline__ void prefetch_kept(const uint2* unit_slots, int nfa, uint2 (&pre)[PRE]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int p = 0; p < PRE; ++p) pre[p] = unit_slots[int64_t(min(wave + p * (NTH / 64), nfa - 1)) * FCH + lane];
+}
+
+// Chunk counts of a unit, CPT per thread (chunk CPT t + k), loaded unconditionally.
+__device__ __forceinline__ void load_counts(const int32_t* unit_counts, int nfa, int (&cnt)[CPT]) {
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) cnt[k] = unit_counts[min(CPT * int(threadIdx.x) + k, nfa - 1)];
+}
+
+// Exact select of one unit that is not keep-all, from the filter's kept pairs
+// (nfc chunks, counts cnt and first pairs pre already loaded), into out[0..Bc)
+// -- global or LDS.  b1: the coarse bin the filter kept keys from.  Falls back
+// to the whole score row when the kept pairs are fewer than Bc or do not fit.
+template <int NTH, int PRE>
+__device__ void select_from_kept(SelState<NTH>& s, int32_t* chunk_off, uint32_t* key, int32_t* idx, int cap_lds,
+                                 const uint2* unit_slots, const float* row, int max_t, int nfc, const int (&cnt)[CPT],
+                                 const uint2 (&pre)[PRE], int c_lo, int c_hi, int Bc, int b1, int32_t* out) {
+  const int N = gather_kept<NTH, PRE>(s, chunk_off, unit_slots, nfc, cap_lds, cnt, pre, key, idx);
+  if (N >= Bc) lds_select<NTH>(s, key, idx, N, Bc, b1, out);
+  else row_select<NTH>(s, row, max_t, c_lo, c_hi, Bc, out);
+}
+
+}  // namespace sel
+}  // namespace fasa

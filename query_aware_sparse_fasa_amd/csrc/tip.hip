@@ -32,7 +32,6 @@ struct TipArgs {
   const int32_t* fc_idx;
   float* scores;
   uint32_t* hist;       // [units][kHistBins] coarse key histogram (HIST only)
-  uint32_t* arrive;     // [units] arrival counters of the filter that follows, zeroed here (HIST only)
 };
 
 // FT > 0: compile-time F (all loads of a block issued back to back); FT == 0: runtime F.
@@ -67,7 +66,6 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
   __shared__ int cols[kHeadDim / 2];
   __shared__ uint32_t hist_s[HIST ? kHistBins : 1];
   if constexpr (HIST) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.arrive[int64_t(b) * c.n_kv_heads + g] = 0u;
     for (int i = threadIdx.x; i < kHistBins; i += 256) hist_s[i] = 0u;
   }
   const bool live = blk * kBlock < t;          // wave-uniform
@@ -201,8 +199,8 @@ hipError_t launch_src(const TipArgs& a, dim3 grid, bool slab, hipStream_t s) {
 
 hipError_t launch_tip(const Common& c, const void* q, const void* slab, const void* k_pool,
                       const int32_t* block_table, const int32_t* seq_lens, const int32_t* fc_idx,
-                      float* scores, uint32_t* hist, uint32_t* arrive, hipStream_t s) {
-  TipArgs a{c, q, slab ? slab : k_pool, block_table, seq_lens, fc_idx, scores, hist, arrive};
+                      float* scores, uint32_t* hist, hipStream_t s) {
+  TipArgs a{c, q, slab ? slab : k_pool, block_table, seq_lens, fc_idx, scores, hist};
   const int nblk = (c.max_t + kBlock - 1) / kBlock;
   const dim3 grid((nblk + 3) / 4, c.n_kv_heads, c.batch);
   const bool sl = slab != nullptr;
