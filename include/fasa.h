@@ -109,7 +109,10 @@ fasa_status fasa_validate_shape(const fasa_shape* shape);
 fasa_status fasa_selection_capacity(const fasa_shape* shape, int32_t max_t, int32_t* cap);
 
 /* Bytes of workspace that fasa_decode, fasa_topk and fasa_fac need for contexts
- * up to max_t (one size for all three).  The workspace must be 256-byte aligned.
+ * up to max_t (one size for all three): about 12 bytes per token of max_t per
+ * (sequence, kv head) -- scores and the select's kept (key, index) pairs --
+ * plus 8 KB per (sequence, kv head) and the FAC partials.  The workspace must
+ * be 256-byte aligned.
  * It carries one small per-unit histogram from call to call: the select leaves
  * it zero, and a workspace that starts zero-filled takes the fast path from the
  * first call.  Its contents never change any result (a non-zero histogram only

@@ -54,39 +54,46 @@ struct FacArgs {
 };
 
 // Log-sum-exp merge of the P partials of query heads head0 .. head0+nh-1 by one
-// 256-thread workgroup: every output channel is owned by one thread, which
-// streams the (max, sum, acc) of all P partials -- 8 partials' loads in flight
-// at a time, all independent -- and folds them with a running maximum.
+// 256-thread workgroup: thread t owns V consecutive output channels (V = HG/2,
+// at least 1) and streams the (max, sum, acc) of all P partials -- 8 partials'
+// loads in flight at a time, all independent -- folding them with a running
+// maximum.
 template <typename Acc, int HG>
 __device__ void merge_heads(const FacArgs& a, int64_t head0, int nh) {
+  constexpr int V = HG >= 2 ? HG / 2 : 1;
   const int P = a.p.n_partials;
+  const int o0 = int(threadIdx.x) * V;
+  const int hh = o0 / kHeadDim, ch = o0 % kHeadDim;
+  if (hh >= nh) return;
   const Acc* pml = static_cast<const Acc*>(a.part_ml);
   const Acc* pacc = static_cast<const Acc*>(a.part_acc);
-  for (int idx = threadIdx.x; idx < nh * kHeadDim; idx += 256) {
-    const int hh = idx / kHeadDim, ch = idx % kHeadDim;
-    const int64_t base = (head0 + hh) * P;
-    Acc M = neg_inf<Acc>(), L = Acc(0), O = Acc(0);
-    for (int p0 = 0; p0 < P; p0 += 8) {
-      Acc m[8], l[8], o[8];
+  const int64_t base = (head0 + hh) * P;
+  Acc M = neg_inf<Acc>(), L = Acc(0), O[V];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t sl = base + min(p0 + u, P - 1);
-        m[u] = pml[sl * 2 + 0];
-        l[u] = pml[sl * 2 + 1];
-        o[u] = pacc[sl * kHeadDim + ch];
-      }
+  for (int v = 0; v < V; ++v) O[v] = Acc(0);
+  for (int p0 = 0; p0 < P; p0 += 8) {
+    Acc m[8], l[8], o[8][V];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const Acc mu = (p0 + u < P) ? m[u] : neg_inf<Acc>();
-        const Acc mn = fmax(M, mu);
-        const Acc cs = merge_weight(M, mn), cu = merge_weight(mu, mn);
-        L = L * cs + l[u] * cu;
-        O = O * cs + o[u] * cu;
-        M = mn;
-      }
+    for (int u = 0; u < 8; ++u) {
+      const int64_t sl = base + min(p0 + u, P - 1);
+      m[u] = pml[sl * 2 + 0];
+      l[u] = pml[sl * 2 + 1];
+#pragma unroll
+      for (int v = 0; v < V; ++v) o[u][v] = pacc[sl * kHeadDim + ch + v];
     }
-    a.out[(head0 + hh) * kHeadDim + ch] = L > Acc(0) ? float(O / L) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const Acc mu = (p0 + u < P) ? m[u] : neg_inf<Acc>();
+      const Acc mn = fmax(M, mu);
+      const Acc cs = merge_weight(M, mn), cu = merge_weight(mu, mn);
+      L = L * cs + l[u] * cu;
+#pragma unroll
+      for (int v = 0; v < V; ++v) O[v] = O[v] * cs + o[u][v] * cu;
+      M = mn;
+    }
   }
+#pragma unroll
+  for (int v = 0; v < V; ++v) a.out[(head0 + hh) * kHeadDim + ch + v] = L > Acc(0) ? float(O[v] / L) : 0.f;
 }
 
 // LDS area in which the 4 waves of a workgroup fold their states.
@@ -211,6 +218,7 @@ struct FacSelShared {
     WaveFold<Acc, HG> fold;
   } u;
   int32_t chosen[kSmallBudget];
+  int32_t btab[kBtabLds];
   uint32_t last;
 };
 
@@ -228,15 +236,22 @@ __global__ __launch_bounds__(256) void fac_select_kernel(FacArgs a) {
   __shared__ FacSelShared<Acc, HG> sm;
 
   // Independent loads first: the first kept pairs of every chunk (up to 16
-  // chunks), the chunk counts, b1, the length and the query slices.
+  // chunks), the chunk counts, b1, the query slices, the block-table row and
+  // the length.
   uint2 pre[4];
   sel::prefetch_kept<256, 4>(unit_slots, nfa, pre);
   int cnt[sel::CPT];
   sel::load_counts(a.w.counts + unit * nfa, nfa, cnt);
   const int b1 = a.w.b1[unit];
   const int64_t head0 = int64_t(b) * c.n_q_heads + g * c.group + h0;
-  FacWave<T, Acc, HG> w;
-  w.init(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, c.scale);
+  Raw8<T> qraw[HG];
+  FacWave<T, Acc, HG>::load_q(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, qraw);
+  // The sequence's block-table row (at most kBtabLds entries), held in
+  // registers through the select and moved to LDS after it.
+  const int32_t* btab = a.block_table + int64_t(b) * c.max_blocks;
+  int32_t bt[kBtabLds / 256];
+#pragma unroll
+  for (int k = 0; k < kBtabLds / 256; ++k) bt[k] = btab[min(tid + 256 * k, c.max_blocks - 1)];
   int t, c_lo, c_hi;
   sel::unit_range(c, a.seq_lens[b], t, c_lo, c_hi);
   const int nC = c_hi - c_lo;
@@ -247,20 +262,24 @@ __global__ __launch_bounds__(256) void fac_select_kernel(FacArgs a) {
   if (!keep_all)
     sel::select_from_kept<256, 4>(sm.u.s.st, sm.u.s.chunk_off, sm.u.s.key, sm.u.s.idx, kSmallCand, unit_slots,
                                   a.scores + unit * c.max_t, c.max_t, nfa, cnt, pre, c_lo, c_hi, Bc, b1, sm.chosen);
-  __syncthreads();                          // the list is complete; the select area is free
+#pragma unroll
+  for (int k = 0; k < kBtabLds / 256; ++k)
+    if (tid + 256 * k < c.max_blocks) sm.btab[tid + 256 * k] = bt[k];
+  __syncthreads();                          // the list and the block table are in LDS; the select area is free
 
   // Row r of the list: the forced prefix, the chosen, then the forced suffix.
+  FacWave<T, Acc, HG> w;
+  w.init_raw(qraw, nh, c.scale);
   auto token = [&](int r) -> int {
     const int ch = sm.chosen[min(max(r - c_lo, 0), kSmallBudget - 1)];
     return (keep_all || r < c_lo) ? r : (r < c_lo + Bc ? ch : c_hi + (r - c_lo - Bc));
   };
   const int r0 = (blockIdx.x * kFacWaves + wave) * p.rows_per_wave;
   const int r1 = min(r0 + p.rows_per_wave, count);
-  const int32_t* btab = a.block_table + int64_t(b) * c.max_blocks;
   auto lane_offset = [&](int r) -> int64_t {
     const int j = token(r);
     const bool ok = r < r1 && j >= 0 && j < c.max_blocks * kBlock;
-    const int64_t pb = btab[ok ? (j >> 8) : 0];
+    const int64_t pb = sm.btab[ok ? (j >> 8) : 0];
     return ok ? pb * c.kv_block_stride + int64_t(j & (kBlock - 1)) * kHeadDim : -1;
   };
   const T* kbase = static_cast<const T*>(a.k_pool) + int64_t(g) * c.kv_head_stride;
@@ -269,6 +288,9 @@ __global__ __launch_bounds__(256) void fac_select_kernel(FacArgs a) {
   w.fold_row_groups();
   store_partial<Acc, HG>(a, w, sm.u.fold, head0, nh);
 
+  const bool last = arrive_last(&a.arrive[int64_t(blockIdx.z) * gridDim.y + blockIdx.y], uint32_t(p.n_split),
+                                &sm.last);
+  // Outputs nothing in this launch waits on go after the arrival.
   if (blockIdx.x == 0 && hc == 0) {
     int32_t* list = a.sel_idx + unit * c.cap;
     for (int i = tid; i < c.cap; i += 256) list[i] = i < count ? token(i) : -1;
@@ -276,8 +298,7 @@ __global__ __launch_bounds__(256) void fac_select_kernel(FacArgs a) {
     uint4* hg = reinterpret_cast<uint4*>(a.w.hist + unit * sel::HB);
     for (int i = tid; i < sel::HB / 4; i += 256) hg[i] = make_uint4(0u, 0u, 0u, 0u);
   }
-  if (!arrive_last(&a.arrive[int64_t(blockIdx.z) * gridDim.y + blockIdx.y], uint32_t(p.n_split), &sm.last)) return;
-  merge_heads<Acc, HG>(a, head0, nh);
+  if (last) merge_heads<Acc, HG>(a, head0, nh);
 }
 
 // One workgroup per (sequence, query head): log-sum-exp merge of the partials.
@@ -383,7 +404,7 @@ FacArgs make_args(const Common& c, const FacPlan& p, const void* q, const void* 
 }  // namespace
 
 bool fac_selects(const Common& c, const FacPlan& p) {
-  return c.max_t > 0 && c.budget <= kSmallBudget && p.n_split <= kFacMergeMax;
+  return c.max_t > 0 && c.budget <= kSmallBudget && p.n_split <= kFacMergeMax && c.max_blocks <= kBtabLds;
 }
 
 FacPlan fac_plan(const Common& c) {

@@ -38,12 +38,23 @@ __device__ __forceinline__ double neg_inf<double>() { return -(double)INFINITY; 
 __device__ __forceinline__ float shfl_xor_acc(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ double shfl_xor_acc(double v, int m) { return __shfl_xor(v, m, 64); }
 
-// Sum over the 16 lanes of a row group, in every lane of it: DPP rotations for
-// fp32, cross-lane shuffles for fp64.
+// An fp64 value moved by a DPP lane pattern (both 32-bit halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(u)), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(u >> 32)), CTRL, 0xF, 0xF, false));
+  return __longlong_as_double(int64_t((uint64_t(hi) << 32) | lo));
+}
+
+// Sum over the 16 lanes of a row group, in every lane of it: DPP rotations by
+// 8, 4, 2, 1 inside the row.
 __device__ __forceinline__ float row_sum(float v) { return row16_sum(v); }
 __device__ __forceinline__ double row_sum(double v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  v += dpp_f64<kDppRowRor + 8>(v);
+  v += dpp_f64<kDppRowRor + 4>(v);
+  v += dpp_f64<kDppRowRor + 2>(v);
+  v += dpp_f64<kDppRowRor + 1>(v);
   return v;
 }
 
@@ -54,18 +65,56 @@ __device__ __forceinline__ Acc merge_weight(Acc mi, Acc M) {
   return (mi == neg_inf<Acc>()) ? Acc(0) : fexp<Acc>(mi - M);
 }
 
+// The values of a lane pair that differ in lane bit 4 (PAIR 16) or bit 5
+// (PAIR 32), returned in every lane of the pair as (lower-lane value,
+// upper-lane value): v_permlane16_swap exchanges the odd 16-lane rows of one
+// operand with the even rows of the other, v_permlane32_swap the upper half of
+// one with the lower half of the other -- VALU moves, no LDS round trip.
+template <int PAIR>
+__device__ __forceinline__ void lane_pair(uint32_t v, uint32_t& lo, uint32_t& hi) {
+  const auto r = PAIR == 16 ? __builtin_amdgcn_permlane16_swap(v, v, false, false)
+                            : __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  lo = r[0];
+  hi = r[1];
+}
+template <int PAIR>
+__device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
+  uint32_t a, b;
+  lane_pair<PAIR>(__float_as_uint(v), a, b);
+  lo = __uint_as_float(a);
+  hi = __uint_as_float(b);
+}
+template <int PAIR>
+__device__ __forceinline__ void lane_pair(double v, double& lo, double& hi) {
+  const uint64_t u = __double_as_longlong(v);
+  uint32_t a0, b0, a1, b1;
+  lane_pair<PAIR>(uint32_t(u), a0, b0);
+  lane_pair<PAIR>(uint32_t(u >> 32), a1, b1);
+  lo = __longlong_as_double(int64_t((uint64_t(a1) << 32) | a0));
+  hi = __longlong_as_double(int64_t((uint64_t(b1) << 32) | b0));
+}
+
 template <typename T, typename Acc, int HG>
 struct FacWave {
   Acc qv[HG][8];
   Acc m[HG], l[HG], acc[HG][8];
 
-  // Query slices of heads h_first .. h_first+nh-1 (rows of q, each kHeadDim long),
-  // pre-scaled; unused head slots are zero.  Loads are unconditional.
-  __device__ __forceinline__ void init(const T* q_head0, int nh, float scale) {
+  // This lane's raw query slices of heads 0 .. nh-1 from q_head0 (rows of q,
+  // each kHeadDim long); loads are unconditional (slots past nh repeat the last).
+  static __device__ __forceinline__ void load_q(const T* q_head0, int nh, Raw8<T> (&qr)[HG]) {
     const int sub = threadIdx.x & 15;
-    Raw8<T> qr[HG];
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) qr[hh].load(q_head0 + int64_t(min(hh, nh - 1)) * kHeadDim + 8 * sub);
+  }
+
+  // Query slices of heads h_first .. h_first+nh-1, pre-scaled; unused head
+  // slots are zero.
+  __device__ __forceinline__ void init(const T* q_head0, int nh, float scale) {
+    Raw8<T> qr[HG];
+    load_q(q_head0, nh, qr);
+    init_raw(qr, nh, scale);
+  }
+  __device__ __forceinline__ void init_raw(const Raw8<T> (&qr)[HG], int nh, float scale) {
     const Acc qscale = sizeof(Acc) == 4 ? Acc(scale) * Acc(1.4426950408889634) : Acc(scale);
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
@@ -142,26 +191,31 @@ struct FacWave {
   }
 
   // Fold the four row groups (lanes sub, sub+16, sub+32, sub+48 own the same
-  // channels); afterwards every lane holds the wave's state for its channels.
-  __device__ __forceinline__ void fold_row_groups() {
+  // channels) with the log-sum-exp rule, row pairs (0,1), (2,3) first, then the
+  // two halves; afterwards every lane holds the wave's state for its channels.
+  template <int PAIR>
+  __device__ __forceinline__ void fold_pairs() {
 #pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
+    for (int hh = 0; hh < HG; ++hh) {
+      Acc ma, mb, la, lb;
+      lane_pair<PAIR>(m[hh], ma, mb);
+      lane_pair<PAIR>(l[hh], la, lb);
+      const Acc mn = fmax(ma, mb);
+      const Acc wa = merge_weight(ma, mn);
+      const Acc wb = merge_weight(mb, mn);
+      l[hh] = la * wa + lb * wb;
 #pragma unroll
-      for (int hh = 0; hh < HG; ++hh) {
-        const Acc mo = shfl_xor_acc(m[hh], o);
-        const Acc lo = shfl_xor_acc(l[hh], o);
-        const Acc mn = fmax(m[hh], mo);
-        const Acc ca = merge_weight(m[hh], mn);
-        const Acc cb = merge_weight(mo, mn);
-        l[hh] = l[hh] * ca + lo * cb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const Acc ao = shfl_xor_acc(acc[hh][e], o);
-          acc[hh][e] = acc[hh][e] * ca + ao * cb;
-        }
-        m[hh] = mn;
+      for (int e = 0; e < 8; ++e) {
+        Acc aa, ab;
+        lane_pair<PAIR>(acc[hh][e], aa, ab);
+        acc[hh][e] = aa * wa + ab * wb;
       }
+      m[hh] = mn;
     }
+  }
+  __device__ __forceinline__ void fold_row_groups() {
+    fold_pairs<16>();
+    fold_pairs<32>();
   }
 };
 

@@ -31,6 +31,9 @@ constexpr int kSmallCand = 4096;
 // workgroup of the split launch; beyond that a separate merge launch runs.
 constexpr int kFacWaves = 4;
 constexpr int kFacMergeMax = 64;
+// The selecting FAC launch keeps the sequence's block-table row in LDS (up to
+// kBtabLds blocks, 512K tokens).
+constexpr int kBtabLds = 2048;
 
 struct Common {
   int batch, n_q_heads, n_kv_heads, group, n_fc, budget, n_sink, n_recent;

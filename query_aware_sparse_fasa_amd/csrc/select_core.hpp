@@ -194,7 +194,8 @@ __device__ __forceinline__ void unit_range(const Common& c, int t_raw, int& t, i
 // number of kept pairs, or -1 when they do not fit (then nothing is gathered).
 template <int NTH, int PRE>
 __device__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off, const uint2* slots, int nfc, int cap_lds,
-                           const int (&cnt_raw)[CPT], const uint2 (&pre)[PRE], uint32_t* key, int32_t* idx) {
+                           const int (&cnt_raw)[CPT], const uint2 (&pre)[PRE], uint32_t* key, int32_t* idx,
+                           int b1, uint32_t& above) {
   constexpr int NW = NTH / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (nfc > CPT * NTH) return -1;           // uniform
@@ -217,16 +218,26 @@ __device__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off, const uint2* sl
   if (N > uint32_t(cap_lds)) return -1;     // uniform
   __syncthreads();
   // The prefetched pairs first (no memory access), then whatever is beyond them.
+  // With b1 >= 0 every copied key also goes into the second-digit histogram
+  // (bits 20..10) if it lies in bin b1, or is counted if it lies above b1 (the
+  // histogram was zeroed by the caller before this call).
+  uint32_t n_above = 0;
+  auto put = [&](int at, uint2 e) {
+    key[at] = e.x;
+    idx[at] = int32_t(e.y);
+    if (b1 >= 0) {
+      const uint32_t bin = e.x >> kHistShift;
+      n_above += bin > uint32_t(b1) ? 1u : 0u;
+      if (bin == uint32_t(b1)) atomicAdd(&s.hist[(e.x >> 10) & 2047u], 1u);
+    }
+  };
   bool more = false;
 #pragma unroll
   for (int p = 0; p < PRE; ++p) {
     const int ch = wave + p * NW;
     if (ch < nfc) {
       const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
-      if (lane < n) {
-        key[o + lane] = pre[p].x;
-        idx[o + lane] = int32_t(pre[p].y);
-      }
+      if (lane < n) put(o + lane, pre[p]);
       more = more || n > 64;
     }
   }
@@ -235,57 +246,44 @@ __device__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off, const uint2* sl
     for (int ch = wave; ch < nfc; ch += NW) {
       const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
       const int k0 = (ch < PRE * NW) ? 64 : 0;
-      for (int k = k0 + lane; k < n; k += 64) {
-        const uint2 e = slots[int64_t(ch) * FCH + k];
-        key[o + k] = e.x;
-        idx[o + k] = int32_t(e.y);
-      }
+      for (int k = k0 + lane; k < n; k += 64) put(o + k, slots[int64_t(ch) * FCH + k]);
     }
   }
-  __syncthreads();
+  // The barrier inside the scan also publishes the copied pairs and the histogram.
+  (void)block_excl_scan(s, n_above, above);
   return int(N);
 }
 
 // Exact select of the Bc largest of the N keys key[0..N) (index order, with token
 // indices idx) held in LDS; writes the chosen tokens ascending to out[0..Bc).
 // Thread t owns a contiguous run of the keys.  With b1 >= 0 every key is known
-// to lie in a coarse bin >= b1 (the filter kept exactly those): the first digit
-// is then b1 itself unless more than Bc keys lie above it, and only the keys
-// above b1 are counted instead of a first histogram pass.
+// to lie in a coarse bin >= b1 (the filter kept exactly those), `above` keys lie
+// above it and s.hist holds the second-digit histogram of the keys in b1 (both
+// built by the gather): the first digit is then b1 itself unless at least Bc
+// keys lie above it.  When a digit's bin holds exactly the keys still needed,
+// the remaining digits are skipped and one scan places every key at or above
+// the prefix.
 template <int NTH>
 __device__ void lds_select(SelState<NTH>& s, const uint32_t* key, const int32_t* idx, int N, int Bc, int b1,
-                           int32_t* out) {
+                           uint32_t above, int32_t* out) {
   const int tid = threadIdx.x;
   const int per = (N + NTH - 1) / NTH;
   const int i0 = min(N, tid * per), i1 = min(N, i0 + per);
   uint32_t prefix = 0, pmask = 0, rem = uint32_t(Bc);
+  bool all_eq = false;                 // every key equal to the prefix is taken
   int pass = 0;
-  if (b1 >= 0) {
-    // Second-digit histogram of the keys in bin b1, and the count above b1.
-    zero_bins<NTH, HB>(s);
-    __syncthreads();
-    RunHist rh;
-    uint32_t n_above = 0;
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t k = key[i];
-      const uint32_t bin = k >> kHistShift;
-      n_above += bin > uint32_t(b1) ? 1u : 0u;
-      rh.add(s.hist, bin == uint32_t(b1), (k >> 10) & 2047u);
-    }
-    rh.flush(s.hist);
-    uint32_t above;
-    (void)block_excl_scan(s, n_above, above);   // block total of the keys above b1
-    if (above < rem) {               // uniform; otherwise start from the first digit
-      rem -= above;
-      prefix = uint32_t(b1) << 21;
-      pmask = 0x7ffu << 21;
-      find_digit<NTH, 2048>(s, rem);
-      const uint32_t d = s.digit, full = s.full;
-      rem = s.rem;
-      prefix |= d << 10;
-      pmask |= 0x7ffu << 10;
-      pass = full ? 3 : 2;
-    }
+  if (b1 >= 0 && above < rem) {        // uniform; otherwise start from the first digit
+    // The second-digit histogram of the keys in bin b1 was built by the gather.
+    rem -= above;
+    prefix = uint32_t(b1) << 21;
+    pmask = 0x7ffu << 21;
+    find_digit<NTH, 2048>(s, rem);
+    const uint32_t d = s.digit, full = s.full;
+    rem = s.rem;
+    prefix |= d << 10;
+    pmask |= 0x7ffu << 10;
+    all_eq = full != 0u;
+    pass = full ? 3 : 2;
   }
 #pragma unroll 1
   for (; pass < 3; ++pass) {
@@ -307,7 +305,23 @@ __device__ void lds_select(SelState<NTH>& s, const uint32_t* key, const int32_t*
     rem = s.rem;
     prefix |= d << shift;
     pmask |= dmask << shift;
-    if (full) break;
+    if (full) {
+      all_eq = true;
+      break;
+    }
+  }
+  if (all_eq) {
+    // Every key at or above the prefix is taken: one scan places them.
+    uint32_t n_take = 0;
+    for (int i = i0; i < i1; ++i) n_take += (key[i] & pmask) >= prefix ? 1u : 0u;
+    uint32_t tot;
+    int pos = int(block_excl_scan(s, n_take, tot));
+    for (int i = i0; i < i1; ++i) {
+      const bool take = (key[i] & pmask) >= prefix;
+      if (take && pos < Bc) out[pos] = idx[i];   // the guard never fails when the counts agree
+      pos += take ? 1 : 0;
+    }
+    return;
   }
   uint32_t n_gt = 0, n_eq = 0;
   for (int i = i0; i < i1; ++i) {
@@ -478,8 +492,10 @@ template <int NTH, int PRE>
 __device__ void select_from_kept(SelState<NTH>& s, int32_t* chunk_off, uint32_t* key, int32_t* idx, int cap_lds,
                                  const uint2* unit_slots, const float* row, int max_t, int nfc, const int (&cnt)[CPT],
                                  const uint2 (&pre)[PRE], int c_lo, int c_hi, int Bc, int b1, int32_t* out) {
-  const int N = gather_kept<NTH, PRE>(s, chunk_off, unit_slots, nfc, cap_lds, cnt, pre, key, idx);
-  if (N >= Bc) lds_select<NTH>(s, key, idx, N, Bc, b1, out);
+  zero_bins<NTH, HB>(s);               // the gather's second-digit histogram; published by its first barrier
+  uint32_t above = 0;
+  const int N = gather_kept<NTH, PRE>(s, chunk_off, unit_slots, nfc, cap_lds, cnt, pre, key, idx, b1, above);
+  if (N >= Bc) lds_select<NTH>(s, key, idx, N, Bc, b1, above, out);
   else row_select<NTH>(s, row, max_t, c_lo, c_hi, Bc, out);
 }
 
