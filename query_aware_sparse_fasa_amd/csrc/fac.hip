@@ -97,10 +97,10 @@ __device__ void merge_heads(const FacArgs& a, int64_t head0, int nh) {
 }
 
 // LDS area in which the 4 waves of a workgroup fold their states.
-template <typename Acc, int HG>
+template <typename Acc, int HG, int NWV = kFacWaves>
 struct WaveFold {
-  Acc acc[kFacWaves][HG][kHeadDim];
-  Acc m[kFacWaves][HG], l[kFacWaves][HG];
+  Acc acc[NWV][HG][kHeadDim];
+  Acc m[NWV][HG], l[NWV][HG];
 };
 
 // Fold the 4 wave states of heads head0 .. head0+nh-1 (after fold_row_groups)
@@ -198,60 +198,63 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   }
 }
 
-// The selecting launch of a decode step (budgets up to kSmallBudget): every
-// workgroup first makes its unit's exact top-B selection itself, from the
-// filter's kept pairs (select_core.hpp), into LDS -- redundantly across the
-// split, since a unit keeps only a few hundred pairs -- and then runs the
-// split-K FAC above over its rows of the list, reading the row indices from
-// LDS.  Workgroup 0 of each unit publishes the list and its count and clears
-// the unit's histogram for the next step; the last workgroup of each head
-// chunk merges the partials.  Grid and plan as fac_split_kernel.
-template <typename Acc, int HG>
+// The selecting launch of a decode step (budgets up to kSmallBudget).  One
+// workgroup per (sequence, query head): it first makes its unit's exact top-B
+// selection itself, from the filter's kept pairs (select_core.hpp), into LDS --
+// redundantly across the G heads of the unit, since a unit keeps only a few
+// hundred pairs -- then runs FAC for its head over every row of the list, 16
+// row quads of K/V loads in flight per wave, and writes the head's output
+// directly: no partials and no merge.  The G workgroups of a unit read the same
+// K/V rows; after the first, mostly from the shared Infinity Cache.  Workgroup
+// 0 of each unit also publishes the list and its count and clears the unit's
+// histogram for the next step.  Grid (G, kv heads, batch).
+constexpr int kSelThreads = 512;            // workgroup of the selecting launch
+constexpr int kSelWaves = kSelThreads / 64;
+
+template <typename Acc>
 struct FacSelShared {
   union {
     struct {
-      sel::SelState<256> st;
-      int32_t chunk_off[sel::CPT * 256 + 1];
+      sel::SelState<kSelThreads> st;
+      int32_t chunk_off[sel::CPT * kSelThreads + 1];
       uint32_t key[kSmallCand];
       int32_t idx[kSmallCand];
     } s;
-    WaveFold<Acc, HG> fold;
+    WaveFold<Acc, 1, kSelWaves> fold;
   } u;
   int32_t chosen[kSmallBudget];
   int32_t btab[kBtabLds];
-  uint32_t last;
 };
 
-template <typename T, typename Acc, int HG>
-__global__ __launch_bounds__(256) void fac_select_kernel(FacArgs a) {
+template <typename T, typename Acc>
+__global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   const Common& c = a.c;
-  const FacPlan& p = a.p;
-  const int b = blockIdx.z;
-  const int g = blockIdx.y / p.head_chunks, hc = blockIdx.y % p.head_chunks;
-  const int h0 = hc * HG, nh = min(HG, c.group - h0);
+  const int b = blockIdx.z, g = blockIdx.y, hq = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t unit = int64_t(b) * c.n_kv_heads + g;
   const int nfa = sel::filter_chunks(c);
   const uint2* unit_slots = static_cast<const uint2*>(a.w.slots) + unit * nfa * int64_t(sel::FCH);
-  __shared__ FacSelShared<Acc, HG> sm;
+  const float* row = a.scores + unit * c.score_stride;   // a decode step's rows: 16-byte aligned, padded
+  const int lim = c.score_stride;
+  __shared__ FacSelShared<Acc> sm;
 
   // Independent loads first: the first kept pairs of every chunk (up to 16
-  // chunks), the chunk counts, b1, the query slices, the block-table row and
+  // chunks), the chunk counts and b1; the query slice, the block-table row and
   // the length.
-  uint2 pre[4];
-  sel::prefetch_kept<256, 4>(unit_slots, nfa, pre);
+  uint2 pre[16 / kSelWaves];
+  sel::prefetch_kept<kSelThreads, 16 / kSelWaves>(unit_slots, nfa, pre);
   int cnt[sel::CPT];
   sel::load_counts(a.w.counts + unit * nfa, nfa, cnt);
   const int b1 = a.w.b1[unit];
-  const int64_t head0 = int64_t(b) * c.n_q_heads + g * c.group + h0;
-  Raw8<T> qraw[HG];
-  FacWave<T, Acc, HG>::load_q(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, qraw);
+  const int64_t head = int64_t(b) * c.n_q_heads + g * c.group + hq;
+  Raw8<T> qraw[1];
+  FacWave<T, Acc, 1>::load_q(static_cast<const T*>(a.q) + head * kHeadDim, 1, qraw);
   // The sequence's block-table row (at most kBtabLds entries), held in
   // registers through the select and moved to LDS after it.
   const int32_t* btab = a.block_table + int64_t(b) * c.max_blocks;
-  int32_t bt[kBtabLds / 256];
+  int32_t bt[kBtabLds / kSelThreads];
 #pragma unroll
-  for (int k = 0; k < kBtabLds / 256; ++k) bt[k] = btab[min(tid + 256 * k, c.max_blocks - 1)];
+  for (int k = 0; k < kBtabLds / kSelThreads; ++k) bt[k] = btab[min(tid + kSelThreads * k, c.max_blocks - 1)];
   int t, c_lo, c_hi;
   sel::unit_range(c, a.seq_lens[b], t, c_lo, c_hi);
   const int nC = c_hi - c_lo;
@@ -260,22 +263,24 @@ __global__ __launch_bounds__(256) void fac_select_kernel(FacArgs a) {
   const bool keep_all = Bc == nC;
 
   if (!keep_all)
-    sel::select_from_kept<256, 4>(sm.u.s.st, sm.u.s.chunk_off, sm.u.s.key, sm.u.s.idx, kSmallCand, unit_slots,
-                                  a.scores + unit * c.max_t, c.max_t, nfa, cnt, pre, c_lo, c_hi, Bc, b1, sm.chosen);
+    sel::select_from_kept<kSelThreads, 16 / kSelWaves, true>(sm.u.s.st, sm.u.s.chunk_off, sm.u.s.key, sm.u.s.idx,
+                                                             kSmallCand, unit_slots, row, lim, c.max_t, nfa, cnt, pre,
+                                                             c_lo, c_hi, Bc, b1, sm.chosen);
 #pragma unroll
-  for (int k = 0; k < kBtabLds / 256; ++k)
-    if (tid + 256 * k < c.max_blocks) sm.btab[tid + 256 * k] = bt[k];
+  for (int k = 0; k < kBtabLds / kSelThreads; ++k)
+    if (tid + kSelThreads * k < c.max_blocks) sm.btab[tid + kSelThreads * k] = bt[k];
   __syncthreads();                          // the list and the block table are in LDS; the select area is free
 
   // Row r of the list: the forced prefix, the chosen, then the forced suffix.
-  FacWave<T, Acc, HG> w;
-  w.init_raw(qraw, nh, c.scale);
+  FacWave<T, Acc, 1> w;
+  w.init_raw(qraw, 1, c.scale);
   auto token = [&](int r) -> int {
     const int ch = sm.chosen[min(max(r - c_lo, 0), kSmallBudget - 1)];
     return (keep_all || r < c_lo) ? r : (r < c_lo + Bc ? ch : c_hi + (r - c_lo - Bc));
   };
-  const int r0 = (blockIdx.x * kFacWaves + wave) * p.rows_per_wave;
-  const int r1 = min(r0 + p.rows_per_wave, count);
+  const int rpw = ((count + kSelWaves - 1) / kSelWaves + 3) & ~3;
+  const int r0 = wave * rpw;
+  const int r1 = min(r0 + rpw, count);
   auto lane_offset = [&](int r) -> int64_t {
     const int j = token(r);
     const bool ok = r < r1 && j >= 0 && j < c.max_blocks * kBlock;
@@ -284,21 +289,45 @@ __global__ __launch_bounds__(256) void fac_select_kernel(FacArgs a) {
   };
   const T* kbase = static_cast<const T*>(a.k_pool) + int64_t(g) * c.kv_head_stride;
   const T* vbase = static_cast<const T*>(a.v_pool) + int64_t(g) * c.kv_head_stride;
-  w.run(r0, r1, lane_offset, kbase, vbase);
+  w.template run<64 / kSelWaves>(r0, r1, lane_offset, kbase, vbase);
   w.fold_row_groups();
-  store_partial<Acc, HG>(a, w, sm.u.fold, head0, nh);
 
-  const bool last = arrive_last(&a.arrive[int64_t(blockIdx.z) * gridDim.y + blockIdx.y], uint32_t(p.n_split),
-                                &sm.last);
-  // Outputs nothing in this launch waits on go after the arrival.
-  if (blockIdx.x == 0 && hc == 0) {
+  // Fold the 4 waves through LDS and write the head's output.
+  WaveFold<Acc, 1, kSelWaves>& f = sm.u.fold;
+  const int lane = tid & 63, sub = lane & 15;
+  if (lane < 16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.acc[wave][0][8 * sub + e] = w.acc[0][e];
+    if (sub == 0) {
+      f.m[wave][0] = w.m[0];
+      f.l[wave][0] = w.l[0];
+    }
+  }
+  __syncthreads();
+  if (tid < kHeadDim) {
+    Acc M = neg_inf<Acc>();
+#pragma unroll
+    for (int v = 0; v < kSelWaves; ++v) M = fmax(M, f.m[v][0]);
+    Acc L = Acc(0), O = Acc(0);
+    if (M != neg_inf<Acc>()) {
+#pragma unroll
+      for (int v = 0; v < kSelWaves; ++v) {
+        const Acc wgt = merge_weight(f.m[v][0], M);
+        L = fma(f.l[v][0], wgt, L);
+        O = fma(f.acc[v][0][tid], wgt, O);
+      }
+    }
+    a.out[head * kHeadDim + tid] = L > Acc(0) ? float(O / L) : 0.f;
+  }
+  if (hq == 0) {
+    // Workgroup 0 of the unit publishes the list and leaves the consumed
+    // histogram zero for the next step (the filter launch read it).
     int32_t* list = a.sel_idx + unit * c.cap;
-    for (int i = tid; i < c.cap; i += 256) list[i] = i < count ? token(i) : -1;
+    for (int i = tid; i < c.cap; i += kSelThreads) list[i] = i < count ? token(i) : -1;
     if (tid == 0) a.sel_count[unit] = count;
     uint4* hg = reinterpret_cast<uint4*>(a.w.hist + unit * sel::HB);
-    for (int i = tid; i < sel::HB / 4; i += 256) hg[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < sel::HB / 4; i += kSelThreads) hg[i] = make_uint4(0u, 0u, 0u, 0u);
   }
-  if (last) merge_heads<Acc, HG>(a, head0, nh);
 }
 
 // One workgroup per (sequence, query head): log-sum-exp merge of the partials.
@@ -377,14 +406,8 @@ hipError_t launch_fac_t(FacArgs& a, hipStream_t s) {
 
 template <typename T, typename Acc>
 hipError_t launch_fac_select_t(const FacArgs& a, hipStream_t s) {
-  const FacPlan& p = a.p;
-  const dim3 grid(p.n_split, a.c.n_kv_heads * p.head_chunks, a.c.batch);
-  switch (p.heads_per_pass) {
-    case 1: hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((fac_select_kernel<T, Acc, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((fac_select_kernel<T, Acc, 4>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((fac_select_kernel<T, Acc, 8>), grid, dim3(256), 0, s, a); break;
-  }
+  hipLaunchKernelGGL((fac_select_kernel<T, Acc>), dim3(a.c.group, a.c.n_kv_heads, a.c.batch), dim3(kSelThreads), 0, s,
+                     a);
   return hipGetLastError();
 }
 
@@ -404,7 +427,8 @@ FacArgs make_args(const Common& c, const FacPlan& p, const void* q, const void* 
 }  // namespace
 
 bool fac_selects(const Common& c, const FacPlan& p) {
-  return c.max_t > 0 && c.budget <= kSmallBudget && p.n_split <= kFacMergeMax && c.max_blocks <= kBtabLds;
+  (void)p;
+  return c.max_t > 0 && c.budget <= kSmallBudget && c.max_blocks <= kBtabLds && (c.score_stride & 3) == 0;
 }
 
 FacPlan fac_plan(const Common& c) {
@@ -435,7 +459,8 @@ size_t fac_workspace_bytes(const Common& c, const FacPlan& p) {
 }
 
 size_t scores_bytes(const Common& c) {
-  return align256(size_t(c.batch) * c.n_kv_heads * size_t(c.max_t) * sizeof(float));
+  // Rows padded to a multiple of 4 (a decode step's stride).
+  return align256(size_t(c.batch) * c.n_kv_heads * size_t((c.max_t + 3) & ~3) * sizeof(float));
 }
 
 hipError_t launch_fac(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
@@ -450,8 +475,8 @@ hipError_t launch_fac(const Common& c, const FacPlan& p, const void* q, const vo
 hipError_t launch_fac_select(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
                              const void* v_pool, const int32_t* block_table, const float* scores,
                              const int32_t* seq_lens, const SelectBuffers& sb, int32_t* sel_idx,
-                             int32_t* sel_count, float* out, void* ws, uint32_t* arrive, hipStream_t s) {
-  FacArgs a = make_args(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out, ws, arrive);
+                             int32_t* sel_count, float* out, hipStream_t s) {
+  FacArgs a = make_args(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out, nullptr, nullptr);
   a.scores = scores;
   a.seq_lens = seq_lens;
   a.w = sb;

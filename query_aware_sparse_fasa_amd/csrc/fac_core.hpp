@@ -135,13 +135,14 @@ struct FacWave {
   // called once per 64 rows with r = base + lane (two dependent loads at most).
   // Invalid rows load a valid row of the wave instead and are then ignored, so
   // the row loads need no branch and go out together.
-  template <typename LaneOffset>
+  // U: row quads whose loads are in flight together (2 U raw registers of 4 or 8
+  // VGPRs each); U = 16 covers all 64 rows of a step with one round trip.
+  template <int U = 2, typename LaneOffset>
   __device__ __forceinline__ void run(int r0, int r1, LaneOffset lane_offset, const T* kbase,
                                       const T* vbase) {
     const int lane = threadIdx.x & 63, rg = lane >> 4, sub = lane & 15;
     kbase += 8 * sub;
     vbase += 8 * sub;
-    constexpr int U = 2;   // row quads whose loads are in flight together
     for (int base = r0; base < r1; base += 64) {   // wave-uniform
       const int64_t my_off = lane_offset(base + lane);
       const uint64_t ok = __ballot(my_off >= 0);

@@ -72,6 +72,7 @@ Common make_common(const fasa_shape* s, int32_t max_t) {
   c.max_blocks = s->max_blocks_per_seq;
   c.max_t = max_t;
   c.cap = capacity(s, max_t);
+  c.score_stride = max_t;
   c.kv_block_stride = s->kv_block_stride;
   c.kv_head_stride = s->kv_head_stride;
   c.slab_block_stride = s->slab_block_stride;
@@ -261,12 +262,14 @@ fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_po
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16)) return FASA_ERR_INVALID_ARG;
   if (slab && !aligned(slab, 16)) return FASA_ERR_INVALID_ARG;
   Common c = make_common(shape, max_t);
+  c.score_stride = (max_t + 3) & ~3;   // the workspace's scores rows: 16-byte loads throughout
   const FacPlan p = fasa::fac_plan(c);
   const Layout l = layout(c, p);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < l.total) return FASA_ERR_WORKSPACE;
   // TIP (+ unit histograms) -> filter (+ FAC counters zeroed) -> FAC that
-  // selects its own rows and merges in its last workgroups; for large budgets
-  // the exact select is a launch of its own before the FAC.
+  // selects its own rows and writes out directly (small budgets); for large
+  // budgets the exact select is a launch of its own, followed by a split-K FAC
+  // merged in its last workgroups.
   char* w = static_cast<char*>(workspace);
   const fasa::SelectBuffers sb = select_buffers(workspace, l);
   float* scores = reinterpret_cast<float*>(w + l.scores);
@@ -281,7 +284,7 @@ fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_po
     return st;
   if (fasa::fac_selects(c, p))
     return hip_status(fasa::launch_fac_select(c, p, q, k_pool, v_pool, block_table, scores, seq_lens, sb, sel_idx,
-                                              sel_count, out, w + l.fac, fac_arrive, stream));
+                                              sel_count, out, stream));
   if ((st = hip_status(fasa::launch_finish(c, scores, seq_lens, sel_idx, sel_count, sb, fac_arrive, p.head_chunks,
                                            stream))) != FASA_OK)
     return st;

@@ -38,6 +38,7 @@ constexpr int kBtabLds = 2048;
 struct Common {
   int batch, n_q_heads, n_kv_heads, group, n_fc, budget, n_sink, n_recent;
   int max_blocks, max_t, cap;
+  int score_stride;   // elements per row of the scores array (>= max_t; a multiple of 4 in a decode step)
   int64_t kv_block_stride, kv_head_stride, slab_block_stride, slab_head_stride;
   int bf16;     // 1: bf16 storage, 0: fp32 storage
   float scale;
@@ -96,14 +97,15 @@ hipError_t launch_finish(const Common& c, const float* scores, const int32_t* se
 hipError_t launch_fac(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
                       const void* v_pool, const int32_t* block_table, const int32_t* sel_idx,
                       const int32_t* sel_count, float* out, void* ws, uint32_t* arrive, hipStream_t s);
-// Whether a decode step may use launch_fac_select (small budget, merge in the split).
+// Whether a decode step may use launch_fac_select (small budget, block-table
+// rows that fit in LDS).
 bool fac_selects(const Common& c, const FacPlan& p);
 // Top-B stage 3 and FAC in one launch, after launch_filter: writes the
-// selection lists and counts, zeroes the histograms, and computes out.
-// arrive: FAC arrival counters zeroed by launch_filter.
+// selection lists and counts, zeroes the histograms, and computes out (one
+// workgroup per query head, no merge).
 hipError_t launch_fac_select(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
                              const void* v_pool, const int32_t* block_table, const float* scores,
                              const int32_t* seq_lens, const SelectBuffers& sb, int32_t* sel_idx,
-                             int32_t* sel_count, float* out, void* ws, uint32_t* arrive, hipStream_t s);
+                             int32_t* sel_count, float* out, hipStream_t s);
 
 }  // namespace fasa

@@ -148,19 +148,32 @@ __device__ __forceinline__ int tile_index(int base, int q, int r) {
 
 // Raw scores of this lane's KPT slots of the tile at `base`, loaded without
 // branches (indices clamped into the row).
-__device__ __forceinline__ void load_tile(const float* row, int max_t, int base, float (&v)[KPT]) {
+// Scores row[j0 + 256 q + r] for q < Q, r < 4 (4 consecutive per step; steps
+// 256 apart; j0 a multiple of 4), clamped into the row's lim readable elements.
+// VEC (lim a multiple of 4, the row 16-byte aligned): one 16-byte load per
+// step -- a clamped vector only ever covers slots past the valid tokens, which
+// are never used; otherwise 4 scalar loads per step.  The choice is a template
+// parameter, not a branch, so every load is in flight before the first wait.
+template <int Q, bool VEC>
+__device__ __forceinline__ void load_steps(const float* row, int lim, int j0, float (&v)[4 * Q]) {
+  if constexpr (VEC) {
 #pragma unroll
-  for (int q = 0; q < KPT / 4; ++q) {
-    const int j = tile_index(base, q, 0);
-    if ((max_t & 3) == 0) {
-      // A clamped vector only ever covers slots >= max_t, which are never used.
-      const float4 x = *reinterpret_cast<const float4*>(row + min(j, max_t - 4));
+    for (int q = 0; q < Q; ++q) {
+      const float4 x = *reinterpret_cast<const float4*>(row + min(j0 + 256 * q, lim - 4));
       v[4 * q + 0] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
-    } else {
+    }
+  } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[4 * q + r] = row[min(j + r, max_t - 1)];
+    for (int q = 0; q < Q; ++q) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[4 * q + r] = row[min(j0 + 256 * q + r, lim - 1)];
     }
   }
+}
+
+template <bool VEC>
+__device__ __forceinline__ void load_tile(const float* row, int lim, int base, float (&v)[KPT]) {
+  load_steps<KPT / 4, VEC>(row, lim, tile_index(base, 0, 0), v);
 }
 
 // Index-order placement of flagged slots of a tile.  For each step q, lane l's
@@ -348,8 +361,9 @@ __device__ void lds_select(SelState<NTH>& s, const uint32_t* key, const int32_t*
 // streamed from memory in tiles.  A bound from group maxima prunes the first
 // pass: the Bc-th largest of the maxima of >= Bc disjoint slot groups is <= the
 // Bc-th largest key.
-template <int NTH>
-__device__ void row_select(SelState<NTH>& s, const float* row, int max_t, int c_lo, int c_hi, int Bc,
+// lim: readable elements of the row (see load_steps); the tokens are [0, max_t).
+template <int NTH, bool VEC>
+__device__ void row_select(SelState<NTH>& s, const float* row, int lim, int max_t, int c_lo, int c_hi, int Bc,
                            int32_t* out) {
   constexpr int TILE = NTH * KPT;
   const int tid = threadIdx.x;
@@ -357,7 +371,7 @@ __device__ void row_select(SelState<NTH>& s, const float* row, int max_t, int c_
   uint32_t k[KPT];
   auto keys_of = [&](int ch) {
     float v[KPT];
-    load_tile(row, max_t, ch * TILE, v);
+    load_tile<VEC>(row, lim, ch * TILE, v);
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
       const int j = tile_index(ch * TILE, e >> 2, e & 3);
@@ -488,15 +502,16 @@ __device__ __forceinline__ void load_counts(const int32_t* unit_counts, int nfa,
 // (nfc chunks, counts cnt and first pairs pre already loaded), into out[0..Bc)
 // -- global or LDS.  b1: the coarse bin the filter kept keys from.  Falls back
 // to the whole score row when the kept pairs are fewer than Bc or do not fit.
-template <int NTH, int PRE>
+template <int NTH, int PRE, bool VEC>
 __device__ void select_from_kept(SelState<NTH>& s, int32_t* chunk_off, uint32_t* key, int32_t* idx, int cap_lds,
-                                 const uint2* unit_slots, const float* row, int max_t, int nfc, const int (&cnt)[CPT],
+                                 const uint2* unit_slots, const float* row, int lim, int max_t, int nfc,
+                                 const int (&cnt)[CPT],
                                  const uint2 (&pre)[PRE], int c_lo, int c_hi, int Bc, int b1, int32_t* out) {
   zero_bins<NTH, HB>(s);               // the gather's second-digit histogram; published by its first barrier
   uint32_t above = 0;
   const int N = gather_kept<NTH, PRE>(s, chunk_off, unit_slots, nfc, cap_lds, cnt, pre, key, idx, b1, above);
   if (N >= Bc) lds_select<NTH>(s, key, idx, N, Bc, b1, above, out);
-  else row_select<NTH>(s, row, max_t, c_lo, c_hi, Bc, out);
+  else row_select<NTH, VEC>(s, row, lim, max_t, c_lo, c_hi, Bc, out);
 }
 
 }  // namespace sel

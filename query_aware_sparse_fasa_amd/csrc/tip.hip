@@ -144,8 +144,8 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
 
   const int j0 = blk * kBlock + lane * 4;
   if (live) {
-    float* dst = a.scores + (int64_t(b) * c.n_kv_heads + g) * c.max_t + j0;
-    if (j0 + 3 < t && (c.max_t & 3) == 0) {
+    float* dst = a.scores + (int64_t(b) * c.n_kv_heads + g) * c.score_stride + j0;
+    if (j0 + 3 < t && (c.score_stride & 3) == 0) {
       *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     } else {
 #pragma unroll

@@ -57,19 +57,27 @@ struct TopkArgs {
 
 // The 8 scores of filter thread tid in the 2048-token chunk at `base`: two
 // coalesced 1 KB-per-wave loads, slot e is token base + 1024 (e / 4) + 4 tid + e % 4.
-__device__ __forceinline__ void load_chunk8(const float* row, int max_t, int base, float (&v)[8]) {
+// lim and VEC as in load_steps.
+template <bool VEC>
+__device__ __forceinline__ void load_chunk8(const float* row, int lim, int base, float (&v)[8]) {
+  const int j0 = base + int(threadIdx.x) * 4;
+  if constexpr (VEC) {
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int j = base + q * 1024 + threadIdx.x * 4;
-    if ((max_t & 3) == 0) {
-      const float4 x = *reinterpret_cast<const float4*>(row + min(j, max_t - 4));
+    for (int q = 0; q < 2; ++q) {
+      const float4 x = *reinterpret_cast<const float4*>(row + min(j0 + 1024 * q, lim - 4));
       v[4 * q + 0] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
-    } else {
+    }
+  } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[4 * q + r] = row[min(j + r, max_t - 1)];
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[4 * q + r] = row[min(j0 + 1024 * q + r, lim - 1)];
     }
   }
 }
+// Readable elements of a scores row for the loaders.
+template <bool VEC>
+__device__ __forceinline__ int row_lim(const Common& c) { return VEC ? c.score_stride : c.max_t; }
 __device__ __forceinline__ int chunk8_index(int base, int e) {
   return base + (e >> 2) * 1024 + int(threadIdx.x) * 4 + (e & 3);
 }
@@ -82,14 +90,15 @@ __device__ __forceinline__ void zero_fac_arrive(const TopkArgs& a, int64_t unit)
 // ---------------------------------------------------------------------------
 // Stage 1 for the standalone select: the unit histogram of given scores.
 // Grid (ceil(max_t / 2048), kv heads, batch), 256 threads with 8 slots each.
+template <bool VEC>
 __global__ __launch_bounds__(FNT) void hist_kernel(TopkArgs a) {
   const Common& c = a.c;
   const int b = blockIdx.z;
   const int64_t unit = int64_t(b) * c.n_kv_heads + blockIdx.y;
-  const float* row = a.scores + unit * c.max_t;
+  const float* row = a.scores + unit * c.score_stride;
   const int base = blockIdx.x * FCH;
   float v[8];
-  load_chunk8(row, c.max_t, base, v);
+  load_chunk8<VEC>(row, row_lim<VEC>(c), base, v);
   int t, c_lo, c_hi;
   unit_range(c, a.seq_lens[b], t, c_lo, c_hi);
   __shared__ uint32_t h[HB];
@@ -112,18 +121,19 @@ __global__ __launch_bounds__(FNT) void hist_kernel(TopkArgs a) {
 
 // ---------------------------------------------------------------------------
 // Stage 2.  Grid (ceil(max_t / 2048), kv heads, batch), 256 threads.
+template <bool VEC>
 __global__ __launch_bounds__(FNT) void filter_kernel(TopkArgs a) {
   const Common& c = a.c;
   const int b = blockIdx.z, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t unit = int64_t(b) * c.n_kv_heads + blockIdx.y;
   const int nfa = filter_chunks(c);
-  const float* row = a.scores + unit * c.max_t;
+  const float* row = a.scores + unit * c.score_stride;
   const int base = blockIdx.x * FCH;
 
   // Independent loads: this thread's 8 scores and its 8 histogram bins.  Thread
   // t owns bins 2047-8t down to 2040-8t, so a scan over threads counts from the top.
   float v[8];
-  load_chunk8(row, c.max_t, base, v);
+  load_chunk8<VEC>(row, row_lim<VEC>(c), base, v);
   const uint32_t* hg = a.w.hist + unit * HB;
   const uint4 hlo = *reinterpret_cast<const uint4*>(hg + HB - 8 - 8 * tid);
   const uint4 hhi = *reinterpret_cast<const uint4*>(hg + HB - 4 - 8 * tid);
@@ -208,6 +218,7 @@ struct FinishShared {
   int32_t idx[kCandLds];
 };
 
+template <bool VEC>
 __global__ __launch_bounds__(BIG) void finish_kernel(TopkArgs a) {
   const Common& c = a.c;
   const int b = blockIdx.y, tid = threadIdx.x;
@@ -230,8 +241,9 @@ __global__ __launch_bounds__(BIG) void finish_kernel(TopkArgs a) {
   zero_fac_arrive(a, unit);
   if (!keep_all) {
     __shared__ FinishShared sm;
-    select_from_kept<BIG, 1>(sm.sel, sm.chunk_off, sm.key, sm.idx, kCandLds, unit_slots, a.scores + unit * c.max_t,
-                             c.max_t, nfa, cnt, pre, c_lo, c_hi, Bc, b1, out + c_lo);
+    select_from_kept<BIG, 1, VEC>(sm.sel, sm.chunk_off, sm.key, sm.idx, kCandLds, unit_slots,
+                                  a.scores + unit * c.score_stride, row_lim<VEC>(c), c.max_t, nfa, cnt, pre, c_lo,
+                                  c_hi, Bc, b1, out + c_lo);
   }
   // Outputs that nothing above waits on go last: the forced part of the list,
   // its padding and count, and the consumed histogram (zero for the next step).
@@ -261,12 +273,15 @@ hipError_t launch_filter(const Common& c, const float* scores, const int32_t* se
   if (c.max_t == 0) return hipSuccess;
   const TopkArgs a{c, scores, seq_lens, nullptr, nullptr, w, fac_arrive, head_chunks};
   const dim3 grid(filter_chunks(c), c.n_kv_heads, c.batch);
+  const bool vec = (c.score_stride & 3) == 0;
   if (!have_hist) {
-    hipLaunchKernelGGL(hist_kernel, grid, dim3(FNT), 0, s, a);
+    if (vec) hipLaunchKernelGGL(hist_kernel<true>, grid, dim3(FNT), 0, s, a);
+    else hipLaunchKernelGGL(hist_kernel<false>, grid, dim3(FNT), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(filter_kernel, grid, dim3(FNT), 0, s, a);
+  if (vec) hipLaunchKernelGGL(filter_kernel<true>, grid, dim3(FNT), 0, s, a);
+  else hipLaunchKernelGGL(filter_kernel<false>, grid, dim3(FNT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -274,7 +289,10 @@ hipError_t launch_finish(const Common& c, const float* scores, const int32_t* se
                          int32_t* sel_count, const SelectBuffers& w, uint32_t* fac_arrive, int head_chunks,
                          hipStream_t s) {
   const TopkArgs a{c, scores, seq_lens, sel_idx, sel_count, w, fac_arrive, head_chunks};
-  hipLaunchKernelGGL(finish_kernel, dim3(c.n_kv_heads, c.batch), dim3(BIG), 0, s, a);
+  if ((c.score_stride & 3) == 0)
+    hipLaunchKernelGGL(finish_kernel<true>, dim3(c.n_kv_heads, c.batch), dim3(BIG), 0, s, a);
+  else
+    hipLaunchKernelGGL(finish_kernel<false>, dim3(c.n_kv_heads, c.batch), dim3(BIG), 0, s, a);
   return hipGetLastError();
 }
 
