@@ -184,7 +184,10 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   };
   const T* kbase = static_cast<const T*>(a.k_pool) + int64_t(g) * c.kv_head_stride;
   const T* vbase = static_cast<const T*>(a.v_pool) + int64_t(g) * c.kv_head_stride;
-  w.run(r0, r1, lane_offset, kbase, vbase);
+  // Row quads of loads in flight per wave: as many as the registers allow at
+  // two waves per SIMD (about 64 KB in flight per CU hides HBM latency).
+  constexpr int U = (sizeof(Acc) == 4 && HG <= 4) ? 8 : (HG <= 2 ? 4 : 2);
+  w.template run<U>(r0, r1, lane_offset, kbase, vbase);
   w.fold_row_groups();
 
   __shared__ WaveFold<Acc, HG> fold;
@@ -198,20 +201,22 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   }
 }
 
-// The selecting launch of a decode step (budgets up to kSmallBudget).  One
-// workgroup per (sequence, query head): it first makes its unit's exact top-B
-// selection itself, from the filter's kept pairs (select_core.hpp), into LDS --
-// redundantly across the G heads of the unit, since a unit keeps only a few
-// hundred pairs -- then runs FAC for its head over every row of the list, 16
-// row quads of K/V loads in flight per wave, and writes the head's output
-// directly: no partials and no merge.  The G workgroups of a unit read the same
-// K/V rows; after the first, mostly from the shared Infinity Cache.  Workgroup
-// 0 of each unit also publishes the list and its count and clears the unit's
-// histogram for the next step.  Grid (G, kv heads, batch).
 constexpr int kSelThreads = 512;            // workgroup of the selecting launch
 constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelWideUnits = 256;          // units from which a workgroup covers several heads
 
-template <typename Acc>
+// The selecting launch of a decode step (budgets up to kSmallBudget).  One
+// workgroup per (sequence, query head chunk): it first makes its unit's exact
+// top-B selection itself, from the filter's kept pairs (select_core.hpp), into
+// LDS -- redundantly across the head chunks of the unit, since a unit keeps
+// only a few hundred pairs -- then runs FAC for its heads over every row of the
+// list with kSelWaves waves, and writes the heads' outputs directly: no
+// partials and no merge.  With one head per workgroup (few units) the G
+// workgroups of a unit read the same K/V rows, after the first mostly from the
+// shared Infinity Cache.  Workgroup 0 of each unit also publishes the list and
+// its count and clears the unit's histogram for the next step.
+// Grid (head chunks, kv heads, batch).
+template <typename Acc, int HG>
 struct FacSelShared {
   union {
     struct {
@@ -220,35 +225,39 @@ struct FacSelShared {
       uint32_t key[kSmallCand];
       int32_t idx[kSmallCand];
     } s;
-    WaveFold<Acc, 1, kSelWaves> fold;
+    WaveFold<Acc, HG, kSelWaves> fold;
   } u;
   int32_t chosen[kSmallBudget];
   int32_t btab[kBtabLds];
 };
 
-template <typename T, typename Acc>
+// HG query heads per workgroup (blockIdx.x picks the head chunk): 1 when there
+// are few units and latency rules, up to 8 when many units fill the chip and
+// each K/V row should be read once.
+template <typename T, typename Acc, int HG>
 __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   const Common& c = a.c;
-  const int b = blockIdx.z, g = blockIdx.y, hq = blockIdx.x;
+  const int b = blockIdx.z, g = blockIdx.y, hc = blockIdx.x;
+  const int h0 = hc * HG, nh = min(HG, c.group - h0);
   const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t unit = int64_t(b) * c.n_kv_heads + g;
   const int nfa = sel::filter_chunks(c);
   const uint2* unit_slots = static_cast<const uint2*>(a.w.slots) + unit * nfa * int64_t(sel::FCH);
   const float* row = a.scores + unit * c.score_stride;   // a decode step's rows: 16-byte aligned, padded
   const int lim = c.score_stride;
-  __shared__ FacSelShared<Acc> sm;
+  __shared__ FacSelShared<Acc, HG> sm;
 
   // Independent loads first: the first kept pairs of every chunk (up to 16
-  // chunks), the chunk counts and b1; the query slice, the block-table row and
+  // chunks), the chunk counts and b1; the query slices, the block-table row and
   // the length.
   uint2 pre[16 / kSelWaves];
   sel::prefetch_kept<kSelThreads, 16 / kSelWaves>(unit_slots, nfa, pre);
   int cnt[sel::CPT];
   sel::load_counts(a.w.counts + unit * nfa, nfa, cnt);
   const int b1 = a.w.b1[unit];
-  const int64_t head = int64_t(b) * c.n_q_heads + g * c.group + hq;
-  Raw8<T> qraw[1];
-  FacWave<T, Acc, 1>::load_q(static_cast<const T*>(a.q) + head * kHeadDim, 1, qraw);
+  const int64_t head0 = int64_t(b) * c.n_q_heads + g * c.group + h0;
+  Raw8<T> qraw[HG];
+  FacWave<T, Acc, HG>::load_q(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, qraw);
   // The sequence's block-table row (at most kBtabLds entries), held in
   // registers through the select and moved to LDS after it.
   const int32_t* btab = a.block_table + int64_t(b) * c.max_blocks;
@@ -272,8 +281,8 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   __syncthreads();                          // the list and the block table are in LDS; the select area is free
 
   // Row r of the list: the forced prefix, the chosen, then the forced suffix.
-  FacWave<T, Acc, 1> w;
-  w.init_raw(qraw, 1, c.scale);
+  FacWave<T, Acc, HG> w;
+  w.init_raw(qraw, nh, c.scale);
   auto token = [&](int r) -> int {
     const int ch = sm.chosen[min(max(r - c_lo, 0), kSmallBudget - 1)];
     return (keep_all || r < c_lo) ? r : (r < c_lo + Bc ? ch : c_hi + (r - c_lo - Bc));
@@ -289,37 +298,44 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   };
   const T* kbase = static_cast<const T*>(a.k_pool) + int64_t(g) * c.kv_head_stride;
   const T* vbase = static_cast<const T*>(a.v_pool) + int64_t(g) * c.kv_head_stride;
-  w.template run<64 / kSelWaves>(r0, r1, lane_offset, kbase, vbase);
+  // Row quads in flight per wave: 8 (a whole 32-row share of a 256-row list in
+  // one round trip) for one head; fewer as the per-head state grows.
+  constexpr int U = HG == 1 ? 8 : (HG <= 4 && sizeof(Acc) == 4 ? 4 : 2);
+  w.template run<U>(r0, r1, lane_offset, kbase, vbase);
   w.fold_row_groups();
 
-  // Fold the 4 waves through LDS and write the head's output.
-  WaveFold<Acc, 1, kSelWaves>& f = sm.u.fold;
+  // Fold the waves through LDS and write the heads' outputs.
+  WaveFold<Acc, HG, kSelWaves>& f = sm.u.fold;
   const int lane = tid & 63, sub = lane & 15;
   if (lane < 16) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f.acc[wave][0][8 * sub + e] = w.acc[0][e];
-    if (sub == 0) {
-      f.m[wave][0] = w.m[0];
-      f.l[wave][0] = w.l[0];
+    for (int hh = 0; hh < HG; ++hh) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f.acc[wave][hh][8 * sub + e] = w.acc[hh][e];
+      if (sub == 0) {
+        f.m[wave][hh] = w.m[hh];
+        f.l[wave][hh] = w.l[hh];
+      }
     }
   }
   __syncthreads();
-  if (tid < kHeadDim) {
+  for (int idx = tid; idx < nh * kHeadDim; idx += kSelThreads) {
+    const int hh = idx / kHeadDim, ch = idx % kHeadDim;
     Acc M = neg_inf<Acc>();
 #pragma unroll
-    for (int v = 0; v < kSelWaves; ++v) M = fmax(M, f.m[v][0]);
+    for (int v = 0; v < kSelWaves; ++v) M = fmax(M, f.m[v][hh]);
     Acc L = Acc(0), O = Acc(0);
     if (M != neg_inf<Acc>()) {
 #pragma unroll
       for (int v = 0; v < kSelWaves; ++v) {
-        const Acc wgt = merge_weight(f.m[v][0], M);
-        L = fma(f.l[v][0], wgt, L);
-        O = fma(f.acc[v][0][tid], wgt, O);
+        const Acc wgt = merge_weight(f.m[v][hh], M);
+        L = fma(f.l[v][hh], wgt, L);
+        O = fma(f.acc[v][hh][ch], wgt, O);
       }
     }
-    a.out[head * kHeadDim + tid] = L > Acc(0) ? float(O / L) : 0.f;
+    a.out[(head0 + hh) * kHeadDim + ch] = L > Acc(0) ? float(O / L) : 0.f;
   }
-  if (hq == 0) {
+  if (hc == 0) {
     // Workgroup 0 of the unit publishes the list and leaves the consumed
     // histogram zero for the next step (the filter launch read it).
     int32_t* list = a.sel_idx + unit * c.cap;
@@ -404,10 +420,27 @@ hipError_t launch_fac_t(FacArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Heads per workgroup of the selecting launch: one while the (sequence, kv
+// head) units are fewer than the CUs; otherwise the whole group, up to 8.
+// (fp64 state for fp32 caches: at most 2 heads, which keeps the registers.)
+int select_heads(const Common& c) {
+  if (int64_t(c.batch) * c.n_kv_heads < kSelWideUnits) return 1;
+  const int most = c.bf16 ? 8 : 2;
+  int hg = 1;
+  while (hg < c.group && hg < most) hg <<= 1;
+  return hg;
+}
+
 template <typename T, typename Acc>
 hipError_t launch_fac_select_t(const FacArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((fac_select_kernel<T, Acc>), dim3(a.c.group, a.c.n_kv_heads, a.c.batch), dim3(kSelThreads), 0, s,
-                     a);
+  const int hg = select_heads(a.c);
+  const dim3 grid((a.c.group + hg - 1) / hg, a.c.n_kv_heads, a.c.batch);
+  if (hg == 1) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1>), grid, dim3(kSelThreads), 0, s, a);
+  else if (hg == 2) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 2>), grid, dim3(kSelThreads), 0, s, a);
+  else if constexpr (sizeof(Acc) == 4) {
+    if (hg == 4) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 4>), grid, dim3(kSelThreads), 0, s, a);
+    else hipLaunchKernelGGL((fac_select_kernel<T, Acc, 8>), grid, dim3(kSelThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -32,6 +32,13 @@ SMALL = {
                                 t_range=(2000, 2000), budget=300),
     "fp32-g7-f64": C["c4"].replace(dtype="fp32", batch=1, t=None, t_range=(1200, 1300), n_fc=64,
                                    budget=77),
+    # At least 256 (sequence, kv head) units: the selecting FAC launch then
+    # covers several query heads per workgroup (4, 8 and, for fp32 caches, 2).
+    "wide-g4": C["c2"].replace(batch=40, t=None, t_range=(300, 700), budget=48),
+    "wide-g8-sink": C["c2"].replace(batch=64, n_kv_heads=4, t=None, t_range=(260, 520), budget=40,
+                                    n_sink=2, n_recent=9),
+    "wide-fp32-g2": C["c2"].replace(dtype="fp32", batch=64, n_q_heads=8, n_kv_heads=4, t=None,
+                                    t_range=(300, 600), budget=40),
 }
 
 
