@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   const T* vbase = static_cast<const T*>(a.v_pool) + int64_t(g) * c.kv_head_stride;
   // Row quads of loads in flight per wave: as many as the registers allow at
   // two waves per SIMD (about 64 KB in flight per CU hides HBM latency).
-  constexpr int U = (sizeof(Acc) == 4 && HG <= 4) ? 8 : (HG <= 2 ? 4 : 2);
+  constexpr int U = (sizeof(Acc) == 4 && HG <= 4) ? 8 : (HG <= 2 ? 4 : (HG <= 4 || sizeof(Acc) == 4 ? 2 : 1));
   w.template run<U>(r0, r1, lane_offset, kbase, vbase);
   w.fold_row_groups();
 

@@ -94,9 +94,27 @@ __device__ __forceinline__ void lane_pair(double v, double& lo, double& hi) {
   hi = __longlong_as_double(int64_t((uint64_t(b1) << 32) | b0));
 }
 
+// q.k of one lane's 8 channels.  bf16 caches: four v_dot2_f32_bf16 on the raw
+// bf16 pairs of q and k (bf16 products are exact in fp32; sums round in fp32),
+// no widening of k; fp32 caches: eight fp64 FMAs.
+__device__ __forceinline__ float dot8(const uint4& q, const Raw8<uint16_t>& k) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  auto h = [](uint32_t x) { return __builtin_bit_cast(bf16x2, x); };
+  const float a = __builtin_amdgcn_fdot2_f32_bf16(h(k.v.x), h(q.x), 0.f, false);
+  const float b = __builtin_amdgcn_fdot2_f32_bf16(h(k.v.y), h(q.y), 0.f, false);
+  const float c = __builtin_amdgcn_fdot2_f32_bf16(h(k.v.z), h(q.z), a, false);
+  const float d = __builtin_amdgcn_fdot2_f32_bf16(h(k.v.w), h(q.w), b, false);
+  return c + d;
+}
+
 template <typename T, typename Acc, int HG>
 struct FacWave {
-  Acc qv[HG][8];
+  static constexpr bool kBf16 = sizeof(T) == 2;
+  // Query slices: raw bf16 pairs (logits scaled afterwards by zscale), or
+  // pre-scaled fp64 values for fp32 caches.
+  uint4 q2[kBf16 ? HG : 1];
+  Acc qv[kBf16 ? 1 : HG][8];
+  Acc zscale;
   Acc m[HG], l[HG], acc[HG][8];
 
   // This lane's raw query slices of heads 0 .. nh-1 from q_head0 (rows of q,
@@ -107,8 +125,9 @@ struct FacWave {
     for (int hh = 0; hh < HG; ++hh) qr[hh].load(q_head0 + int64_t(min(hh, nh - 1)) * kHeadDim + 8 * sub);
   }
 
-  // Query slices of heads h_first .. h_first+nh-1, pre-scaled; unused head
-  // slots are zero.
+  // Query slices of heads h_first .. h_first+nh-1; unused head slots are zero.
+  // Logits come out scaled by scale (and by log2(e) for fp32 accumulation,
+  // whose exponentials are exp2).
   __device__ __forceinline__ void init(const T* q_head0, int nh, float scale) {
     Raw8<T> qr[HG];
     load_q(q_head0, nh, qr);
@@ -120,14 +139,19 @@ struct FacWave {
     for (int hh = 0; hh < HG; ++hh) {
       m[hh] = neg_inf<Acc>();
       l[hh] = Acc(0);
-      float x[8];
-      qr[hh].unpack(x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        acc[hh][e] = Acc(0);
-        qv[hh][e] = (hh < nh) ? Acc(x[e]) * qscale : Acc(0);
+      for (int e = 0; e < 8; ++e) acc[hh][e] = Acc(0);
+      if constexpr (kBf16) {
+        const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+        q2[hh] = (hh < nh) ? reinterpret_cast<const uint4&>(qr[hh]) : z4;
+      } else {
+        float x[8];
+        qr[hh].unpack(x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[hh][e] = (hh < nh) ? Acc(x[e]) * qscale : Acc(0);
       }
     }
+    zscale = kBf16 ? qscale : Acc(1);
   }
 
   // Rows r0 .. r1-1 of the selection.  lane_offset(r) returns the element offset
@@ -136,7 +160,9 @@ struct FacWave {
   // Invalid rows load a valid row of the wave instead and are then ignored, so
   // the row loads need no branch and go out together.
   // U: row quads whose loads are in flight together (2 U raw registers of 4 or 8
-  // VGPRs each); U = 16 covers all 64 rows of a step with one round trip.
+  // VGPRs each).  The online softmax is updated once per U quads: the logits of
+  // all U quads first, then one rescale of each head's state to the new
+  // maximum, then the U weighted rows added.
   template <int U = 2, typename LaneOffset>
   __device__ __forceinline__ void run(int r0, int r1, LaneOffset lane_offset, const T* kbase,
                                       const T* vbase) {
@@ -161,30 +187,49 @@ struct FacWave {
           kr[u].load(kbase + o);
           vr[u].load(vbase + o);
         }
+        // Logits of the U quads (this row group's row in each), and the new maxima.
+        Acc z[U][HG], mn[HG];
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) mn[hh] = m[hh];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          float kx[8], vx[8];
-          kr[u].unpack(kx);
-          vr[u].unpack(vx);
-          Acc z[HG];
+          float kx[8];
+          if constexpr (!kBf16) kr[u].unpack(kx);
 #pragma unroll
           for (int hh = 0; hh < HG; ++hh) {
-            Acc s = Acc(0);
+            Acc sdot;
+            if constexpr (kBf16) {
+              sdot = Acc(dot8(q2[hh], reinterpret_cast<const Raw8<uint16_t>&>(kr[u])));
+            } else {
+              sdot = Acc(0);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s = fma(qv[hh][e], Acc(kx[e]), s);
-            z[hh] = row_sum(s);
-          }
-          if (valid[u]) {
-#pragma unroll
-            for (int hh = 0; hh < HG; ++hh) {
-              const Acc mn = fmax(m[hh], z[hh]);
-              const Acc corr = fexp<Acc>(m[hh] - mn);
-              const Acc pz = fexp<Acc>(z[hh] - mn);
-              m[hh] = mn;
-              l[hh] = fma(l[hh], corr, pz);
-#pragma unroll
-              for (int e = 0; e < 8; ++e) acc[hh][e] = fma(acc[hh][e], corr, pz * Acc(vx[e]));
+              for (int e = 0; e < 8; ++e) sdot = fma(qv[hh][e], Acc(kx[e]), sdot);
             }
+            const Acc zz = row_sum(sdot) * zscale;
+            z[u][hh] = valid[u] ? zz : neg_inf<Acc>();
+            mn[hh] = fmax(mn[hh], z[u][hh]);
+          }
+        }
+        // Rescale each head's state to its new maximum once.
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) {
+          const Acc corr = merge_weight(m[hh], mn[hh]);
+          l[hh] *= corr;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[hh][e] *= corr;
+          m[hh] = mn[hh];
+        }
+        // Add the weighted rows.
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float vx[8];
+          vr[u].unpack(vx);
+#pragma unroll
+          for (int hh = 0; hh < HG; ++hh) {
+            const Acc pz = merge_weight(z[u][hh], mn[hh]);
+            l[hh] += pz;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[hh][e] = fma(pz, Acc(vx[e]), acc[hh][e]);
           }
         }
       }
