@@ -409,7 +409,8 @@ template <typename T, typename Acc>
 hipError_t launch_fac_t(FacArgs& a, hipStream_t s) {
   const FacPlan& p = a.p;
   const dim3 grid(p.n_split, a.c.n_kv_heads * p.head_chunks, a.c.batch);
-  if (a.arrive != nullptr && p.n_split <= kFacMergeMax) {
+  const int64_t n_wg = int64_t(grid.x) * grid.y * grid.z;
+  if (a.arrive != nullptr && p.n_split <= kFacMergeMax && n_wg <= kFacMergeGrid) {
     launch_split<T, Acc, true>(a, grid, s);
     return hipGetLastError();
   }

@@ -28,9 +28,13 @@ constexpr int kSmallCand = 4096;
 
 // FAC: 4 waves per workgroup; the waves' states are folded in LDS into one
 // partial.  Up to kFacMergeMax partials per head are merged by the last
-// workgroup of the split launch; beyond that a separate merge launch runs.
+// workgroup of the split launch, when the launch has at most kFacMergeGrid
+// workgroups; otherwise a separate merge launch runs.  (Each workgroup's
+// device-scope release writes back its XCD's L2; a few of those cost less
+// than a launch, thousands cost far more.)
 constexpr int kFacWaves = 4;
 constexpr int kFacMergeMax = 64;
+constexpr int kFacMergeGrid = 128;
 // The selecting FAC launch keeps the sequence's block-table row in LDS (up to
 // kBtabLds blocks, 512K tokens).
 constexpr int kBtabLds = 2048;
