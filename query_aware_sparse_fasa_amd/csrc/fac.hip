@@ -187,7 +187,9 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   // Row quads of loads in flight per wave: as many as the registers allow at
   // two waves per SIMD (about 64 KB in flight per CU hides HBM latency).
   constexpr int U = (sizeof(Acc) == 4 && HG <= 4) ? 8 : (HG <= 2 ? 4 : (HG <= 4 || sizeof(Acc) == 4 ? 2 : 1));
-  w.template run<U>(r0, r1, lane_offset, kbase, vbase);
+  // All heads of a chunk share this workgroup's rows, and no other workgroup
+  // of the launch reads them unless the group spans several chunks.
+  w.template run<U, true>(r0, r1, lane_offset, kbase, vbase);
   w.fold_row_groups();
 
   __shared__ WaveFold<Acc, HG> fold;

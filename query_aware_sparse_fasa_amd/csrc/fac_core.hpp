@@ -163,7 +163,8 @@ struct FacWave {
   // VGPRs each).  The online softmax is updated once per U quads: the logits of
   // all U quads first, then one rescale of each head's state to the new
   // maximum, then the U weighted rows added.
-  template <int U = 2, typename LaneOffset>
+  // NT: non-temporal row loads, for rows that no other workgroup reads.
+  template <int U = 2, bool NT = false, typename LaneOffset>
   __device__ __forceinline__ void run(int r0, int r1, LaneOffset lane_offset, const T* kbase,
                                       const T* vbase) {
     const int lane = threadIdx.x & 63, rg = lane >> 4, sub = lane & 15;
@@ -184,8 +185,13 @@ struct FacWave {
           const int64_t off = __shfl(my_off, src < 64 ? src : 0, 64);
           valid[u] = (src < nrows) && off >= 0;
           const int64_t o = valid[u] ? off : dummy;
-          kr[u].load(kbase + o);
-          vr[u].load(vbase + o);
+          if constexpr (NT) {
+            kr[u].load_nt(kbase + o);
+            vr[u].load_nt(vbase + o);
+          } else {
+            kr[u].load(kbase + o);
+            vr[u].load(vbase + o);
+          }
         }
         // Logits of the U quads (this row group's row in each), and the new maxima.
         Acc z[U][HG], mn[HG];

@@ -34,6 +34,13 @@ template <>
 struct Raw8<uint16_t> {
   uint4 v;
   __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  // Streaming load: data read once (the slab, K/V rows no other workgroup
+  // reads) is marked non-temporal so it does not displace reused lines.
+  __device__ __forceinline__ void load_nt(const uint16_t* p) {
+    typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+    const u4v t = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p));
+    v = make_uint4(t.x, t.y, t.z, t.w);
+  }
   __device__ __forceinline__ void unpack(float (&x)[8]) const {
     x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
     x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
@@ -48,6 +55,9 @@ struct Raw8<float> {
     a = reinterpret_cast<const float4*>(p)[0];
     b = reinterpret_cast<const float4*>(p)[1];
   }
+  // fp32 caches keep ordinary loads (the non-temporal form measured slower
+  // on the small fp32 workloads).
+  __device__ __forceinline__ void load_nt(const float* p) { load(p); }
   __device__ __forceinline__ void unpack(float (&x)[8]) const {
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
   if constexpr (FROM_SLAB && FT > 0) {
     if (live) {
 #pragma unroll
-      for (int f = 0; f < FT; ++f) x[f].load(sbase + f * kSlabFcStride);
+      for (int f = 0; f < FT; ++f) x[f].load_nt(sbase + f * kSlabFcStride);
     }
   }
   {
