@@ -13,7 +13,9 @@ timed with HIP events on the launch stream.
 
 Printed: one JSON line with steps/s (value), the achieved HBM bandwidth of the
 step's algorithmic bytes, the roofline of the dominant kernel (TIP, timed on
-its own in the same way), and the fp64 CPU oracle timed on the host cores.
+its own in the same way), the dense decode (full attention over every cached
+token, the decode FASA replaces) timed on the same layers, and the fp64 CPU
+oracle timed on the host cores.
 Progress goes to stderr.
 """
 from __future__ import annotations
@@ -198,6 +200,7 @@ def main():
             lay.tip(use_slab=use_slab)
             lay.topk()
             lay.fac()
+            lay.dense()
     torch.cuda.synchronize()
 
     log("[bench] capturing HIP graphs")
@@ -207,6 +210,7 @@ def main():
     g_tip = graph_of(torch, stream, [lambda l=l: l.tip(use_slab=use_slab) for l in layers])
     g_topk = graph_of(torch, stream, [lambda l=l: l.topk() for l in layers])
     g_fac = graph_of(torch, stream, [lambda l=l: l.fac() for l in layers])
+    g_dense = graph_of(torch, stream, [lambda l=l: l.dense() for l in layers])
 
     log(f"[bench] warm-up {args.warmup} steps")
     time_graph(torch, stream, [g_full], max(1, -(-args.warmup // L)))
@@ -238,6 +242,12 @@ def main():
     t_topk = time_graph(torch, stream, [g_topk], reps) / (reps * L)
     t_fac = time_graph(torch, stream, [g_fac], reps) / (reps * L)
     log(f"[bench] alone: tip {t_tip * 1e6:.2f} us, topk {t_topk * 1e6:.2f} us, fac {t_fac * 1e6:.2f} us")
+    # Dense decode (full attention over every cached token) on the same layers:
+    # the decode that FASA replaces.
+    t_dense = time_graph(torch, stream, [g_dense], reps) / (reps * L)
+    dense_gbps = sb["dense"] / t_dense / 1e9
+    log(f"[bench] dense decode {t_dense * 1e6:.2f} us ({dense_gbps:,.0f} GB/s); "
+        f"FASA step is {t_dense / (el / args.steps):.2f}x faster")
 
     tip_bytes = sb["slab"] if use_slab else int(inp.seq_lens.sum()) * cfg.n_kv_heads * 128 * cfg.elem_bytes
     tip_gbps = tip_bytes / t_tip / 1e9
@@ -280,6 +290,9 @@ def main():
                      "traffic": measured_traffic(args.config, use_slab),
                      "algorithmic_bytes_per_launch": int(tip_bytes),
                      "avg_launch_us": t_tip * 1e6},
+        "dense_decode": {"us_per_step": t_dense * 1e6, "bytes": int(sb["dense"]), "achieved_GBps": dense_gbps,
+                         "hbm_frac": dense_gbps / HBM_PEAK_GBPS,
+                         "fasa_speedup": t_dense / (el / args.steps)},
         "cpu_baseline": cpu,
         "pages_context": "the pages report 2.56x decode speedup over full-KV FlashAttention using 18.9% "
                          "of the cache (hardware not stated); context only",

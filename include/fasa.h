@@ -178,6 +178,26 @@ fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_po
                         float* out, int32_t* sel_idx, int32_t* sel_count,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of workspace that fasa_dense_decode needs for contexts up to max_t:
+ * the split partials, about 4 * (128 + 2) bytes per query head per 512 tokens
+ * of max_t (fp32 caches: twice that).  256-byte aligned; contents are
+ * scratch. */
+fasa_status fasa_dense_workspace_size(const fasa_shape* shape, int32_t max_t, size_t* bytes);
+
+/* Full attention over every cached token, the dense decode that FASA replaces:
+ * out[b][h] = softmax(q_h K^T * scale) V over tokens 0..t_b-1 of kv head g(h)
+ * (the full-KV reference of the review's experimental section, and the
+ * standard attention whose 2*t*d loaded elements Equation 8 of section 3.4,
+ * "Hardware-Aware Variants", compares with).  It is FAC with the selection
+ * "every token": same kernels, same per-row arithmetic and precision as
+ * fasa_fac.  Reads q, k_pool, v_pool, block_table, seq_lens (t_b is clamped
+ * into [0, max_t]); writes out [batch][n_q_heads][128] fp32 (zeros for
+ * t_b == 0).  fc_idx, budget, n_sink and n_recent are not used. */
+fasa_status fasa_dense_decode(const fasa_shape* shape, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* block_table,
+                              const int32_t* seq_lens, int32_t max_t, float* out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

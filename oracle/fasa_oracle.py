@@ -182,3 +182,31 @@ def decode(q, k_pool, v_pool, block_table, seq_lens, fc_idx, budget,
         res[(b, g)] = decode_unit(q[b, g * G:(g + 1) * G], K, V, fc_idx[g], budget,
                                   n_sink, n_recent, scale)
     return res
+
+
+# ---------------------------------------------------------------------------
+# dense decode: the full-KV attention that FASA replaces
+# ---------------------------------------------------------------------------
+def dense_decode(q, k_pool, v_pool, block_table, seq_lens, scale=None, units=None):
+    """Full attention over every cached token, for every query head.
+
+    The full-KV (FKV) reference of the review's experimental section, and the
+    standard attention whose loads Equation 8 (section 3.4, "Hardware-Aware
+    Variants") counts as 2td elements: out_h = softmax(q_h K^T * scale) V over
+    tokens 0..t_b-1 of kv head g(h).  No TIP and no selection.  Returns
+    {(b, g): out [G][d]}.
+    """
+    H = k_pool.shape[1]
+    Hq = q.shape[1]
+    G = Hq // H
+    d = k_pool.shape[-1]
+    scale = 1.0 / np.sqrt(d) if not scale else scale
+    res = {}
+    if units is None:
+        units = [(b, g) for b in range(q.shape[0]) for g in range(H)]
+    for b, g in units:
+        t = int(seq_lens[b])
+        K = cache_rows(k_pool, block_table[b], g, t)
+        V = cache_rows(v_pool, block_table[b], g, t)
+        res[(b, g)] = fac(q[b, g * G:(g + 1) * G], K, V, scale)[0]
+    return res

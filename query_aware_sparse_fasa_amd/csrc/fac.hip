@@ -150,7 +150,9 @@ __device__ __forceinline__ void store_partial(const FacArgs& a, const W& w, Wave
 // MERGE: the last workgroup of a (sequence, kv head, head chunk) to finish --
 // counted on an arrival counter -- merges the partials of its heads, so no
 // second launch is needed (used when n_split <= kFacMergeMax).
-template <typename T, typename Acc, int HG, bool MERGE>
+// DENSE: no selection -- row r is token r, for every r < t_b (full attention
+// over the whole cache; sel_idx and sel_count are not read).
+template <typename T, typename Acc, int HG, bool MERGE, bool DENSE = false>
 __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   const Common& c = a.c;
   const FacPlan& p = a.p;
@@ -168,16 +170,16 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   // selected indices) are independent; the block-table entries depend on the
   // indices; the K/V rows depend on those.  Loads are unconditional with clamped
   // indices -- validity is applied afterwards -- so nothing serialises them.
-  int count = a.sel_count[unit];
+  int count = DENSE ? clamp_len(a.seq_lens[b], c.max_t, c.max_blocks) : a.sel_count[unit];
   const int cap1 = c.cap > 0 ? c.cap - 1 : 0;
-  const int j_first = c.cap > 0 ? sel[min(r0 + lane, cap1)] : -1;
+  const int j_first = (!DENSE && c.cap > 0) ? sel[min(r0 + lane, cap1)] : -1;
   FacWave<T, Acc, HG> w;
   w.init(static_cast<const T*>(a.q) + (int64_t(b) * c.n_q_heads + g * c.group + h0) * kHeadDim, nh,
          c.scale);
   count = count < 0 ? 0 : (count > c.cap ? c.cap : count);   // contents are preconditions; stay in bounds
   const int r1 = min(r0 + p.rows_per_wave, count);
   auto lane_offset = [&](int r) -> int64_t {
-    const int j = (r - lane == r0) ? j_first : sel[min(r, cap1)];
+    const int j = DENSE ? r : ((r - lane == r0) ? j_first : sel[min(r, cap1)]);
     const bool ok = r < r1 && j >= 0 && j < c.max_blocks * kBlock;
     const int64_t pb = btab[ok ? (j >> 8) : 0];
     return ok ? pb * c.kv_block_stride + int64_t(j & (kBlock - 1)) * kHeadDim : -1;
@@ -397,14 +399,26 @@ __global__ __launch_bounds__(kHeadDim) void fac_merge_kernel(FacArgs a) {
   a.out[(int64_t(b) * a.c.n_q_heads + h) * kHeadDim + d] = res;
 }
 
-template <typename T, typename Acc, bool MERGE>
+template <typename T, typename Acc, bool MERGE, bool DENSE = false>
 void launch_split(const FacArgs& a, const dim3& grid, hipStream_t s) {
   switch (a.p.heads_per_pass) {
-    case 1: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 1, MERGE>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 2, MERGE>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 4, MERGE>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 8, MERGE>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 1, MERGE, DENSE>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 2, MERGE, DENSE>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 4, MERGE, DENSE>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 8, MERGE, DENSE>), grid, dim3(256), 0, s, a); break;
   }
+}
+
+// Full attention: the split launch over every cached row, then the merge launch.
+template <typename T, typename Acc>
+hipError_t launch_dense_t(const FacArgs& a, hipStream_t s) {
+  const FacPlan& p = a.p;
+  const dim3 grid(p.n_split, a.c.n_kv_heads * p.head_chunks, a.c.batch);
+  launch_split<T, Acc, false, true>(a, grid, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fac_merge_kernel<Acc>, dim3(a.c.n_q_heads, a.c.batch), dim3(kHeadDim), 0, s, a);
+  return hipGetLastError();
 }
 
 template <typename T, typename Acc>
@@ -488,6 +502,24 @@ FacPlan fac_plan(const Common& c) {
   return p;
 }
 
+FacPlan dense_plan(const Common& c) {
+  // Every cached row is read: aim at about 512 workgroups (two per CU, all
+  // resident at once) for short contexts, and give each wave up to 256 rows as
+  // the context grows (fewer partials).  Longer runs per wave measured slower
+  // on ragged batches, whose short sequences leave many workgroups idle.
+  FacPlan p = fac_plan(c);
+  const int64_t rows = int64_t(c.batch) * c.n_kv_heads * p.head_chunks * int64_t(c.cap);
+  int64_t rpw = (rows + 512 * kFacWaves - 1) / (512 * kFacWaves);
+  rpw = (rpw + 3) & ~int64_t(3);
+  if (rpw < 32) rpw = 32;
+  if (rpw > 256) rpw = 256;
+  p.rows_per_wave = int(rpw);
+  const int per_wg = kFacWaves * p.rows_per_wave;
+  p.n_split = c.cap > 0 ? (c.cap + per_wg - 1) / per_wg : 1;
+  p.n_partials = p.n_split;
+  return p;
+}
+
 size_t fac_workspace_bytes(const Common& c, const FacPlan& p) {
   const size_t acc_sz = c.bf16 ? sizeof(float) : sizeof(double);
   const size_t slots = size_t(c.batch) * c.n_q_heads * p.n_partials;
@@ -506,6 +538,15 @@ hipError_t launch_fac(const Common& c, const FacPlan& p, const void* q, const vo
                         const_cast<int32_t*>(sel_count), out, ws, arrive);
   if (c.bf16) return launch_fac_t<uint16_t, float>(a, s);
   return launch_fac_t<float, double>(a, s);
+}
+
+hipError_t launch_dense(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table, const int32_t* seq_lens, float* out,
+                        void* ws, hipStream_t s) {
+  FacArgs a = make_args(c, p, q, k_pool, v_pool, block_table, nullptr, nullptr, out, ws, nullptr);
+  a.seq_lens = seq_lens;
+  if (c.bf16) return launch_dense_t<uint16_t, float>(a, s);
+  return launch_dense_t<float, double>(a, s);
 }
 
 hipError_t launch_fac_select(const Common& c, const FacPlan& p, const void* q, const void* k_pool,

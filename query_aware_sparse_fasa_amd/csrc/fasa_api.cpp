@@ -113,6 +113,18 @@ fasa::SelectBuffers select_buffers(void* workspace, const Layout& l) {
 }
 size_t decode_workspace(const Common& c, const FacPlan& p) { return layout(c, p).total; }
 
+// Full attention: every cached token is a row, so the FAC plan is made for
+// cap = max_t; the workspace holds the split partials only.
+Common dense_common(const fasa_shape* s, int32_t max_t) {
+  Common c = make_common(s, max_t);
+  c.cap = max_t;
+  return c;
+}
+size_t dense_workspace(const Common& c, const FacPlan& p) {
+  const size_t n = fasa::fac_workspace_bytes(c, p);
+  return n > 0 ? n : 256;
+}
+
 fasa_status hip_status(hipError_t e) { return e == hipSuccess ? FASA_OK : FASA_ERR_HIP; }
 
 // Largest block-table / slab / pool pointers are only checked for null and
@@ -290,6 +302,30 @@ fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_po
     return st;
   return hip_status(fasa::launch_fac(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out,
                                      w + l.fac, fac_arrive, stream));
+}
+
+fasa_status fasa_dense_workspace_size(const fasa_shape* shape, int32_t max_t, size_t* bytes) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
+  if (!bytes) return FASA_ERR_INVALID_ARG;
+  const Common c = dense_common(shape, max_t);
+  *bytes = dense_workspace(c, fasa::dense_plan(c));
+  return FASA_OK;
+}
+
+fasa_status fasa_dense_decode(const fasa_shape* shape, const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, const int32_t* seq_lens, int32_t max_t, float* out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out) return FASA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16)) return FASA_ERR_INVALID_ARG;
+  const Common c = dense_common(shape, max_t);
+  const FacPlan p = fasa::dense_plan(c);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < dense_workspace(c, p)) return FASA_ERR_WORKSPACE;
+  return hip_status(fasa::launch_dense(c, p, q, k_pool, v_pool, block_table, seq_lens, out, workspace, stream));
 }
 
 }  // extern "C"

@@ -58,6 +58,7 @@ struct FacPlan {
 };
 
 FacPlan fac_plan(const Common& c);
+FacPlan dense_plan(const Common& c);   // full attention: c.cap == max_t
 size_t fac_workspace_bytes(const Common& c, const FacPlan& p);
 size_t scores_bytes(const Common& c);
 
@@ -101,6 +102,12 @@ hipError_t launch_finish(const Common& c, const float* scores, const int32_t* se
 hipError_t launch_fac(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
                       const void* v_pool, const int32_t* block_table, const int32_t* sel_idx,
                       const int32_t* sel_count, float* out, void* ws, uint32_t* arrive, hipStream_t s);
+// Full attention over rows 0 .. t_b-1 of every sequence (no selection): the
+// split launch with row r = token r, then the merge launch.  c.cap must be
+// max_t and p = dense_plan(c); ws holds the partials (fac_workspace_bytes).
+hipError_t launch_dense(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table, const int32_t* seq_lens, float* out,
+                        void* ws, hipStream_t s);
 // Whether a decode step may use launch_fac_select (small budget, block-table
 // rows that fit in LDS).
 bool fac_selects(const Common& c, const FacPlan& p);

@@ -25,7 +25,8 @@ BLOCK = 256
 
 EXPORTS = ["fasa_status_str", "fasa_validate_shape", "fasa_selection_capacity",
            "fasa_workspace_size", "fasa_check_fc_idx", "fasa_slab_build", "fasa_slab_append",
-           "fasa_tip", "fasa_topk", "fasa_fac", "fasa_decode"]
+           "fasa_tip", "fasa_topk", "fasa_fac", "fasa_decode", "fasa_dense_workspace_size",
+           "fasa_dense_decode"]
 
 
 class fasa_shape(ctypes.Structure):
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
         "fasa_fac": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
         "fasa_decode": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _P]),
+        "fasa_dense_workspace_size": (ctypes.c_int, [_S, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+        "fasa_dense_decode": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -216,10 +219,32 @@ def fasa_decode(shape, q, k_pool, v_pool, slab, block_table, seq_lens, max_t, fc
            "fasa_decode")
 
 
+def fasa_dense_workspace_size(shape: fasa_shape, max_t: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().fasa_dense_workspace_size(ctypes.byref(shape), max_t, ctypes.byref(n)),
+           "fasa_dense_workspace_size")
+    return n.value
+
+
+def fasa_dense_decode(shape, q, k_pool, v_pool, block_table, seq_lens, max_t, out, workspace,
+                      stream=None) -> None:
+    _need(out, torch.float32, "out")
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fasa_dense_decode(ctypes.byref(shape), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                   _ptr(block_table), _ptr(seq_lens), max_t, _ptr(out), _ptr(workspace),
+                                   nbytes, _stream(stream)), "fasa_dense_decode")
+
+
 # --------------------------------------------------------------------------- buffers
 def alloc_slab(shape: fasa_shape, n_blocks: int, device="cuda") -> torch.Tensor:
     dt = torch.bfloat16 if shape.kv_dtype == FASA_BF16 else torch.float32
     return torch.empty(n_blocks, shape.n_kv_heads, shape.n_fc, BLOCK, 2, dtype=dt, device=device)
+
+
+def alloc_dense_workspace(shape: fasa_shape, max_t: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(fasa_dense_workspace_size(shape, max_t), 256), dtype=torch.uint8, device=device)
 
 
 def alloc_workspace(shape: fasa_shape, max_t: int, device="cuda") -> torch.Tensor:

@@ -65,6 +65,14 @@ class DeviceLayer:
                          self.block_table, self.seq_lens, self.max_t, self.fc_idx, self.out,
                          self.sel_idx, self.sel_count, self.workspace, stream)
 
+    def dense(self, out=None, stream=None):
+        """Full attention over every cached token (into out, default self.dense_out)."""
+        if getattr(self, "dense_ws", None) is None:
+            self.dense_ws = fasa.alloc_dense_workspace(self.shape, self.max_t, device=self.q.device)
+            self.dense_out = torch.zeros_like(self.out)
+        fasa.fasa_dense_decode(self.shape, self.q, self.k_pool, self.v_pool, self.block_table, self.seq_lens,
+                               self.max_t, self.dense_out if out is None else out, self.dense_ws, stream)
+
     # -- host copies ----------------------------------------------------------------
     def selection(self, b: int, g: int) -> np.ndarray:
         n = int(self.sel_count[b, g].item())

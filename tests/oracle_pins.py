@@ -255,6 +255,44 @@ def pin_paged_rows(O):
             np.testing.assert_array_equal(rows[:, 2], np.arange(t))
 
 
+def pin_dense_is_library_attention(O):
+    """Dense decode over a paged cache (permuted block table, ragged lengths
+    including 0 and 1) equals torch's scaled_dot_product_attention in fp64 on
+    the logical rows, head by head of each group; t = 0 gives zeros."""
+    rng = np.random.default_rng(21)
+    lens = [300, 0, 1, 513]
+    H, G = 2, 3
+    nblk = [(t + 255) // 256 for t in lens]
+    perm = rng.permutation(sum(nblk))
+    kp = np.full((sum(nblk) + 1, H, 256, D), np.nan)
+    vp = np.full_like(kp, np.nan)
+    table = np.full((len(lens), max(max(nblk), 1)), sum(nblk), dtype=np.int32)
+    q = rng.standard_normal((len(lens), H * G, D)) * 1.5
+    rows = {}
+    o = 0
+    for b, t in enumerate(lens):
+        table[b, :nblk[b]] = perm[o:o + nblk[b]]
+        o += nblk[b]
+        for g in range(H):
+            K = rng.standard_normal((t, D)) * 1.5
+            V = rng.standard_normal((t, D))
+            rows[(b, g)] = (K, V)
+            for j in range(t):
+                kp[table[b, j // 256], g, j % 256] = K[j]
+                vp[table[b, j // 256], g, j % 256] = V[j]
+    res = O.dense_decode(q, kp, vp, table, np.array(lens))
+    for (b, g), (K, V) in rows.items():
+        t = lens[b]
+        qg = q[b, g * G:(g + 1) * G]
+        if t == 0:
+            np.testing.assert_array_equal(res[(b, g)], 0.0)
+            continue
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(qg)[None, :, None, :], torch.from_numpy(K)[None, None].expand(1, G, t, D),
+            torch.from_numpy(V)[None, None].expand(1, G, t, D))[0, :, 0, :].numpy()
+        np.testing.assert_allclose(res[(b, g)], ref, rtol=1e-12, atol=1e-12)
+
+
 def pin_slab(O):
     """The dominant-key cache holds exactly the FC pairs of every key."""
     K = np.arange(5 * D, dtype=np.float64).reshape(5, D)
@@ -268,7 +306,8 @@ def pin_slab(O):
 ALL_PINS = [pin_tip_closed_form, pin_tip_relative_form, pin_tip_all_fc_is_full_dot,
             pin_tip_reads_only_dominant, pin_topb_full_sort, pin_topb_exhaustive,
             pin_topb_signed_and_zero, pin_forced_union, pin_fac_is_library_attention,
-            pin_fac_special_cases, pin_fac_duplicate_keys_tie, pin_paged_rows, pin_slab]
+            pin_fac_special_cases, pin_fac_duplicate_keys_tie, pin_paged_rows, pin_slab,
+            pin_dense_is_library_attention]
 
 
 def golden():

@@ -23,7 +23,7 @@ def header_functions():
 def test_exports_every_declared_symbol():
     L = fasa.lib()
     names = header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(fasa.EXPORTS) == names
@@ -139,6 +139,15 @@ def test_entry_points_reject_before_launch():
     assert raw("fasa_decode", *args, FAKE, ws - 1, None) == W
     assert raw("fasa_decode", *args, FAKE + 16, ws, None) == W
     assert raw("fasa_fac", sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, 1024, None) == W
+    # dense decode: null pointers, max_t, workspace
+    dws = fasa.fasa_dense_workspace_size(s, 4096)
+    assert raw("fasa_dense_decode", sp, FAKE, FAKE, FAKE, FAKE, None, 4096, FAKE, FAKE, dws, None) == E
+    assert raw("fasa_dense_decode", sp, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, None, FAKE, dws, None) == E
+    assert raw("fasa_dense_decode", sp, FAKE + 2, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, dws, None) == E
+    assert raw("fasa_dense_decode", sp, FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, FAKE, dws, None) == E
+    assert raw("fasa_dense_decode", sp, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, dws - 1, None) == W
+    assert raw("fasa_dense_decode", sp, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, None, dws, None) == W
+    assert raw("fasa_dense_decode", sp, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE + 16, dws, None) == W
     # sel_idx may be NULL only when the capacity is 0
     assert raw("fasa_topk", sp, FAKE, FAKE, 4096, None, FAKE, None, 0, None) == E
     # bad shape propagates
@@ -155,6 +164,9 @@ def test_workspace_grows_with_context_and_batch():
     assert b > a and c > a
     f32 = fasa.fasa_workspace_size(good(kv_dtype=torch.float32), 4096)
     assert f32 > a     # fp64 partials for fp32 caches
+    d1 = fasa.fasa_dense_workspace_size(good(), 4096)
+    d2 = fasa.fasa_dense_workspace_size(good(kv_dtype=torch.float32), 4096)
+    assert d2 > d1 > 0  # fp64 partials for fp32 caches
 
 
 def test_binding_refuses_host_tensors():

@@ -313,6 +313,60 @@ def test_all_fcs_and_full_budget_is_dense_attention():
             assert np.abs(out[b, g * G:(g + 1) * G] - ref).max() <= 2e-3
 
 
+# ------------------------------------------------------------------------ dense decode
+def _dense_ref(inp, b, g):
+    """The oracle's dense decode of one unit: its rows copied into a one-head
+    pool in logical order, read through an identity block table."""
+    G = inp.cfg.group
+    q = inp.q[b, g * G:(g + 1) * G].double().cpu().numpy()[None]
+    K = unit_rows(inp, b, g, inp.k_pool).double().cpu().numpy()
+    V = unit_rows(inp, b, g, inp.v_pool).double().cpu().numpy()
+    t = K.shape[0]
+    nblk = max((t + 255) // 256, 1)
+    kp = np.zeros((nblk * 256, 128))
+    vp = np.zeros((nblk * 256, 128))
+    kp[:t], vp[:t] = K, V
+    table = np.arange(nblk, dtype=np.int32)[None]
+    return O.dense_decode(q, kp.reshape(nblk, 1, 256, 128), vp.reshape(nblk, 1, 256, 128), table,
+                          np.array([t]))[(0, 0)]
+
+
+def _check_dense(inp, L, units, label):
+    """fasa_dense_decode against the oracle's full attention, unit by unit."""
+    cfg = inp.cfg
+    torch.cuda.synchronize()
+    out = L.dense_out.cpu().numpy()
+    G = cfg.group
+    for b, g in sorted(units):
+        err = np.abs(out[b, g * G:(g + 1) * G] - _dense_ref(inp, b, g)).max()
+        assert err <= PR.OUT_ATOL[cfg.dtype], f"{label} b={b} g={g}: {err:.3e}"
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_dense_decode(name):
+    say(f"[dense] {name}")
+    inp, L = layer_for(name)
+    L.dense()
+    L.dense_out.fill_(float("nan"))
+    L.dense()
+    units = [(b, g) for b in range(inp.cfg.batch) for g in range(inp.cfg.n_kv_heads)]
+    if len(units) > 64:
+        units = units[::len(units) // 48]
+    _check_dense(inp, L, units, name)
+
+
+def test_dense_decode_edge_lengths():
+    """t = 0 gives zeros; 1, 255, 256, 257 tokens cross the block edges."""
+    cfg = C["c5"].replace(batch=6)
+    say("[dense edge lengths]")
+    inp = synth.make_inputs(cfg, seed=11, seq_lens=[0, 1, 255, 256, 257, 1100])
+    L = DeviceLayer(inp, with_slab=False)
+    L.dense()
+    torch.cuda.synchronize()
+    assert (L.dense_out[0] == 0).all()
+    _check_dense(inp, L, [(b, g) for b in range(1, 6) for g in range(cfg.n_kv_heads)], "dense edge")
+
+
 def test_empty_and_tiny_sequences():
     cfg = C["c5"].replace(batch=5, budget=16, n_sink=4, n_recent=8)
     say("[edge lengths]")
@@ -376,5 +430,8 @@ def test_full_size_configs(key):
         pick = [(int(order[0]), 0), (int(order[-1]), 7), (int(order[len(order) // 2]), 3)]
     units = oracle_units(inp, set(pick) if pick else None)
     _check_decode(inp, L, units, key)
+    say(f"[full dense] {key}")
+    L.dense()
+    _check_dense(inp, L, list(units), key + " dense")
     del L, inp
     torch.cuda.empty_cache()

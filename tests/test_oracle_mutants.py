@@ -61,6 +61,12 @@ MUTANTS = [
     ("rows_wrong_block",
      "out[j0:j0 + n] = pool[int(block_table_row[j0 // BLOCK]), g, :n, :]",
      "out[j0:j0 + n] = pool[int(block_table_row[0]), g, :n, :]"),
+    ("dense_wrong_group_slice",
+     "res[(b, g)] = fac(q[b, g * G:(g + 1) * G], K, V, scale)[0]",
+     "res[(b, g)] = fac(q[b, g:g + G], K, V, scale)[0]"),
+    ("dense_drops_last_token",
+     "        res[(b, g)] = fac(q[b, g * G:(g + 1) * G], K, V, scale)[0]",
+     "        res[(b, g)] = fac(q[b, g * G:(g + 1) * G], K[:-1], V[:-1], scale)[0]"),
     ("slab_swapped_pair",
      "out[f, :, 0] = K[:, 2 * fc[f]]",
      "out[f, :, 0] = K[:, 2 * fc[f] + 1]"),
