@@ -206,7 +206,7 @@ __device__ __forceinline__ void unit_range(const Common& c, int t_raw, int& t, i
 // w + p * waves (loaded early by the caller, unconditionally).  Returns the
 // number of kept pairs, or -1 when they do not fit (then nothing is gathered).
 template <int NTH, int PRE>
-__device__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off, const uint2* slots, int nfc, int cap_lds,
+__device__ __forceinline__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off, const uint2* slots, int nfc, int cap_lds,
                            const int (&cnt_raw)[CPT], const uint2 (&pre)[PRE], uint32_t* key, int32_t* idx,
                            int b1, uint32_t& above) {
   constexpr int NW = NTH / 64;
@@ -277,7 +277,7 @@ __device__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off, const uint2* sl
 // the remaining digits are skipped and one scan places every key at or above
 // the prefix.
 template <int NTH>
-__device__ void lds_select(SelState<NTH>& s, const uint32_t* key, const int32_t* idx, int N, int Bc, int b1,
+__device__ __forceinline__ void lds_select(SelState<NTH>& s, const uint32_t* key, const int32_t* idx, int N, int Bc, int b1,
                            uint32_t above, int32_t* out) {
   const int tid = threadIdx.x;
   const int per = (N + NTH - 1) / NTH;
@@ -363,7 +363,7 @@ __device__ void lds_select(SelState<NTH>& s, const uint32_t* key, const int32_t*
 // Bc-th largest key.
 // lim: readable elements of the row (see load_steps); the tokens are [0, max_t).
 template <int NTH, bool VEC>
-__device__ void row_select(SelState<NTH>& s, const float* row, int lim, int max_t, int c_lo, int c_hi, int Bc,
+__device__ __forceinline__ void row_select(SelState<NTH>& s, const float* row, int lim, int max_t, int c_lo, int c_hi, int Bc,
                            int32_t* out) {
   constexpr int TILE = NTH * KPT;
   const int tid = threadIdx.x;
