@@ -58,9 +58,11 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
   const int64_t phys_raw = a.block_table[int64_t(b) * c.max_blocks + min(blk, c.max_blocks - 1)];
   const int col = 2 * a.fc_idx[g * F + f_q] + comp;
   const int t = clamp_len(t_raw, c.max_t, c.max_blocks);
-  // No early exit before the barrier: a workgroup past the end of a short
-  // sequence still folds the query and then leaves (an early return here would
-  // make every load wait for the sequence length first).
+  // A workgroup whose four blocks all lie past the end of a short sequence has
+  // nothing to do (the whole workgroup leaves together, before any barrier).
+  // The slab loads need the length and the block-table entry anyway, so this
+  // adds no wait for the others.
+  if (blockIdx.x * 4 * kBlock >= t) return;
 
   __shared__ float qf[kHeadDim];   // folded query, [f][2]
   __shared__ int cols[kHeadDim / 2];
