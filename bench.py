@@ -14,8 +14,9 @@ timed with HIP events on the launch stream.
 Printed: one JSON line with steps/s (value), the achieved HBM bandwidth of the
 step's algorithmic bytes, the roofline of the dominant kernel (TIP, timed on
 its own in the same way), the dense decode (full attention over every cached
-token, the decode FASA replaces) timed on the same layers, and the fp64 CPU
-oracle timed on the host cores.
+token, the decode FASA replaces) timed on the same layers, the FASA-M step
+(non-dominant keys and values in pinned host memory) on two of them, and the
+fp64 CPU oracle timed on the host cores.
 Progress goes to stderr.
 """
 from __future__ import annotations
@@ -128,6 +129,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-slab", action="store_true", help="TIP gathers from the key rows instead")
+    ap.add_argument("--no-fasa-m", action="store_true", help="skip the FASA-M (host-offloaded) timing")
     ap.add_argument("--mode", choices=["step", "tip"], default="step",
                     help="step: the benchmark; tip: only --steps TIP launches and one 1 GiB "
                          "reference copy (for hardware-counter runs)")
@@ -249,6 +251,39 @@ def main():
     log(f"[bench] dense decode {t_dense * 1e6:.2f} us ({dense_gbps:,.0f} GB/s); "
         f"FASA step is {t_dense / (el / args.steps):.2f}x faster")
 
+    # FASA-M: the same step with the non-dominant key columns and the values in
+    # pinned host memory (two layer copies; the host arrays are per layer).
+    fasa_m = None
+    m_host = sum(fasa.fasa_m_host_sizes(base.shape, inp.n_blocks))
+    if use_slab and not args.no_fasa_m and m_host > 4 << 30:
+        fasa_m = {"skipped": f"host arrays of {m_host / 2**30:.1f} GiB per layer exceed the 4 GiB this run pins"}
+    elif use_slab and not args.no_fasa_m:
+        m_layers = layers[:max(1, min(L, (4 << 30) // m_host, 2))]
+        for lay in m_layers:
+            lay.m_setup()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for lay in m_layers:
+                lay.m_decode()
+        torch.cuda.synchronize()
+        g_m = graph_of(torch, stream, [lambda l=l: l.m_decode() for l in m_layers])
+        mreps = max(1, 200 // len(m_layers))
+        t_m = time_graph(torch, stream, [g_m], mreps) / (mreps * len(m_layers))
+        e = cfg.elem_bytes
+        nd = fasa.fasa_m_host_sizes(base.shape, 1)[0] // (e * cfg.n_kv_heads * 256)
+        sel_rows = sb["rows"] // (2 * 128 * e)
+        host_bytes = sel_rows * (nd + 128) * e
+        t_all = int(inp.seq_lens.sum())
+        gpu_m = t_all * cfg.n_kv_heads * 2 * cfg.n_fc * e + sel_rows * 2 * 128 * e   # slab + staged rows
+        gpu_fkv = t_all * cfg.n_kv_heads * 2 * 128 * e
+        fasa_m = {"us_per_step": t_m * 1e6, "host_bytes_per_step": int(host_bytes),
+                  "host_GBps": host_bytes / t_m / 1e9, "gpu_cache_bytes": int(gpu_m),
+                  "fkv_cache_bytes": int(gpu_fkv), "gpu_memory_reduction": gpu_fkv / gpu_m,
+                  "layers_rotated": len(m_layers)}
+        log(f"[bench] FASA-M step {t_m * 1e6:.2f} us ({host_bytes / 1e6:.2f} MB from host, "
+            f"{host_bytes / t_m / 1e9:.1f} GB/s); GPU cache {gpu_m / 1e6:.1f} MB vs {gpu_fkv / 1e6:.1f} MB full "
+            f"({gpu_fkv / gpu_m:.2f}x less)")
+
     tip_bytes = sb["slab"] if use_slab else int(inp.seq_lens.sum()) * cfg.n_kv_heads * 128 * cfg.elem_bytes
     tip_gbps = tip_bytes / t_tip / 1e9
     step_gbps = per_layer_touch * steps_per_s / 1e9
@@ -293,6 +328,7 @@ def main():
         "dense_decode": {"us_per_step": t_dense * 1e6, "bytes": int(sb["dense"]), "achieved_GBps": dense_gbps,
                          "hbm_frac": dense_gbps / HBM_PEAK_GBPS,
                          "fasa_speedup": t_dense / (el / args.steps)},
+        "fasa_m": fasa_m,
         "cpu_baseline": cpu,
         "pages_context": "the pages report 2.56x decode speedup over full-KV FlashAttention using 18.9% "
                          "of the cache (hardware not stated); context only",

@@ -178,6 +178,50 @@ fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_po
                         float* out, int32_t* sel_idx, int32_t* sel_count,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- FASA-M: the memory-optimised placement (section 3.4, "Hardware-Aware
+ * Variants", FASA-M and Equation 10).  The GPU keeps only the dominant-key
+ * cache (the slab) and per-step buffers; the non-dominant key columns and all
+ * value rows live in pinned host memory, which the GPU reads directly after
+ * the selection.  Host arrays (element type = the cache type), indexed by the
+ * pool's physical block like the pool and the slab:
+ *   k_nd [block][n_kv_heads][256][nd]: the 128 - 2*n_fc non-dominant key
+ *        columns of every token, ascending, each row zero-padded to nd
+ *        elements, nd = (128 - 2*n_fc) rounded up to a multiple of 16 bytes;
+ *   v    [block][n_kv_heads][256][128]: the value rows.
+ * Both must be page-locked host memory known to the HIP runtime (hipHostMalloc,
+ * or a pinned torch tensor) and 16-byte aligned; anything else is
+ * FASA_ERR_INVALID_ARG.  The caller owns them. */
+
+/* Bytes of the two host arrays for a pool of n_blocks physical blocks. */
+fasa_status fasa_m_host_sizes(const fasa_shape* shape, int64_t n_blocks, size_t* k_nd_bytes,
+                              size_t* v_bytes);
+
+/* Copy blocks 0 .. ceil(t_b/256)-1 of every sequence from the device pools
+ * (post-RoPE keys, values) into the host arrays: the offload after prefill.
+ * Whole blocks are copied; blocks past a sequence's end are left untouched.
+ * The slab (fasa_slab_build) holds the dominant columns. */
+fasa_status fasa_m_offload(const fasa_shape* shape, const void* k_pool, const void* v_pool,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           const int32_t* fc_idx, void* k_nd_host, void* v_host,
+                           hipStream_t stream);
+
+/* Workspace of fasa_m_decode: fasa_workspace_size's layout plus two staging
+ * arrays of batch * n_kv_heads * cap rows of 128 elements (K and V). */
+fasa_status fasa_m_workspace_size(const fasa_shape* shape, int32_t max_t, size_t* bytes);
+
+/* One FASA-M decode step: TIP on the slab, the exact top-B (sel_idx and
+ * sel_count are outputs, as in fasa_decode), then the selected rows' key
+ * (non-dominant columns from k_nd, dominant pairs from the slab) and value
+ * rows are rebuilt into the workspace's staging arrays, and FAC runs over
+ * them.  Same selection and the same FAC arithmetic as fasa_decode, so the
+ * same results up to the order of the softmax sums; the device never reads
+ * the full-cache K/V pools. */
+fasa_status fasa_m_decode(const fasa_shape* shape, const void* q, const void* slab,
+                          const void* k_nd_host, const void* v_host, const int32_t* block_table,
+                          const int32_t* seq_lens, int32_t max_t, const int32_t* fc_idx,
+                          float* out, int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace that fasa_dense_decode needs for contexts up to max_t:
  * the split partials, about 4 * (128 + 2) bytes per query head per 512 tokens
  * of max_t (fp32 caches: twice that).  256-byte aligned; contents are

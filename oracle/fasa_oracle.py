@@ -185,6 +185,28 @@ def decode(q, k_pool, v_pool, block_table, seq_lens, fc_idx, budget,
 
 
 # ---------------------------------------------------------------------------
+# FASA-M: the host-resident part of the keys
+# ---------------------------------------------------------------------------
+def nondominant_rows(K: np.ndarray, fc: np.ndarray) -> np.ndarray:
+    """C_key^nondom of one unit: the key columns outside the dominant FC pairs,
+    in ascending column order, [t][d - 2F].
+
+    FASA-M keeps only the dominant dimensions of past keys on the GPU and
+    offloads the remaining key dimensions, with all values, to host memory
+    (review section 3.4, "Hardware-Aware Variants", FASA-M's three-way split of
+    the cache).  Together with slab_rows they hold every key column once.
+    """
+    K = np.asarray(K)
+    d = K.shape[1]
+    dominant = set()
+    for i in np.asarray(fc).tolist():
+        dominant.add(2 * int(i))
+        dominant.add(2 * int(i) + 1)
+    keep = [c for c in range(d) if c not in dominant]
+    return K[:, keep]
+
+
+# ---------------------------------------------------------------------------
 # dense decode: the full-KV attention that FASA replaces
 # ---------------------------------------------------------------------------
 def dense_decode(q, k_pool, v_pool, block_table, seq_lens, scale=None, units=None):

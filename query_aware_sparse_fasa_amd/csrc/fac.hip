@@ -150,10 +150,17 @@ __device__ __forceinline__ void store_partial(const FacArgs& a, const W& w, Wave
 // MERGE: the last workgroup of a (sequence, kv head, head chunk) to finish --
 // counted on an arrival counter -- merges the partials of its heads, so no
 // second launch is needed (used when n_split <= kFacMergeMax).
-// DENSE: no selection -- row r is token r, for every r < t_b (full attention
-// over the whole cache; sel_idx and sel_count are not read).
-template <typename T, typename Acc, int HG, bool MERGE, bool DENSE = false>
+// ROWS picks where row r of a unit comes from:
+//   kSelRows:    token sel_idx[unit][r] of the paged pool, r < sel_count[unit];
+//   kDenseRows:  token r of the paged pool, every r < t_b (full attention; the
+//                selection is not read);
+//   kStagedRows: row r of the unit's contiguous staging area, rows
+//                [unit * cap, unit * cap + sel_count[unit]) of k_pool / v_pool
+//                (selected rows already gathered there).
+enum { kSelRows = 0, kDenseRows = 1, kStagedRows = 2 };
+template <typename T, typename Acc, int HG, bool MERGE, int ROWS = kSelRows>
 __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
+  constexpr bool DENSE = ROWS == kDenseRows;
   const Common& c = a.c;
   const FacPlan& p = a.p;
   const int b = blockIdx.z;
@@ -172,20 +179,25 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   // indices -- validity is applied afterwards -- so nothing serialises them.
   int count = DENSE ? clamp_len(a.seq_lens[b], c.max_t, c.max_blocks) : a.sel_count[unit];
   const int cap1 = c.cap > 0 ? c.cap - 1 : 0;
-  const int j_first = (!DENSE && c.cap > 0) ? sel[min(r0 + lane, cap1)] : -1;
+  const int j_first = (ROWS == kSelRows && c.cap > 0) ? sel[min(r0 + lane, cap1)] : -1;
   FacWave<T, Acc, HG> w;
   w.init(static_cast<const T*>(a.q) + (int64_t(b) * c.n_q_heads + g * c.group + h0) * kHeadDim, nh,
          c.scale);
   count = count < 0 ? 0 : (count > c.cap ? c.cap : count);   // contents are preconditions; stay in bounds
   const int r1 = min(r0 + p.rows_per_wave, count);
   auto lane_offset = [&](int r) -> int64_t {
-    const int j = DENSE ? r : ((r - lane == r0) ? j_first : sel[min(r, cap1)]);
-    const bool ok = r < r1 && j >= 0 && j < c.max_blocks * kBlock;
-    const int64_t pb = btab[ok ? (j >> 8) : 0];
-    return ok ? pb * c.kv_block_stride + int64_t(j & (kBlock - 1)) * kHeadDim : -1;
+    if constexpr (ROWS == kStagedRows) {
+      return r < r1 ? (unit * c.cap + r) * int64_t(kHeadDim) : -1;
+    } else {
+      const int j = DENSE ? r : ((r - lane == r0) ? j_first : sel[min(r, cap1)]);
+      const bool ok = r < r1 && j >= 0 && j < c.max_blocks * kBlock;
+      const int64_t pb = btab[ok ? (j >> 8) : 0];
+      return ok ? pb * c.kv_block_stride + int64_t(j & (kBlock - 1)) * kHeadDim : -1;
+    }
   };
-  const T* kbase = static_cast<const T*>(a.k_pool) + int64_t(g) * c.kv_head_stride;
-  const T* vbase = static_cast<const T*>(a.v_pool) + int64_t(g) * c.kv_head_stride;
+  const int64_t head_off = ROWS == kStagedRows ? 0 : int64_t(g) * c.kv_head_stride;
+  const T* kbase = static_cast<const T*>(a.k_pool) + head_off;
+  const T* vbase = static_cast<const T*>(a.v_pool) + head_off;
   // Row quads of loads in flight per wave: as many as the registers allow at
   // two waves per SIMD (about 64 KB in flight per CU hides HBM latency).
   constexpr int U = (sizeof(Acc) == 4 && HG <= 4) ? 8 : (HG <= 2 ? 4 : (HG <= 4 || sizeof(Acc) == 4 ? 2 : 1));
@@ -399,13 +411,13 @@ __global__ __launch_bounds__(kHeadDim) void fac_merge_kernel(FacArgs a) {
   a.out[(int64_t(b) * a.c.n_q_heads + h) * kHeadDim + d] = res;
 }
 
-template <typename T, typename Acc, bool MERGE, bool DENSE = false>
+template <typename T, typename Acc, bool MERGE, int ROWS = kSelRows>
 void launch_split(const FacArgs& a, const dim3& grid, hipStream_t s) {
   switch (a.p.heads_per_pass) {
-    case 1: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 1, MERGE, DENSE>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 2, MERGE, DENSE>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 4, MERGE, DENSE>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 8, MERGE, DENSE>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 1, MERGE, ROWS>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 2, MERGE, ROWS>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 4, MERGE, ROWS>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 8, MERGE, ROWS>), grid, dim3(256), 0, s, a); break;
   }
 }
 
@@ -414,23 +426,23 @@ template <typename T, typename Acc>
 hipError_t launch_dense_t(const FacArgs& a, hipStream_t s) {
   const FacPlan& p = a.p;
   const dim3 grid(p.n_split, a.c.n_kv_heads * p.head_chunks, a.c.batch);
-  launch_split<T, Acc, false, true>(a, grid, s);
+  launch_split<T, Acc, false, kDenseRows>(a, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fac_merge_kernel<Acc>, dim3(a.c.n_q_heads, a.c.batch), dim3(kHeadDim), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename T, typename Acc>
+template <typename T, typename Acc, int ROWS = kSelRows>
 hipError_t launch_fac_t(FacArgs& a, hipStream_t s) {
   const FacPlan& p = a.p;
   const dim3 grid(p.n_split, a.c.n_kv_heads * p.head_chunks, a.c.batch);
   const int64_t n_wg = int64_t(grid.x) * grid.y * grid.z;
   if (a.arrive != nullptr && p.n_split <= kFacMergeMax && n_wg <= kFacMergeGrid) {
-    launch_split<T, Acc, true>(a, grid, s);
+    launch_split<T, Acc, true, ROWS>(a, grid, s);
     return hipGetLastError();
   }
-  launch_split<T, Acc, false>(a, grid, s);
+  launch_split<T, Acc, false, ROWS>(a, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fac_merge_kernel<Acc>, dim3(a.c.n_q_heads, a.c.batch), dim3(kHeadDim), 0, s, a);
@@ -538,6 +550,15 @@ hipError_t launch_fac(const Common& c, const FacPlan& p, const void* q, const vo
                         const_cast<int32_t*>(sel_count), out, ws, arrive);
   if (c.bf16) return launch_fac_t<uint16_t, float>(a, s);
   return launch_fac_t<float, double>(a, s);
+}
+
+hipError_t launch_fac_staged(const Common& c, const FacPlan& p, const void* q, const void* stage_k,
+                             const void* stage_v, const int32_t* sel_count, float* out, void* ws, uint32_t* arrive,
+                             hipStream_t s) {
+  FacArgs a = make_args(c, p, q, stage_k, stage_v, nullptr, nullptr, const_cast<int32_t*>(sel_count), out, ws,
+                        arrive);
+  if (c.bf16) return launch_fac_t<uint16_t, float, kStagedRows>(a, s);
+  return launch_fac_t<float, double, kStagedRows>(a, s);
 }
 
 hipError_t launch_dense(const Common& c, const FacPlan& p, const void* q, const void* k_pool,

@@ -127,6 +127,48 @@ size_t dense_workspace(const Common& c, const FacPlan& p) {
 
 fasa_status hip_status(hipError_t e) { return e == hipSuccess ? FASA_OK : FASA_ERR_HIP; }
 
+// FASA-M: the decode workspace followed by the two staging arrays
+// [b][H_kv][cap][128] (K, then V).
+struct MLayout {
+  Layout d;
+  size_t stage_k, stage_v, total;
+};
+MLayout m_layout(const Common& c, const FacPlan& p) {
+  MLayout m;
+  m.d = layout(c, p);
+  const size_t e = c.bf16 ? 2 : 4;
+  const size_t st = align256(size_t(c.batch) * c.n_kv_heads * size_t(c.cap) * fasa::kHeadDim * e);
+  m.stage_k = m.d.total;
+  m.stage_v = m.stage_k + st;
+  m.total = m.stage_v + st;
+  return m;
+}
+
+// Host arrays of FASA-M (element counts, for n_blocks physical blocks).
+int64_t m_knd_elems(const fasa_shape* s, int64_t n_blocks) {
+  const Common c = make_common(s, 0);
+  return n_blocks * s->n_kv_heads * int64_t(fasa::kBlock) * fasa::m_nd_stride(c);
+}
+int64_t m_v_elems(const fasa_shape* s, int64_t n_blocks) {
+  return n_blocks * s->n_kv_heads * int64_t(fasa::kBlock) * fasa::kHeadDim;
+}
+
+// The device-visible address of pinned host memory, or nullptr when ptr is not
+// page-locked host memory known to the HIP runtime.
+void* host_alias(const void* ptr) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, ptr) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (at.type != hipMemoryTypeHost) return nullptr;
+  if (at.devicePointer == nullptr) return const_cast<void*>(ptr);
+  // The attributes describe the allocation that holds ptr: keep ptr's offset.
+  if (at.hostPointer != nullptr)
+    return static_cast<char*>(at.devicePointer) + (static_cast<const char*>(ptr) - static_cast<char*>(at.hostPointer));
+  return at.devicePointer;
+}
+
 // Largest block-table / slab / pool pointers are only checked for null and
 // alignment; their extents are preconditions.
 size_t elem_align(const fasa_shape*) { return 16; }   // 16-byte vector loads
@@ -302,6 +344,86 @@ fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_po
     return st;
   return hip_status(fasa::launch_fac(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out,
                                      w + l.fac, fac_arrive, stream));
+}
+
+fasa_status fasa_m_host_sizes(const fasa_shape* shape, int64_t n_blocks, size_t* k_nd_bytes, size_t* v_bytes) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if (n_blocks < 1 || !k_nd_bytes || !v_bytes) return FASA_ERR_INVALID_ARG;
+  const size_t e = shape->kv_dtype == FASA_BF16 ? 2 : 4;
+  *k_nd_bytes = size_t(m_knd_elems(shape, n_blocks)) * e;
+  *v_bytes = size_t(m_v_elems(shape, n_blocks)) * e;
+  return FASA_OK;
+}
+
+fasa_status fasa_m_offload(const fasa_shape* shape, const void* k_pool, const void* v_pool,
+                           const int32_t* block_table, const int32_t* seq_lens, const int32_t* fc_idx,
+                           void* k_nd_host, void* v_host, hipStream_t stream) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if (!k_pool || !v_pool || !block_table || !seq_lens || !fc_idx || !k_nd_host || !v_host)
+    return FASA_ERR_INVALID_ARG;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_nd_host, 16) || !aligned(v_host, 16))
+    return FASA_ERR_INVALID_ARG;
+  void* knd = host_alias(k_nd_host);
+  void* vh = host_alias(v_host);
+  if (!knd || !vh) return FASA_ERR_INVALID_ARG;
+  const Common c = make_common(shape, shape->max_blocks_per_seq * fasa::kBlock);
+  return hip_status(fasa::launch_m_offload(c, k_pool, v_pool, block_table, seq_lens, fc_idx, knd, vh, stream));
+}
+
+fasa_status fasa_m_workspace_size(const fasa_shape* shape, int32_t max_t, size_t* bytes) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
+  if (!bytes) return FASA_ERR_INVALID_ARG;
+  const Common c = make_common(shape, max_t);
+  *bytes = m_layout(c, fasa::fac_plan(c)).total;
+  return FASA_OK;
+}
+
+fasa_status fasa_m_decode(const fasa_shape* shape, const void* q, const void* slab, const void* k_nd_host,
+                          const void* v_host, const int32_t* block_table, const int32_t* seq_lens, int32_t max_t,
+                          const int32_t* fc_idx, float* out, int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
+  if (!q || !slab || !k_nd_host || !v_host || !block_table || !seq_lens || !fc_idx || !out || !sel_count)
+    return FASA_ERR_INVALID_ARG;
+  if (!sel_idx && capacity(shape, max_t) > 0) return FASA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(slab, 16) || !aligned(k_nd_host, 16) || !aligned(v_host, 16))
+    return FASA_ERR_INVALID_ARG;
+  const void* knd = host_alias(k_nd_host);
+  const void* vh = host_alias(v_host);
+  if (!knd || !vh) return FASA_ERR_INVALID_ARG;
+  Common c = make_common(shape, max_t);
+  c.score_stride = (max_t + 3) & ~3;
+  const FacPlan p = fasa::fac_plan(c);
+  const MLayout m = m_layout(c, p);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < m.total) return FASA_ERR_WORKSPACE;
+  // TIP on the slab -> filter -> exact select (the list is needed to gather)
+  // -> rows from the host into staging -> FAC over the staged rows.
+  char* w = static_cast<char*>(workspace);
+  const fasa::SelectBuffers sb = select_buffers(workspace, m.d);
+  float* scores = reinterpret_cast<float*>(w + m.d.scores);
+  uint32_t* fac_arrive = reinterpret_cast<uint32_t*>(w + m.d.fac_arrive);
+  if (max_t > 0) {
+    if ((st = hip_status(fasa::launch_tip(c, q, slab, nullptr, block_table, seq_lens, fc_idx, scores, sb.hist,
+                                          stream))) != FASA_OK)
+      return st;
+  }
+  if ((st = hip_status(fasa::launch_filter(c, scores, seq_lens, sb, true, fac_arrive, p.head_chunks, stream))) !=
+      FASA_OK)
+    return st;
+  if ((st = hip_status(fasa::launch_finish(c, scores, seq_lens, sel_idx, sel_count, sb, fac_arrive, p.head_chunks,
+                                           stream))) != FASA_OK)
+    return st;
+  if ((st = hip_status(fasa::launch_m_gather(c, knd, vh, slab, block_table, fc_idx, sel_idx, sel_count,
+                                             w + m.stage_k, w + m.stage_v, stream))) != FASA_OK)
+    return st;
+  return hip_status(fasa::launch_fac_staged(c, p, q, w + m.stage_k, w + m.stage_v, sel_count, out, w + m.d.fac,
+                                            fac_arrive, stream));
 }
 
 fasa_status fasa_dense_workspace_size(const fasa_shape* shape, int32_t max_t, size_t* bytes) {

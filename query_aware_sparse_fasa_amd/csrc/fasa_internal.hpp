@@ -108,6 +108,25 @@ hipError_t launch_fac(const Common& c, const FacPlan& p, const void* q, const vo
 hipError_t launch_dense(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
                         const void* v_pool, const int32_t* block_table, const int32_t* seq_lens, float* out,
                         void* ws, hipStream_t s);
+// FAC over rows staged contiguously per unit: row r of unit u at
+// stage_k / stage_v + (u * c.cap + r) * 128, for r < sel_count[u].
+hipError_t launch_fac_staged(const Common& c, const FacPlan& p, const void* q, const void* stage_k,
+                             const void* stage_v, const int32_t* sel_count, float* out, void* ws, uint32_t* arrive,
+                             hipStream_t s);
+
+// FASA-M (fasam.hip): host-resident non-dominant key columns and values.
+// Elements per row of the host non-dominant key array (128 - 2F, padded to 16 bytes).
+int m_nd_stride(const Common& c);
+// Copy tokens' blocks [0, ceil(t_b / 256)) of the device pools into the host arrays.
+hipError_t launch_m_offload(const Common& c, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                            const int32_t* seq_lens, const int32_t* fc_idx, void* k_nd, void* v_host,
+                            hipStream_t s);
+// Rebuild the selected rows (non-dominant columns and values from the host,
+// dominant pairs from the slab) into the staging arrays [b][H_kv][cap][128].
+hipError_t launch_m_gather(const Common& c, const void* k_nd, const void* v_host, const void* slab,
+                           const int32_t* block_table, const int32_t* fc_idx, const int32_t* sel_idx,
+                           const int32_t* sel_count, void* stage_k, void* stage_v, hipStream_t s);
+
 // Whether a decode step may use launch_fac_select (small budget, block-table
 // rows that fit in LDS).
 bool fac_selects(const Common& c, const FacPlan& p);

@@ -26,7 +26,8 @@ BLOCK = 256
 EXPORTS = ["fasa_status_str", "fasa_validate_shape", "fasa_selection_capacity",
            "fasa_workspace_size", "fasa_check_fc_idx", "fasa_slab_build", "fasa_slab_append",
            "fasa_tip", "fasa_topk", "fasa_fac", "fasa_decode", "fasa_dense_workspace_size",
-           "fasa_dense_decode"]
+           "fasa_dense_decode", "fasa_m_host_sizes", "fasa_m_offload", "fasa_m_workspace_size",
+           "fasa_m_decode"]
 
 
 class fasa_shape(ctypes.Structure):
@@ -80,6 +81,12 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_size_t, _P]),
         "fasa_dense_workspace_size": (ctypes.c_int, [_S, _I32, ctypes.POINTER(ctypes.c_size_t)]),
         "fasa_dense_decode": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
+        "fasa_m_host_sizes": (ctypes.c_int, [_S, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t),
+                                             ctypes.POINTER(ctypes.c_size_t)]),
+        "fasa_m_offload": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "fasa_m_workspace_size": (ctypes.c_int, [_S, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+        "fasa_m_decode": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
+                                         ctypes.c_size_t, _P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -237,10 +244,69 @@ def fasa_dense_decode(shape, q, k_pool, v_pool, block_table, seq_lens, max_t, ou
                                    nbytes, _stream(stream)), "fasa_dense_decode")
 
 
+def _host_ptr(x) -> Optional[int]:
+    """Pointer of a pinned host tensor (FASA-M's host arrays)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"expected a torch.Tensor, got {type(x)}")
+    if x.is_cuda or not x.is_pinned():
+        raise ValueError("FASA-M host arrays must be pinned host tensors (pin_memory=True)")
+    if not x.is_contiguous():
+        raise ValueError("FASA buffers must be contiguous")
+    return x.data_ptr()
+
+
+def fasa_m_host_sizes(shape: fasa_shape, n_blocks: int):
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().fasa_m_host_sizes(ctypes.byref(shape), n_blocks, ctypes.byref(a), ctypes.byref(b)),
+           "fasa_m_host_sizes")
+    return a.value, b.value
+
+
+def fasa_m_offload(shape, k_pool, v_pool, block_table, seq_lens, fc_idx, k_nd_host, v_host, stream=None) -> None:
+    for x, n in ((block_table, "block_table"), (seq_lens, "seq_lens"), (fc_idx, "fc_idx")):
+        _need(x, torch.int32, n)
+    _check(lib().fasa_m_offload(ctypes.byref(shape), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                _ptr(seq_lens), _ptr(fc_idx), _host_ptr(k_nd_host), _host_ptr(v_host),
+                                _stream(stream)), "fasa_m_offload")
+
+
+def fasa_m_workspace_size(shape: fasa_shape, max_t: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().fasa_m_workspace_size(ctypes.byref(shape), max_t, ctypes.byref(n)), "fasa_m_workspace_size")
+    return n.value
+
+
+def fasa_m_decode(shape, q, slab, k_nd_host, v_host, block_table, seq_lens, max_t, fc_idx, out, sel_idx,
+                  sel_count, workspace, stream=None) -> None:
+    _need(out, torch.float32, "out")
+    _need(sel_idx, torch.int32, "sel_idx")
+    _need(sel_count, torch.int32, "sel_count")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fasa_m_decode(ctypes.byref(shape), _ptr(q), _ptr(slab), _host_ptr(k_nd_host), _host_ptr(v_host),
+                               _ptr(block_table), _ptr(seq_lens), max_t, _ptr(fc_idx), _ptr(out), _ptr(sel_idx),
+                               _ptr(sel_count), _ptr(workspace), nbytes, _stream(stream)), "fasa_m_decode")
+
+
 # --------------------------------------------------------------------------- buffers
 def alloc_slab(shape: fasa_shape, n_blocks: int, device="cuda") -> torch.Tensor:
     dt = torch.bfloat16 if shape.kv_dtype == FASA_BF16 else torch.float32
     return torch.empty(n_blocks, shape.n_kv_heads, shape.n_fc, BLOCK, 2, dtype=dt, device=device)
+
+
+def alloc_m_host(shape: fasa_shape, n_blocks: int):
+    """Pinned host arrays (k_nd, v) of FASA-M for a pool of n_blocks blocks."""
+    kb, vb = fasa_m_host_sizes(shape, n_blocks)
+    dt = torch.bfloat16 if shape.kv_dtype == FASA_BF16 else torch.float32
+    es = 2 if shape.kv_dtype == FASA_BF16 else 4
+    nd = kb // es // (n_blocks * shape.n_kv_heads * BLOCK)
+    k_nd = torch.zeros(n_blocks, shape.n_kv_heads, BLOCK, nd, dtype=dt, pin_memory=True)
+    v = torch.zeros(n_blocks, shape.n_kv_heads, BLOCK, HEAD_DIM, dtype=dt, pin_memory=True)
+    assert k_nd.numel() * es == kb and v.numel() * es == vb
+    return k_nd, v
 
 
 def alloc_dense_workspace(shape: fasa_shape, max_t: int, device="cuda") -> torch.Tensor:

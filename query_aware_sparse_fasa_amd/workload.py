@@ -73,6 +73,22 @@ class DeviceLayer:
         fasa.fasa_dense_decode(self.shape, self.q, self.k_pool, self.v_pool, self.block_table, self.seq_lens,
                                self.max_t, self.dense_out if out is None else out, self.dense_ws, stream)
 
+    def m_setup(self, stream=None):
+        """FASA-M: pinned host arrays of this layer's non-dominant keys and values."""
+        if getattr(self, "m_knd", None) is None:
+            self.m_knd, self.m_v = fasa.alloc_m_host(self.shape, self.inp.n_blocks)
+            n = fasa.fasa_m_workspace_size(self.shape, self.max_t)
+            self.m_ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=self.q.device)
+            self.m_out = torch.zeros_like(self.out)
+            self.m_sel_idx = torch.zeros_like(self.sel_idx)
+            self.m_sel_count = torch.zeros_like(self.sel_count)
+        fasa.fasa_m_offload(self.shape, self.k_pool, self.v_pool, self.block_table, self.seq_lens, self.fc_idx,
+                            self.m_knd, self.m_v, stream)
+
+    def m_decode(self, stream=None):
+        fasa.fasa_m_decode(self.shape, self.q, self.slab, self.m_knd, self.m_v, self.block_table, self.seq_lens,
+                           self.max_t, self.fc_idx, self.m_out, self.m_sel_idx, self.m_sel_count, self.m_ws, stream)
+
     # -- host copies ----------------------------------------------------------------
     def selection(self, b: int, g: int) -> np.ndarray:
         n = int(self.sel_count[b, g].item())

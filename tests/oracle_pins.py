@@ -293,6 +293,27 @@ def pin_dense_is_library_attention(O):
         np.testing.assert_allclose(res[(b, g)], ref, rtol=1e-12, atol=1e-12)
 
 
+def pin_fasa_m_split(O):
+    """FASA-M's split of the keys: every column appears exactly once, either in
+    the dominant-key cache (slab) or among the non-dominant columns, which keep
+    ascending order; rows carry their own (token, column) so the check is by
+    coordinates, against explicit set arithmetic."""
+    rng = np.random.default_rng(23)
+    t = 7
+    for F in (1, 5, 16, 64):
+        fc = np.sort(rng.choice(D // 2, F, replace=False))
+        K = 1000.0 * np.arange(t)[:, None] + np.arange(D)[None, :]
+        nd = O.nondominant_rows(K, fc)
+        dom = {2 * int(i) for i in fc} | {2 * int(i) + 1 for i in fc}
+        expect = sorted(set(range(D)) - dom)
+        assert nd.shape == (t, D - 2 * F)
+        for j in range(t):
+            assert list(nd[j] - 1000.0 * j) == expect
+        sl = O.slab_rows(K, fc)                  # [F][t][2]
+        cols = sorted(set(sl[:, 0, :].ravel().astype(int).tolist()) | set(nd[0].astype(int).tolist()))
+        assert cols == list(range(D))
+
+
 def pin_slab(O):
     """The dominant-key cache holds exactly the FC pairs of every key."""
     K = np.arange(5 * D, dtype=np.float64).reshape(5, D)
@@ -307,7 +328,7 @@ ALL_PINS = [pin_tip_closed_form, pin_tip_relative_form, pin_tip_all_fc_is_full_d
             pin_tip_reads_only_dominant, pin_topb_full_sort, pin_topb_exhaustive,
             pin_topb_signed_and_zero, pin_forced_union, pin_fac_is_library_attention,
             pin_fac_special_cases, pin_fac_duplicate_keys_tie, pin_paged_rows, pin_slab,
-            pin_dense_is_library_attention]
+            pin_dense_is_library_attention, pin_fasa_m_split]
 
 
 def golden():

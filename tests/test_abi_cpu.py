@@ -23,7 +23,7 @@ def header_functions():
 def test_exports_every_declared_symbol():
     L = fasa.lib()
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(fasa.EXPORTS) == names
@@ -167,6 +167,38 @@ def test_workspace_grows_with_context_and_batch():
     d1 = fasa.fasa_dense_workspace_size(good(), 4096)
     d2 = fasa.fasa_dense_workspace_size(good(kv_dtype=torch.float32), 4096)
     assert d2 > d1 > 0  # fp64 partials for fp32 caches
+
+
+def test_fasa_m_sizes_and_rejections():
+    # host arrays: the non-dominant row is 128 - 2F elements padded to 16 bytes
+    kb, vb = fasa.fasa_m_host_sizes(good(), 10)
+    assert kb == 10 * 8 * 256 * 96 * 2 and vb == 10 * 8 * 256 * 128 * 2
+    kb, _ = fasa.fasa_m_host_sizes(good(n_fc=5), 3)
+    assert kb == 3 * 8 * 256 * 120 * 2            # 118 bf16 -> 120
+    kb, _ = fasa.fasa_m_host_sizes(good(n_fc=5, kv_dtype=torch.float32), 3)
+    assert kb == 3 * 8 * 256 * 120 * 4            # 118 fp32 -> 120
+    kb, _ = fasa.fasa_m_host_sizes(good(n_fc=64), 1)
+    assert kb == 0
+    s = good()
+    sp = ctypes.byref(s)
+    assert fasa.fasa_m_workspace_size(s, 4096) > fasa.fasa_workspace_size(s, 4096)
+    mws = fasa.fasa_m_workspace_size(s, 4096)
+    E = fasa.FASA_ERR_INVALID_ARG
+    n = ctypes.c_size_t()
+    assert raw("fasa_m_host_sizes", sp, 0, ctypes.byref(n), ctypes.byref(n)) == E
+    assert raw("fasa_m_offload", sp, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == E
+    assert raw("fasa_m_offload", sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, None) == E
+    args = [sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, mws, None]
+    for k in (1, 2, 3, 4):                      # q, slab, k_nd, v missing
+        bad = list(args)
+        bad[k] = None
+        assert raw("fasa_m_decode", *bad) == E
+    bad = list(args)
+    bad[7] = -1
+    assert raw("fasa_m_decode", *bad) == E
+    bad = list(args)
+    bad[3] = FAKE + 4                           # misaligned host array
+    assert raw("fasa_m_decode", *bad) == E
 
 
 def test_binding_refuses_host_tensors():

@@ -221,12 +221,13 @@ def test_fac_on_oracle_selection(name):
 
 
 # ------------------------------------------------------------------------ whole step
-def _check_decode(inp, L, units, label):
+def _check_decode(inp, L, units, label, m=False):
+    """Selections and outputs of the last fasa_decode (m: fasa_m_decode) on L."""
     cfg = inp.cfg
     torch.cuda.synchronize()
-    out = L.out.cpu().numpy()
-    sel = L.sel_idx.cpu().numpy()
-    cnt = L.sel_count.cpu().numpy()
+    out = (L.m_out if m else L.out).cpu().numpy()
+    sel = (L.m_sel_idx if m else L.sel_idx).cpu().numpy()
+    cnt = (L.m_sel_count if m else L.sel_count).cpu().numpy()
     G = cfg.group
     same = 0
     for (b, g), (q, K, V, r) in units.items():
@@ -365,6 +366,64 @@ def test_dense_decode_edge_lengths():
     torch.cuda.synchronize()
     assert (L.dense_out[0] == 0).all()
     _check_dense(inp, L, [(b, g) for b in range(1, 6) for g in range(cfg.n_kv_heads)], "dense edge")
+
+
+# ------------------------------------------------------------------------ FASA-M
+M_CASES = ["c1", "c2-ragged", "c5-ragged", "fp32-gqa4", "g16-f5", "g2-f1-sink", "f32-fc32"]
+
+
+@pytest.mark.parametrize("name", M_CASES)
+def test_m_offload_bit_exact(name):
+    """The host arrays hold exactly the non-dominant key columns (ascending,
+    zero-padded) and the value rows of every cached token."""
+    say(f"[fasa-m offload] {name}")
+    inp, L = layer_for(name)
+    L.m_setup()
+    torch.cuda.synchronize()
+    cfg = inp.cfg
+    nd_n = 128 - 2 * cfg.n_fc
+    for b in range(cfg.batch):
+        t = int(inp.seq_lens[b])
+        n = (t + 255) // 256
+        blocks = torch.as_tensor(inp.block_table[b, :n].astype(np.int64))
+        for g in range(cfg.n_kv_heads):
+            K = unit_rows(inp, b, g, inp.k_pool)
+            V = unit_rows(inp, b, g, inp.v_pool)
+            got = L.m_knd[blocks, g].reshape(n * 256, -1)[:t]
+            np.testing.assert_array_equal(got[:, :nd_n].float().numpy(),
+                                          O.nondominant_rows(K.float().numpy(), inp.fc_idx[g]),
+                                          err_msg=f"{name} b={b} g={g}")
+            assert (got[:, nd_n:].float() == 0).all()
+            assert torch.equal(L.m_v[blocks, g].reshape(n * 256, -1)[:t], V), f"{name} b={b} g={g}"
+
+
+@pytest.mark.parametrize("name", M_CASES)
+def test_m_decode(name):
+    """FASA-M decode against the oracle, and its selection against fasa_decode's."""
+    say(f"[fasa-m decode] {name}")
+    inp, L = layer_for(name)
+    L.m_setup()
+    L.m_out.fill_(float("nan"))
+    L.m_decode()
+    L.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(L.m_sel_count, L.sel_count)
+    cap = L.cap
+    assert torch.equal(L.m_sel_idx[..., :cap], L.sel_idx[..., :cap])
+    _check_decode(inp, L, oracle_units(inp), name + " fasa-m", m=True)
+
+
+def test_m_decode_full_size_8b_layer():
+    """FASA-M on the Llama-3-8B-shaped layer at t = 32768, every unit."""
+    cfg = C["c2"]
+    say(f"[fasa-m full] {cfg.name}")
+    inp = synth.make_inputs(cfg, seed=0, device="cuda")
+    L = DeviceLayer(inp)
+    L.m_setup()
+    L.m_decode()
+    _check_decode(inp, L, oracle_units(inp), "c2 fasa-m", m=True)
+    del L, inp
+    torch.cuda.empty_cache()
 
 
 def test_empty_and_tiny_sequences():

@@ -67,6 +67,12 @@ MUTANTS = [
     ("dense_drops_last_token",
      "        res[(b, g)] = fac(q[b, g * G:(g + 1) * G], K, V, scale)[0]",
      "        res[(b, g)] = fac(q[b, g * G:(g + 1) * G], K[:-1], V[:-1], scale)[0]"),
+    ("nondominant_keeps_odd_dominant",
+     "        dominant.add(2 * int(i) + 1)\n",
+     "        pass\n"),
+    ("nondominant_wrong_pair_index",
+     "        dominant.add(2 * int(i))\n",
+     "        dominant.add(int(i))\n"),
     ("slab_swapped_pair",
      "out[f, :, 0] = K[:, 2 * fc[f]]",
      "out[f, :, 0] = K[:, 2 * fc[f] + 1]"),
