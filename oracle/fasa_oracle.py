@@ -185,6 +185,61 @@ def decode(q, k_pool, v_pool, block_table, seq_lens, fc_idx, budget,
 
 
 # ---------------------------------------------------------------------------
+# offline calibration: Contextual Agreement and the dominant FCs
+# ---------------------------------------------------------------------------
+def ca_score_vectors(q_group: np.ndarray, K: np.ndarray) -> np.ndarray:
+    """The full-head score vector alpha and the 64 single-FC vectors alpha^(i)
+    of one unit, [1 + d/2][t] float32 (review section 3.4, the CA metric: raw
+    pre-softmax dot products of the query with every past key, over all of
+    q.k and over FC i's pair of columns).
+
+    Grouped-query attention: one vector per kv head, from the group's queries
+    summed per column (as TIP scores them).  Because the top-K of these
+    vectors decides integer results, the arithmetic is fixed in float32 and in
+    this order, exactly as the kernel does it: q~ = sum of the group's heads in
+    head order; alpha^(i)_j = fl(fl(q~_2i k_2i) + fl(q~_2i+1 k_2i+1));
+    alpha_j = alpha^(0)_j + alpha^(1)_j + ... added in FC order.
+    """
+    qf = np.zeros(np.asarray(q_group).shape[1], dtype=np.float32)
+    for h in range(np.asarray(q_group).shape[0]):
+        qf = (qf + np.asarray(q_group[h], dtype=np.float32)).astype(np.float32)
+    K32 = np.asarray(K, dtype=np.float32)
+    d = K32.shape[1]
+    t = K32.shape[0]
+    out = np.empty((1 + d // 2, t), dtype=np.float32)
+    full = np.zeros(t, dtype=np.float32)
+    for i in range(d // 2):
+        a = (qf[2 * i] * K32[:, 2 * i]).astype(np.float32)
+        b = (qf[2 * i + 1] * K32[:, 2 * i + 1]).astype(np.float32)
+        out[1 + i] = (a + b).astype(np.float32)
+        full = (full + out[1 + i]).astype(np.float32)
+    out[0] = full
+    return out
+
+
+def contextual_agreement(q_group: np.ndarray, K: np.ndarray, k_top: int) -> np.ndarray:
+    """CA_K for every FC of one unit, [d/2]: |TopK-I(alpha) n TopK-I(alpha^(i))| / K
+    (review section 3.4, the CA equation).  TopK-I is top_b (largest first,
+    lower index on ties); with fewer than K tokens it keeps them all."""
+    vec = ca_score_vectors(q_group, K)
+    full, _ = top_b(vec[0].astype(np.float64), k_top)
+    full = set(full.tolist())
+    ca = np.empty(vec.shape[0] - 1)
+    for i in range(vec.shape[0] - 1):
+        fc_set, _ = top_b(vec[1 + i].astype(np.float64), k_top)
+        ca[i] = len(full & set(fc_set.tolist())) / float(k_top)
+    return ca
+
+
+def dominant_fcs(mean_ca: np.ndarray, n_tip: int) -> np.ndarray:
+    """I_dom of one head: the n_tip FCs with the highest mean CA (review section
+    3.4, offline calibration: sort by mean CA, take the top N_tip; equal means
+    go to the lower FC index), returned in ascending FC order."""
+    chosen, _ = top_b(np.asarray(mean_ca, dtype=np.float64), n_tip)
+    return np.sort(chosen)
+
+
+# ---------------------------------------------------------------------------
 # FASA-M: the host-resident part of the keys
 # ---------------------------------------------------------------------------
 def nondominant_rows(K: np.ndarray, fc: np.ndarray) -> np.ndarray:

@@ -314,6 +314,57 @@ def pin_fasa_m_split(O):
         assert cols == list(range(D))
 
 
+def _exact_topk(vals, k):
+    """Indices of the k largest of a list of exact numbers, lower index on ties."""
+    return set(sorted(range(len(vals)), key=lambda j: (-vals[j], j))[:k])
+
+
+def pin_ca_exact_small(O):
+    """CA on small-integer inputs, where float32 arithmetic is exact: the
+    oracle's alpha and alpha^(i) equal integer dot products computed in Python,
+    and its CA equals explicit set intersections over those (with K larger
+    than t in one case, where TopK-I keeps every token and CA divides by K)."""
+    rng = np.random.default_rng(25)
+    for G, t, k in ((1, 9, 3), (3, 12, 5), (2, 6, 8)):
+        q = rng.integers(-3, 4, size=(G, D)).astype(np.float64)
+        K = rng.integers(-3, 4, size=(t, D)).astype(np.float64)
+        qs = [int(sum(q[h, c] for h in range(G))) for c in range(D)]
+        vec = O.ca_score_vectors(q, K)
+        full = [sum(qs[c] * int(K[j, c]) for c in range(D)) for j in range(t)]
+        assert vec[0].tolist() == full
+        top_full = _exact_topk(full, k)
+        ca = O.contextual_agreement(q, K, k)
+        for i in range(D // 2):
+            fc = [qs[2 * i] * int(K[j, 2 * i]) + qs[2 * i + 1] * int(K[j, 2 * i + 1]) for j in range(t)]
+            assert vec[1 + i].tolist() == fc
+            assert ca[i] == len(top_full & _exact_topk(fc, k)) / k
+
+
+def pin_ca_single_fc_query(O):
+    """A query that lives in one FC: that FC agrees with the head completely
+    (CA 1); every other FC scores all tokens 0, so its top-K is the K lowest
+    indices and its CA is their share of the head's top-K."""
+    rng = np.random.default_rng(26)
+    t, k, i0 = 300, 16, 11
+    q = np.zeros((1, D))
+    q[0, 2 * i0], q[0, 2 * i0 + 1] = 1.5, -0.75
+    K = rng.standard_normal((t, D))
+    ca = O.contextual_agreement(q, K, k)
+    assert ca[i0] == 1.0
+    full = O.ca_score_vectors(q, K)[0].astype(np.float64).tolist()
+    share = len(_exact_topk(full, k) & set(range(k))) / k
+    assert all(ca[i] == share for i in range(D // 2) if i != i0)
+
+
+def pin_dominant_fcs(O):
+    """The N_tip FCs of highest mean CA, ties to the lower FC index, ascending."""
+    m = np.zeros(D // 2)
+    m[[40, 3, 17, 60, 9]] = [0.9, 0.5, 0.5, 0.7, 0.5]
+    assert list(O.dominant_fcs(m, 3)) == [3, 40, 60]
+    assert list(O.dominant_fcs(m, 4)) == [3, 9, 40, 60]
+    assert list(O.dominant_fcs(m, 64)) == list(range(64))
+
+
 def pin_slab(O):
     """The dominant-key cache holds exactly the FC pairs of every key."""
     K = np.arange(5 * D, dtype=np.float64).reshape(5, D)
@@ -328,7 +379,8 @@ ALL_PINS = [pin_tip_closed_form, pin_tip_relative_form, pin_tip_all_fc_is_full_d
             pin_tip_reads_only_dominant, pin_topb_full_sort, pin_topb_exhaustive,
             pin_topb_signed_and_zero, pin_forced_union, pin_fac_is_library_attention,
             pin_fac_special_cases, pin_fac_duplicate_keys_tie, pin_paged_rows, pin_slab,
-            pin_dense_is_library_attention, pin_fasa_m_split]
+            pin_dense_is_library_attention, pin_fasa_m_split, pin_ca_exact_small, pin_ca_single_fc_query,
+            pin_dominant_fcs]
 
 
 def golden():

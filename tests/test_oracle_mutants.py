@@ -73,6 +73,18 @@ MUTANTS = [
     ("nondominant_wrong_pair_index",
      "        dominant.add(2 * int(i))\n",
      "        dominant.add(int(i))\n"),
+    ("ca_pair_wrong_column",
+     "b = (qf[2 * i + 1] * K32[:, 2 * i + 1]).astype(np.float32)",
+     "b = (qf[2 * i + 1] * K32[:, 2 * i]).astype(np.float32)"),
+    ("ca_first_head_only",
+     "    for h in range(np.asarray(q_group).shape[0]):\n        qf = (qf +",
+     "    for h in range(1):\n        qf = (qf +"),
+    ("ca_divides_by_set_size",
+     "ca[i] = len(full & set(fc_set.tolist())) / float(k_top)",
+     "ca[i] = len(full & set(fc_set.tolist())) / float(max(len(full), 1))"),
+    ("dominant_lowest_ca",
+     "chosen, _ = top_b(np.asarray(mean_ca, dtype=np.float64), n_tip)",
+     "chosen, _ = top_b(-np.asarray(mean_ca, dtype=np.float64), n_tip)"),
     ("slab_swapped_pair",
      "out[f, :, 0] = K[:, 2 * fc[f]]",
      "out[f, :, 0] = K[:, 2 * fc[f] + 1]"),
