@@ -130,6 +130,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-slab", action="store_true", help="TIP gathers from the key rows instead")
     ap.add_argument("--no-fasa-m", action="store_true", help="skip the FASA-M (host-offloaded) timing")
+    ap.add_argument("--no-calib", action="store_true", help="skip the CA calibration timing")
     ap.add_argument("--mode", choices=["step", "tip"], default="step",
                     help="step: the benchmark; tip: only --steps TIP launches and one 1 GiB "
                          "reference copy (for hardware-counter runs)")
@@ -284,6 +285,32 @@ def main():
             f"{host_bytes / t_m / 1e9:.1f} GB/s); GPU cache {gpu_m / 1e6:.1f} MB vs {gpu_fkv / 1e6:.1f} MB full "
             f"({gpu_fkv / gpu_m:.2f}x less)")
 
+    # Offline calibration (Contextual Agreement at K = 256): one calibration row
+    # per sequence of the workload, on up to four layer copies.
+    calib = None
+    ca_ws_bytes = fasa.fasa_ca_workspace_size(base.shape, base.max_t, 256)
+    if ca_ws_bytes > 2 << 30:
+        calib = {"skipped": f"workspace of {ca_ws_bytes / 2**30:.1f} GiB per call"}
+    elif not args.no_calib:
+        c_layers = layers[:min(L, 4)]
+        ca_ws = [torch.zeros(ca_ws_bytes, dtype=torch.uint8, device=dev) for _ in c_layers]
+        ca_hits = torch.zeros(cfg.batch, cfg.n_kv_heads, 64, dtype=torch.int32, device=dev)
+        calls = [lambda l=l, w=w: fasa.fasa_ca_hits(l.shape, l.q, l.k_pool, l.block_table, l.seq_lens, l.max_t,
+                                                    256, ca_hits, w) for l, w in zip(c_layers, ca_ws)]
+        with torch.cuda.stream(stream):
+            for f in calls:
+                f()
+        torch.cuda.synchronize()
+        g_ca = graph_of(torch, stream, calls)
+        creps = max(1, 40 // len(c_layers))
+        t_ca = time_graph(torch, stream, [g_ca], creps) / (creps * len(c_layers))
+        k_bytes = int(inp.seq_lens.sum()) * cfg.n_kv_heads * 128 * cfg.elem_bytes
+        calib = {"k_top": 256, "us_per_call": t_ca * 1e6, "calibration_rows_per_call": cfg.batch,
+                 "key_bytes": k_bytes, "key_GBps": k_bytes / t_ca / 1e9}
+        log(f"[bench] CA calibration (K=256) {t_ca * 1e6:.1f} us per call of {cfg.batch} rows "
+            f"({k_bytes / t_ca / 1e9:,.0f} GB/s of keys)")
+        del ca_ws
+
     tip_bytes = sb["slab"] if use_slab else int(inp.seq_lens.sum()) * cfg.n_kv_heads * 128 * cfg.elem_bytes
     tip_gbps = tip_bytes / t_tip / 1e9
     step_gbps = per_layer_touch * steps_per_s / 1e9
@@ -329,6 +356,7 @@ def main():
                          "hbm_frac": dense_gbps / HBM_PEAK_GBPS,
                          "fasa_speedup": t_dense / (el / args.steps)},
         "fasa_m": fasa_m,
+        "ca_calibration": calib,
         "cpu_baseline": cpu,
         "pages_context": "the pages report 2.56x decode speedup over full-KV FlashAttention using 18.9% "
                          "of the cache (hardware not stated); context only",

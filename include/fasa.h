@@ -222,6 +222,40 @@ fasa_status fasa_m_decode(const fasa_shape* shape, const void* q, const void* sl
                           float* out, int32_t* sel_idx, int32_t* sel_count, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Offline calibration: Contextual Agreement (section 3.4, the CA metric
+ * and the offline calibration).  A calibration row is one decode query
+ * (sequence b, its query at position t_b) against the keys 0..t_b-1 of the
+ * paged cache; several steps of one calibration sample are several sequences
+ * whose block tables share their prefix blocks.  Per kv head, the group's
+ * queries are summed per column (as TIP scores them). */
+
+/* Workspace of fasa_ca_hits: the 65 score rows of every (sequence, kv head)
+ * and the exact top-K state for them.  1 <= k_top <= 4096. */
+fasa_status fasa_ca_workspace_size(const fasa_shape* shape, int32_t max_t, int32_t k_top,
+                                   size_t* bytes);
+
+/* hits[b][g][i] (int32, [batch][n_kv_heads][64]) = the size of the
+ * intersection of TopK-I(alpha, K) and TopK-I(alpha^(i), K), where alpha_j is
+ * the full q.k_j score and alpha^(i)_j the score of FC i alone, over tokens
+ * j < t_b; CA of FC i is hits / k_top.  TopK-I takes the largest values, the
+ * lower index on ties, and every token when t_b < k_top.  The scores are
+ * float32 in one fixed order without fused multiply-adds (the group's heads
+ * summed in head order; each FC as fl(fl(q x k) + fl(q x k)); alpha as the 64
+ * FC terms added in FC order), so the sets are reproducible bit for bit.
+ * fc_idx, budget, n_sink and n_recent are not used. */
+fasa_status fasa_ca_hits(const fasa_shape* shape, const void* q, const void* k_pool,
+                         const int32_t* block_table, const int32_t* seq_lens, int32_t max_t,
+                         int32_t k_top, int32_t* hits, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* The dominant FCs from n_rows calibration rows of hits ([n_rows][n_kv_heads][64]):
+ * per kv head, the n_tip FCs with the largest total hits (the largest mean
+ * CA), the lower FC index on ties, written ascending to fc_idx
+ * [n_kv_heads][n_tip] -- a valid fc_idx for the other entry points when
+ * n_tip == n_fc.  1 <= n_tip <= 64. */
+fasa_status fasa_ca_dominant(const fasa_shape* shape, const int32_t* hits, int32_t n_rows,
+                             int32_t n_tip, int32_t* fc_idx, hipStream_t stream);
+
 /* Bytes of workspace that fasa_dense_decode needs for contexts up to max_t:
  * the split partials, about 4 * (128 + 2) bytes per query head per 512 tokens
  * of max_t (fp32 caches: twice that).  256-byte aligned; contents are

@@ -127,6 +127,38 @@ size_t dense_workspace(const Common& c, const FacPlan& p) {
 
 fasa_status hip_status(hipError_t e) { return e == hipSuccess ? FASA_OK : FASA_ERR_HIP; }
 
+// Calibration: the selection runs over 65 rows per (sequence, kv head) --
+// alpha and the 64 single-FC vectors -- as if they were 65 * H_kv kv heads.
+// Workspace: [scores | unit histograms | b1 | kept pairs | kept counts |
+// lists | list counts].
+Common ca_select_common(const fasa_shape* s, int32_t max_t, int32_t k_top) {
+  Common c = make_common(s, max_t);
+  c.n_kv_heads = s->n_kv_heads * (fasa::kHeadDim / 2 + 1);
+  c.n_q_heads = c.n_kv_heads * c.group;
+  c.budget = k_top;
+  c.n_sink = 0;
+  c.n_recent = 0;
+  c.cap = k_top < max_t ? k_top : max_t;
+  c.score_stride = (max_t + 3) & ~3;
+  return c;
+}
+struct CaLayout {
+  size_t scores, hist, b1, slots, counts, sel_idx, sel_count, total;
+};
+CaLayout ca_layout(const Common& cs) {
+  const size_t units = size_t(cs.batch) * cs.n_kv_heads;
+  CaLayout l;
+  l.scores = 0;
+  l.hist = l.scores + align256(units * size_t(cs.score_stride) * sizeof(float));
+  l.b1 = l.hist + fasa::hist_bytes(cs);
+  l.slots = l.b1 + align256(units * sizeof(int32_t));
+  l.counts = l.slots + fasa::slots_bytes(cs);
+  l.sel_idx = l.counts + fasa::counts_bytes(cs);
+  l.sel_count = l.sel_idx + align256(units * size_t(cs.cap > 0 ? cs.cap : 1) * sizeof(int32_t));
+  l.total = l.sel_count + align256(units * sizeof(int32_t));
+  return l;
+}
+
 // FASA-M: the decode workspace followed by the two staging arrays
 // [b][H_kv][cap][128] (K, then V).
 struct MLayout {
@@ -424,6 +456,57 @@ fasa_status fasa_m_decode(const fasa_shape* shape, const void* q, const void* sl
     return st;
   return hip_status(fasa::launch_fac_staged(c, p, q, w + m.stage_k, w + m.stage_v, sel_count, out, w + m.d.fac,
                                             fac_arrive, stream));
+}
+
+fasa_status fasa_ca_workspace_size(const fasa_shape* shape, int32_t max_t, int32_t k_top, size_t* bytes) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
+  if (!bytes || k_top < 1 || k_top > fasa::kCaMaxK) return FASA_ERR_INVALID_ARG;
+  *bytes = ca_layout(ca_select_common(shape, max_t, k_top)).total;
+  return FASA_OK;
+}
+
+fasa_status fasa_ca_hits(const fasa_shape* shape, const void* q, const void* k_pool, const int32_t* block_table,
+                         const int32_t* seq_lens, int32_t max_t, int32_t k_top, int32_t* hits, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
+  if (!q || !k_pool || !block_table || !seq_lens || !hits || k_top < 1 || k_top > fasa::kCaMaxK)
+    return FASA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_pool, 16)) return FASA_ERR_INVALID_ARG;
+  const Common cs = ca_select_common(shape, max_t, k_top);
+  const CaLayout l = ca_layout(cs);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < l.total) return FASA_ERR_WORKSPACE;
+  char* w = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(w + l.scores);
+  int32_t* sel_idx = reinterpret_cast<int32_t*>(w + l.sel_idx);
+  int32_t* sel_count = reinterpret_cast<int32_t*>(w + l.sel_count);
+  const fasa::SelectBuffers sb{reinterpret_cast<uint32_t*>(w + l.hist), w + l.slots,
+                               reinterpret_cast<int32_t*>(w + l.counts), reinterpret_cast<int32_t*>(w + l.b1)};
+  Common c = make_common(shape, max_t);
+  c.score_stride = cs.score_stride;
+  if (max_t > 0) {
+    if ((st = hip_status(fasa::launch_ca_scores(c, q, k_pool, block_table, seq_lens, scores, stream))) != FASA_OK)
+      return st;
+  }
+  if ((st = hip_status(fasa::launch_filter(cs, scores, seq_lens, sb, false, nullptr, 0, stream))) != FASA_OK)
+    return st;
+  if ((st = hip_status(fasa::launch_finish(cs, scores, seq_lens, sel_idx, sel_count, sb, nullptr, 0, stream))) !=
+      FASA_OK)
+    return st;
+  Common ch = cs;
+  ch.n_kv_heads = shape->n_kv_heads;
+  return hip_status(fasa::launch_ca_hits(ch, sel_idx, sel_count, hits, stream));
+}
+
+fasa_status fasa_ca_dominant(const fasa_shape* shape, const int32_t* hits, int32_t n_rows, int32_t n_tip,
+                             int32_t* fc_idx, hipStream_t stream) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if (!hits || !fc_idx || n_rows < 1 || n_tip < 1 || n_tip > fasa::kHeadDim / 2) return FASA_ERR_INVALID_ARG;
+  return hip_status(fasa::launch_ca_dominant(hits, n_rows, shape->n_kv_heads, n_tip, fc_idx, stream));
 }
 
 fasa_status fasa_dense_workspace_size(const fasa_shape* shape, int32_t max_t, size_t* bytes) {

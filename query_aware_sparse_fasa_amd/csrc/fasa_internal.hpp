@@ -127,6 +127,18 @@ hipError_t launch_m_gather(const Common& c, const void* k_nd, const void* v_host
                            const int32_t* block_table, const int32_t* fc_idx, const int32_t* sel_idx,
                            const int32_t* sel_count, void* stage_k, void* stage_v, hipStream_t s);
 
+// Offline calibration (calib.hip).  kCaMaxK: largest calibration window K.
+constexpr int kCaMaxK = 4096;
+// The 65 score rows (alpha, alpha^(0..63)) of every unit into scores
+// [b][H_kv][65][c.score_stride].
+hipError_t launch_ca_scores(const Common& c, const void* q, const void* k_pool, const int32_t* block_table,
+                            const int32_t* seq_lens, float* scores, hipStream_t s);
+// hits[b][g][i] from the top-K lists of the 65 rows of each unit; c is the
+// selection's Common (cap = the lists' row length; c.n_kv_heads = H_kv).
+hipError_t launch_ca_hits(const Common& c, const int32_t* sel_idx, const int32_t* sel_count, int32_t* hits,
+                          hipStream_t s);
+hipError_t launch_ca_dominant(const int32_t* hits, int n_rows, int n_kv, int n_tip, int32_t* fc_idx, hipStream_t s);
+
 // Whether a decode step may use launch_fac_select (small budget, block-table
 // rows that fit in LDS).
 bool fac_selects(const Common& c, const FacPlan& p);

@@ -27,7 +27,7 @@ EXPORTS = ["fasa_status_str", "fasa_validate_shape", "fasa_selection_capacity",
            "fasa_workspace_size", "fasa_check_fc_idx", "fasa_slab_build", "fasa_slab_append",
            "fasa_tip", "fasa_topk", "fasa_fac", "fasa_decode", "fasa_dense_workspace_size",
            "fasa_dense_decode", "fasa_m_host_sizes", "fasa_m_offload", "fasa_m_workspace_size",
-           "fasa_m_decode"]
+           "fasa_m_decode", "fasa_ca_workspace_size", "fasa_ca_hits", "fasa_ca_dominant"]
 
 
 class fasa_shape(ctypes.Structure):
@@ -87,6 +87,9 @@ def lib() -> ctypes.CDLL:
         "fasa_m_workspace_size": (ctypes.c_int, [_S, _I32, ctypes.POINTER(ctypes.c_size_t)]),
         "fasa_m_decode": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                                          ctypes.c_size_t, _P]),
+        "fasa_ca_workspace_size": (ctypes.c_int, [_S, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+        "fasa_ca_hits": (ctypes.c_int, [_S, _P, _P, _P, _P, _I32, _I32, _P, _P, ctypes.c_size_t, _P]),
+        "fasa_ca_dominant": (ctypes.c_int, [_S, _P, _I32, _I32, _P, _P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -289,6 +292,29 @@ def fasa_m_decode(shape, q, slab, k_nd_host, v_host, block_table, seq_lens, max_
     _check(lib().fasa_m_decode(ctypes.byref(shape), _ptr(q), _ptr(slab), _host_ptr(k_nd_host), _host_ptr(v_host),
                                _ptr(block_table), _ptr(seq_lens), max_t, _ptr(fc_idx), _ptr(out), _ptr(sel_idx),
                                _ptr(sel_count), _ptr(workspace), nbytes, _stream(stream)), "fasa_m_decode")
+
+
+def fasa_ca_workspace_size(shape: fasa_shape, max_t: int, k_top: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().fasa_ca_workspace_size(ctypes.byref(shape), max_t, k_top, ctypes.byref(n)),
+           "fasa_ca_workspace_size")
+    return n.value
+
+
+def fasa_ca_hits(shape, q, k_pool, block_table, seq_lens, max_t, k_top, hits, workspace, stream=None) -> None:
+    _need(hits, torch.int32, "hits")
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fasa_ca_hits(ctypes.byref(shape), _ptr(q), _ptr(k_pool), _ptr(block_table), _ptr(seq_lens), max_t,
+                              k_top, _ptr(hits), _ptr(workspace), nbytes, _stream(stream)), "fasa_ca_hits")
+
+
+def fasa_ca_dominant(shape, hits, n_rows, n_tip, fc_idx, stream=None) -> None:
+    _need(hits, torch.int32, "hits")
+    _need(fc_idx, torch.int32, "fc_idx")
+    _check(lib().fasa_ca_dominant(ctypes.byref(shape), _ptr(hits), n_rows, n_tip, _ptr(fc_idx), _stream(stream)),
+           "fasa_ca_dominant")
 
 
 # --------------------------------------------------------------------------- buffers

@@ -23,7 +23,7 @@ def header_functions():
 def test_exports_every_declared_symbol():
     L = fasa.lib()
     names = header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(fasa.EXPORTS) == names
@@ -199,6 +199,27 @@ def test_fasa_m_sizes_and_rejections():
     bad = list(args)
     bad[3] = FAKE + 4                           # misaligned host array
     assert raw("fasa_m_decode", *bad) == E
+
+
+def test_ca_sizes_and_rejections():
+    s = good()
+    sp = ctypes.byref(s)
+    a = fasa.fasa_ca_workspace_size(s, 4096, 256)
+    assert a > 0 and fasa.fasa_ca_workspace_size(s, 8192 // 2, 256) == a
+    assert fasa.fasa_ca_workspace_size(good(max_blocks_per_seq=32), 8192, 256) > a
+    E = fasa.FASA_ERR_INVALID_ARG
+    n = ctypes.c_size_t()
+    for k in (0, 4097):
+        assert raw("fasa_ca_workspace_size", sp, 4096, k, ctypes.byref(n)) == E
+        assert raw("fasa_ca_hits", sp, FAKE, FAKE, FAKE, FAKE, 4096, k, FAKE, FAKE, a, None) == E
+    assert raw("fasa_ca_hits", sp, None, FAKE, FAKE, FAKE, 4096, 256, FAKE, FAKE, a, None) == E
+    assert raw("fasa_ca_hits", sp, FAKE, FAKE, FAKE, FAKE, 4096, 256, None, FAKE, a, None) == E
+    assert raw("fasa_ca_hits", sp, FAKE, FAKE, FAKE, FAKE, 4096, 256, FAKE, FAKE, a - 1, None) == \
+        fasa.FASA_ERR_WORKSPACE
+    for n_tip in (0, 65):
+        assert raw("fasa_ca_dominant", sp, FAKE, 4, n_tip, FAKE, None) == E
+    assert raw("fasa_ca_dominant", sp, FAKE, 0, 16, FAKE, None) == E
+    assert raw("fasa_ca_dominant", sp, None, 4, 16, FAKE, None) == E
 
 
 def test_binding_refuses_host_tensors():

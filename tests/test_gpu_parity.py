@@ -426,6 +426,67 @@ def test_m_decode_full_size_8b_layer():
     torch.cuda.empty_cache()
 
 
+# ------------------------------------------------------------------------ CA calibration
+CA_CASES = ["c1", "c2-ragged", "c5-ragged", "fp32-gqa4", "g16-f5"]
+
+
+def _ca_hits(L, k_top):
+    cfg = L.cfg
+    ws = torch.zeros(fasa.fasa_ca_workspace_size(L.shape, L.max_t, k_top), dtype=torch.uint8, device="cuda")
+    hits = torch.full((cfg.batch, cfg.n_kv_heads, 64), -1, dtype=torch.int32, device="cuda")
+    fasa.fasa_ca_hits(L.shape, L.q, L.k_pool, L.block_table, L.seq_lens, L.max_t, k_top, hits, ws)
+    torch.cuda.synchronize()
+    return hits
+
+
+def _ca_expect(inp, b, g, k_top):
+    G = inp.cfg.group
+    q = inp.q[b, g * G:(g + 1) * G].float().cpu().numpy()
+    K = unit_rows(inp, b, g, inp.k_pool).float().cpu().numpy()
+    return np.rint(O.contextual_agreement(q, K, k_top) * k_top).astype(np.int32)
+
+
+@pytest.mark.parametrize("k_top", [64, 256])
+@pytest.mark.parametrize("name", CA_CASES)
+def test_ca_hits_exact(name, k_top):
+    """The top-K overlaps of every FC with its head, bit-exact against the oracle."""
+    say(f"[ca hits] {name} K={k_top}")
+    inp, L = layer_for(name)
+    h = _ca_hits(L, k_top).cpu().numpy()
+    cfg = inp.cfg
+    units = [(b, g) for b in range(cfg.batch) for g in range(cfg.n_kv_heads)]
+    if len(units) > 12:
+        units = units[::len(units) // 12]
+    for b, g in units:
+        np.testing.assert_array_equal(h[b, g], _ca_expect(inp, b, g, k_top), err_msg=f"{name} b={b} g={g}")
+
+
+def test_ca_calibration_sample_steps():
+    """Eight steps of one calibration sample (block tables sharing one
+    sequence's blocks, lengths 1990..1997), K = 256, then the dominant FCs of
+    the summed hits against the oracle's choice from its own CA."""
+    cfg = C["c2"].replace(batch=8, t=2000)
+    say("[ca sample steps]")
+    inp = synth.make_inputs(cfg, seed=13)
+    inp.block_table[:] = inp.block_table[0]
+    inp.seq_lens[:] = 1990 + np.arange(8, dtype=np.int32)
+    L = DeviceLayer(inp, with_slab=False)
+    k_top = 256
+    hits = _ca_hits(L, k_top)
+    h = hits.cpu().numpy()
+    expect = np.stack([np.stack([_ca_expect(inp, b, g, k_top) for g in range(cfg.n_kv_heads)])
+                       for b in range(cfg.batch)])
+    np.testing.assert_array_equal(h, expect)
+    fc = torch.full((cfg.n_kv_heads, 16), -1, dtype=torch.int32, device="cuda")
+    fasa.fasa_ca_dominant(L.shape, hits, cfg.batch, 16, fc)
+    torch.cuda.synchronize()
+    got = fc.cpu().numpy()
+    for g in range(cfg.n_kv_heads):
+        mean = expect[:, g, :].sum(axis=0) / float(cfg.batch * k_top)
+        assert list(got[g]) == list(O.dominant_fcs(mean, 16)), g
+    fasa.fasa_check_fc_idx(L.shape, got)     # a valid fc_idx for the decode path
+
+
 def test_empty_and_tiny_sequences():
     cfg = C["c5"].replace(batch=5, budget=16, n_sink=4, n_recent=8)
     say("[edge lengths]")
