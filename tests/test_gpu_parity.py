@@ -534,6 +534,23 @@ FULL_SAMPLES = {
 }
 
 
+@pytest.mark.parametrize("t", [524288, 524289 + 300])
+def test_longest_contexts(t):
+    """The selecting FAC keeps a sequence's block-table row in LDS, up to 2048
+    blocks (524288 tokens); one token more takes the select-then-split path.
+    Both sides of that boundary, every unit against the oracle."""
+    cfg = C["c2"].replace(batch=1, n_q_heads=4, n_kv_heads=1, t=t)
+    say(f"[longest] t={t}")
+    inp = synth.make_inputs(cfg, seed=17, device="cuda")
+    L = DeviceLayer(inp)
+    L.decode()
+    _check_decode(inp, L, oracle_units(inp), f"t={t}")
+    L.dense()
+    _check_dense(inp, L, [(0, 0)], f"t={t} dense")
+    del L, inp
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5"])
 def test_full_size_configs(key):
     """The workloads at their full sizes, in the launch configuration the benchmark
