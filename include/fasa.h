@@ -122,7 +122,11 @@ fasa_status fasa_workspace_size(const fasa_shape* shape, int32_t max_t, size_t* 
 
 /* Host check of a HOST copy of fc_idx [n_kv_heads][n_fc]: every entry in
  * [0, head_dim/2) and no duplicate within a row (an FC is an indivisible unit
- * and is counted once: section 3.4, "FCs Are Indivisible Units"). */
+ * and is counted once: section 3.4, "FCs Are Indivisible Units").  A row may
+ * end in -1 entries after at least one FC: kv head g then uses only its first
+ * N_tip(g) FCs (per-head N_tip, an extension the pages leave to future work);
+ * the slab keeps zeros in those slots and TIP still reads n_fc slots per
+ * token.  FASA-M (fasa_m_*) needs rows without -1 entries. */
 fasa_status fasa_check_fc_idx(const fasa_shape* shape, const int32_t* fc_idx_host);
 
 /* Build the dominant-key cache for tokens 0..t_b-1 of every sequence from the

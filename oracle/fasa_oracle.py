@@ -61,11 +61,14 @@ def slab_rows(K: np.ndarray, fc: np.ndarray) -> np.ndarray:
 
     Section 3.4 "Hardware-Aware Variants": the dominant key cache holds only the
     dimensions of the dominant FCs of every cached key.  Entry [f][j] is the
-    pair (K[j, 2 fc[f]], K[j, 2 fc[f] + 1]).
+    pair (K[j, 2 fc[f]], K[j, 2 fc[f] + 1]); an unused slot (fc[f] < 0, a head
+    with fewer dominant FCs than the row has slots) holds zeros.
     """
     F = len(fc)
-    out = np.empty((F, K.shape[0], 2), dtype=K.dtype)
+    out = np.zeros((F, K.shape[0], 2), dtype=K.dtype)
     for f in range(F):
+        if int(fc[f]) < 0:
+            continue
         out[f, :, 0] = K[:, 2 * fc[f]]
         out[f, :, 1] = K[:, 2 * fc[f] + 1]
     return out
@@ -78,7 +81,9 @@ def tip_scores(q_group: np.ndarray, K: np.ndarray, fc: np.ndarray) -> np.ndarray
     """S[j] = sum_h sum_{i in I_dom} (q_h[2i] K[j,2i] + q_h[2i+1] K[j,2i+1]).
 
     q_group: [G][d] post-RoPE queries of the heads sharing this kv head.
-    K: [t][d] post-RoPE cached keys.  fc: the dominant FC indices I_dom.
+    K: [t][d] post-RoPE cached keys.  fc: the dominant FC indices I_dom; entries
+    < 0 are unused slots (a head with fewer dominant FCs, per-head N_tip) and
+    contribute nothing.
     """
     q_group = np.asarray(q_group, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -86,6 +91,8 @@ def tip_scores(q_group: np.ndarray, K: np.ndarray, fc: np.ndarray) -> np.ndarray
     for h in range(q_group.shape[0]):
         for i in fc:
             i = int(i)
+            if i < 0:
+                continue
             S += q_group[h, 2 * i] * K[:, 2 * i] + q_group[h, 2 * i + 1] * K[:, 2 * i + 1]
     return S
 

@@ -248,9 +248,14 @@ fasa_status fasa_check_fc_idx(const fasa_shape* shape, const int32_t* fc_idx_hos
   const int nfc_all = shape->head_dim / 2;
   for (int g = 0; g < shape->n_kv_heads; ++g) {
     uint64_t seen[2] = {0, 0};   // head_dim/2 <= 64 when head_dim == 128
+    bool padding = false;
     for (int f = 0; f < shape->n_fc; ++f) {
       const int32_t i = fc_idx_host[int64_t(g) * shape->n_fc + f];
-      if (i < 0 || i >= nfc_all) return FASA_ERR_INVALID_ARG;
+      if (i == -1 && f > 0) {    // unused slots: only after at least one FC, to the end of the row
+        padding = true;
+        continue;
+      }
+      if (padding || i < 0 || i >= nfc_all) return FASA_ERR_INVALID_ARG;
       uint64_t& w = seen[i >> 6];
       const uint64_t bit = uint64_t(1) << (i & 63);
       if (w & bit) return FASA_ERR_INVALID_ARG;

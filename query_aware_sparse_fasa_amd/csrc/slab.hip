@@ -39,8 +39,9 @@ __global__ __launch_bounds__(256) void slab_build_kernel(Common c, const T* __re
   const T* src = k_pool + phys * c.kv_block_stride + int64_t(g) * c.kv_head_stride + int64_t(s) * kHeadDim;
   T* dst = slab + phys * c.slab_block_stride + int64_t(g) * c.slab_head_stride + 2 * s;
   for (int f = 0; f < c.n_fc; ++f) {
-    const int col = 2 * fc_idx[g * c.n_fc + f];
-    *reinterpret_cast<P*>(dst + int64_t(f) * kSlabFcStride) = *reinterpret_cast<const P*>(src + col);
+    const int fi = fc_idx[g * c.n_fc + f];     // < 0: an unused slot of a head with fewer FCs, kept zero
+    *reinterpret_cast<P*>(dst + int64_t(f) * kSlabFcStride) =
+        fi >= 0 ? *reinterpret_cast<const P*>(src + 2 * fi) : P{};
   }
 }
 
@@ -59,8 +60,9 @@ __global__ __launch_bounds__(64) void slab_append_kernel(Common c, const T* __re
   const T* src = k_pool + phys * c.kv_block_stride + int64_t(g) * c.kv_head_stride + int64_t(s) * kHeadDim;
   T* dst = slab + phys * c.slab_block_stride + int64_t(g) * c.slab_head_stride + 2 * s;
   for (int f = threadIdx.x; f < c.n_fc; f += 64) {
-    const int col = 2 * fc_idx[g * c.n_fc + f];
-    *reinterpret_cast<P*>(dst + int64_t(f) * kSlabFcStride) = *reinterpret_cast<const P*>(src + col);
+    const int fi = fc_idx[g * c.n_fc + f];
+    *reinterpret_cast<P*>(dst + int64_t(f) * kSlabFcStride) =
+        fi >= 0 ? *reinterpret_cast<const P*>(src + 2 * fi) : P{};
   }
 }
 

@@ -56,7 +56,8 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
   const int f_q = ec >> 1, comp = ec & 1;
   const int t_raw = a.seq_lens[b];
   const int64_t phys_raw = a.block_table[int64_t(b) * c.max_blocks + min(blk, c.max_blocks - 1)];
-  const int col = 2 * a.fc_idx[g * F + f_q] + comp;
+  const int fi = a.fc_idx[g * F + f_q];          // < 0: unused slot (a head with fewer FCs)
+  const int col = 2 * (fi < 0 ? 0 : fi) + comp;
   const int t = clamp_len(t_raw, c.max_t, c.max_blocks);
   // A workgroup whose four blocks all lie past the end of a short sequence has
   // nothing to do (the whole workgroup leaves together, before any barrier).
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
 #pragma unroll
     for (int h = 0; h < 16; ++h) s += (h < c.group) ? to_f32(qv[h]) : 0.f;
     if (e < 2 * F) {
-      qf[e] = s;
+      qf[e] = fi < 0 ? 0.f : s;                  // an unused slot scores nothing
       if (comp == 0) cols[f_q] = col;
     }
   }

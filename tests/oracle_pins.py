@@ -365,6 +365,28 @@ def pin_dominant_fcs(O):
     assert list(O.dominant_fcs(m, 64)) == list(range(64))
 
 
+def pin_per_head_fc_padding(O):
+    """Per-head N_tip: a row of FC indices padded with -1 scores exactly as its
+    valid prefix (closed form: with unit query pairs only on the valid FCs, S is
+    their key pairs' sum), and the padded slab slots are zero."""
+    rng = np.random.default_rng(27)
+    K = rng.standard_normal((50, D))
+    q = np.zeros((2, D))
+    valid = [5, 9, 33]
+    for i in valid:
+        q[0, 2 * i] = 1.0
+        q[1, 2 * i + 1] = 1.0
+    for i in (1, 2, 60, 63):                    # FCs present in q but not in the row
+        q[0, 2 * i] = 7.0
+        q[1, 2 * i + 1] = -3.0
+    S = O.tip_scores(q, K, np.array(valid + [-1, -1]))
+    expect = sum(K[:, 2 * i] + K[:, 2 * i + 1] for i in valid)
+    np.testing.assert_allclose(S, expect, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(S, O.tip_scores(q, K, np.array(valid)))
+    sl = O.slab_rows(K, np.array([7, -1]))
+    assert (sl[1] == 0).all() and (sl[0, :, 0] == K[:, 14]).all()
+
+
 def pin_slab(O):
     """The dominant-key cache holds exactly the FC pairs of every key."""
     K = np.arange(5 * D, dtype=np.float64).reshape(5, D)
@@ -380,7 +402,7 @@ ALL_PINS = [pin_tip_closed_form, pin_tip_relative_form, pin_tip_all_fc_is_full_d
             pin_topb_signed_and_zero, pin_forced_union, pin_fac_is_library_attention,
             pin_fac_special_cases, pin_fac_duplicate_keys_tie, pin_paged_rows, pin_slab,
             pin_dense_is_library_attention, pin_fasa_m_split, pin_ca_exact_small, pin_ca_single_fc_query,
-            pin_dominant_fcs]
+            pin_dominant_fcs, pin_per_head_fc_padding]
 
 
 def golden():

@@ -102,7 +102,9 @@ def test_group_limit():
 def test_fc_idx_check():
     s = good(n_kv_heads=2, n_q_heads=4, n_fc=3)
     fasa.fasa_check_fc_idx(s, [[0, 5, 63], [1, 2, 3]])
-    for bad in ([[0, 5, 64], [1, 2, 3]], [[0, 5, 5], [1, 2, 3]], [[0, 5, 6], [1, -1, 3]]):
+    fasa.fasa_check_fc_idx(s, [[0, 5, -1], [1, -1, -1]])      # per-head N_tip: trailing unused slots
+    for bad in ([[0, 5, 64], [1, 2, 3]], [[0, 5, 5], [1, 2, 3]], [[0, 5, 6], [1, -1, 3]],
+                [[-1, 5, 6], [1, 2, 3]], [[0, 5, -2], [1, 2, 3]], [[-1, -1, -1], [1, 2, 3]]):
         with pytest.raises(fasa.FasaError) as e:
             fasa.fasa_check_fc_idx(s, bad)
         assert e.value.status == fasa.FASA_ERR_INVALID_ARG

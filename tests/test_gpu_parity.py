@@ -534,6 +534,57 @@ FULL_SAMPLES = {
 }
 
 
+@pytest.mark.parametrize("name", ["c2-ragged", "fp32-gqa4", "c5-ragged", "c3-shape"])
+def test_per_head_fc_counts(name):
+    """Per-head N_tip: kv head g uses only the first F - (g mod F) of its FCs
+    (the rest of its fc_idx row is -1); TIP, the select and FAC against the
+    oracle on the same rows."""
+    cfg = SMALL[name]
+    say(f"[per-head n_fc] {name}")
+    inp = synth.make_inputs(cfg, seed=29)
+    F = cfg.n_fc
+    for g in range(cfg.n_kv_heads):
+        drop = g % F
+        if drop:
+            inp.fc_idx[g, F - drop:] = -1
+    L = DeviceLayer(inp)
+    fasa.fasa_check_fc_idx(L.shape, inp.fc_idx)
+    L.out.fill_(float("nan"))
+    L.decode()
+    _check_decode(inp, L, oracle_units(inp), name + " per-head n_fc")
+
+
+def test_per_layer_budgets_in_one_graph():
+    """Per-layer budgets (PyramidKV-style): each layer's call carries its own
+    shape, so layers with budgets 48, 300 and 1500 run back to back in one
+    captured graph; every replay matches the oracle at each layer's budget."""
+    say("[per-layer budgets]")
+    layers = []
+    for k, budget in enumerate((48, 300, 1500)):
+        cfg = C["c2"].replace(batch=2, t=None, t_range=(2500, 4000), budget=budget)
+        inp = synth.make_inputs(cfg, seed=31 + k)
+        layers.append((inp, DeviceLayer(inp)))
+    for _, L in layers:
+        L.decode()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for _, L in layers:
+                L.decode()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(2):
+        for _, L in layers:
+            L.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for inp, L in layers:
+            _check_decode(inp, L, oracle_units(inp), f"budget {inp.cfg.budget} replay {rep}")
+
+
 @pytest.mark.parametrize("t", [524288, 524289 + 300])
 def test_longest_contexts(t):
     """The selecting FAC keeps a sequence's block-table row in LDS, up to 2048

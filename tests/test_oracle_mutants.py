@@ -85,6 +85,9 @@ MUTANTS = [
     ("dominant_lowest_ca",
      "chosen, _ = top_b(np.asarray(mean_ca, dtype=np.float64), n_tip)",
      "chosen, _ = top_b(-np.asarray(mean_ca, dtype=np.float64), n_tip)"),
+    ("tip_padding_slot_counted",
+     "            if i < 0:\n                continue\n            S += q_group",
+     "            S += q_group"),
     ("slab_swapped_pair",
      "out[f, :, 0] = K[:, 2 * fc[f]]",
      "out[f, :, 0] = K[:, 2 * fc[f] + 1]"),
