@@ -14,16 +14,22 @@
 // heads of the group (GQA).  A wave's logits need a 16-lane reduction; the four
 // row groups of a wave are folded together with cross-lane shuffles at the end
 // and the workgroup folds its waves into one partial.  The partials of a head
-// are merged with the log-sum-exp rule, in a decode step by the last workgroup
-// of the head's split to finish (an arrival counter decides which), otherwise
-// by a second launch.  With at most 8 query heads per pass the q.K
-// product is an 8 x 128 by 128 x rows contraction at a few flops per loaded
-// byte -- HBM/latency bound, so it runs on the vector ALUs, not MFMA.
+// are merged with the log-sum-exp rule, in a decode step with a small grid by
+// the last workgroup of the head's split to finish (an arrival counter decides
+// which), otherwise by a second launch.  With at most 8 query heads per pass
+// the q.K product is an 8 x 128 by 128 x rows contraction at a few flops per
+// loaded byte -- HBM/latency bound, so it runs on the vector ALUs, not MFMA.
 //
-// Precision: bf16 caches accumulate in fp32 (logits pre-scaled by log2(e) and
-// exponentiated with exp2); fp32 caches run the logits, softmax and weighted
-// sum in fp64 and round once at the end (fp32 logits of magnitude ~30 carry
-// ~2e-6 absolute error, enough to move a fp32 output by more than 1e-5).
+// The same split kernel also runs full attention over every cached row (the
+// dense decode) and FAC over rows already gathered into a staging area
+// (FASA-M).  In a decode step with a small budget a different launch,
+// fac_select_kernel, finishes the selection itself and needs no partials.
+//
+// Precision: bf16 caches accumulate in fp32 (logits from v_dot2 on the raw
+// bf16 pairs, scaled by scale * log2(e) and exponentiated with exp2); fp32
+// caches run the logits, softmax and weighted sum in fp64 and round once at
+// the end (fp32 logits of magnitude ~30 carry ~2e-6 absolute error, enough to
+// move a fp32 output by more than 1e-5).
 #include <math.h>
 
 #include "fac_core.hpp"
