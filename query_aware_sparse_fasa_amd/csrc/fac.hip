@@ -270,10 +270,11 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   __shared__ FacSelShared<Acc, HG> sm;
 
   // Independent loads first: the first kept pairs of every chunk (up to 16
-  // chunks), the chunk counts and b1; the query slices, the block-table row and
-  // the length.
-  uint2 pre[16 / kSelWaves];
-  sel::prefetch_kept<kSelThreads, 16 / kSelWaves>(unit_slots, nfa, pre);
+  // chunks; the gather fetches the rest 8 chunks per wave at a time), the
+  // chunk counts and b1; the query slices, the block-table row and the length.
+  constexpr int PRE = 16 / kSelWaves;
+  uint2 pre[PRE];
+  sel::prefetch_kept<kSelThreads, PRE>(unit_slots, nfa, pre);
   int cnt[sel::CPT];
   sel::load_counts(a.w.counts + unit * nfa, nfa, cnt);
   const int b1 = a.w.b1[unit];
@@ -294,9 +295,9 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   const bool keep_all = Bc == nC;
 
   if (!keep_all)
-    sel::select_from_kept<kSelThreads, 16 / kSelWaves, true>(sm.u.s.st, sm.u.s.chunk_off, sm.u.s.key, sm.u.s.idx,
-                                                             kSmallCand, unit_slots, row, lim, c.max_t, nfa, cnt, pre,
-                                                             c_lo, c_hi, Bc, b1, sm.chosen);
+    sel::select_from_kept<kSelThreads, PRE, true>(sm.u.s.st, sm.u.s.chunk_off, sm.u.s.key, sm.u.s.idx, kSmallCand,
+                                                  unit_slots, row, lim, c.max_t, nfa, cnt, pre, c_lo, c_hi, Bc, b1,
+                                                  sm.chosen);
 #pragma unroll
   for (int k = 0; k < kBtabLds / kSelThreads; ++k)
     if (tid + kSelThreads * k < c.max_blocks) sm.btab[tid + kSelThreads * k] = bt[k];

@@ -256,10 +256,26 @@ __device__ __forceinline__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off,
   }
   more = more || nfc > PRE * NW;
   if (__builtin_amdgcn_readfirstlane(int(more)) != 0) {
+    // The first 64 pairs of the chunks past the prefetched ones, 8 chunks of
+    // this wave at a time: their loads go out together (clamped chunk, always
+    // readable), then they are copied.
+    for (int c0 = wave + PRE * NW; c0 < nfc; c0 += 8 * NW) {   // wave-uniform
+      uint2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = slots[int64_t(min(c0 + u * NW, nfc - 1)) * FCH + lane];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int ch = c0 + u * NW;
+        if (ch < nfc) {
+          const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
+          if (lane < n) put(o + lane, v[u]);
+        }
+      }
+    }
+    // Pairs past the first 64 of a chunk (a chunk keeps up to FCH).
     for (int ch = wave; ch < nfc; ch += NW) {
       const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
-      const int k0 = (ch < PRE * NW) ? 64 : 0;
-      for (int k = k0 + lane; k < n; k += 64) put(o + k, slots[int64_t(ch) * FCH + k]);
+      for (int k = 64 + lane; k < n; k += 64) put(o + k, slots[int64_t(ch) * FCH + k]);
     }
   }
   // The barrier inside the scan also publishes the copied pairs and the histogram.
