@@ -15,12 +15,14 @@ from .synth import Inputs
 class DeviceLayer:
     """One decode layer's inputs and outputs resident on the GPU."""
 
-    def __init__(self, inp: Inputs, device="cuda", with_slab: bool = True, build_slab: bool = True):
+    def __init__(self, inp: Inputs, device="cuda", with_slab: bool = True, build_slab: bool = True,
+                 max_t: int = None):
+        """max_t: the longest context the buffers are sized for (default: the inputs' longest)."""
         cfg = inp.cfg
         dev = torch.device(device)
         self.inp = inp
         self.cfg = cfg
-        self.max_t = inp.max_t
+        self.max_t = inp.max_t if max_t is None else max_t
         self.shape = fasa.make_shape(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.n_fc, cfg.budget,
                                      inp.max_blocks, cfg.torch_dtype, cfg.n_sink, cfg.n_recent)
         fasa.fasa_check_fc_idx(self.shape, inp.fc_idx)

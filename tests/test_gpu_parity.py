@@ -119,6 +119,38 @@ def test_slab_append_writes_one_slot():
     assert torch.isnan(rest.float()).all()
 
 
+def test_decode_steps_with_append():
+    """Three consecutive decode steps: each appends the new token's key and
+    value to the cache (pool rows written by the caller, slab by
+    fasa_slab_append), grows seq_lens by one and decodes a fresh query;
+    every step against the oracle on the grown cache."""
+    cfg = C["c5"].replace(batch=3, budget=40, n_sink=2, n_recent=8)
+    say("[decode steps with append]")
+    inp = synth.make_inputs(cfg, seed=37, seq_lens=[1000, 700, 513])
+    L = DeviceLayer(inp, max_t=1003)               # room for the three appended tokens (block 3 of 4)
+    rng = np.random.default_rng(37)
+    for step in range(3):
+        pos = inp.seq_lens.copy()                      # the new token's position per sequence
+        for b in range(cfg.batch):
+            blk, slot = int(inp.block_table[b, pos[b] // 256]), int(pos[b]) % 256
+            for g in range(cfg.n_kv_heads):
+                k = torch.from_numpy(rng.standard_normal(128).astype(np.float32)).to(inp.k_pool.dtype)
+                v = torch.from_numpy(rng.standard_normal(128).astype(np.float32)).to(inp.v_pool.dtype)
+                inp.k_pool[blk, g, slot] = k
+                inp.v_pool[blk, g, slot] = v
+                L.k_pool[blk, g, slot] = k.cuda()
+                L.v_pool[blk, g, slot] = v.cuda()
+        fasa.fasa_slab_append(L.shape, L.k_pool, L.block_table, torch.from_numpy(pos).cuda(), L.fc_idx, L.slab)
+        inp.seq_lens += 1
+        L.seq_lens.copy_(torch.from_numpy(inp.seq_lens))
+        q = torch.from_numpy(rng.standard_normal((cfg.batch, cfg.n_q_heads, 128)).astype(np.float32))
+        inp.q = q.to(inp.q.dtype)
+        L.q.copy_(inp.q.cuda())
+        L.out.fill_(float("nan"))
+        L.decode()
+        _check_decode(inp, L, oracle_units(inp), f"append step {step}")
+
+
 # ------------------------------------------------------------------------ TIP
 @pytest.mark.parametrize("name", list(SMALL))
 def test_tip_scores(name):
