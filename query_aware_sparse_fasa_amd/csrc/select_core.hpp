@@ -32,26 +32,28 @@ __host__ __device__ __forceinline__ int filter_chunks(const Common& c) {
 template <int NTH>
 struct SelState {
   alignas(16) uint32_t hist[HB];
-  uint32_t wave_sum[NTH / 64];
+  uint32_t wave_sum[2][NTH / 64];   // two buffers: back-to-back scans alternate
   uint32_t digit, rem, full;
 };
 
 // Block-wide exclusive scan of one value per thread; returns the exclusive
-// prefix and writes the block total.
-template <int NTH>
+// prefix and writes the block total.  One barrier: the wave totals go through
+// buffer BUF, so a scan may only follow another scan on the same buffer once a
+// barrier has passed since that one returned (scans with nothing between them
+// alternate buffers).
+template <int BUF = 0, int NTH>
 __device__ __forceinline__ uint32_t block_excl_scan(SelState<NTH>& s, uint32_t v, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t incl = wave_inclusive_scan(v);
-  if (lane == 63) s.wave_sum[wave] = incl;
+  if (lane == 63) s.wave_sum[BUF][wave] = incl;
   __syncthreads();
   uint32_t base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NTH / 64; ++w) {
-    const uint32_t x = s.wave_sum[w];
+    const uint32_t x = s.wave_sum[BUF][w];
     base += (w < wave) ? x : 0u;
     tot += x;
   }
-  __syncthreads();
   total = tot;
   return base + incl - v;
 }
@@ -61,12 +63,12 @@ __device__ __forceinline__ uint32_t block_excl_scan(SelState<NTH>& s, uint32_t v
 template <int NTH>
 __device__ __forceinline__ uint32_t wave_base(SelState<NTH>& s, uint32_t wave_val, uint32_t& total) {
   const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) s.wave_sum[wave] = wave_val;
+  if ((threadIdx.x & 63) == 0) s.wave_sum[0][wave] = wave_val;
   __syncthreads();
   uint32_t base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NTH / 64; ++w) {
-    const uint32_t x = s.wave_sum[w];
+    const uint32_t x = s.wave_sum[0][w];
     base += (w < wave) ? x : 0u;
     tot += x;
   }
@@ -100,7 +102,7 @@ __device__ __forceinline__ void find_digit(SelState<NTH>& s, uint32_t rem) {
 #pragma unroll
   for (int i = 0; i < BPT; ++i) sum += h[i];
   uint32_t total;
-  const uint32_t above = block_excl_scan(s, sum, total);    // keys in bins above the owned ones
+  const uint32_t above = block_excl_scan<1>(s, sum, total);  // keys in bins above the owned ones
   if (above < rem && rem <= above + sum) {
     uint32_t cum = above;
 #pragma unroll
@@ -361,7 +363,7 @@ __device__ __forceinline__ void lds_select(SelState<NTH>& s, const uint32_t* key
   uint32_t eq_tot, sel_tot;
   const uint32_t eq_base = block_excl_scan(s, n_eq, eq_tot);
   const uint32_t take_eq = (rem > eq_base) ? min(rem - eq_base, n_eq) : 0u;
-  int pos = int(block_excl_scan(s, n_gt + take_eq, sel_tot));
+  int pos = int(block_excl_scan<1>(s, n_gt + take_eq, sel_tot));   // right after the previous scan: the other buffer
   uint32_t eq_seen = eq_base;
   for (int i = i0; i < i1; ++i) {
     const uint32_t m = key[i] & pmask;
