@@ -8,17 +8,18 @@
 // straight from the paged pool through the block table.
 //
 // Split-K flash decode.  A workgroup is 4 waves; each wave walks its own run of
-// selected rows, four rows at a time (16 lanes per row, 8 channels per lane),
-// and keeps a running (max m, sum l, acc[128]) per query head -- the online
-// softmax.  Every K/V row is loaded once per kv head and reused by all query
-// heads of the group (GQA).  A wave's logits need a 16-lane reduction; the four
-// row groups of a wave are folded together with cross-lane shuffles at the end
-// and the workgroup folds its waves into one partial.  The partials of a head
-// are merged with the log-sum-exp rule, in a decode step with a small grid by
-// the last workgroup of the head's split to finish (an arrival counter decides
-// which), otherwise by a second launch.  With at most 8 query heads per pass
-// the q.K product is an 8 x 128 by 128 x rows contraction at a few flops per
-// loaded byte -- HBM/latency bound, so it runs on the vector ALUs, not MFMA.
+// selected rows and keeps a running (max m, sum l, acc[128]) per query head --
+// the online softmax.  Every K/V row is loaded once per kv head and reused by
+// all query heads of the group (GQA).  The workgroup folds its waves into one
+// partial.  The partials of a head are merged with the log-sum-exp rule, in a
+// decode step with a small grid by the last workgroup of the head's split to
+// finish (an arrival counter decides which), otherwise by a second launch.
+// Per wave, bf16 caches run on the matrix cores (FacWaveMfma: 32-row blocks,
+// logits and the weighted sum as 16 x 16 x 32 products with the heads padded
+// to 16): with G query heads per row the vector-ALU version spent more issue
+// time than the rows take to arrive, and dense decode over every row was
+// bound by it.  fp32 caches keep the vector path (FacWave: four rows at a
+// time, 16 lanes per row, fp64 arithmetic).
 //
 // The same split kernel also runs full attention over every cached row (the
 // dense decode) and FAC over rows already gathered into a staging area
@@ -186,9 +187,14 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   int count = DENSE ? clamp_len(a.seq_lens[b], c.max_t, c.max_blocks) : a.sel_count[unit];
   const int cap1 = c.cap > 0 ? c.cap - 1 : 0;
   const int j_first = (ROWS == kSelRows && c.cap > 0) ? sel[min(r0 + lane, cap1)] : -1;
-  FacWave<T, Acc, HG> w;
-  w.init(static_cast<const T*>(a.q) + (int64_t(b) * c.n_q_heads + g * c.group + h0) * kHeadDim, nh,
-         c.scale);
+  // bf16 caches run the logits and the weighted sum on the matrix cores
+  // (FacWaveMfma, one LDS tile per wave); fp32 caches keep the fp64 vector path.
+  constexpr bool kMfma = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) uint16_t mfma_tile[kMfma ? kFacWaves : 1][kMfma ? kMfmaTileElems : 1];
+  std::conditional_t<kMfma, FacWaveMfma<HG>, FacWave<T, Acc, HG>> w;
+  const T* q_head0 = static_cast<const T*>(a.q) + (int64_t(b) * c.n_q_heads + g * c.group + h0) * kHeadDim;
+  if constexpr (kMfma) w.init(q_head0, nh, c.scale, mfma_tile[wave]);
+  else w.init(q_head0, nh, c.scale);
   count = count < 0 ? 0 : (count > c.cap ? c.cap : count);   // contents are preconditions; stay in bounds
   const int r1 = min(r0 + p.rows_per_wave, count);
   auto lane_offset = [&](int r) -> int64_t {
@@ -209,7 +215,8 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   constexpr int U = (sizeof(Acc) == 4 && HG <= 4) ? 8 : (HG <= 2 ? 4 : (HG <= 4 || sizeof(Acc) == 4 ? 2 : 1));
   // All heads of a chunk share this workgroup's rows, and no other workgroup
   // of the launch reads them unless the group spans several chunks.
-  w.template run<U, true>(r0, r1, lane_offset, kbase, vbase);
+  if constexpr (kMfma) w.template run<true>(r0, r1, lane_offset, kbase, vbase);
+  else w.template run<U, true>(r0, r1, lane_offset, kbase, vbase);
   w.fold_row_groups();
 
   __shared__ WaveFold<Acc, HG> fold;

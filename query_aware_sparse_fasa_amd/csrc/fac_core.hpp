@@ -271,4 +271,200 @@ struct FacWave {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Matrix-core variant for bf16 caches (v_mfma_f32_16x16x32_bf16), the same
+// online softmax over 32-row blocks.  With G query heads per kv head the
+// per-row work is a G x 128 contraction with K and a G-wide P times V; on the
+// vector ALUs it costs more issue time than the rows take to arrive from HBM,
+// on the matrix cores a small part of it.
+//
+// Operand layout of the instruction (lane l, g = l / 16, n = l % 16, j < 8):
+// A[n][8 g + j], B[8 g + j][n]; the 16 x 16 result D[4 g + i][n], i < 4.
+//   Logits, one 16-row tile t of a 32-row block at a time: S_t = K_t Q^T, heads
+//     padded to 16 (columns n >= HG are zero).  A = K rows: lane l loads 16
+//     bytes of its row, channels 32 s + 8 g .. +7 for step s < 4; B = Q^T in the
+//     same channel order (loaded once).  Tile t's row i is block row
+//     8 (i / 4) + 4 t + i % 4, so that lane l ends up with the logits of block
+//     rows 8 g .. 8 g + 7 for head n -- exactly its part of P as the B operand
+//     of the next product.
+//   Weighted sum: O^T += V^T P.  A = V^T: lane l needs channel 16 dt + n of
+//     block rows 8 g .. 8 g + 7, a transposed access, so each wave first writes
+//     its 32 V rows into its own LDS tile (rows padded to 264 bytes: the four
+//     row groups of a read land in different banks) and reads them back 16 bits
+//     at a time.  B = P, split into a bf16 high part and a bf16 low part (the
+//     rounding error of a single bf16 P, about 2^-9 of |v|, would exceed the
+//     2e-3 bound on outputs with large channels); the two products add up to P
+//     within about 2^-17.  D: lane l holds channels 16 dt + 4 g + i of head n.
+// Lane l keeps the running max of head n (the same in the four lanes of the
+// column), its own partial sum, and the 32 channels of O^T above, so the
+// rescale to a new maximum is lane-local.  fold_row_groups() moves the result
+// into FacWave's layout (lane sub holds channels 8 sub .. +7 of every head)
+// through the same LDS tile.
+constexpr int kMfmaTileRows = 32;
+constexpr int kMfmaTilePitch = 132;   // bf16 per LDS row (264 bytes)
+constexpr int kMfmaTileElems = kMfmaTileRows * kMfmaTilePitch;
+
+template <int HG>
+struct FacWaveMfma {
+  typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+  typedef __attribute__((ext_vector_type(4))) float f32x4;
+  static_assert(HG <= 16, "heads are padded to 16 columns");
+  // The result, in FacWave's layout, after fold_row_groups().
+  float m[HG], l[HG], acc[HG][8];
+  bf16x8 qb[4];       // Q^T operand for channel steps 0..3
+  float zscale;
+  float mrun, lrun;   // head lane % 16
+  f32x4 o[8];         // O^T channels 16 dt + 4 g + i, head lane % 16
+  uint16_t* tile;     // this wave's LDS tile (kMfmaTileElems)
+
+  __device__ __forceinline__ void init(const uint16_t* q_head0, int nh, float scale, uint16_t* lds_tile) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+    const uint16_t* qh = q_head0 + int64_t(min(n, nh - 1)) * kHeadDim + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      Raw8<uint16_t> x;
+      x.load(qh + 32 * s);
+      const uint4 v = n < nh ? x.v : make_uint4(0u, 0u, 0u, 0u);
+      qb[s] = __builtin_bit_cast(bf16x8, v);
+    }
+    zscale = scale * 1.4426950408889634f;
+    mrun = -INFINITY;
+    lrun = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    tile = lds_tile;
+  }
+
+  // Rows r0 .. r1-1; lane_offset as for FacWave::run (called once per 64 rows
+  // with r = base + lane).  Invalid rows load a valid row of the batch and get
+  // a -inf logit.  NT: non-temporal row loads.
+  template <bool NT = false, typename LaneOffset>
+  __device__ __forceinline__ void run(int r0, int r1, LaneOffset lane_offset, const uint16_t* kbase,
+                                      const uint16_t* vbase) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+    auto ld = [](const uint16_t* p) -> uint4 {
+      Raw8<uint16_t> x;
+      if constexpr (NT) x.load_nt(p);
+      else x.load(p);
+      return x.v;
+    };
+    for (int base = r0; base < r1; base += 64) {   // wave-uniform
+      const int64_t my_off = lane_offset(base + lane);
+      const int nrows = min(64, r1 - base);
+      const uint64_t in_range = nrows >= 64 ? ~uint64_t(0) : ((uint64_t(1) << nrows) - 1);
+      const uint64_t ok = __ballot(my_off >= 0) & in_range;
+      if (ok == 0) continue;
+      const int64_t dummy = __shfl(my_off, __ffsll((unsigned long long)ok) - 1, 64);
+      auto row_off = [&](int x) -> int64_t {   // x < 64
+        const int64_t o = __shfl(my_off, x, 64);
+        return ((ok >> x) & 1) ? o : dummy;
+      };
+      for (int b = 0; b < nrows; b += kMfmaTileRows) {   // wave-uniform
+        // K: this lane's row of tiles 0 and 1; V: rows 4 k + g, channels 8 n .. +7.
+        const int kr = b + 8 * (n >> 2) + (n & 3);
+        const int64_t k0 = row_off(kr), k1 = row_off(kr + 4);
+        uint4 ka[2][4], va[8];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          ka[0][s] = ld(kbase + k0 + 32 * s + 8 * g);
+          ka[1][s] = ld(kbase + k1 + 32 * s + 8 * g);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) va[k] = ld(vbase + row_off(b + 4 * k + g) + 8 * n);
+        f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          st[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[0][s]), qb[s], st[0], 0, 0, 0);
+          st[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[1][s]), qb[s], st[1], 0, 0, 0);
+        }
+        // V rows into the LDS tile (8-byte writes; the tile rows are 8-byte aligned).
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          uint2* dst = reinterpret_cast<uint2*>(tile + (4 * k + g) * kMfmaTilePitch + 8 * n);
+          dst[0] = make_uint2(va[k].x, va[k].y);
+          dst[1] = make_uint2(va[k].z, va[k].w);
+        }
+        // Logits of block rows 8 g + 4 t + i, head n; the block maximum of the column.
+        float z[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int x = b + 8 * g + 4 * t + i;
+            const bool v = ((ok >> x) & 1) != 0;
+            z[4 * t + i] = v ? st[t][i] * zscale : -INFINITY;
+            mx = fmaxf(mx, z[4 * t + i]);
+          }
+        }
+        float xa, xb;
+        lane_pair<16>(mx, xa, xb);
+        mx = fmaxf(xa, xb);
+        lane_pair<32>(mx, xa, xb);
+        mx = fmaxf(xa, xb);
+        const float mn = fmaxf(mrun, mx);
+        const float corr = merge_weight(mrun, mn);
+        mrun = mn;
+        bf16x8 phi, plo;
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = merge_weight(z[e], mn);
+          psum += p;
+          const __bf16 h = (__bf16)p;
+          phi[e] = h;
+          plo[e] = (__bf16)(p - (float)h);
+        }
+        lrun = lrun * corr + psum;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          bf16x8 vt;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            vt[j] = __builtin_bit_cast(__bf16, tile[(8 * g + j) * kMfmaTilePitch + 16 * dt + n]);
+          o[dt] = o[dt] * corr;
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi, o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, plo, o[dt], 0, 0, 0);
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+  }
+
+  // The wave's state in FacWave's layout, through the LDS tile: O^T into
+  // [head][channel] floats, the column sums and maxima after it.
+  __device__ __forceinline__ void fold_row_groups() {
+    const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15, sub = lane & 15;
+    float la, lb;
+    lane_pair<16>(lrun, la, lb);
+    lrun = la + lb;
+    lane_pair<32>(lrun, la, lb);
+    lrun = la + lb;
+    float* f = reinterpret_cast<float*>(tile);
+    __builtin_amdgcn_wave_barrier();
+    if (n < HG) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[n * kHeadDim + 16 * dt + 4 * g + i] = o[dt][i];
+      }
+      if (g == 0) {
+        f[HG * kHeadDim + n] = mrun;
+        f[HG * kHeadDim + HG + n] = lrun;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] = f[hh * kHeadDim + 8 * sub + e];
+      m[hh] = f[HG * kHeadDim + hh];
+      l[hh] = f[HG * kHeadDim + HG + hh];
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+};
+static_assert(16 * kHeadDim * 4 + 2 * 16 * 4 <= kMfmaTileElems * 2, "the fold fits in the LDS tile");
+
 }  // namespace fasa
