@@ -165,8 +165,8 @@ __device__ __forceinline__ void store_partial(const FacArgs& a, const W& w, Wave
 //                [unit * cap, unit * cap + sel_count[unit]) of k_pool / v_pool
 //                (selected rows already gathered there).
 enum { kSelRows = 0, kDenseRows = 1, kStagedRows = 2 };
-template <typename T, typename Acc, int HG, bool MERGE, int ROWS = kSelRows>
-__global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
+template <typename T, typename Acc, int HG, bool MERGE, int ROWS>
+__device__ __forceinline__ void fac_split_body(const FacArgs& a) {
   constexpr bool DENSE = ROWS == kDenseRows;
   const Common& c = a.c;
   const FacPlan& p = a.p;
@@ -228,6 +228,22 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
       return;
     merge_heads<Acc, HG>(a, int64_t(b) * c.n_q_heads + g * c.group + h0, nh);
   }
+}
+
+// fp32 caches (fp64 vector arithmetic).
+template <int HG, bool MERGE, int ROWS>
+__global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
+  fac_split_body<float, double, HG, MERGE, ROWS>(a);
+}
+
+// bf16 caches (matrix-core waves), held to three waves per SIMD: each wave
+// waits for a whole 32-row block before it computes, so the waves of a SIMD
+// overlap each other's loads (measured faster than two waves per SIMD on the
+// dense and split launches, at the cost of a register or two spilled with
+// 4 and 8 heads per pass).
+template <int HG, bool MERGE, int ROWS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void fac_split_mfma_kernel(FacArgs a) {
+  fac_split_body<uint16_t, float, HG, MERGE, ROWS>(a);
 }
 
 constexpr int kSelThreads = 512;            // workgroup of the selecting launch
@@ -425,13 +441,20 @@ __global__ __launch_bounds__(kHeadDim) void fac_merge_kernel(FacArgs a) {
   a.out[(int64_t(b) * a.c.n_q_heads + h) * kHeadDim + d] = res;
 }
 
+template <int HG, bool MERGE, int ROWS>
+void launch_split_hg(bool bf16, const FacArgs& a, const dim3& grid, hipStream_t s) {
+  if (bf16) hipLaunchKernelGGL((fac_split_mfma_kernel<HG, MERGE, ROWS>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((fac_split_kernel<HG, MERGE, ROWS>), grid, dim3(256), 0, s, a);
+}
+
 template <typename T, typename Acc, bool MERGE, int ROWS = kSelRows>
 void launch_split(const FacArgs& a, const dim3& grid, hipStream_t s) {
+  constexpr bool bf16 = sizeof(T) == 2;
   switch (a.p.heads_per_pass) {
-    case 1: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 1, MERGE, ROWS>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 2, MERGE, ROWS>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 4, MERGE, ROWS>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((fac_split_kernel<T, Acc, 8, MERGE, ROWS>), grid, dim3(256), 0, s, a); break;
+    case 1: launch_split_hg<1, MERGE, ROWS>(bf16, a, grid, s); break;
+    case 2: launch_split_hg<2, MERGE, ROWS>(bf16, a, grid, s); break;
+    case 4: launch_split_hg<4, MERGE, ROWS>(bf16, a, grid, s); break;
+    default: launch_split_hg<8, MERGE, ROWS>(bf16, a, grid, s); break;
   }
 }
 
