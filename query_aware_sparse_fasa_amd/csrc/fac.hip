@@ -271,6 +271,7 @@ struct FacSelShared {
       int32_t idx[kSmallCand];
     } s;
     WaveFold<Acc, HG, kSelWaves> fold;
+    alignas(16) uint16_t tiles[kSelWaves][kMfmaTileElems16];   // bf16 FAC: one LDS tile per wave
   } u;
   int32_t chosen[kSmallBudget];
   int32_t btab[kBtabLds];
@@ -302,8 +303,16 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   sel::load_counts(a.w.counts + unit * nfa, nfa, cnt);
   const int b1 = a.w.b1[unit];
   const int64_t head0 = int64_t(b) * c.n_q_heads + g * c.group + h0;
-  Raw8<T> qraw[HG];
-  FacWave<T, Acc, HG>::load_q(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, qraw);
+  // bf16 caches with 4 or more heads per workgroup run the FAC on the matrix
+  // cores (FacWaveMfma, 16-row blocks, whose LDS tiles take the select area
+  // once the select is done).  With fewer heads the vector path wins (measured:
+  // the matrix tiles mostly idle, and its 32 rows per wave in one round trip
+  // against two 16-row blocks); fp32 caches always take the vector path.
+  constexpr bool kMfma = sizeof(T) == 2 && HG >= 4;
+  Raw8<T> qraw[kMfma ? 1 : HG];
+  uint4 qm[kMfma ? 4 : 1];
+  if constexpr (kMfma) FacWaveMfma<HG, 16>::load_q(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, qm);
+  else FacWave<T, Acc, HG>::load_q(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, qraw);
   // The sequence's block-table row (at most kBtabLds entries), held in
   // registers through the select and moved to LDS after it.
   const int32_t* btab = a.block_table + int64_t(b) * c.max_blocks;
@@ -327,8 +336,9 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   __syncthreads();                          // the list and the block table are in LDS; the select area is free
 
   // Row r of the list: the forced prefix, the chosen, then the forced suffix.
-  FacWave<T, Acc, HG> w;
-  w.init_raw(qraw, nh, c.scale);
+  std::conditional_t<kMfma, FacWaveMfma<HG, 16>, FacWave<T, Acc, HG>> w;
+  if constexpr (kMfma) w.init_raw(qm, nh, c.scale, sm.u.tiles[wave]);
+  else w.init_raw(qraw, nh, c.scale);
   auto token = [&](int r) -> int {
     const int ch = sm.chosen[min(max(r - c_lo, 0), kSmallBudget - 1)];
     return (keep_all || r < c_lo) ? r : (r < c_lo + Bc ? ch : c_hi + (r - c_lo - Bc));
@@ -347,8 +357,14 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   // Row quads in flight per wave: 8 (a whole 32-row share of a 256-row list in
   // one round trip) for one head; fewer as the per-head state grows.
   constexpr int U = HG == 1 ? 8 : (HG <= 4 && sizeof(Acc) == 4 ? 4 : 2);
-  w.template run<U>(r0, r1, lane_offset, kbase, vbase);
-  w.fold_row_groups();
+  if constexpr (kMfma) {
+    w.template run<false>(r0, r1, lane_offset, kbase, vbase);
+    w.fold_row_groups();
+    __syncthreads();                        // the fold area below overlaps the other waves' tiles
+  } else {
+    w.template run<U>(r0, r1, lane_offset, kbase, vbase);
+    w.fold_row_groups();
+  }
 
   // Fold the waves through LDS and write the heads' outputs.
   WaveFold<Acc, HG, kSelWaves>& f = sm.u.fold;

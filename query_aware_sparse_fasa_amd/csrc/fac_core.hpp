@@ -300,15 +300,24 @@ struct FacWave {
 // rescale to a new maximum is lane-local.  fold_row_groups() moves the result
 // into FacWave's layout (lane sub holds channels 8 sub .. +7 of every head)
 // through the same LDS tile.
-constexpr int kMfmaTileRows = 32;
+//
+// BR = 16 (16-row blocks, half the LDS tile): one logit tile whose row i is
+// block row i, and P.V as v_mfma_f32_16x16x16bf16_1k (lane l: A[n][4 g + j],
+// B[4 g + j][n], j < 4), so lane l's logits (rows 4 g .. 4 g + 3) are its B
+// operand directly.
 constexpr int kMfmaTilePitch = 132;   // bf16 per LDS row (264 bytes)
+constexpr int kMfmaTileRows = 32;
 constexpr int kMfmaTileElems = kMfmaTileRows * kMfmaTilePitch;
+constexpr int kMfmaTileElems16 = 16 * kMfmaTilePitch;
 
-template <int HG>
+template <int HG, int BR = 32>
 struct FacWaveMfma {
   typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+  typedef __attribute__((ext_vector_type(4))) short s16x4;
   typedef __attribute__((ext_vector_type(4))) float f32x4;
   static_assert(HG <= 16, "heads are padded to 16 columns");
+  static_assert(BR == 16 || BR == 32, "16- or 32-row blocks");
+  static_assert(HG * kHeadDim * 4 + 2 * HG * 4 <= BR * kMfmaTilePitch * 2, "the fold fits in the LDS tile");
   // The result, in FacWave's layout, after fold_row_groups().
   float m[HG], l[HG], acc[HG][8];
   bf16x8 qb[4];       // Q^T operand for channel steps 0..3
@@ -317,16 +326,27 @@ struct FacWaveMfma {
   f32x4 o[8];         // O^T channels 16 dt + 4 g + i, head lane % 16
   uint16_t* tile;     // this wave's LDS tile (kMfmaTileElems)
 
-  __device__ __forceinline__ void init(const uint16_t* q_head0, int nh, float scale, uint16_t* lds_tile) {
+  // This lane's query slices (head lane % 16, channels 32 s + 8 g .. +7),
+  // loaded unconditionally (heads past nh repeat the last; init zeroes them).
+  static __device__ __forceinline__ void load_q(const uint16_t* q_head0, int nh, uint4 (&qm)[4]) {
     const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
     const uint16_t* qh = q_head0 + int64_t(min(n, nh - 1)) * kHeadDim + 8 * g;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       Raw8<uint16_t> x;
       x.load(qh + 32 * s);
-      const uint4 v = n < nh ? x.v : make_uint4(0u, 0u, 0u, 0u);
-      qb[s] = __builtin_bit_cast(bf16x8, v);
+      qm[s] = x.v;
     }
+  }
+  __device__ __forceinline__ void init(const uint16_t* q_head0, int nh, float scale, uint16_t* lds_tile) {
+    uint4 qm[4];
+    load_q(q_head0, nh, qm);
+    init_raw(qm, nh, scale, lds_tile);
+  }
+  __device__ __forceinline__ void init_raw(const uint4 (&qm)[4], int nh, float scale, uint16_t* lds_tile) {
+    const int n = threadIdx.x & 15;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qb[s] = __builtin_bit_cast(bf16x8, n < nh ? qm[s] : make_uint4(0u, 0u, 0u, 0u));
     zscale = scale * 1.4426950408889634f;
     mrun = -INFINITY;
     lrun = 0.f;
@@ -359,6 +379,12 @@ struct FacWaveMfma {
         const int64_t o = __shfl(my_off, x, 64);
         return ((ok >> x) & 1) ? o : dummy;
       };
+      if constexpr (BR == 16) {
+        for (int b = 0; b < nrows; b += 16) {   // wave-uniform
+          block16(b, ok, row_off, ld, kbase, vbase);
+        }
+        continue;
+      }
       for (int b = 0; b < nrows; b += kMfmaTileRows) {   // wave-uniform
         // K: this lane's row of tiles 0 and 1; V: rows 4 k + g, channels 8 n .. +7.
         const int kr = b + 8 * (n >> 2) + (n & 3);
@@ -432,6 +458,67 @@ struct FacWaveMfma {
     }
   }
 
+  // One 16-row block at block row b of the batch (BR = 16).
+  template <typename RowOff, typename Ld>
+  __device__ __forceinline__ void block16(int b, uint64_t ok, RowOff& row_off, Ld& ld, const uint16_t* kbase,
+                                          const uint16_t* vbase) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+    const int64_t k0 = row_off(b + n);
+    uint4 ka[4], va[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) ka[s] = ld(kbase + k0 + 32 * s + 8 * g);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) va[k] = ld(vbase + row_off(b + 4 * k + g) + 8 * n);
+    f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[s]), qb[s], st, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint2* dst = reinterpret_cast<uint2*>(tile + (4 * k + g) * kMfmaTilePitch + 8 * n);
+      dst[0] = make_uint2(va[k].x, va[k].y);
+      dst[1] = make_uint2(va[k].z, va[k].w);
+    }
+    float z[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int x = b + 4 * g + i;
+      z[i] = (((ok >> x) & 1) != 0) ? st[i] * zscale : -INFINITY;
+      mx = fmaxf(mx, z[i]);
+    }
+    float xa, xb;
+    lane_pair<16>(mx, xa, xb);
+    mx = fmaxf(xa, xb);
+    lane_pair<32>(mx, xa, xb);
+    mx = fmaxf(xa, xb);
+    const float mn = fmaxf(mrun, mx);
+    const float corr = merge_weight(mrun, mn);
+    mrun = mn;
+    s16x4 phi, plo;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = merge_weight(z[i], mn);
+      psum += p;
+      const __bf16 h = (__bf16)p;
+      phi[i] = __builtin_bit_cast(short, h);
+      plo[i] = __builtin_bit_cast(short, (__bf16)(p - (float)h));
+    }
+    lrun = lrun * corr + psum;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      s16x4 vt;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vt[j] = short(tile[(4 * g + j) * kMfmaTilePitch + 16 * dt + n]);
+      o[dt] = o[dt] * corr;
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo, o[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
   // The wave's state in FacWave's layout, through the LDS tile: O^T into
   // [head][channel] floats, the column sums and maxima after it.
   __device__ __forceinline__ void fold_row_groups() {
@@ -465,6 +552,5 @@ struct FacWaveMfma {
     __builtin_amdgcn_wave_barrier();
   }
 };
-static_assert(16 * kHeadDim * 4 + 2 * 16 * 4 <= kMfmaTileElems * 2, "the fold fits in the LDS tile");
 
 }  // namespace fasa
