@@ -188,10 +188,12 @@ __device__ __forceinline__ void fac_split_body(const FacArgs& a) {
   const int cap1 = c.cap > 0 ? c.cap - 1 : 0;
   const int j_first = (ROWS == kSelRows && c.cap > 0) ? sel[min(r0 + lane, cap1)] : -1;
   // bf16 caches run the logits and the weighted sum on the matrix cores
-  // (FacWaveMfma, one LDS tile per wave); fp32 caches keep the fp64 vector path.
+  // (FacWaveMfma, 16-row blocks, one LDS tile per wave: measured faster than
+  // 32-row blocks everywhere but dense decode at batch 16, +2%); fp32 caches
+  // keep the fp64 vector path.
   constexpr bool kMfma = sizeof(T) == 2;
-  __shared__ __attribute__((aligned(16))) uint16_t mfma_tile[kMfma ? kFacWaves : 1][kMfma ? kMfmaTileElems : 1];
-  std::conditional_t<kMfma, FacWaveMfma<HG>, FacWave<T, Acc, HG>> w;
+  __shared__ __attribute__((aligned(16))) uint16_t mfma_tile[kMfma ? kFacWaves : 1][kMfma ? kMfmaTileElems16 : 1];
+  std::conditional_t<kMfma, FacWaveMfma<HG, 16>, FacWave<T, Acc, HG>> w;
   const T* q_head0 = static_cast<const T*>(a.q) + (int64_t(b) * c.n_q_heads + g * c.group + h0) * kHeadDim;
   if constexpr (kMfma) w.init(q_head0, nh, c.scale, mfma_tile[wave]);
   else w.init(q_head0, nh, c.scale);
@@ -236,11 +238,10 @@ __global__ __launch_bounds__(256) void fac_split_kernel(FacArgs a) {
   fac_split_body<float, double, HG, MERGE, ROWS>(a);
 }
 
-// bf16 caches (matrix-core waves), held to three waves per SIMD: each wave
-// waits for a whole 32-row block before it computes, so the waves of a SIMD
-// overlap each other's loads (measured faster than two waves per SIMD on the
-// dense and split launches, at the cost of a register or two spilled with
-// 4 and 8 heads per pass).
+// bf16 caches (matrix-core waves), held to at least three waves per SIMD: each
+// wave waits for a whole block before it computes, so the waves of a SIMD
+// overlap each other's loads (three measured faster than two; forcing four
+// spilled registers and measured much slower).
 template <int HG, bool MERGE, int ROWS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void fac_split_mfma_kernel(FacArgs a) {
   fac_split_body<uint16_t, float, HG, MERGE, ROWS>(a);
