@@ -14,8 +14,8 @@
 // partial.  The partials of a head are merged with the log-sum-exp rule, in a
 // decode step with a small grid by the last workgroup of the head's split to
 // finish (an arrival counter decides which), otherwise by a second launch.
-// Per wave, bf16 caches run on the matrix cores (FacWaveMfma: 32-row blocks,
-// logits and the weighted sum as 16 x 16 x 32 products with the heads padded
+// Per wave, bf16 caches run on the matrix cores (FacWaveMfma: 16-row blocks,
+// logits and the weighted sum as 16 x 16 matrix products with the heads padded
 // to 16): with G query heads per row the vector-ALU version spent more issue
 // time than the rows take to arrive, and dense decode over every row was
 // bound by it.  fp32 caches keep the vector path (FacWave: four rows at a
@@ -188,12 +188,10 @@ __device__ __forceinline__ void fac_split_body(const FacArgs& a) {
   const int cap1 = c.cap > 0 ? c.cap - 1 : 0;
   const int j_first = (ROWS == kSelRows && c.cap > 0) ? sel[min(r0 + lane, cap1)] : -1;
   // bf16 caches run the logits and the weighted sum on the matrix cores
-  // (FacWaveMfma, 16-row blocks, one LDS tile per wave: measured faster than
-  // 32-row blocks everywhere but dense decode at batch 16, +2%); fp32 caches
-  // keep the fp64 vector path.
+  // (FacWaveMfma, one LDS tile per wave); fp32 caches keep the fp64 vector path.
   constexpr bool kMfma = sizeof(T) == 2;
-  __shared__ __attribute__((aligned(16))) uint16_t mfma_tile[kMfma ? kFacWaves : 1][kMfma ? kMfmaTileElems16 : 1];
-  std::conditional_t<kMfma, FacWaveMfma<HG, 16>, FacWave<T, Acc, HG>> w;
+  __shared__ __attribute__((aligned(16))) uint16_t mfma_tile[kMfma ? kFacWaves : 1][kMfma ? kMfmaTileElems : 1];
+  std::conditional_t<kMfma, FacWaveMfma<HG>, FacWave<T, Acc, HG>> w;
   const T* q_head0 = static_cast<const T*>(a.q) + (int64_t(b) * c.n_q_heads + g * c.group + h0) * kHeadDim;
   if constexpr (kMfma) w.init(q_head0, nh, c.scale, mfma_tile[wave]);
   else w.init(q_head0, nh, c.scale);
@@ -272,7 +270,7 @@ struct FacSelShared {
       int32_t idx[kSmallCand];
     } s;
     WaveFold<Acc, HG, kSelWaves> fold;
-    alignas(16) uint16_t tiles[kSelWaves][kMfmaTileElems16];   // bf16 FAC: one LDS tile per wave
+    alignas(16) uint16_t tiles[kSelWaves][kMfmaTileElems];   // bf16 FAC: one LDS tile per wave
   } u;
   int32_t chosen[kSmallBudget];
   int32_t btab[kBtabLds];
@@ -312,7 +310,7 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   constexpr bool kMfma = sizeof(T) == 2 && HG >= 4;
   Raw8<T> qraw[kMfma ? 1 : HG];
   uint4 qm[kMfma ? 4 : 1];
-  if constexpr (kMfma) FacWaveMfma<HG, 16>::load_q(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, qm);
+  if constexpr (kMfma) FacWaveMfma<HG>::load_q(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, qm);
   else FacWave<T, Acc, HG>::load_q(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, qraw);
   // The sequence's block-table row (at most kBtabLds entries), held in
   // registers through the select and moved to LDS after it.
@@ -337,7 +335,7 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   __syncthreads();                          // the list and the block table are in LDS; the select area is free
 
   // Row r of the list: the forced prefix, the chosen, then the forced suffix.
-  std::conditional_t<kMfma, FacWaveMfma<HG, 16>, FacWave<T, Acc, HG>> w;
+  std::conditional_t<kMfma, FacWaveMfma<HG>, FacWave<T, Acc, HG>> w;
   if constexpr (kMfma) w.init_raw(qm, nh, c.scale, sm.u.tiles[wave]);
   else w.init_raw(qraw, nh, c.scale);
   auto token = [&](int r) -> int {

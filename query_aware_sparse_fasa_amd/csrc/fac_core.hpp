@@ -272,52 +272,44 @@ struct FacWave {
 };
 
 // ---------------------------------------------------------------------------
-// Matrix-core variant for bf16 caches (v_mfma_f32_16x16x32_bf16), the same
-// online softmax over 32-row blocks.  With G query heads per kv head the
-// per-row work is a G x 128 contraction with K and a G-wide P times V; on the
-// vector ALUs it costs more issue time than the rows take to arrive from HBM,
-// on the matrix cores a small part of it.
+// Matrix-core variant for bf16 caches, the same online softmax over 16-row
+// blocks.  With G query heads per kv head the per-row work is a G x 128
+// contraction with K and a G-wide P times V; on the vector ALUs it costs more
+// issue time than the rows take to arrive from HBM, on the matrix cores a small
+// part of it.
 //
-// Operand layout of the instruction (lane l, g = l / 16, n = l % 16, j < 8):
-// A[n][8 g + j], B[8 g + j][n]; the 16 x 16 result D[4 g + i][n], i < 4.
-//   Logits, one 16-row tile t of a 32-row block at a time: S_t = K_t Q^T, heads
-//     padded to 16 (columns n >= HG are zero).  A = K rows: lane l loads 16
-//     bytes of its row, channels 32 s + 8 g .. +7 for step s < 4; B = Q^T in the
-//     same channel order (loaded once).  Tile t's row i is block row
-//     8 (i / 4) + 4 t + i % 4, so that lane l ends up with the logits of block
-//     rows 8 g .. 8 g + 7 for head n -- exactly its part of P as the B operand
-//     of the next product.
-//   Weighted sum: O^T += V^T P.  A = V^T: lane l needs channel 16 dt + n of
-//     block rows 8 g .. 8 g + 7, a transposed access, so each wave first writes
-//     its 32 V rows into its own LDS tile (rows padded to 264 bytes: the four
-//     row groups of a read land in different banks) and reads them back 16 bits
-//     at a time.  B = P, split into a bf16 high part and a bf16 low part (the
-//     rounding error of a single bf16 P, about 2^-9 of |v|, would exceed the
-//     2e-3 bound on outputs with large channels); the two products add up to P
-//     within about 2^-17.  D: lane l holds channels 16 dt + 4 g + i of head n.
+// Lane l, g = l / 16, n = l % 16.  Both instructions give the 16 x 16 result as
+// D[4 g + i][n], i < 4.
+//   Logits: S = K Q^T with v_mfma_f32_16x16x32_bf16 (A[n][8 g + j],
+//     B[8 g + j][n], j < 8), heads padded to 16 columns (n >= HG are zero).
+//     A = K rows: lane l loads 16 bytes of block row n, channels 32 s + 8 g .. +7
+//     for step s < 4; B = Q^T in the same channel order (loaded once).  Lane l
+//     ends up with the logits of block rows 4 g .. 4 g + 3 for head n.
+//   Weighted sum: O^T += V^T P with v_mfma_f32_16x16x16bf16_1k (A[n][4 g + j],
+//     B[4 g + j][n], j < 4).  B = P: lane l's own four logits' weights.  A = V^T:
+//     lane l needs channel 16 dt + n of block rows 4 g .. 4 g + 3, a transposed
+//     access, so each wave first writes its 16 V rows into its own LDS tile
+//     (rows padded to 264 bytes: the four row groups of a read land in
+//     different banks) and reads them back 16 bits at a time.  P enters as a
+//     bf16 high part and a bf16 low part (the rounding error of a single bf16
+//     P, about 2^-9 of |v|, would exceed the 2e-3 bound on outputs with large
+//     channels); the two products add up to P within about 2^-17.  D: lane l
+//     holds channels 16 dt + 4 g + i of head n.
 // Lane l keeps the running max of head n (the same in the four lanes of the
 // column), its own partial sum, and the 32 channels of O^T above, so the
 // rescale to a new maximum is lane-local.  fold_row_groups() moves the result
 // into FacWave's layout (lane sub holds channels 8 sub .. +7 of every head)
 // through the same LDS tile.
-//
-// BR = 16 (16-row blocks, half the LDS tile): one logit tile whose row i is
-// block row i, and P.V as v_mfma_f32_16x16x16bf16_1k (lane l: A[n][4 g + j],
-// B[4 g + j][n], j < 4), so lane l's logits (rows 4 g .. 4 g + 3) are its B
-// operand directly.
-constexpr int kMfmaTilePitch = 132;   // bf16 per LDS row (264 bytes)
-constexpr int kMfmaTileRows = 32;
-constexpr int kMfmaTileElems = kMfmaTileRows * kMfmaTilePitch;
-constexpr int kMfmaTileElems16 = 16 * kMfmaTilePitch;
+constexpr int kMfmaTilePitch = 132;                  // bf16 per LDS row (264 bytes)
+constexpr int kMfmaTileElems = 16 * kMfmaTilePitch;  // one wave's tile
 
-template <int HG, int BR = 32>
+template <int HG>
 struct FacWaveMfma {
   typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
   typedef __attribute__((ext_vector_type(4))) short s16x4;
   typedef __attribute__((ext_vector_type(4))) float f32x4;
   static_assert(HG <= 16, "heads are padded to 16 columns");
-  static_assert(BR == 16 || BR == 32, "16- or 32-row blocks");
-  static_assert(HG * kHeadDim * 4 + 2 * HG * 4 <= BR * kMfmaTilePitch * 2, "the fold fits in the LDS tile");
+  static_assert(HG * kHeadDim * 4 + 2 * HG * 4 <= kMfmaTileElems * 2, "the fold fits in the LDS tile");
   // The result, in FacWave's layout, after fold_row_groups().
   float m[HG], l[HG], acc[HG][8];
   bf16x8 qb[4];       // Q^T operand for channel steps 0..3
@@ -362,12 +354,6 @@ struct FacWaveMfma {
   __device__ __forceinline__ void run(int r0, int r1, LaneOffset lane_offset, const uint16_t* kbase,
                                       const uint16_t* vbase) {
     const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-    auto ld = [](const uint16_t* p) -> uint4 {
-      Raw8<uint16_t> x;
-      if constexpr (NT) x.load_nt(p);
-      else x.load(p);
-      return x.v;
-    };
     for (int base = r0; base < r1; base += 64) {   // wave-uniform
       const int64_t my_off = lane_offset(base + lane);
       const int nrows = min(64, r1 - base);
@@ -379,49 +365,33 @@ struct FacWaveMfma {
         const int64_t o = __shfl(my_off, x, 64);
         return ((ok >> x) & 1) ? o : dummy;
       };
-      if constexpr (BR == 16) {
-        for (int b = 0; b < nrows; b += 16) {   // wave-uniform
-          block16(b, ok, row_off, ld, kbase, vbase);
-        }
-        continue;
-      }
-      for (int b = 0; b < nrows; b += kMfmaTileRows) {   // wave-uniform
-        // K: this lane's row of tiles 0 and 1; V: rows 4 k + g, channels 8 n .. +7.
-        const int kr = b + 8 * (n >> 2) + (n & 3);
-        const int64_t k0 = row_off(kr), k1 = row_off(kr + 4);
-        uint4 ka[2][4], va[8];
+      for (int b = 0; b < nrows; b += 16) {   // wave-uniform
+        // K: block row n; V: rows 4 k + g, channels 8 n .. +7.
+        const int64_t k0 = row_off(b + n);
+        uint4 ka[4], va[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          ka[0][s] = ld(kbase + k0 + 32 * s + 8 * g);
-          ka[1][s] = ld(kbase + k1 + 32 * s + 8 * g);
-        }
+        for (int s = 0; s < 4; ++s) ka[s] = load16<NT>(kbase + k0 + 32 * s + 8 * g);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) va[k] = ld(vbase + row_off(b + 4 * k + g) + 8 * n);
-        f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        for (int k = 0; k < 4; ++k) va[k] = load16<NT>(vbase + row_off(b + 4 * k + g) + 8 * n);
+        f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          st[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[0][s]), qb[s], st[0], 0, 0, 0);
-          st[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[1][s]), qb[s], st[1], 0, 0, 0);
-        }
+        for (int s = 0; s < 4; ++s)
+          st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[s]), qb[s], st, 0, 0, 0);
         // V rows into the LDS tile (8-byte writes; the tile rows are 8-byte aligned).
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < 4; ++k) {
           uint2* dst = reinterpret_cast<uint2*>(tile + (4 * k + g) * kMfmaTilePitch + 8 * n);
           dst[0] = make_uint2(va[k].x, va[k].y);
           dst[1] = make_uint2(va[k].z, va[k].w);
         }
-        // Logits of block rows 8 g + 4 t + i, head n; the block maximum of the column.
-        float z[8];
+        // Logits of block rows 4 g + i, head n; the block maximum of the column.
+        float z[4];
         float mx = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int x = b + 8 * g + 4 * t + i;
-            const bool v = ((ok >> x) & 1) != 0;
-            z[4 * t + i] = v ? st[t][i] * zscale : -INFINITY;
-            mx = fmaxf(mx, z[4 * t + i]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int x = b + 4 * g + i;
+          z[i] = (((ok >> x) & 1) != 0) ? st[i] * zscale : -INFINITY;
+          mx = fmaxf(mx, z[i]);
         }
         float xa, xb;
         lane_pair<16>(mx, xa, xb);
@@ -431,92 +401,38 @@ struct FacWaveMfma {
         const float mn = fmaxf(mrun, mx);
         const float corr = merge_weight(mrun, mn);
         mrun = mn;
-        bf16x8 phi, plo;
+        s16x4 phi, plo;
         float psum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = merge_weight(z[e], mn);
+        for (int i = 0; i < 4; ++i) {
+          const float p = merge_weight(z[i], mn);
           psum += p;
           const __bf16 h = (__bf16)p;
-          phi[e] = h;
-          plo[e] = (__bf16)(p - (float)h);
+          phi[i] = __builtin_bit_cast(short, h);
+          plo[i] = __builtin_bit_cast(short, (__bf16)(p - (float)h));
         }
         lrun = lrun * corr + psum;
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          bf16x8 vt;
+          s16x4 vt;
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            vt[j] = __builtin_bit_cast(__bf16, tile[(8 * g + j) * kMfmaTilePitch + 16 * dt + n]);
+          for (int j = 0; j < 4; ++j) vt[j] = short(tile[(4 * g + j) * kMfmaTilePitch + 16 * dt + n]);
           o[dt] = o[dt] * corr;
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi, o[dt], 0, 0, 0);
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, plo, o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi, o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo, o[dt], 0, 0, 0);
         }
         __builtin_amdgcn_wave_barrier();
       }
     }
   }
 
-  // One 16-row block at block row b of the batch (BR = 16).
-  template <typename RowOff, typename Ld>
-  __device__ __forceinline__ void block16(int b, uint64_t ok, RowOff& row_off, Ld& ld, const uint16_t* kbase,
-                                          const uint16_t* vbase) {
-    const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-    const int64_t k0 = row_off(b + n);
-    uint4 ka[4], va[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) ka[s] = ld(kbase + k0 + 32 * s + 8 * g);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) va[k] = ld(vbase + row_off(b + 4 * k + g) + 8 * n);
-    f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[s]), qb[s], st, 0, 0, 0);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint2* dst = reinterpret_cast<uint2*>(tile + (4 * k + g) * kMfmaTilePitch + 8 * n);
-      dst[0] = make_uint2(va[k].x, va[k].y);
-      dst[1] = make_uint2(va[k].z, va[k].w);
-    }
-    float z[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int x = b + 4 * g + i;
-      z[i] = (((ok >> x) & 1) != 0) ? st[i] * zscale : -INFINITY;
-      mx = fmaxf(mx, z[i]);
-    }
-    float xa, xb;
-    lane_pair<16>(mx, xa, xb);
-    mx = fmaxf(xa, xb);
-    lane_pair<32>(mx, xa, xb);
-    mx = fmaxf(xa, xb);
-    const float mn = fmaxf(mrun, mx);
-    const float corr = merge_weight(mrun, mn);
-    mrun = mn;
-    s16x4 phi, plo;
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = merge_weight(z[i], mn);
-      psum += p;
-      const __bf16 h = (__bf16)p;
-      phi[i] = __builtin_bit_cast(short, h);
-      plo[i] = __builtin_bit_cast(short, (__bf16)(p - (float)h));
-    }
-    lrun = lrun * corr + psum;
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      s16x4 vt;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vt[j] = short(tile[(4 * g + j) * kMfmaTilePitch + 16 * dt + n]);
-      o[dt] = o[dt] * corr;
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi, o[dt], 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo, o[dt], 0, 0, 0);
-    }
-    __builtin_amdgcn_wave_barrier();
+  template <bool NT>
+  static __device__ __forceinline__ uint4 load16(const uint16_t* p) {
+    Raw8<uint16_t> x;
+    if constexpr (NT) x.load_nt(p);
+    else x.load(p);
+    return x.v;
   }
 
   // The wave's state in FacWave's layout, through the LDS tile: O^T into
