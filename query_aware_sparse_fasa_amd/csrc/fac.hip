@@ -112,10 +112,10 @@ struct WaveFold {
 
 // Fold the 4 wave states of heads head0 .. head0+nh-1 (after fold_row_groups)
 // through LDS into one partial (m, l, acc[128]) per head, stored in slot
-// blockIdx.x of the head's partials.
+// `split` of the head's partials.
 template <typename Acc, int HG, typename W>
 __device__ __forceinline__ void store_partial(const FacArgs& a, const W& w, WaveFold<Acc, HG>& f, int64_t head0,
-                                              int nh) {
+                                              int nh, int split) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, sub = lane & 15;
   if (lane < 16) {
 #pragma unroll
@@ -145,7 +145,7 @@ __device__ __forceinline__ void store_partial(const FacArgs& a, const W& w, Wave
         O = fma(f.acc[v][hh][ch], wgt, O);
       }
     }
-    const int64_t slot = (head0 + hh) * a.p.n_partials + blockIdx.x;
+    const int64_t slot = (head0 + hh) * a.p.n_partials + split;
     pacc[slot * kHeadDim + ch] = O;
     if (ch == 0) {
       pml[slot * 2 + 0] = M;
@@ -170,13 +170,14 @@ __device__ __forceinline__ void fac_split_body(const FacArgs& a) {
   constexpr bool DENSE = ROWS == kDenseRows;
   const Common& c = a.c;
   const FacPlan& p = a.p;
-  const int b = blockIdx.z;
-  const int g = blockIdx.y / p.head_chunks;
-  const int h0 = (blockIdx.y % p.head_chunks) * HG;      // first head of this pass, within the group
+  const WgCoord wg = xcd_grouped();
+  const int b = wg.z;
+  const int g = wg.y / p.head_chunks;
+  const int h0 = (wg.y % p.head_chunks) * HG;      // first head of this pass, within the group
   const int nh = min(HG, c.group - h0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, sub = lane & 15;
   const int64_t unit = int64_t(b) * c.n_kv_heads + g;
-  const int r0 = (blockIdx.x * kFacWaves + wave) * p.rows_per_wave;
+  const int r0 = (wg.x * kFacWaves + wave) * p.rows_per_wave;
   const int32_t* sel = a.sel_idx + unit * c.cap;
   const int32_t* btab = a.block_table + int64_t(b) * c.max_blocks;
 
@@ -220,11 +221,11 @@ __device__ __forceinline__ void fac_split_body(const FacArgs& a) {
   w.fold_row_groups();
 
   __shared__ WaveFold<Acc, HG> fold;
-  store_partial<Acc, HG>(a, w, fold, int64_t(b) * c.n_q_heads + g * c.group + h0, nh);
+  store_partial<Acc, HG>(a, w, fold, int64_t(b) * c.n_q_heads + g * c.group + h0, nh, wg.x);
   if constexpr (MERGE) {
     // The workgroup that completes the head chunk's split merges it.
     __shared__ uint32_t s_last;
-    if (!arrive_last(&a.arrive[int64_t(blockIdx.z) * gridDim.y + blockIdx.y], uint32_t(p.n_split), &s_last))
+    if (!arrive_last(&a.arrive[int64_t(wg.z) * gridDim.y + wg.y], uint32_t(p.n_split), &s_last))
       return;
     merge_heads<Acc, HG>(a, int64_t(b) * c.n_q_heads + g * c.group + h0, nh);
   }
@@ -276,13 +277,14 @@ struct FacSelShared {
   int32_t btab[kBtabLds];
 };
 
-// HG query heads per workgroup (blockIdx.x picks the head chunk): 1 when there
+// HG query heads per workgroup (the x coordinate picks the head chunk): 1 when there
 // are few units and latency rules, up to 8 when many units fill the chip and
 // each K/V row should be read once.
 template <typename T, typename Acc, int HG>
 __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   const Common& c = a.c;
-  const int b = blockIdx.z, g = blockIdx.y, hc = blockIdx.x;
+  const WgCoord wg = xcd_grouped();
+  const int b = wg.z, g = wg.y, hc = wg.x;
   const int h0 = hc * HG, nh = min(HG, c.group - h0);
   const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t unit = int64_t(b) * c.n_kv_heads + g;
@@ -415,7 +417,8 @@ __global__ __launch_bounds__(kHeadDim) void fac_merge_kernel(FacArgs a) {
   constexpr int MAXP = 512;
   __shared__ Acc s_w[MAXP], s_lw[MAXP];
   __shared__ Acc s_red[2];
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const WgCoord wg = xcd_grouped();
+  const int h = wg.x, b = wg.y, d = threadIdx.x;
   const int P = a.p.n_partials;
   const int64_t base = (int64_t(b) * a.c.n_q_heads + h) * P;
   const Acc* pacc = static_cast<const Acc*>(a.part_acc) + base * kHeadDim + d;

@@ -125,6 +125,29 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Workgroup coordinates in XCD-aware order.  The dispatcher hands the
+// workgroup with linear id L (x fastest) to XCD L mod 8, so consecutive
+// workgroups land on different XCDs and each XCD has its own L2.  Renumbering
+// L to l = (L mod 8) * (N / 8) + L / 8 (N workgroups; the last N mod 8 keep
+// their number) gives every XCD one contiguous run of logical ids.  Every
+// launch of a step orders its grid with the (sequence, kv head) unit as the
+// slow index, so a unit's workgroups share one L2 (the query heads of a group
+// reading the same rows, the chunks of one score row), and with N a multiple
+// of 8 a unit stays on the same XCD from launch to launch.  A bijection on
+// [0, N): every logical workgroup still runs exactly once.
+struct WgCoord {
+  int x, y, z;
+};
+__device__ __forceinline__ WgCoord xcd_grouped() {
+  const uint32_t X = gridDim.x, Y = gridDim.y;
+  const uint32_t n = X * Y * gridDim.z;
+  const uint32_t L = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
+  const uint32_t per = n >> 3;
+  const uint32_t l = L < (per << 3) ? (L & 7u) * per + (L >> 3) : L;
+  const uint32_t yz = l / X;
+  return WgCoord{int(l - yz * X), int(yz % Y), int(yz / Y)};
+}
+
 // Hand-off between the workgroups of one launch: the last one to arrive on
 // `counter` (which must start at zero) sees everything the others stored before
 // arriving.  Every wave waits until its own stores are acknowledged, the

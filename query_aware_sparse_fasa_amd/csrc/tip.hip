@@ -41,12 +41,13 @@ struct TipArgs {
 template <typename T, int FT, bool FROM_SLAB, bool HIST>
 __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
   const Common& c = a.c;
-  const int b = blockIdx.z, g = blockIdx.y;
+  const WgCoord wg = xcd_grouped();
+  const int b = wg.z, g = wg.y;
   const int F = FT > 0 ? FT : c.n_fc;
   // The wave index is made explicitly uniform so the block-table entry is a
   // scalar load, issued at once and waited on its own counter.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int blk = blockIdx.x * 4 + wave;
+  const int blk = wg.x * 4 + wave;
 
   // Dependency chain kept to two memory round trips: (sequence length, block
   // table entry, FC index) are independent loads; then the slab loads and the
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
   // nothing to do (the whole workgroup leaves together, before any barrier).
   // The slab loads need the length and the block-table entry anyway, so this
   // adds no wait for the others.
-  if (blockIdx.x * 4 * kBlock >= t) return;
+  if (wg.x * 4 * kBlock >= t) return;
 
   __shared__ float qf[kHeadDim];   // folded query, [f][2]
   __shared__ int cols[kHeadDim / 2];

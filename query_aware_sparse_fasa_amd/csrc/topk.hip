@@ -93,10 +93,11 @@ __device__ __forceinline__ void zero_fac_arrive(const TopkArgs& a, int64_t unit)
 template <bool VEC>
 __global__ __launch_bounds__(FNT) void hist_kernel(TopkArgs a) {
   const Common& c = a.c;
-  const int b = blockIdx.z;
-  const int64_t unit = int64_t(b) * c.n_kv_heads + blockIdx.y;
+  const WgCoord wg = xcd_grouped();
+  const int b = wg.z;
+  const int64_t unit = int64_t(b) * c.n_kv_heads + wg.y;
   const float* row = a.scores + unit * c.score_stride;
-  const int base = blockIdx.x * FCH;
+  const int base = wg.x * FCH;
   float v[8];
   load_chunk8<VEC>(row, row_lim<VEC>(c), base, v);
   int t, c_lo, c_hi;
@@ -124,11 +125,12 @@ __global__ __launch_bounds__(FNT) void hist_kernel(TopkArgs a) {
 template <bool VEC>
 __global__ __launch_bounds__(FNT) void filter_kernel(TopkArgs a) {
   const Common& c = a.c;
-  const int b = blockIdx.z, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t unit = int64_t(b) * c.n_kv_heads + blockIdx.y;
+  const WgCoord wg = xcd_grouped();
+  const int b = wg.z, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t unit = int64_t(b) * c.n_kv_heads + wg.y;
   const int nfa = filter_chunks(c);
   const float* row = a.scores + unit * c.score_stride;
-  const int base = blockIdx.x * FCH;
+  const int base = wg.x * FCH;
 
   // Independent loads: this thread's 8 scores and its 8 histogram bins.  Thread
   // t owns bins 2047-8t down to 2040-8t, so a scan over threads counts from the top.
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(FNT) void filter_kernel(TopkArgs a) {
   unit_range(c, a.seq_lens[b], t, c_lo, c_hi);
   const int nC = c_hi - c_lo;
   const int Bc = min(c.budget, nC);
-  if (blockIdx.x == 0) zero_fac_arrive(a, unit);
+  if (wg.x == 0) zero_fac_arrive(a, unit);
   if (Bc == nC) return;                // every candidate is kept: no kept-pair list
 
   __shared__ uint32_t s_w[FNT / 64];
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(FNT) void filter_kernel(TopkArgs a) {
   }
   const uint32_t tot0 = tot & 0xffffu, tot1 = tot >> 16;
   uint32_t pos0 = ex & 0xffffu, pos1 = tot0 + (ex >> 16);
-  uint2* out = static_cast<uint2*>(a.w.slots) + (unit * nfa + blockIdx.x) * int64_t(FCH);
+  uint2* out = static_cast<uint2*>(a.w.slots) + (unit * nfa + wg.x) * int64_t(FCH);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     uint32_t& pos = e < 4 ? pos0 : pos1;
@@ -203,8 +205,8 @@ __global__ __launch_bounds__(FNT) void filter_kernel(TopkArgs a) {
     pos += keep[e] ? 1u : 0u;
   }
   if (tid == 0) {
-    a.w.counts[unit * nfa + blockIdx.x] = int32_t(tot0 + tot1);
-    if (blockIdx.x == 0) a.w.b1[unit] = int32_t(b1);
+    a.w.counts[unit * nfa + wg.x] = int32_t(tot0 + tot1);
+    if (wg.x == 0) a.w.b1[unit] = int32_t(b1);
   }
 }
 
@@ -221,8 +223,9 @@ struct FinishShared {
 template <bool VEC>
 __global__ __launch_bounds__(BIG) void finish_kernel(TopkArgs a) {
   const Common& c = a.c;
-  const int b = blockIdx.y, tid = threadIdx.x;
-  const int64_t unit = int64_t(b) * c.n_kv_heads + blockIdx.x;
+  const WgCoord wg = xcd_grouped();
+  const int b = wg.y, tid = threadIdx.x;
+  const int64_t unit = int64_t(b) * c.n_kv_heads + wg.x;
   const int nfa = filter_chunks(c);
   const uint2* unit_slots = static_cast<const uint2*>(a.w.slots) + unit * nfa * int64_t(FCH);
   // Loads that do not depend on t_b go out first (clamped into the arrays).
