@@ -349,7 +349,8 @@ struct FacWaveMfma {
 
   // Rows r0 .. r1-1; lane_offset as for FacWave::run (called once per 64 rows
   // with r = base + lane).  Invalid rows load a valid row of the batch and get
-  // a -inf logit.  NT: non-temporal row loads.
+  // a -inf logit.  NT: non-temporal row loads.  One 16-row block's loads are in
+  // flight per wave at a time.
   template <bool NT = false, typename LaneOffset>
   __device__ __forceinline__ void run(int r0, int r1, LaneOffset lane_offset, const uint16_t* kbase,
                                       const uint16_t* vbase) {
@@ -373,58 +374,130 @@ struct FacWaveMfma {
         for (int s = 0; s < 4; ++s) ka[s] = load16<NT>(kbase + k0 + 32 * s + 8 * g);
 #pragma unroll
         for (int k = 0; k < 4; ++k) va[k] = load16<NT>(vbase + row_off(b + 4 * k + g) + 8 * n);
-        f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[s]), qb[s], st, 0, 0, 0);
-        // V rows into the LDS tile (8-byte writes; the tile rows are 8-byte aligned).
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          uint2* dst = reinterpret_cast<uint2*>(tile + (4 * k + g) * kMfmaTilePitch + 8 * n);
-          dst[0] = make_uint2(va[k].x, va[k].y);
-          dst[1] = make_uint2(va[k].z, va[k].w);
-        }
-        // Logits of block rows 4 g + i, head n; the block maximum of the column.
-        float z[4];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int x = b + 4 * g + i;
-          z[i] = (((ok >> x) & 1) != 0) ? st[i] * zscale : -INFINITY;
-          mx = fmaxf(mx, z[i]);
-        }
-        float xa, xb;
-        lane_pair<16>(mx, xa, xb);
-        mx = fmaxf(xa, xb);
-        lane_pair<32>(mx, xa, xb);
-        mx = fmaxf(xa, xb);
-        const float mn = fmaxf(mrun, mx);
-        const float corr = merge_weight(mrun, mn);
-        mrun = mn;
-        s16x4 phi, plo;
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = merge_weight(z[i], mn);
-          psum += p;
-          const __bf16 h = (__bf16)p;
-          phi[i] = __builtin_bit_cast(short, h);
-          plo[i] = __builtin_bit_cast(short, (__bf16)(p - (float)h));
-        }
-        lrun = lrun * corr + psum;
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          s16x4 vt;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) vt[j] = short(tile[(4 * g + j) * kMfmaTilePitch + 16 * dt + n]);
-          o[dt] = o[dt] * corr;
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi, o[dt], 0, 0, 0);
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo, o[dt], 0, 0, 0);
-        }
-        __builtin_amdgcn_wave_barrier();
+        block(ka, va, uint32_t(ok >> (b + 4 * g)) & 0xFu);
       }
     }
+  }
+
+  // Rows r0 .. r1-1 with the next block's loads in flight while a block is
+  // computed (two 16-row blocks, 16 KB per wave).  The row offsets of up to
+  // kPfRows rows are resolved first -- all of lane_offset's dependent loads in
+  // one go -- into this wave's LDS area `offs` (kPfRows entries; negative:
+  // invalid row, which loads the chunk's first valid row and gets a -inf logit).
+  static constexpr int kPfRows = 512;
+  template <bool NT, typename LaneOffset>
+  __device__ __forceinline__ void run_pipelined(int r0, int r1, LaneOffset lane_offset, const uint16_t* kbase,
+                                                const uint16_t* vbase, int64_t* offs) {
+    const int lane = threadIdx.x & 63;
+    for (int cb = r0; cb < r1; cb += kPfRows) {   // wave-uniform
+      int64_t o[kPfRows / 64];
+#pragma unroll
+      for (int k = 0; k < kPfRows / 64; ++k) o[k] = lane_offset(cb + 64 * k + lane);
+      int64_t dummy = -1;
+#pragma unroll
+      for (int k = kPfRows / 64 - 1; k >= 0; --k) {   // the lowest valid row wins
+        const uint64_t m = __ballot(o[k] >= 0);
+        if (m != 0) dummy = __shfl(o[k], __ffsll((unsigned long long)m) - 1, 64);
+      }
+      if (dummy < 0) continue;                       // no valid row in this chunk
+      __builtin_amdgcn_wave_barrier();               // the previous chunk's reads of offs are done
+#pragma unroll
+      for (int k = 0; k < kPfRows / 64; ++k) offs[64 * k + lane] = o[k];
+      __builtin_amdgcn_wave_barrier();
+      const int nb = (min(kPfRows, r1 - cb) + 15) >> 4;
+      uint4 ka[4], va[4];
+      uint32_t ra;
+      load_block<NT>(offs, 0, dummy, kbase, vbase, ka, va, ra);
+      for (int i = 1; i < nb; ++i) {                 // wave-uniform
+        uint4 kb[4], vb[4];
+        uint32_t rb;
+        load_block<NT>(offs, 16 * i, dummy, kbase, vbase, kb, vb, rb);
+        block(ka, va, ra);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          ka[s] = kb[s];
+          va[s] = vb[s];
+        }
+        ra = rb;
+      }
+      block(ka, va, ra);
+    }
+  }
+
+  // Loads of the 16-row block at row b of `offs` (see run_pipelined); rv bit i:
+  // block row 4 g + i is valid.
+  template <bool NT>
+  static __device__ __forceinline__ void load_block(const int64_t* offs, int b, int64_t dummy, const uint16_t* kbase,
+                                                    const uint16_t* vbase, uint4 (&ka)[4], uint4 (&va)[4],
+                                                    uint32_t& rv) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+    const int64_t kr = offs[b + n];
+    const uint16_t* kp = kbase + (kr >= 0 ? kr : dummy) + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) ka[s] = load16<NT>(kp + 32 * s);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t vr = offs[b + 4 * k + g];
+      va[k] = load16<NT>(vbase + (vr >= 0 ? vr : dummy) + 8 * n);
+    }
+    rv = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rv |= offs[b + 4 * g + i] >= 0 ? (1u << i) : 0u;
+  }
+
+  // One 16-row block: ka holds K block row n (channels 32 s + 8 g .. +7), va V
+  // rows 4 k + g (channels 8 n .. +7); rv bit i: block row 4 g + i is valid.
+  __device__ __forceinline__ void block(const uint4 (&ka)[4], const uint4 (&va)[4], uint32_t rv) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+    f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[s]), qb[s], st, 0, 0, 0);
+    // V rows into the LDS tile (8-byte writes; the tile rows are 8-byte aligned).
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint2* dst = reinterpret_cast<uint2*>(tile + (4 * k + g) * kMfmaTilePitch + 8 * n);
+      dst[0] = make_uint2(va[k].x, va[k].y);
+      dst[1] = make_uint2(va[k].z, va[k].w);
+    }
+    // Logits of block rows 4 g + i, head n; the block maximum of the column.
+    float z[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = ((rv >> i) & 1u) != 0u ? st[i] * zscale : -INFINITY;
+      mx = fmaxf(mx, z[i]);
+    }
+    float xa, xb;
+    lane_pair<16>(mx, xa, xb);
+    mx = fmaxf(xa, xb);
+    lane_pair<32>(mx, xa, xb);
+    mx = fmaxf(xa, xb);
+    const float mn = fmaxf(mrun, mx);
+    const float corr = merge_weight(mrun, mn);
+    mrun = mn;
+    s16x4 phi, plo;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = merge_weight(z[i], mn);
+      psum += p;
+      const __bf16 h = (__bf16)p;
+      phi[i] = __builtin_bit_cast(short, h);
+      plo[i] = __builtin_bit_cast(short, (__bf16)(p - (float)h));
+    }
+    lrun = lrun * corr + psum;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      s16x4 vt;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vt[j] = short(tile[(4 * g + j) * kMfmaTilePitch + 16 * dt + n]);
+      o[dt] = o[dt] * corr;
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo, o[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 
   template <bool NT>
