@@ -274,10 +274,22 @@ __device__ __forceinline__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off,
         }
       }
     }
-    // Pairs past the first 64 of a chunk (a chunk keeps up to FCH).
+    // Pairs past the first 64 of a chunk (a chunk keeps up to FCH), 8 x 64 of
+    // them per wave at a time: the loads go out together (clamped into the
+    // chunk's slots, always readable), then the valid ones are copied.
     for (int ch = wave; ch < nfc; ch += NW) {
       const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
-      for (int k = 64 + lane; k < n; k += 64) put(o + k, slots[int64_t(ch) * FCH + k]);
+      const uint2* cs = slots + int64_t(ch) * FCH;
+      for (int k0 = 64; k0 < n; k0 += 8 * 64) {   // wave-uniform
+        uint2 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = cs[min(k0 + 64 * u + lane, FCH - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int k = k0 + 64 * u + lane;
+          if (k < n) put(o + k, v[u]);
+        }
+      }
     }
   }
   // The barrier inside the scan also publishes the copied pairs and the histogram.
