@@ -166,7 +166,11 @@ fasa_status fasa_topk(const fasa_shape* shape, const float* scores,
 
 /* FAC over a given selection (sel_idx / sel_count laid out for max_t).
  * bf16 caches compute in fp32; fp32 caches compute logits, softmax and the
- * weighted sum in fp64 and round the result to fp32 once. */
+ * weighted sum in fp64 and round the result to fp32 once.  sel_count is
+ * clamped into [0, cap]; entries of sel_idx[0..sel_count) below 0 or at or past
+ * max_blocks_per_seq * block_size contribute nothing, and a head whose
+ * selection holds no such valid entry gets an all-zero output.  Entries that
+ * are in range but past t_b read whatever the cache holds there. */
 fasa_status fasa_fac(const fasa_shape* shape, const void* q, const void* k_pool,
                      const void* v_pool, const int32_t* block_table,
                      const int32_t* sel_idx, const int32_t* sel_count, int32_t max_t,

@@ -252,6 +252,63 @@ def test_fac_on_oracle_selection(name):
         assert err <= PR.OUT_ATOL[cfg.dtype], f"{name} b={b} g={g}: {err:.3e}"
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_fac_skips_entries_outside_the_cache(dtype):
+    """fasa_fac over long, ragged selections with entries outside the cache mixed in.
+
+    Entries of sel_idx[0..sel_count) below 0 or past the block table's last slot
+    contribute nothing; the result is the oracle's FAC over the remaining rows (0
+    for a unit with none).  At about 9000 rows per unit the bf16 launch gives each
+    wave more than 64 rows, so the matrix-core waves take the pipelined loop (row
+    offsets resolved up front, next block in flight); the fp32 launch runs the
+    vector waves."""
+    say(f"[fac-skip] {dtype}")
+    cfg = C["c2"].replace(dtype=dtype, batch=2, t=9000, budget=9000)
+    inp = synth.make_inputs(cfg, seed=5, device="cpu")
+    L = DeviceLayer(inp, device="cuda", with_slab=False)
+    t = int(inp.seq_lens[0])
+    lim = inp.max_blocks * 256
+    rng = np.random.default_rng(11)
+    sel = np.full((cfg.batch, cfg.n_kv_heads, L.cap), -1, dtype=np.int32)
+    cnt = np.zeros((cfg.batch, cfg.n_kv_heads), dtype=np.int32)
+    valid = {}
+    for b in range(cfg.batch):
+        for g in range(cfg.n_kv_heads):
+            if (b, g) == (1, 7):
+                valid[(b, g)] = np.zeros(0, dtype=np.int64)      # empty selection
+                continue
+            if (b, g) == (1, 6):
+                row = np.array([-1, lim, -100, lim + 77, 2**31 - 1] * 20, dtype=np.int64)
+                valid[(b, g)] = np.zeros(0, dtype=np.int64)      # nothing valid
+            else:
+                n = int(rng.integers(7000, L.cap + 1))
+                keep = np.sort(rng.choice(t, size=n, replace=False))
+                row = keep.copy()
+                bad = rng.choice(n, size=n // 50, replace=False)
+                row[bad] = rng.choice([-1, -100, lim, lim + 77, 2**31 - 1], size=len(bad))
+                valid[(b, g)] = np.delete(keep, bad)
+            cnt[b, g] = len(row)
+            sel[b, g, :len(row)] = row
+    L.sel_idx.copy_(torch.from_numpy(sel))
+    L.sel_count.copy_(torch.from_numpy(cnt))
+    L.out.fill_(float("nan"))
+    L.fac()
+    torch.cuda.synchronize()
+    out = L.out.cpu().numpy()
+    G = cfg.group
+    for (b, g), rows in valid.items():
+        got = out[b, g * G:(g + 1) * G]
+        if len(rows) == 0:
+            assert (got == 0).all(), f"{dtype} b={b} g={g}: no valid row, output not zero"
+            continue
+        q = inp.q[b, g * G:(g + 1) * G].double().cpu().numpy()
+        K = unit_rows(inp, b, g, inp.k_pool).double().cpu().numpy()
+        V = unit_rows(inp, b, g, inp.v_pool).double().cpu().numpy()
+        ref, _ = O.fac(q, K[rows], V[rows], 1 / np.sqrt(128))
+        err = np.abs(got - ref).max()
+        assert err <= PR.OUT_ATOL[dtype], f"{dtype} b={b} g={g}: {err:.3e}"
+
+
 # ------------------------------------------------------------------------ whole step
 def _check_decode(inp, L, units, label, m=False):
     """Selections and outputs of the last fasa_decode (m: fasa_m_decode) on L."""
