@@ -11,6 +11,8 @@
 // written as ascending token indices.
 #pragma once
 
+#include <type_traits>
+
 #include "fasa_device.hpp"
 #include "fasa_internal.hpp"
 
@@ -274,22 +276,28 @@ __device__ __forceinline__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off,
         }
       }
     }
-    // Pairs past the first 64 of a chunk (a chunk keeps up to FCH), 8 x 64 of
-    // them per wave at a time: the loads go out together (clamped into the
-    // chunk's slots, always readable), then the valid ones are copied.
+    // Pairs past the first 64 of a chunk (a chunk keeps up to FCH), U x 64 of
+    // them per wave at a time: the loads go out together (clamped to the
+    // chunk's last kept pair, so loads past the end all read one line), then
+    // the valid ones are copied.  U is 8 while more than 128 pairs remain, 2
+    // for the last few (each width is straight-line code with its own wait).
+    auto copy_run = [&](auto width, const uint2* cs, int o, int n, int k0) {
+      constexpr int U = decltype(width)::value;
+      uint2 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = cs[min(k0 + 64 * u + lane, n - 1)];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + 64 * u + lane;
+        if (k < n) put(o + k, v[u]);
+      }
+    };
     for (int ch = wave; ch < nfc; ch += NW) {
       const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
       const uint2* cs = slots + int64_t(ch) * FCH;
-      for (int k0 = 64; k0 < n; k0 += 8 * 64) {   // wave-uniform
-        uint2 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = cs[min(k0 + 64 * u + lane, FCH - 1)];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int k = k0 + 64 * u + lane;
-          if (k < n) put(o + k, v[u]);
-        }
-      }
+      int k0 = 64;
+      for (; n - k0 > 128; k0 += 8 * 64) copy_run(std::integral_constant<int, 8>(), cs, o, n, k0);   // wave-uniform
+      if (k0 < n) copy_run(std::integral_constant<int, 2>(), cs, o, n, k0);
     }
   }
   // The barrier inside the scan also publishes the copied pairs and the histogram.
