@@ -252,6 +252,35 @@ def main():
     log(f"[bench] dense decode {t_dense * 1e6:.2f} us ({dense_gbps:,.0f} GB/s); "
         f"FASA step is {t_dense / (el / args.steps):.2f}x faster")
 
+    # Measured reference rates on this GPU, same stream and event timing: a
+    # 1 GiB device-to-device copy (1 GiB read + 1 GiB written) and a 1 GiB
+    # read reduction (torch.sum over fp32).  The HBM peak is the published one;
+    # these say how far a plain library kernel gets on the same part.
+    ref_src = torch.empty(1 << 28, dtype=torch.float32, device=dev).uniform_()
+    ref_dst = torch.empty_like(ref_src)
+    ref_out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def time_ref(fn, n=20):
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                fn()
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for _ in range(n):
+                fn()
+            s1.record(stream)
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) / 1e3 / n
+
+    t_copy = time_ref(lambda: ref_dst.copy_(ref_src))
+    t_read = time_ref(lambda: torch.sum(ref_src, dim=0, out=ref_out))
+    copy_gbps = 2 * (1 << 30) / t_copy / 1e9
+    read_gbps = (1 << 30) / t_read / 1e9
+    del ref_src, ref_dst, ref_out
+    log(f"[bench] reference kernels: 1 GiB copy {copy_gbps:,.0f} GB/s (read + write), "
+        f"1 GiB sum {read_gbps:,.0f} GB/s")
+
     # FASA-M: the same step with the non-dominant key columns and the values in
     # pinned host memory (two layer copies; the host arrays are per layer).
     fasa_m = None
@@ -352,6 +381,10 @@ def main():
                      "traffic": measured_traffic(args.config, use_slab),
                      "algorithmic_bytes_per_launch": int(tip_bytes),
                      "avg_launch_us": t_tip * 1e6},
+        "measured_references": {"copy_1GiB_GBps": copy_gbps, "sum_1GiB_GBps": read_gbps,
+                                "tip_frac_of_copy": tip_gbps / copy_gbps, "tip_frac_of_sum": tip_gbps / read_gbps,
+                                "step_frac_of_sum": step_gbps / read_gbps,
+                                "dense_frac_of_sum": dense_gbps / read_gbps},
         "dense_decode": {"us_per_step": t_dense * 1e6, "bytes": int(sb["dense"]), "achieved_GBps": dense_gbps,
                          "hbm_frac": dense_gbps / HBM_PEAK_GBPS,
                          "fasa_speedup": t_dense / (el / args.steps)},
