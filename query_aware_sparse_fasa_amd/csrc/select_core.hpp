@@ -206,12 +206,12 @@ __device__ __forceinline__ void unit_range(const Common& c, int t_raw, int& t, i
 
 // Gather the kept pairs of the nfc chunks into LDS, in index order.  cnt_raw[k]
 // is the count of chunk CPT t + k (loaded by the caller, clamped); wave w
-// copies chunks w, w + waves, ...; pre[p] holds the first 64 pairs of chunk
-// w + p * waves (loaded early by the caller, unconditionally).  Returns the
-// number of kept pairs, or -1 when they do not fit (then nothing is gathered).
-template <int NTH, int PRE>
+// copies chunks w, w + waves, ...; pre[p * D + d] holds pairs 64 d .. 64 d + 63
+// of chunk w + p * waves (loaded early by the caller, unconditionally).  Returns
+// the number of kept pairs, or -1 when they do not fit (then nothing is gathered).
+template <int NTH, int PRE, int D = 1>
 __device__ __forceinline__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off, const uint2* slots, int nfc, int cap_lds,
-                           const int (&cnt_raw)[CPT], const uint2 (&pre)[PRE], uint32_t* key, int32_t* idx,
+                           const int (&cnt_raw)[CPT], const uint2 (&pre)[PRE * D], uint32_t* key, int32_t* idx,
                            int b1, uint32_t& above) {
   constexpr int NW = NTH / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -254,8 +254,10 @@ __device__ __forceinline__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off,
     const int ch = wave + p * NW;
     if (ch < nfc) {
       const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
-      if (lane < n) put(o + lane, pre[p]);
-      more = more || n > 64;
+#pragma unroll
+      for (int d = 0; d < D; ++d)
+        if (64 * d + lane < n) put(o + 64 * d + lane, pre[p * D + d]);
+      more = more || n > 64 * D;
     }
   }
   more = more || nfc > PRE * NW;
@@ -295,7 +297,7 @@ __device__ __forceinline__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off,
     for (int ch = wave; ch < nfc; ch += NW) {
       const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
       const uint2* cs = slots + int64_t(ch) * FCH;
-      int k0 = 64;
+      int k0 = ch < PRE * NW ? 64 * D : 64;         // pairs already prefetched
       for (; n - k0 > 128; k0 += 8 * 64) copy_run(std::integral_constant<int, 8>(), cs, o, n, k0);   // wave-uniform
       if (k0 < n) copy_run(std::integral_constant<int, 2>(), cs, o, n, k0);
     }
@@ -523,11 +525,18 @@ __device__ __forceinline__ void row_select(SelState<NTH>& s, const float* row, i
 
 // First 64 kept pairs of chunks wave, wave + waves, ... of a unit's slots
 // (clamped to the unit's nfa chunks; loaded unconditionally).
-template <int NTH, int PRE>
-__device__ __forceinline__ void prefetch_kept(const uint2* unit_slots, int nfa, uint2 (&pre)[PRE]) {
+// D > 1: also pairs 64 .. 64 D - 1 of each of those chunks (read whatever the
+// slots hold; only the first count of them are used).
+template <int NTH, int PRE, int D = 1>
+__device__ __forceinline__ void prefetch_kept(const uint2* unit_slots, int nfa, uint2 (&pre)[PRE * D]) {
+  static_assert(64 * D <= FCH, "a chunk holds FCH slots");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int p = 0; p < PRE; ++p) pre[p] = unit_slots[int64_t(min(wave + p * (NTH / 64), nfa - 1)) * FCH + lane];
+  for (int p = 0; p < PRE; ++p) {
+    const uint2* cs = unit_slots + int64_t(min(wave + p * (NTH / 64), nfa - 1)) * FCH;
+#pragma unroll
+    for (int d = 0; d < D; ++d) pre[p * D + d] = cs[64 * d + lane];
+  }
 }
 
 // Chunk counts of a unit, CPT per thread (chunk CPT t + k), loaded unconditionally.
@@ -540,14 +549,14 @@ __device__ __forceinline__ void load_counts(const int32_t* unit_counts, int nfa,
 // (nfc chunks, counts cnt and first pairs pre already loaded), into out[0..Bc)
 // -- global or LDS.  b1: the coarse bin the filter kept keys from.  Falls back
 // to the whole score row when the kept pairs are fewer than Bc or do not fit.
-template <int NTH, int PRE, bool VEC>
+template <int NTH, int PRE, bool VEC, int D = 1>
 __device__ void select_from_kept(SelState<NTH>& s, int32_t* chunk_off, uint32_t* key, int32_t* idx, int cap_lds,
                                  const uint2* unit_slots, const float* row, int lim, int max_t, int nfc,
                                  const int (&cnt)[CPT],
-                                 const uint2 (&pre)[PRE], int c_lo, int c_hi, int Bc, int b1, int32_t* out) {
+                                 const uint2 (&pre)[PRE * D], int c_lo, int c_hi, int Bc, int b1, int32_t* out) {
   zero_bins<NTH, HB>(s);               // the gather's second-digit histogram; published by its first barrier
   uint32_t above = 0;
-  const int N = gather_kept<NTH, PRE>(s, chunk_off, unit_slots, nfc, cap_lds, cnt, pre, key, idx, b1, above);
+  const int N = gather_kept<NTH, PRE, D>(s, chunk_off, unit_slots, nfc, cap_lds, cnt, pre, key, idx, b1, above);
   if (N >= Bc) lds_select<NTH>(s, key, idx, N, Bc, b1, above, out);
   else row_select<NTH, VEC>(s, row, lim, max_t, c_lo, c_hi, Bc, out);
 }

@@ -228,9 +228,12 @@ __global__ __launch_bounds__(BIG) void finish_kernel(TopkArgs a) {
   const int64_t unit = int64_t(b) * c.n_kv_heads + wg.x;
   const int nfa = filter_chunks(c);
   const uint2* unit_slots = static_cast<const uint2*>(a.w.slots) + unit * nfa * int64_t(FCH);
-  // Loads that do not depend on t_b go out first (clamped into the arrays).
-  uint2 pre[1];
-  prefetch_kept<BIG, 1>(unit_slots, nfa, pre);
+  // Loads that do not depend on t_b go out first (clamped into the arrays),
+  // among them the first 512 slots of this wave's chunk: large budgets keep
+  // hundreds of pairs per chunk, which then need no second round trip.
+  constexpr int DEEP = 8;
+  uint2 pre[DEEP];
+  prefetch_kept<BIG, 1, DEEP>(unit_slots, nfa, pre);
   int cnt[CPT];
   load_counts(a.w.counts + unit * nfa, nfa, cnt);
   const int b1 = a.w.b1[unit];
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(BIG) void finish_kernel(TopkArgs a) {
   zero_fac_arrive(a, unit);
   if (!keep_all) {
     __shared__ FinishShared sm;
-    select_from_kept<BIG, 1, VEC>(sm.sel, sm.chunk_off, sm.key, sm.idx, kCandLds, unit_slots,
+    select_from_kept<BIG, 1, VEC, DEEP>(sm.sel, sm.chunk_off, sm.key, sm.idx, kCandLds, unit_slots,
                                   a.scores + unit * c.score_stride, row_lim<VEC>(c), c.max_t, nfa, cnt, pre, c_lo,
                                   c_hi, Bc, b1, out + c_lo);
   }
