@@ -217,12 +217,12 @@ __device__ __forceinline__ void fac_split_body(const FacArgs& a) {
   // All heads of a chunk share this workgroup's rows, and no other workgroup
   // of the launch reads them unless the group spans several chunks.
   if constexpr (kMfma) {
-    // Waves with more than 64 rows resolve their row offsets up front and keep
+    // Waves with more than 128 rows resolve their row offsets up front and keep
     // the next block's loads in flight while they compute one; shorter ones
-    // (small launches) take the plain loop, whose one batch of lookups is
-    // cheaper than the up-front pass.
+    // take the plain loop, whose one or two batches of lookups cost less than
+    // the up-front pass (measured at 8 and 128 rows per wave).
     __shared__ int64_t row_offs[kFacWaves][FacWaveMfma<HG>::kPfRows];
-    if (r1 - r0 > 64) w.template run_pipelined<true>(r0, r1, lane_offset, kbase, vbase, row_offs[wave]);
+    if (r1 - r0 > 128) w.template run_pipelined<true>(r0, r1, lane_offset, kbase, vbase, row_offs[wave]);
     else w.template run<true>(r0, r1, lane_offset, kbase, vbase);
   }
   else w.template run<U, true>(r0, r1, lane_offset, kbase, vbase);

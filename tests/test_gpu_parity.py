@@ -258,12 +258,12 @@ def test_fac_skips_entries_outside_the_cache(dtype):
 
     Entries of sel_idx[0..sel_count) below 0 or past the block table's last slot
     contribute nothing; the result is the oracle's FAC over the remaining rows (0
-    for a unit with none).  At about 9000 rows per unit the bf16 launch gives each
-    wave more than 64 rows, so the matrix-core waves take the pipelined loop (row
-    offsets resolved up front, next block in flight); the fp32 launch runs the
-    vector waves."""
+    for a unit with none).  With 32 units of about 9000 rows the bf16 launch gives
+    each wave 144 rows, more than the 128 from which the matrix-core waves take
+    the pipelined loop (row offsets resolved up front, next block in flight); the
+    fp32 launch runs the vector waves."""
     say(f"[fac-skip] {dtype}")
-    cfg = C["c2"].replace(dtype=dtype, batch=2, t=9000, budget=9000)
+    cfg = C["c2"].replace(dtype=dtype, batch=4, t=9000, budget=9000)
     inp = synth.make_inputs(cfg, seed=5, device="cpu")
     L = DeviceLayer(inp, device="cuda", with_slab=False)
     t = int(inp.seq_lens[0])
