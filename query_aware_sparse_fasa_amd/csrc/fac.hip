@@ -287,8 +287,10 @@ struct FacSelShared {
 
 // HG query heads per workgroup (the x coordinate picks the head chunk): 1 when there
 // are few units and latency rules, up to 8 when many units fill the chip and
-// each K/V row should be read once.
-template <typename T, typename Acc, int HG>
+// each K/V row should be read once.  DEEP (one head per workgroup and rows of
+// more than 16 filter chunks): the first kept pairs of up to 64 chunks are
+// prefetched at kernel start instead of 16.
+template <typename T, typename Acc, int HG, bool DEEP = false>
 __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   const Common& c = a.c;
   const WgCoord wg = xcd_grouped();
@@ -303,9 +305,10 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   __shared__ FacSelShared<Acc, HG> sm;
 
   // Independent loads first: the first kept pairs of every chunk (up to 16
-  // chunks; the gather fetches the rest 8 chunks per wave at a time), the
-  // chunk counts and b1; the query slices, the block-table row and the length.
-  constexpr int PRE = 16 / kSelWaves;
+  // chunks, or 64 with DEEP; the gather fetches the rest 8 chunks per wave at a
+  // time), the chunk counts and b1; the query slices, the block-table row and
+  // the length.
+  constexpr int PRE = (DEEP ? 64 : 16) / kSelWaves;
   uint2 pre[PRE];
   sel::prefetch_kept<kSelThreads, PRE>(unit_slots, nfa, pre);
   int cnt[sel::CPT];
@@ -527,7 +530,12 @@ template <typename T, typename Acc>
 hipError_t launch_fac_select_t(const FacArgs& a, hipStream_t s) {
   const int hg = select_heads(a.c);
   const dim3 grid((a.c.group + hg - 1) / hg, a.c.n_kv_heads, a.c.batch);
-  if (hg == 1) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1>), grid, dim3(kSelThreads), 0, s, a);
+  // One head per workgroup has the registers for a deeper prefetch; it pays only
+  // when the rows span more than 16 filter chunks (measured: 128K-token rows
+  // gain 0.7 us, 32K-token rows lose 0.4 us to the redundant loads).
+  const bool deep = sel::filter_chunks(a.c) > 16;
+  if (hg == 1 && deep) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, true>), grid, dim3(kSelThreads), 0, s, a);
+  else if (hg == 1) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1>), grid, dim3(kSelThreads), 0, s, a);
   else if (hg == 2) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 2>), grid, dim3(kSelThreads), 0, s, a);
   else if constexpr (sizeof(Acc) == 4) {
     if (hg == 4) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 4>), grid, dim3(kSelThreads), 0, s, a);
