@@ -216,15 +216,17 @@ __device__ __forceinline__ void fac_split_body(const FacArgs& a) {
   constexpr int U = (sizeof(Acc) == 4 && HG <= 4) ? 8 : (HG <= 2 ? 4 : (HG <= 4 || sizeof(Acc) == 4 ? 2 : 1));
   // All heads of a chunk share this workgroup's rows, and no other workgroup
   // of the launch reads them unless the group spans several chunks.
-  if constexpr (kMfma) {
+  if constexpr (kMfma && HG >= 4) {
     // Waves with more than 128 rows resolve their row offsets up front and keep
     // the next block's loads in flight while they compute one; shorter ones
     // take the plain loop, whose one or two batches of lookups cost less than
-    // the up-front pass (measured at 8 and 128 rows per wave).
+    // the up-front pass (measured at 8 and 128 rows per wave).  Groups of 1 or
+    // 2 heads keep the plain loop only: the pipelined one would make them spill.
     __shared__ int64_t row_offs[kFacWaves][FacWaveMfma<HG>::kPfRows];
     if (r1 - r0 > 128) w.template run_pipelined<true>(r0, r1, lane_offset, kbase, vbase, row_offs[wave]);
     else w.template run<true>(r0, r1, lane_offset, kbase, vbase);
   }
+  else if constexpr (kMfma) w.template run<true>(r0, r1, lane_offset, kbase, vbase);
   else w.template run<U, true>(r0, r1, lane_offset, kbase, vbase);
   w.fold_row_groups();
 
