@@ -423,8 +423,9 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
 }
 
 // One workgroup per (sequence, query head): log-sum-exp merge of the partials.
-// The weights e^(m_i - M) and l_i e^(m_i - M) go through LDS; each thread then
-// streams its channel of every partial with 8 loads in flight.
+// Up to 8 partials: one round trip, merged in registers.  More: the weights
+// e^(m_i - M) and l_i e^(m_i - M) go through LDS; each thread then streams its
+// channel of every partial with 8 loads in flight.
 template <typename Acc>
 __global__ __launch_bounds__(kHeadDim) void fac_merge_kernel(FacArgs a) {
   constexpr int MAXP = 512;
@@ -436,6 +437,35 @@ __global__ __launch_bounds__(kHeadDim) void fac_merge_kernel(FacArgs a) {
   const int64_t base = (int64_t(b) * a.c.n_q_heads + h) * P;
   const Acc* pacc = static_cast<const Acc*>(a.part_acc) + base * kHeadDim + d;
   const Acc* pml = static_cast<const Acc*>(a.part_ml) + base * 2;
+  if (P >= 1 && P <= 8) {
+    // Few partials: every (m, l) and this channel of every accumulator in one
+    // round trip (indices clamped; the extra slots are masked), merged in
+    // registers in partial order.
+    Acc m[8], l[8], o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = min(i, P - 1);
+      m[i] = pml[2 * k];
+      l[i] = pml[2 * k + 1];
+      o[i] = pacc[int64_t(k) * kHeadDim];
+    }
+    Acc M = neg_inf<Acc>();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) M = i < P ? fmax(M, m[i]) : M;
+    float res = 0.f;
+    if (M != neg_inf<Acc>()) {
+      Acc L = Acc(0), O = Acc(0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const Acc w = (i >= P || m[i] == neg_inf<Acc>()) ? Acc(0) : fexp<Acc>(m[i] - M);
+        O = fma(o[i], w, O);
+        L += l[i] * w;
+      }
+      res = float(O / L);
+    }
+    a.out[(int64_t(b) * a.c.n_q_heads + h) * kHeadDim + d] = res;
+    return;
+  }
   Acc M = neg_inf<Acc>();
   for (int i = d; i < P; i += kHeadDim) M = fmax(M, pml[2 * i]);
 #pragma unroll
