@@ -380,7 +380,9 @@ def main():
                      "unit": "GB/s", "frac": tip_gbps / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(args.config, use_slab),
                      "algorithmic_bytes_per_launch": int(tip_bytes),
-                     "avg_launch_us": t_tip * 1e6},
+                     "avg_launch_us": t_tip * 1e6,
+                     "variant": "fasa_tip launches (scores only); inside fasa_decode the same kernel also "
+                                "builds the select's coarse histogram, which the kernel trace times separately"},
         "measured_references": {"copy_1GiB_GBps": copy_gbps, "sum_1GiB_GBps": read_gbps,
                                 "tip_frac_of_copy": tip_gbps / copy_gbps, "tip_frac_of_sum": tip_gbps / read_gbps,
                                 "step_frac_of_sum": step_gbps / read_gbps,
