@@ -224,16 +224,36 @@ __device__ __forceinline__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off,
     sum += uint32_t(cnt[k]);
   }
   uint32_t N;
-  uint32_t off = block_excl_scan(s, sum, N);
+  if (nfc <= 64 * CPT) {
+    // Up to 256 chunks (every selecting FAC launch): wave 0 holds all the
+    // counts, scans them itself and writes the chunk offsets and the total; one
+    // barrier publishes them.
+    if (wave == 0) {
+      const uint32_t incl = wave_inclusive_scan(sum);
+      uint32_t off = incl - sum;
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    const int ch = CPT * tid + k;
-    if (ch < nfc) chunk_off[ch] = int32_t(off);
-    off += uint32_t(cnt[k]);
+      for (int k = 0; k < CPT; ++k) {
+        const int ch = CPT * tid + k;
+        if (ch < nfc) chunk_off[ch] = int32_t(off);
+        off += uint32_t(cnt[k]);
+      }
+      if (lane == 63) chunk_off[nfc] = int32_t(incl);
+    }
+    __syncthreads();
+    N = uint32_t(chunk_off[nfc]);
+    if (N > uint32_t(cap_lds)) return -1;   // uniform
+  } else {
+    uint32_t off = block_excl_scan(s, sum, N);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int ch = CPT * tid + k;
+      if (ch < nfc) chunk_off[ch] = int32_t(off);
+      off += uint32_t(cnt[k]);
+    }
+    if (tid == 0) chunk_off[nfc] = int32_t(N);
+    if (N > uint32_t(cap_lds)) return -1;   // uniform
+    __syncthreads();
   }
-  if (tid == 0) chunk_off[nfc] = int32_t(N);
-  if (N > uint32_t(cap_lds)) return -1;     // uniform
-  __syncthreads();
   // The prefetched pairs first (no memory access), then whatever is beyond them.
   // With b1 >= 0 every copied key also goes into the second-digit histogram
   // (bits 20..10) if it lies in bin b1, or is counted if it lies above b1 (the
