@@ -267,9 +267,10 @@ constexpr int kSelWideUnits = 256;          // units from which a workgroup cove
 // only a few hundred pairs -- then runs FAC for its heads over every row of the
 // list with kSelWaves waves, and writes the heads' outputs directly: no
 // partials and no merge.  With one head per workgroup (few units) the G
-// workgroups of a unit read the same K/V rows, after the first mostly from the
-// shared Infinity Cache.  Workgroup 0 of each unit also publishes the list and
-// its count and clears the unit's histogram for the next step.
+// workgroups of a unit read the same K/V rows; the XCD-aware order puts them on
+// one XCD, so after the first they mostly come from its L2.  Workgroup 0 of
+// each unit also publishes the list and its count and clears the unit's
+// histogram for the next step.
 // Grid (head chunks, kv heads, batch).
 template <typename Acc, int HG>
 struct FacSelShared {
