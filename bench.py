@@ -131,9 +131,10 @@ def main():
     ap.add_argument("--no-slab", action="store_true", help="TIP gathers from the key rows instead")
     ap.add_argument("--no-fasa-m", action="store_true", help="skip the FASA-M (host-offloaded) timing")
     ap.add_argument("--no-calib", action="store_true", help="skip the CA calibration timing")
-    ap.add_argument("--mode", choices=["step", "tip"], default="step",
-                    help="step: the benchmark; tip: only --steps TIP launches and one 1 GiB "
-                         "reference copy (for hardware-counter runs)")
+    ap.add_argument("--mode", choices=["step", "tip", "decode", "dense"], default="step",
+                    help="step: the benchmark; tip / decode / dense: only --steps TIP launches, "
+                         "whole decode steps or dense decodes, then one 1 GiB reference copy "
+                         "(for hardware-counter runs)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -180,20 +181,27 @@ def main():
 
     stream = torch.cuda.Stream(device=dev)
     stream.wait_stream(torch.cuda.current_stream())
-    if args.mode == "tip":
-        # Counter runs: exactly `steps` TIP launches over the rotated layers, then
-        # a plain device copy of 1 GiB whose bytes are known (read 1 GiB, write
-        # 1 GiB) to scale the counters.
+    if args.mode in ("tip", "decode", "dense"):
+        # Counter runs: exactly `steps` TIP launches, decode steps or dense
+        # decodes over the rotated layers, then a plain device copy of 1 GiB
+        # whose bytes are known (read 1 GiB, write 1 GiB) to scale the counters.
         with torch.cuda.stream(stream):
             for i in range(args.steps):
-                layers[i % L].tip(use_slab=use_slab)
+                lay = layers[i % L]
+                if args.mode == "tip":
+                    lay.tip(use_slab=use_slab)
+                elif args.mode == "decode":
+                    lay.decode(use_slab=use_slab)
+                else:
+                    lay.dense()
             src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
             dst = torch.empty_like(src)
             dst.copy_(src)
         torch.cuda.synchronize()
         tip_bytes = sb["slab"] if use_slab else int(inp.seq_lens.sum()) * cfg.n_kv_heads * 128 * cfg.elem_bytes
-        print(json.dumps({"mode": "tip", "tip_launches": args.steps, "tip_algorithmic_bytes": tip_bytes,
+        print(json.dumps({"mode": args.mode, "launches": args.steps, "tip_algorithmic_bytes": tip_bytes,
                           "tip_score_bytes_written": int(inp.seq_lens.sum()) * cfg.n_kv_heads * 4,
+                          "step_algorithmic_bytes": int(sb["algorithmic"]), "dense_bytes": int(sb["dense"]),
                           "copy_bytes_each_way": 1 << 30, "layers": L}), flush=True)
         return
 
