@@ -43,6 +43,7 @@ using namespace sel;
 
 constexpr int FNT = 256;                    // filter threads (8 tokens each)
 constexpr int BIG = kTopkThreads;           // 1024 threads of finish_kernel
+constexpr int64_t kFilterLateGrid = 2048;   // filter grids above which a chunk reads the length before its scores
 
 struct TopkArgs {
   Common c;
@@ -122,7 +123,12 @@ __global__ __launch_bounds__(FNT) void hist_kernel(TopkArgs a) {
 
 // ---------------------------------------------------------------------------
 // Stage 2.  Grid (ceil(max_t / 2048), kv heads, batch), 256 threads.
-template <bool VEC>
+// LATE (grids of several rounds): the sequence length comes first, and a chunk
+// with no candidate (past a short sequence's end) writes its zero count and
+// leaves without loading its scores; with several rounds of workgroups per CU
+// the extra round trip is hidden by the others, and ragged batches stop reading
+// the unused ends of their score rows.
+template <bool VEC, bool LATE>
 __global__ __launch_bounds__(FNT) void filter_kernel(TopkArgs a) {
   const Common& c = a.c;
   const WgCoord wg = xcd_grouped();
@@ -135,7 +141,7 @@ __global__ __launch_bounds__(FNT) void filter_kernel(TopkArgs a) {
   // Independent loads: this thread's 8 scores and its 8 histogram bins.  Thread
   // t owns bins 2047-8t down to 2040-8t, so a scan over threads counts from the top.
   float v[8];
-  load_chunk8<VEC>(row, row_lim<VEC>(c), base, v);
+  if constexpr (!LATE) load_chunk8<VEC>(row, row_lim<VEC>(c), base, v);
   const uint32_t* hg = a.w.hist + unit * HB;
   const uint4 hlo = *reinterpret_cast<const uint4*>(hg + HB - 8 - 8 * tid);
   const uint4 hhi = *reinterpret_cast<const uint4*>(hg + HB - 4 - 8 * tid);
@@ -145,6 +151,15 @@ __global__ __launch_bounds__(FNT) void filter_kernel(TopkArgs a) {
   const int Bc = min(c.budget, nC);
   if (wg.x == 0) zero_fac_arrive(a, unit);
   if (Bc == nC) return;                // every candidate is kept: no kept-pair list
+  if constexpr (LATE) {
+    // Chunk 0 always finds b1 (it publishes it); any other chunk without a
+    // candidate only records that it keeps nothing.
+    if (wg.x != 0 && (base >= c_hi || base + FCH <= c_lo)) {
+      if (tid == 0) a.w.counts[unit * nfa + wg.x] = 0;
+      return;
+    }
+    load_chunk8<VEC>(row, row_lim<VEC>(c), base, v);
+  }
 
   __shared__ uint32_t s_w[FNT / 64];
   __shared__ uint32_t s_b1;
@@ -286,8 +301,16 @@ hipError_t launch_filter(const Common& c, const float* scores, const int32_t* se
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (vec) hipLaunchKernelGGL(filter_kernel<true>, grid, dim3(FNT), 0, s, a);
-  else hipLaunchKernelGGL(filter_kernel<false>, grid, dim3(FNT), 0, s, a);
+  // Grids of more than one round of workgroups (8 per CU): load the length
+  // first and skip chunks without candidates (measured on the ragged batch).
+  const bool late = int64_t(grid.x) * grid.y * grid.z > kFilterLateGrid;
+  if (vec) {
+    if (late) hipLaunchKernelGGL((filter_kernel<true, true>), grid, dim3(FNT), 0, s, a);
+    else hipLaunchKernelGGL((filter_kernel<true, false>), grid, dim3(FNT), 0, s, a);
+  } else {
+    if (late) hipLaunchKernelGGL((filter_kernel<false, true>), grid, dim3(FNT), 0, s, a);
+    else hipLaunchKernelGGL((filter_kernel<false, false>), grid, dim3(FNT), 0, s, a);
+  }
   return hipGetLastError();
 }
 
