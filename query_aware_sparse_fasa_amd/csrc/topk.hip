@@ -91,7 +91,9 @@ __device__ __forceinline__ void zero_fac_arrive(const TopkArgs& a, int64_t unit)
 // ---------------------------------------------------------------------------
 // Stage 1 for the standalone select: the unit histogram of given scores.
 // Grid (ceil(max_t / 2048), kv heads, batch), 256 threads with 8 slots each.
-template <bool VEC>
+// LATE as for filter_kernel: the length first, chunks without candidates leave
+// before loading their scores.
+template <bool VEC, bool LATE>
 __global__ __launch_bounds__(FNT) void hist_kernel(TopkArgs a) {
   const Common& c = a.c;
   const WgCoord wg = xcd_grouped();
@@ -100,9 +102,13 @@ __global__ __launch_bounds__(FNT) void hist_kernel(TopkArgs a) {
   const float* row = a.scores + unit * c.score_stride;
   const int base = wg.x * FCH;
   float v[8];
-  load_chunk8<VEC>(row, row_lim<VEC>(c), base, v);
+  if constexpr (!LATE) load_chunk8<VEC>(row, row_lim<VEC>(c), base, v);
   int t, c_lo, c_hi;
   unit_range(c, a.seq_lens[b], t, c_lo, c_hi);
+  if constexpr (LATE) {
+    if (base >= c_hi || base + FCH <= c_lo) return;    // no candidate here: nothing to count
+    load_chunk8<VEC>(row, row_lim<VEC>(c), base, v);
+  }
   __shared__ uint32_t h[HB];
   for (int i = threadIdx.x; i < HB; i += FNT) h[i] = 0u;
   __syncthreads();
@@ -295,15 +301,20 @@ hipError_t launch_filter(const Common& c, const float* scores, const int32_t* se
   const TopkArgs a{c, scores, seq_lens, nullptr, nullptr, w, fac_arrive, head_chunks};
   const dim3 grid(filter_chunks(c), c.n_kv_heads, c.batch);
   const bool vec = (c.score_stride & 3) == 0;
-  if (!have_hist) {
-    if (vec) hipLaunchKernelGGL(hist_kernel<true>, grid, dim3(FNT), 0, s, a);
-    else hipLaunchKernelGGL(hist_kernel<false>, grid, dim3(FNT), 0, s, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   // Grids of more than one round of workgroups (8 per CU): load the length
   // first and skip chunks without candidates (measured on the ragged batch).
   const bool late = int64_t(grid.x) * grid.y * grid.z > kFilterLateGrid;
+  if (!have_hist) {
+    if (vec) {
+      if (late) hipLaunchKernelGGL((hist_kernel<true, true>), grid, dim3(FNT), 0, s, a);
+      else hipLaunchKernelGGL((hist_kernel<true, false>), grid, dim3(FNT), 0, s, a);
+    } else {
+      if (late) hipLaunchKernelGGL((hist_kernel<false, true>), grid, dim3(FNT), 0, s, a);
+      else hipLaunchKernelGGL((hist_kernel<false, false>), grid, dim3(FNT), 0, s, a);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (vec) {
     if (late) hipLaunchKernelGGL((filter_kernel<true, true>), grid, dim3(FNT), 0, s, a);
     else hipLaunchKernelGGL((filter_kernel<true, false>), grid, dim3(FNT), 0, s, a);

@@ -194,6 +194,10 @@ TOPK_CASES = [
     ("normal", 3, 2, 700, [700, 68, 0], 512, 4, 64),     # B >= candidates, t < forced, t = 0
     ("normal", 2, 1, 300, [1, 300], 1, 0, 0),
     ("normal", 1, 1, 6193 * 5, [6193 * 5], 6193, 0, 0),
+    # A ragged batch whose select grid exceeds 2048 workgroups (32 chunks x 8 heads
+    # x 9 sequences): the histogram and filter launches read each sequence's length
+    # before its scores and skip chunks past its end; lengths at chunk edges and 0.
+    ("normal", 9, 8, 65536, [65536, 100, 2047, 2048, 2049, 30000, 4096, 0, 65000], 512, 4, 64),
 ]
 
 
