@@ -32,8 +32,14 @@
  *   fc_idx    [n_kv_heads][n_fc] int32: dominant FC indices I_g, distinct,
  *               each in [0, head_dim/2)
  *   slab      the dominant-key cache (FC-major side copy of the dominant key
- *               columns): element (p, g, f, s, c) = K(p, g, s, 2*fc_idx[g][f]+c)
- *               at p*slab_block_stride + g*slab_head_stride + f*512 + s*2 + c
+ *               columns), indexed by sequence and logical block -- not by the
+ *               pool's physical block, so TIP needs no block-table lookup:
+ *               element (b, k, g, f, s, c) = K of token 256*k + s of sequence b,
+ *               kv head g, column 2*fc_idx[g][f] + c, at
+ *               (b*max_blocks_per_seq + k)*slab_block_stride
+ *                 + g*slab_head_stride + f*512 + s*2 + c
+ *               (default strides (H_kv*F*512, F*512): an array
+ *               [batch][max_blocks_per_seq][H_kv][F][256][2])
  *   scores    [batch][n_kv_heads][max_t] fp32, S of token j at column j
  *   sel_idx   [batch][n_kv_heads][cap] int32, cap = fasa_selection_capacity():
  *               the selected token indices ascending, then -1 padding
@@ -93,7 +99,7 @@ typedef struct fasa_shape {
   int32_t max_blocks_per_seq; /* columns of block_table, >= 1 */
   int64_t kv_block_stride;    /* elements, multiple of 8, >= 256*head_dim */
   int64_t kv_head_stride;     /* elements, multiple of 8, >= 256*head_dim */
-  int64_t slab_block_stride;  /* elements, multiple of 8 */
+  int64_t slab_block_stride;  /* elements between logical blocks, multiple of 8 */
   int64_t slab_head_stride;   /* elements, multiple of 8, >= 512*n_fc */
   int32_t kv_dtype;           /* fasa_dtype of q, k_pool, v_pool and slab */
   float scale;                /* softmax scale; 0 means 1/sqrt(head_dim) */
@@ -132,15 +138,19 @@ fasa_status fasa_check_fc_idx(const fasa_shape* shape, const int32_t* fc_idx_hos
 /* Build the dominant-key cache for tokens 0..t_b-1 of every sequence from the
  * post-RoPE key pool (the GPU-resident dominant key cache of section 3.4,
  * "Hardware-Aware Variants": only the dominant dimensions of every key).
- * Writes whole blocks: slots past t_b in a sequence's last block are copied
- * as they are. */
+ * Writes logical blocks 0 .. ceil(t_b/256)-1 of each sequence whole (slots
+ * past t_b in the last block are copied from the pool as they are); sequences
+ * that share physical blocks get their own copies. */
 fasa_status fasa_slab_build(const fasa_shape* shape, const void* k_pool,
                             const int32_t* block_table, const int32_t* seq_lens,
                             const int32_t* fc_idx, void* slab, hipStream_t stream);
 
 /* After the caller has written the post-RoPE key of token positions[b] of every
- * sequence into k_pool, copy its dominant columns into the slab.  positions[b]
- * < 0 skips sequence b; positions must be < 256*max_blocks_per_seq. */
+ * sequence into k_pool, copy its dominant columns into the slab (slot
+ * positions[b] % 256 of logical block positions[b] / 256 of sequence b; the
+ * dominant-key cache is kept current per token, section 3.4, "Hardware-Aware
+ * Variants").  positions[b] < 0 skips sequence b; positions at or past
+ * 256*max_blocks_per_seq are skipped too. */
 fasa_status fasa_slab_append(const fasa_shape* shape, const void* k_pool,
                              const int32_t* block_table, const int32_t* positions,
                              const int32_t* fc_idx, void* slab, hipStream_t stream);

@@ -291,9 +291,11 @@ struct FacSelShared {
 // HG query heads per workgroup (the x coordinate picks the head chunk): 1 when there
 // are few units and latency rules, up to 8 when many units fill the chip and
 // each K/V row should be read once.  DEEP (one head per workgroup and rows of
-// more than 16 filter chunks): the first kept pairs of up to 64 chunks are
-// prefetched at kernel start instead of 16.
-template <typename T, typename Acc, int HG, bool DEEP = false>
+// more than 16 filter chunks, or more than 32 emitted chunks): the first kept
+// pairs of up to 64 chunks are prefetched at kernel start instead of 16 (32).
+// EMIT: the candidates are the lists TIP emitted per 1024-token chunk (the
+// two-launch step, no filter launch); otherwise the filter's kept pairs.
+template <typename T, typename Acc, int HG, bool DEEP = false, bool EMIT = false>
 __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   const Common& c = a.c;
   const WgCoord wg = xcd_grouped();
@@ -301,22 +303,26 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   const int h0 = hc * HG, nh = min(HG, c.group - h0);
   const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t unit = int64_t(b) * c.n_kv_heads + g;
-  const int nfa = sel::filter_chunks(c);
-  const uint2* unit_slots = static_cast<const uint2*>(a.w.slots) + unit * nfa * int64_t(sel::FCH);
+  constexpr int CHUNK = EMIT ? kEmitChunk : sel::FCH;
+  const int nfa = EMIT ? emit_chunks(c) : sel::filter_chunks(c);
+  const uint2* unit_slots = static_cast<const uint2*>(a.w.slots) + unit * nfa * int64_t(CHUNK);
   const float* row = a.scores + unit * c.score_stride;   // a decode step's rows: 16-byte aligned, padded
   const int lim = c.score_stride;
   __shared__ FacSelShared<Acc, HG> sm;
 
   // Independent loads first: the first kept pairs of every chunk (up to 16
-  // chunks, or 64 with DEEP; the gather fetches the rest 8 chunks per wave at a
-  // time), the chunk counts and b1; the query slices, the block-table row and
-  // the length.
-  constexpr int PRE = (DEEP ? 64 : 16) / kSelWaves;
+  // chunks -- 32 emitted ones -- or 64 with DEEP; the gather fetches the rest 8
+  // chunks per wave at a time), the chunk counts (summaries) and b1; the query
+  // slices, the block-table row and the length.
+  constexpr int PRE = (DEEP ? 64 : (EMIT ? 32 : 16)) / kSelWaves;
   uint2 pre[PRE];
-  sel::prefetch_kept<kSelThreads, PRE>(unit_slots, nfa, pre);
+  if constexpr (EMIT) sel::prefetch_kept<kSelThreads, PRE, 1, kEmitChunk>(unit_slots, nfa, pre);
+  else sel::prefetch_kept<kSelThreads, PRE>(unit_slots, nfa, pre);
   int cnt[sel::CPT];
-  sel::load_counts(a.w.counts + unit * nfa, nfa, cnt);
-  const int b1 = a.w.b1[unit];
+  uint2 meta[sel::CPT];
+  if constexpr (EMIT) sel::load_meta(reinterpret_cast<const uint2*>(a.w.counts) + unit * nfa, nfa, meta);
+  else sel::load_counts(a.w.counts + unit * nfa, nfa, cnt);
+  const int b1 = EMIT ? -1 : a.w.b1[unit];
   const int64_t head0 = int64_t(b) * c.n_q_heads + g * c.group + h0;
   // bf16 caches with 4 or more heads per workgroup run the FAC on the matrix
   // cores (FacWaveMfma, 16-row blocks, whose LDS tiles take the select area
@@ -341,10 +347,16 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   const int count = (t - nC) + Bc;          // forced + chosen, <= cap
   const bool keep_all = Bc == nC;
 
-  if (!keep_all)
-    sel::select_from_kept<kSelThreads, PRE, true>(sm.u.s.st, sm.u.s.chunk_off, sm.u.s.key, sm.u.s.idx, kSmallCand,
-                                                  unit_slots, row, lim, c.max_t, nfa, cnt, pre, c_lo, c_hi, Bc, b1,
-                                                  sm.chosen);
+  if (!keep_all) {
+    if constexpr (EMIT)
+      sel::select_from_emitted<kSelThreads, PRE, true>(sm.u.s.st, sm.u.s.chunk_off, sm.u.s.key, sm.u.s.idx,
+                                                       kSmallCand, unit_slots, row, lim, c.max_t,
+                                                       emit_chunks_of(t), meta, pre, c_lo, c_hi, Bc, sm.chosen);
+    else
+      sel::select_from_kept<kSelThreads, PRE, true>(sm.u.s.st, sm.u.s.chunk_off, sm.u.s.key, sm.u.s.idx, kSmallCand,
+                                                    unit_slots, row, lim, c.max_t, nfa, cnt, pre, c_lo, c_hi, Bc, b1,
+                                                    sm.chosen);
+  }
 #pragma unroll
   for (int k = 0; k < kBtabLds / kSelThreads; ++k)
     if (tid + kSelThreads * k < c.max_blocks) sm.btab[tid + kSelThreads * k] = bt[k];
@@ -413,13 +425,15 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
     a.out[(head0 + hh) * kHeadDim + ch] = L > Acc(0) ? float(O / L) : 0.f;
   }
   if (hc == 0) {
-    // Workgroup 0 of the unit publishes the list and leaves the consumed
-    // histogram zero for the next step (the filter launch read it).
+    // Workgroup 0 of the unit publishes the list and (after a filter launch)
+    // leaves the consumed histogram zero for the next step.
     int32_t* list = a.sel_idx + unit * c.cap;
     for (int i = tid; i < c.cap; i += kSelThreads) list[i] = i < count ? token(i) : -1;
     if (tid == 0) a.sel_count[unit] = count;
-    uint4* hg = reinterpret_cast<uint4*>(a.w.hist + unit * sel::HB);
-    for (int i = tid; i < sel::HB / 4; i += kSelThreads) hg[i] = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (!EMIT) {
+      uint4* hg = reinterpret_cast<uint4*>(a.w.hist + unit * sel::HB);
+      for (int i = tid; i < sel::HB / 4; i += kSelThreads) hg[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
   }
 }
 
@@ -560,12 +574,21 @@ int select_heads(const Common& c) {
 }
 
 template <typename T, typename Acc>
-hipError_t launch_fac_select_t(const FacArgs& a, hipStream_t s) {
+hipError_t launch_fac_select_t(const FacArgs& a, bool emitted, hipStream_t s) {
   const int hg = select_heads(a.c);
   const dim3 grid((a.c.group + hg - 1) / hg, a.c.n_kv_heads, a.c.batch);
   // One head per workgroup has the registers for a deeper prefetch; it pays only
   // when the rows span more than 16 filter chunks (measured: 128K-token rows
-  // gain 0.7 us, 32K-token rows lose 0.4 us to the redundant loads).
+  // gain 0.7 us, 32K-token rows lose 0.4 us to the redundant loads), or more
+  // than 32 emitted chunks.  TIP's lists are only used with one head per
+  // workgroup (decode_emits).
+  if (emitted) {
+    if (emit_chunks(a.c) > 32)
+      hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, true, true>), grid, dim3(kSelThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true>), grid, dim3(kSelThreads), 0, s, a);
+    return hipGetLastError();
+  }
   const bool deep = sel::filter_chunks(a.c) > 16;
   if (hg == 1 && deep) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, true>), grid, dim3(kSelThreads), 0, s, a);
   else if (hg == 1) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1>), grid, dim3(kSelThreads), 0, s, a);
@@ -595,6 +618,19 @@ FacArgs make_args(const Common& c, const FacPlan& p, const void* q, const void* 
 bool fac_selects(const Common& c, const FacPlan& p) {
   (void)p;
   return c.max_t > 0 && c.budget <= kSmallBudget && c.max_blocks <= kBtabLds && (c.score_stride & 3) == 0;
+}
+
+bool decode_emits(const Common& c, const FacPlan& p) {
+  // Few units (one-head selecting workgroups): there the filter launch and its
+  // launch gap are a large part of the step.  Many units keep the filter
+  // launch, whose cost they share, and whose global threshold does not depend
+  // on how the top keys cluster along the row.
+  if (!fac_selects(c, p) || select_heads(c) != 1 || emit_chunks(c) > 64 * sel::CPT) return false;
+  // Every chunk writes emit_target() keys (more only with ties): at the longest
+  // row about 2 Bc + 18 per chunk; a quarter more for ties and short rows.
+  const int64_t bc = c.budget < c.max_t ? c.budget : c.max_t;
+  const int64_t expect = 5 * (2 * bc + 18 * int64_t(emit_chunks(c))) / 4;
+  return expect <= kSmallCand;
 }
 
 FacPlan fac_plan(const Common& c) {
@@ -679,14 +715,14 @@ hipError_t launch_dense(const Common& c, const FacPlan& p, const void* q, const 
 
 hipError_t launch_fac_select(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
                              const void* v_pool, const int32_t* block_table, const float* scores,
-                             const int32_t* seq_lens, const SelectBuffers& sb, int32_t* sel_idx,
+                             const int32_t* seq_lens, const SelectBuffers& sb, bool emitted, int32_t* sel_idx,
                              int32_t* sel_count, float* out, hipStream_t s) {
   FacArgs a = make_args(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out, nullptr, nullptr);
   a.scores = scores;
   a.seq_lens = seq_lens;
   a.w = sb;
-  if (c.bf16) return launch_fac_select_t<uint16_t, float>(a, s);
-  return launch_fac_select_t<float, double>(a, s);
+  if (c.bf16) return launch_fac_select_t<uint16_t, float>(a, emitted, s);
+  return launch_fac_select_t<float, double>(a, emitted, s);
 }
 
 }  // namespace fasa

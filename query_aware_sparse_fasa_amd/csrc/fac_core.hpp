@@ -193,51 +193,59 @@ struct FacWave {
             vr[u].load(vbase + o);
           }
         }
-        // Logits of the U quads (this row group's row in each), and the new maxima.
-        Acc z[U][HG], mn[HG];
+        absorb<U>(kr, vr, valid);
+      }
+    }
+  }
+
+  // Fold U row quads already loaded (kr, vr: this row group's row of each
+  // quad; valid[u] false drops quad u's row) into the online softmax: the
+  // logits of all U quads first, then one rescale of each head's state to the
+  // new maximum, then the U weighted rows added.
+  template <int U>
+  __device__ __forceinline__ void absorb(const Raw8<T> (&kr)[U], const Raw8<T> (&vr)[U], const bool (&valid)[U]) {
+    Acc z[U][HG], mn[HG];
 #pragma unroll
-        for (int hh = 0; hh < HG; ++hh) mn[hh] = m[hh];
+    for (int hh = 0; hh < HG; ++hh) mn[hh] = m[hh];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          float kx[8];
-          if constexpr (!kBf16) kr[u].unpack(kx);
+    for (int u = 0; u < U; ++u) {
+      float kx[8];
+      if constexpr (!kBf16) kr[u].unpack(kx);
 #pragma unroll
-          for (int hh = 0; hh < HG; ++hh) {
-            Acc sdot;
-            if constexpr (kBf16) {
-              sdot = Acc(dot8(q2[hh], reinterpret_cast<const Raw8<uint16_t>&>(kr[u])));
-            } else {
-              sdot = Acc(0);
+      for (int hh = 0; hh < HG; ++hh) {
+        Acc sdot;
+        if constexpr (kBf16) {
+          sdot = Acc(dot8(q2[hh], reinterpret_cast<const Raw8<uint16_t>&>(kr[u])));
+        } else {
+          sdot = Acc(0);
 #pragma unroll
-              for (int e = 0; e < 8; ++e) sdot = fma(qv[hh][e], Acc(kx[e]), sdot);
-            }
-            const Acc zz = row_sum(sdot) * zscale;
-            z[u][hh] = valid[u] ? zz : neg_inf<Acc>();
-            mn[hh] = fmax(mn[hh], z[u][hh]);
-          }
+          for (int e = 0; e < 8; ++e) sdot = fma(qv[hh][e], Acc(kx[e]), sdot);
         }
-        // Rescale each head's state to its new maximum once.
+        const Acc zz = row_sum(sdot) * zscale;
+        z[u][hh] = valid[u] ? zz : neg_inf<Acc>();
+        mn[hh] = fmax(mn[hh], z[u][hh]);
+      }
+    }
+    // Rescale each head's state to its new maximum once.
 #pragma unroll
-        for (int hh = 0; hh < HG; ++hh) {
-          const Acc corr = merge_weight(m[hh], mn[hh]);
-          l[hh] *= corr;
+    for (int hh = 0; hh < HG; ++hh) {
+      const Acc corr = merge_weight(m[hh], mn[hh]);
+      l[hh] *= corr;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[hh][e] *= corr;
-          m[hh] = mn[hh];
-        }
-        // Add the weighted rows.
+      for (int e = 0; e < 8; ++e) acc[hh][e] *= corr;
+      m[hh] = mn[hh];
+    }
+    // Add the weighted rows.
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          float vx[8];
-          vr[u].unpack(vx);
+    for (int u = 0; u < U; ++u) {
+      float vx[8];
+      vr[u].unpack(vx);
 #pragma unroll
-          for (int hh = 0; hh < HG; ++hh) {
-            const Acc pz = merge_weight(z[u][hh], mn[hh]);
-            l[hh] += pz;
+      for (int hh = 0; hh < HG; ++hh) {
+        const Acc pz = merge_weight(z[u][hh], mn[hh]);
+        l[hh] += pz;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[hh][e] = fma(pz, Acc(vx[e]), acc[hh][e]);
-          }
-        }
+        for (int e = 0; e < 8; ++e) acc[hh][e] = fma(pz, Acc(vx[e]), acc[hh][e]);
       }
     }
   }

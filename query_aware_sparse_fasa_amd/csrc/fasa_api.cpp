@@ -300,8 +300,8 @@ fasa_status fasa_tip(const fasa_shape* shape, const void* q, const void* slab, c
   if (!aligned(src, elem_align(shape)) || !aligned(scores, 16)) return FASA_ERR_INVALID_ARG;
   if (max_t == 0) return FASA_OK;
   Common c = make_common(shape, max_t);
-  return hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores, nullptr,
-                                     stream));
+  return hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores,
+                                     fasa::TipOutputs{fasa::kTipScores, nullptr, nullptr, nullptr}, stream));
 }
 
 fasa_status fasa_topk(const fasa_shape* shape, const float* scores, const int32_t* seq_lens,
@@ -357,25 +357,37 @@ fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_po
   const FacPlan p = fasa::fac_plan(c);
   const Layout l = layout(c, p);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < l.total) return FASA_ERR_WORKSPACE;
-  // TIP (+ unit histograms) -> filter (+ FAC counters zeroed) -> FAC that
-  // selects its own rows and writes out directly (small budgets); for large
-  // budgets the exact select is a launch of its own, followed by a split-K FAC
-  // merged in its last workgroups.
+  // Small budgets and rows whose candidate lists fit on chip: TIP (+ each
+  // chunk's candidates) -> FAC that finishes the exact select from them and
+  // writes out directly; two launches.  Otherwise TIP (+ unit histograms) ->
+  // filter (+ FAC counters zeroed) -> the same FAC over the filter's kept keys
+  // (small budgets), or for large budgets the exact select as a launch of its
+  // own, followed by a split-K FAC merged in its last workgroups.
   char* w = static_cast<char*>(workspace);
   const fasa::SelectBuffers sb = select_buffers(workspace, l);
   float* scores = reinterpret_cast<float*>(w + l.scores);
   uint32_t* fac_arrive = reinterpret_cast<uint32_t*>(w + l.fac_arrive);
-  if (max_t > 0) {
-    if ((st = hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores, sb.hist,
+  if (max_t > 0 && fasa::decode_emits(c, p)) {
+    const fasa::TipOutputs to{fasa::kTipEmit, nullptr, static_cast<uint2*>(sb.slots),
+                              reinterpret_cast<uint2*>(sb.counts)};
+    if ((st = hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores, to,
                                           stream))) != FASA_OK)
+      return st;
+    return hip_status(fasa::launch_fac_select(c, p, q, k_pool, v_pool, block_table, scores, seq_lens, sb, true,
+                                              sel_idx, sel_count, out, stream));
+  }
+  if (max_t > 0) {
+    if ((st = hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores,
+                                          fasa::TipOutputs{fasa::kTipHist, sb.hist, nullptr, nullptr}, stream))) !=
+        FASA_OK)
       return st;
   }
   if ((st = hip_status(fasa::launch_filter(c, scores, seq_lens, sb, true, fac_arrive, p.head_chunks, stream))) !=
       FASA_OK)
     return st;
   if (fasa::fac_selects(c, p))
-    return hip_status(fasa::launch_fac_select(c, p, q, k_pool, v_pool, block_table, scores, seq_lens, sb, sel_idx,
-                                              sel_count, out, stream));
+    return hip_status(fasa::launch_fac_select(c, p, q, k_pool, v_pool, block_table, scores, seq_lens, sb, false,
+                                              sel_idx, sel_count, out, stream));
   if ((st = hip_status(fasa::launch_finish(c, scores, seq_lens, sel_idx, sel_count, sb, fac_arrive, p.head_chunks,
                                            stream))) != FASA_OK)
     return st;
@@ -446,8 +458,9 @@ fasa_status fasa_m_decode(const fasa_shape* shape, const void* q, const void* sl
   float* scores = reinterpret_cast<float*>(w + m.d.scores);
   uint32_t* fac_arrive = reinterpret_cast<uint32_t*>(w + m.d.fac_arrive);
   if (max_t > 0) {
-    if ((st = hip_status(fasa::launch_tip(c, q, slab, nullptr, block_table, seq_lens, fc_idx, scores, sb.hist,
-                                          stream))) != FASA_OK)
+    if ((st = hip_status(fasa::launch_tip(c, q, slab, nullptr, block_table, seq_lens, fc_idx, scores,
+                                          fasa::TipOutputs{fasa::kTipHist, sb.hist, nullptr, nullptr}, stream))) !=
+        FASA_OK)
       return st;
   }
   if ((st = hip_status(fasa::launch_filter(c, scores, seq_lens, sb, true, fac_arrive, p.head_chunks, stream))) !=

@@ -26,6 +26,32 @@ constexpr int kFilterChunk = 2048;
 constexpr int kSmallBudget = 1024;
 constexpr int kSmallCand = 4096;
 
+// Candidate emission by TIP (the two-launch step): every 1024-token chunk (one
+// TIP workgroup) writes its candidate keys at or above tau, the lower edge of
+// the coarse bin that holds its k-th largest key, k = emit_target(), as (key,
+// token) pairs in index order, and a summary (count | (some candidate left
+// out) << 31, tau).
+constexpr int kEmitChunk = 1024;
+__host__ __device__ __forceinline__ int emit_chunks_of(int max_t) {
+  const int n = (max_t + kEmitChunk - 1) / kEmitChunk;
+  return n > 0 ? n : 1;
+}
+// Per-chunk target for a unit choosing Bc of nC candidates: twice the chunk's
+// expected share of the top-Bc plus 16, at most a chunk.  The lists fail to
+// cover the top-Bc only if some chunk holds at least this many keys above the
+// Bc-th largest; the select then falls back to the whole scores row.
+__host__ __device__ __forceinline__ int emit_target(int Bc, int nC) {
+  if (nC <= 0) return kEmitChunk;
+  const int64_t share = (int64_t(Bc) * kEmitChunk + nC - 1) / nC;
+  const int64_t k = 2 * share + 16;
+  return int(k < kEmitChunk ? k : kEmitChunk);
+}
+__host__ __device__ __forceinline__ uint32_t emit_word(uint32_t count, bool cut) {
+  return count | (cut ? 0x80000000u : 0u);
+}
+__host__ __device__ __forceinline__ uint32_t emit_count(uint32_t w) { return w & 0xffffu; }
+__host__ __device__ __forceinline__ bool emit_cut(uint32_t w) { return (w & 0x80000000u) != 0u; }
+
 // FAC: 4 waves per workgroup; the waves' states are folded in LDS into one
 // partial.  Up to kFacMergeMax partials per head are merged by the last
 // workgroup of the split launch, when the launch has at most kFacMergeGrid
@@ -47,6 +73,8 @@ struct Common {
   int bf16;     // 1: bf16 storage, 0: fp32 storage
   float scale;
 };
+
+__host__ __device__ __forceinline__ int emit_chunks(const Common& c) { return emit_chunks_of(c.max_t); }
 
 // FAC work split, derived on the host from the shape (workspace size depends on it).
 struct FacPlan {
@@ -81,11 +109,19 @@ struct SelectBuffers {
   int32_t* b1;
 };
 
-// hist == nullptr: scores only.  Otherwise also accumulate the unit histograms
-// (which must hold the counts of nothing else: the select leaves them zero).
+// TIP epilogues: scores only; + the unit's coarse histogram (global atomics,
+// for the filter launch); + this chunk's candidate list for the select that
+// the FAC launch finishes (no filter launch).
+enum { kTipScores = 0, kTipHist = 1, kTipEmit = 2 };
+struct TipOutputs {
+  int mode;
+  uint32_t* hist;   // kTipHist: [units][kHistBins], holding the counts of nothing else
+  uint2* slots;     // kTipEmit: [units][emit_chunks][kEmitChunk] (key, token) pairs
+  uint2* meta;      // kTipEmit: [units][emit_chunks] (emit_word, tau)
+};
 hipError_t launch_tip(const Common& c, const void* q, const void* slab, const void* k_pool,
                       const int32_t* block_table, const int32_t* seq_lens,
-                      const int32_t* fc_idx, float* scores, uint32_t* hist, hipStream_t s);
+                      const int32_t* fc_idx, float* scores, const TipOutputs& o, hipStream_t s);
 // Top-B stages 1-2: the unit histograms (unless have_hist: TIP filled them) and
 // the filter's kept pairs, counts and b1.  Nothing when max_t == 0.
 // fac_arrive (nullable): FAC arrival counters, [units][head_chunks], zeroed here
@@ -145,9 +181,15 @@ bool fac_selects(const Common& c, const FacPlan& p);
 // Top-B stage 3 and FAC in one launch, after launch_filter: writes the
 // selection lists and counts, zeroes the histograms, and computes out (one
 // workgroup per query head, no merge).
+// emitted: the candidates are TIP's per-chunk lists (TIP ran with kTipEmit;
+// sb.slots / sb.counts hold its pairs and summaries); otherwise the filter's.
 hipError_t launch_fac_select(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
                              const void* v_pool, const int32_t* block_table, const float* scores,
-                             const int32_t* seq_lens, const SelectBuffers& sb, int32_t* sel_idx,
+                             const int32_t* seq_lens, const SelectBuffers& sb, bool emitted, int32_t* sel_idx,
                              int32_t* sel_count, float* out, hipStream_t s);
+// Whether a decode step takes two launches (TIP emitting candidates, then the
+// selecting FAC launch): fac_selects() and candidate lists that are expected
+// to fit the selecting launch's LDS.
+bool decode_emits(const Common& c, const FacPlan& p);
 
 }  // namespace fasa

@@ -162,9 +162,10 @@ __global__ __launch_bounds__(256) void fasam_gather_kernel(MArgs a) {
     vx[k] = live ? vh[k] : z;
   }
   __syncthreads();                                          // the column map
-  // Dominant pairs of the lane's 4 FC pairs, from the slab (device).
-  const E* sl = static_cast<const E*>(a.slab) + pb * c.slab_block_stride + int64_t(g) * c.slab_head_stride +
-                s * 2;
+  // Dominant pairs of the lane's 4 FC pairs, from the slab (device; indexed by
+  // the sequence and the logical block).
+  const E* sl = static_cast<const E*>(a.slab) + (int64_t(b) * c.max_blocks + (j >> 8)) * c.slab_block_stride +
+                int64_t(g) * c.slab_head_stride + s * 2;
   E dv[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {

@@ -36,6 +36,7 @@ struct SelState {
   alignas(16) uint32_t hist[HB];
   uint32_t wave_sum[2][NTH / 64];   // two buffers: back-to-back scans alternate
   uint32_t digit, rem, full;
+  uint32_t cut;                     // emitted lists: largest threshold of a chunk that left a candidate out, or 0
 };
 
 // Block-wide exclusive scan of one value per thread; returns the exclusive
@@ -204,6 +205,72 @@ __device__ __forceinline__ void unit_range(const Common& c, int t_raw, int& t, i
   c_hi = max(c_lo, t - c.n_recent);
 }
 
+// Copy the kept pairs of chunks 0 .. nfc-1 (chunk k at slots + k * CHUNK, its
+// pairs at offsets chunk_off[k] .. chunk_off[k+1] of the LDS arrays, already
+// published) through put(at, pair), in index order: wave w copies chunks w,
+// w + waves, ...; pre[p * D + d] holds pairs 64 d .. 64 d + 63 of chunk
+// w + p * waves (loaded early by the caller, unconditionally).  No barrier.
+template <int NTH, int PRE, int D, int CHUNK, typename Put>
+__device__ __forceinline__ void copy_kept(const int32_t* chunk_off, const uint2* slots, int nfc,
+                                          const uint2 (&pre)[PRE * D], Put put) {
+  constexpr int NW = NTH / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  bool more = false;
+#pragma unroll
+  for (int p = 0; p < PRE; ++p) {
+    const int ch = wave + p * NW;
+    if (ch < nfc) {
+      const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
+#pragma unroll
+      for (int d = 0; d < D; ++d)
+        if (64 * d + lane < n) put(o + 64 * d + lane, pre[p * D + d]);
+      more = more || n > 64 * D;
+    }
+  }
+  more = more || nfc > PRE * NW;
+  if (__builtin_amdgcn_readfirstlane(int(more)) != 0) {
+    // The first 64 pairs of the chunks past the prefetched ones, 8 chunks of
+    // this wave at a time: their loads go out together (clamped chunk, always
+    // readable), then they are copied.
+    for (int c0 = wave + PRE * NW; c0 < nfc; c0 += 8 * NW) {   // wave-uniform
+      uint2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = slots[int64_t(min(c0 + u * NW, nfc - 1)) * CHUNK + lane];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int ch = c0 + u * NW;
+        if (ch < nfc) {
+          const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
+          if (lane < n) put(o + lane, v[u]);
+        }
+      }
+    }
+    // Pairs past the first 64 of a chunk (a chunk keeps up to CHUNK), U x 64 of
+    // them per wave at a time: the loads go out together (clamped to the
+    // chunk's last kept pair, so loads past the end all read one line), then
+    // the valid ones are copied.  U is 8 while more than 128 pairs remain, 2
+    // for the last few (each width is straight-line code with its own wait).
+    auto copy_run = [&](auto width, const uint2* cs, int o, int n, int k0) {
+      constexpr int U = decltype(width)::value;
+      uint2 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = cs[min(k0 + 64 * u + lane, n - 1)];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + 64 * u + lane;
+        if (k < n) put(o + k, v[u]);
+      }
+    };
+    for (int ch = wave; ch < nfc; ch += NW) {
+      const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
+      const uint2* cs = slots + int64_t(ch) * CHUNK;
+      int k0 = ch < PRE * NW ? 64 * D : 64;         // pairs already prefetched
+      for (; n - k0 > 128; k0 += 8 * 64) copy_run(std::integral_constant<int, 8>(), cs, o, n, k0);   // wave-uniform
+      if (k0 < n) copy_run(std::integral_constant<int, 2>(), cs, o, n, k0);
+    }
+  }
+}
+
 // Gather the kept pairs of the nfc chunks into LDS, in index order.  cnt_raw[k]
 // is the count of chunk CPT t + k (loaded by the caller, clamped); wave w
 // copies chunks w, w + waves, ...; pre[p * D + d] holds pairs 64 d .. 64 d + 63
@@ -213,7 +280,6 @@ template <int NTH, int PRE, int D = 1>
 __device__ __forceinline__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off, const uint2* slots, int nfc, int cap_lds,
                            const int (&cnt_raw)[CPT], const uint2 (&pre)[PRE * D], uint32_t* key, int32_t* idx,
                            int b1, uint32_t& above) {
-  constexpr int NW = NTH / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (nfc > CPT * NTH) return -1;           // uniform
   int cnt[CPT];
@@ -268,98 +334,30 @@ __device__ __forceinline__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off,
       if (bin == uint32_t(b1)) atomicAdd(&s.hist[(e.x >> 10) & 2047u], 1u);
     }
   };
-  bool more = false;
-#pragma unroll
-  for (int p = 0; p < PRE; ++p) {
-    const int ch = wave + p * NW;
-    if (ch < nfc) {
-      const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
-#pragma unroll
-      for (int d = 0; d < D; ++d)
-        if (64 * d + lane < n) put(o + 64 * d + lane, pre[p * D + d]);
-      more = more || n > 64 * D;
-    }
-  }
-  more = more || nfc > PRE * NW;
-  if (__builtin_amdgcn_readfirstlane(int(more)) != 0) {
-    // The first 64 pairs of the chunks past the prefetched ones, 8 chunks of
-    // this wave at a time: their loads go out together (clamped chunk, always
-    // readable), then they are copied.
-    for (int c0 = wave + PRE * NW; c0 < nfc; c0 += 8 * NW) {   // wave-uniform
-      uint2 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = slots[int64_t(min(c0 + u * NW, nfc - 1)) * FCH + lane];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int ch = c0 + u * NW;
-        if (ch < nfc) {
-          const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
-          if (lane < n) put(o + lane, v[u]);
-        }
-      }
-    }
-    // Pairs past the first 64 of a chunk (a chunk keeps up to FCH), U x 64 of
-    // them per wave at a time: the loads go out together (clamped to the
-    // chunk's last kept pair, so loads past the end all read one line), then
-    // the valid ones are copied.  U is 8 while more than 128 pairs remain, 2
-    // for the last few (each width is straight-line code with its own wait).
-    auto copy_run = [&](auto width, const uint2* cs, int o, int n, int k0) {
-      constexpr int U = decltype(width)::value;
-      uint2 v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = cs[min(k0 + 64 * u + lane, n - 1)];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = k0 + 64 * u + lane;
-        if (k < n) put(o + k, v[u]);
-      }
-    };
-    for (int ch = wave; ch < nfc; ch += NW) {
-      const int o = chunk_off[ch], n = chunk_off[ch + 1] - o;
-      const uint2* cs = slots + int64_t(ch) * FCH;
-      int k0 = ch < PRE * NW ? 64 * D : 64;         // pairs already prefetched
-      for (; n - k0 > 128; k0 += 8 * 64) copy_run(std::integral_constant<int, 8>(), cs, o, n, k0);   // wave-uniform
-      if (k0 < n) copy_run(std::integral_constant<int, 2>(), cs, o, n, k0);
-    }
-  }
+  copy_kept<NTH, PRE, D, FCH>(chunk_off, slots, nfc, pre, put);
   // The barrier inside the scan also publishes the copied pairs and the histogram.
   (void)block_excl_scan(s, n_above, above);
   return int(N);
 }
 
-// Exact select of the Bc largest of the N keys key[0..N) (index order, with token
-// indices idx) held in LDS; writes the chosen tokens ascending to out[0..Bc).
-// Thread t owns a contiguous run of the keys.  With b1 >= 0 every key is known
-// to lie in a coarse bin >= b1 (the filter kept exactly those), `above` keys lie
-// above it and s.hist holds the second-digit histogram of the keys in b1 (both
-// built by the gather): the first digit is then b1 itself unless at least Bc
-// keys lie above it.  When a digit's bin holds exactly the keys still needed,
-// the remaining digits are skipped and one scan places every key at or above
-// the prefix.
+// The radix passes of an exact select from pass `pass` on (0: bits 31..21, 1:
+// bits 20..10, 2: bits 9..0), given the digits found so far (prefix under
+// pmask) and the rem keys still to take among those equal to the prefix, then
+// the index-order compaction: the Bc largest of the N keys key[0..N) (index
+// order, token indices idx) in LDS are written ascending to out[0..Bc).
+// all_eq: every key equal to the prefix is taken (skip to one scan).  Thread t
+// owns a contiguous run of the keys.
+// Returns the determined digits of the Bc-th largest key with the others zero
+// (a lower bound of that key).
 template <int NTH>
-__device__ __forceinline__ void lds_select(SelState<NTH>& s, const uint32_t* key, const int32_t* idx, int N, int Bc, int b1,
-                           uint32_t above, int32_t* out) {
+__device__ __forceinline__ uint32_t lds_select_from(SelState<NTH>& s, const uint32_t* key, const int32_t* idx,
+                                                    int N, int Bc, uint32_t prefix, uint32_t pmask, uint32_t rem,
+                                                    int pass, bool all_eq, int32_t* out) {
   const int tid = threadIdx.x;
   const int per = (N + NTH - 1) / NTH;
   const int i0 = min(N, tid * per), i1 = min(N, i0 + per);
-  uint32_t prefix = 0, pmask = 0, rem = uint32_t(Bc);
-  bool all_eq = false;                 // every key equal to the prefix is taken
-  int pass = 0;
-  if (b1 >= 0 && above < rem) {        // uniform; otherwise start from the first digit
-    // The second-digit histogram of the keys in bin b1 was built by the gather.
-    rem -= above;
-    prefix = uint32_t(b1) << 21;
-    pmask = 0x7ffu << 21;
-    find_digit<NTH, 2048>(s, rem);
-    const uint32_t d = s.digit, full = s.full;
-    rem = s.rem;
-    prefix |= d << 10;
-    pmask |= 0x7ffu << 10;
-    all_eq = full != 0u;
-    pass = full ? 3 : 2;
-  }
 #pragma unroll 1
-  for (; pass < 3; ++pass) {
+  for (; !all_eq && pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const uint32_t dmask = pass == 2 ? 1023u : 2047u;
     if (pass == 2) zero_bins<NTH, 1024>(s);
@@ -378,10 +376,7 @@ __device__ __forceinline__ void lds_select(SelState<NTH>& s, const uint32_t* key
     rem = s.rem;
     prefix |= d << shift;
     pmask |= dmask << shift;
-    if (full) {
-      all_eq = true;
-      break;
-    }
+    all_eq = full != 0u;
   }
   if (all_eq) {
     // Every key at or above the prefix is taken: one scan places them.
@@ -394,7 +389,7 @@ __device__ __forceinline__ void lds_select(SelState<NTH>& s, const uint32_t* key
       if (take && pos < Bc) out[pos] = idx[i];   // the guard never fails when the counts agree
       pos += take ? 1 : 0;
     }
-    return;
+    return prefix;
   }
   uint32_t n_gt = 0, n_eq = 0;
   for (int i = i0; i < i1; ++i) {
@@ -415,6 +410,108 @@ __device__ __forceinline__ void lds_select(SelState<NTH>& s, const uint32_t* key
     if (take && pos < Bc) out[pos] = idx[i];   // the guard never fails when the counts agree
     pos += take ? 1 : 0;
   }
+  return prefix;
+}
+
+// Exact select of the Bc largest of the N keys key[0..N) held in LDS (index
+// order, token indices idx); writes the chosen tokens ascending to out[0..Bc).
+// With b1 >= 0 every key is known to lie in a coarse bin >= b1 (the filter kept
+// exactly those), `above` keys lie above it and s.hist holds the second-digit
+// histogram of the keys in b1 (both built by the gather): the first digit is
+// then b1 itself unless at least Bc keys lie above it.  When a digit's bin
+// holds exactly the keys still needed, the remaining digits are skipped and
+// one scan places every key at or above the prefix.
+template <int NTH>
+__device__ __forceinline__ void lds_select(SelState<NTH>& s, const uint32_t* key, const int32_t* idx, int N, int Bc, int b1,
+                           uint32_t above, int32_t* out) {
+  uint32_t prefix = 0, pmask = 0, rem = uint32_t(Bc);
+  bool all_eq = false;
+  int pass = 0;
+  if (b1 >= 0 && above < rem) {        // uniform; otherwise start from the first digit
+    // The second-digit histogram of the keys in bin b1 was built by the gather.
+    rem -= above;
+    prefix = uint32_t(b1) << 21;
+    pmask = 0x7ffu << 21;
+    find_digit<NTH, 2048>(s, rem);
+    const uint32_t d = s.digit, full = s.full;
+    rem = s.rem;
+    prefix |= d << 10;
+    pmask |= 0x7ffu << 10;
+    all_eq = full != 0u;
+    pass = 2;
+  }
+  (void)lds_select_from<NTH>(s, key, idx, N, Bc, prefix, pmask, rem, pass, all_eq, out);
+}
+
+// Gather the candidate lists TIP emitted for the unit's nfc chunks (chunk k at
+// slots + k * kEmitChunk; meta_raw[k] is the summary (emit_word, tau) of chunk
+// CPT t + k, loaded by the caller, clamped) into LDS in index order, and build
+// the histogram of their first digits (bits 31..21) in s.hist (zeroed by the
+// caller).  s.cut gets the largest threshold tau of a chunk that left some
+// candidate out (0 if none did).  Returns the number of pairs, or -1 when they
+// do not fit cap_lds or there are more than 256 chunks (then nothing is
+// gathered).
+template <int NTH, int PRE, int D = 1>
+__device__ __forceinline__ int gather_emitted(SelState<NTH>& s, int32_t* chunk_off, const uint2* slots, int nfc,
+                                              int cap_lds, const uint2 (&meta_raw)[CPT], const uint2 (&pre)[PRE * D],
+                                              uint32_t* key, int32_t* idx) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (nfc > 64 * CPT) return -1;            // uniform
+  if (wave == 0) {
+    // Wave 0 holds every chunk's summary: it scans the counts, writes the
+    // chunk offsets and the total, and finds the largest threshold of a cut chunk.
+    uint32_t cnt[CPT], sum = 0, cut = 0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const bool in = CPT * tid + k < nfc;
+      const uint32_t w = in ? meta_raw[k].x : 0u;
+      cnt[k] = emit_count(w);
+      sum += cnt[k];
+      cut = (in && emit_cut(w)) ? max(cut, meta_raw[k].y) : cut;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) cut = max(cut, uint32_t(__shfl_xor(int(cut), o, 64)));
+    const uint32_t incl = wave_inclusive_scan(sum);
+    uint32_t off = incl - sum;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int ch = CPT * tid + k;
+      if (ch < nfc) chunk_off[ch] = int32_t(off);
+      off += cnt[k];
+    }
+    if (lane == 63) chunk_off[nfc] = int32_t(incl);
+    if (lane == 0) s.cut = cut;
+  }
+  __syncthreads();
+  const uint32_t N = uint32_t(chunk_off[nfc]);
+  if (N > uint32_t(cap_lds)) return -1;     // uniform
+  auto put = [&](int at, uint2 e) {
+    key[at] = e.x;
+    idx[at] = int32_t(e.y);
+    atomicAdd(&s.hist[e.x >> kHistShift], 1u);
+  };
+  copy_kept<NTH, PRE, D, kEmitChunk>(chunk_off, slots, nfc, pre, put);
+  __syncthreads();                          // publishes the pairs and the histogram
+  return int(N);
+}
+
+// Exact select of the Bc largest of the N (>= Bc) emitted keys in LDS, whose
+// first-digit histogram gather_emitted built, into out[0..Bc) ascending.
+// The emitted lists are the whole story only if no chunk left out a key that
+// could belong: every key a chunk left out lies below that chunk's threshold
+// tau, so if no cut chunk's tau lies above the Bc-th largest emitted key K,
+// every key left out is smaller than K, and the Bc largest of the union are
+// the Bc largest of the unit.  Returns false otherwise (out is then not a
+// valid result): early, when a tau's coarse bin lies above K's, or after the
+// select, when a tau exceeds the digits of K that the select determined.
+template <int NTH>
+__device__ __forceinline__ bool select_emitted(SelState<NTH>& s, const uint32_t* key, const int32_t* idx, int N,
+                                               int Bc, int32_t* out) {
+  find_digit<NTH, 2048>(s, uint32_t(Bc));
+  const uint32_t d = s.digit, full = s.full, rem = s.rem, cut = s.cut;
+  if ((cut >> 21) > d) return false;        // uniform
+  const uint32_t k_low = lds_select_from<NTH>(s, key, idx, N, Bc, d << 21, 0x7ffu << 21, rem, 1, full != 0u, out);
+  return cut <= k_low;                      // uniform
 }
 
 // Fallback: radix select over the whole candidate range [c_lo, c_hi) of a row,
@@ -547,16 +644,22 @@ __device__ __forceinline__ void row_select(SelState<NTH>& s, const float* row, i
 // (clamped to the unit's nfa chunks; loaded unconditionally).
 // D > 1: also pairs 64 .. 64 D - 1 of each of those chunks (read whatever the
 // slots hold; only the first count of them are used).
-template <int NTH, int PRE, int D = 1>
+template <int NTH, int PRE, int D = 1, int CHUNK = FCH>
 __device__ __forceinline__ void prefetch_kept(const uint2* unit_slots, int nfa, uint2 (&pre)[PRE * D]) {
-  static_assert(64 * D <= FCH, "a chunk holds FCH slots");
+  static_assert(64 * D <= CHUNK, "a chunk holds CHUNK slots");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
   for (int p = 0; p < PRE; ++p) {
-    const uint2* cs = unit_slots + int64_t(min(wave + p * (NTH / 64), nfa - 1)) * FCH;
+    const uint2* cs = unit_slots + int64_t(min(wave + p * (NTH / 64), nfa - 1)) * CHUNK;
 #pragma unroll
     for (int d = 0; d < D; ++d) pre[p * D + d] = cs[64 * d + lane];
   }
+}
+
+// Chunk summaries of TIP's lists, CPT per thread (chunk CPT t + k), loaded unconditionally.
+__device__ __forceinline__ void load_meta(const uint2* unit_meta, int nfa, uint2 (&m)[CPT]) {
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) m[k] = unit_meta[min(CPT * int(threadIdx.x) + k, nfa - 1)];
 }
 
 // Chunk counts of a unit, CPT per thread (chunk CPT t + k), loaded unconditionally.
@@ -579,6 +682,22 @@ __device__ void select_from_kept(SelState<NTH>& s, int32_t* chunk_off, uint32_t*
   const int N = gather_kept<NTH, PRE, D>(s, chunk_off, unit_slots, nfc, cap_lds, cnt, pre, key, idx, b1, above);
   if (N >= Bc) lds_select<NTH>(s, key, idx, N, Bc, b1, above, out);
   else row_select<NTH, VEC>(s, row, lim, max_t, c_lo, c_hi, Bc, out);
+}
+
+// Exact select of one unit that is not keep-all from the lists TIP emitted
+// (nfc chunks, summaries meta and first pairs pre already loaded), into
+// out[0..Bc) -- global or LDS.  Falls back to the whole score row when the
+// lists cannot be shown to hold the top-Bc, hold fewer than Bc keys, or do not
+// fit.
+template <int NTH, int PRE, bool VEC, int D = 1>
+__device__ void select_from_emitted(SelState<NTH>& s, int32_t* chunk_off, uint32_t* key, int32_t* idx, int cap_lds,
+                                    const uint2* unit_slots, const float* row, int lim, int max_t, int nfc,
+                                    const uint2 (&meta)[CPT], const uint2 (&pre)[PRE * D], int c_lo, int c_hi, int Bc,
+                                    int32_t* out) {
+  zero_bins<NTH, HB>(s);               // the gather's first-digit histogram; published by its first barrier
+  const int N = gather_emitted<NTH, PRE, D>(s, chunk_off, unit_slots, nfc, cap_lds, meta, pre, key, idx);
+  if (N >= Bc && select_emitted<NTH>(s, key, idx, N, Bc, out)) return;
+  row_select<NTH, VEC>(s, row, lim, max_t, c_lo, c_hi, Bc, out);
 }
 
 }  // namespace sel

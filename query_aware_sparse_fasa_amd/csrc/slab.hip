@@ -6,11 +6,14 @@
 // "Hardware-Aware Variants", FASA-M component 1 and FASA-C).  Read in place
 // from a row-major key cache, 16 scattered FC pairs of a 256-byte bf16 row
 // still touch almost every 32-byte sector, so TIP would pay for the whole key
-// row.  The slab stores those columns FC-major per 256-token block,
-//   [block][kv head][F][256 tokens][2],
+// row.  The slab stores those columns FC-major per 256-token block, indexed by
+// the sequence and the block's logical position in it (not by the physical
+// block of the pool),
+//   [sequence][logical block][kv head][F][256 tokens][2],
 // so one FC of one block is a contiguous 1 KB (bf16) run that a wave reads
-// with one 16-byte load per lane.  It is written once per token (append) or
-// once per prefix (build), never per decode step.
+// with one 16-byte load per lane, and TIP finds it without reading the block
+// table.  It is written once per token (append) or once per prefix (build),
+// never per decode step.
 #include "fasa_device.hpp"
 #include "fasa_internal.hpp"
 
@@ -37,7 +40,7 @@ __global__ __launch_bounds__(256) void slab_build_kernel(Common c, const T* __re
   const int64_t phys = block_table[int64_t(b) * c.max_blocks + blk];
   const int s = threadIdx.x;
   const T* src = k_pool + phys * c.kv_block_stride + int64_t(g) * c.kv_head_stride + int64_t(s) * kHeadDim;
-  T* dst = slab + phys * c.slab_block_stride + int64_t(g) * c.slab_head_stride + 2 * s;
+  T* dst = slab + (int64_t(b) * c.max_blocks + blk) * c.slab_block_stride + int64_t(g) * c.slab_head_stride + 2 * s;
   for (int f = 0; f < c.n_fc; ++f) {
     const int fi = fc_idx[g * c.n_fc + f];     // < 0: an unused slot of a head with fewer FCs, kept zero
     *reinterpret_cast<P*>(dst + int64_t(f) * kSlabFcStride) =
@@ -58,7 +61,8 @@ __global__ __launch_bounds__(64) void slab_append_kernel(Common c, const T* __re
   const int64_t phys = block_table[int64_t(b) * c.max_blocks + (pos >> 8)];
   const int s = pos & (kBlock - 1);
   const T* src = k_pool + phys * c.kv_block_stride + int64_t(g) * c.kv_head_stride + int64_t(s) * kHeadDim;
-  T* dst = slab + phys * c.slab_block_stride + int64_t(g) * c.slab_head_stride + 2 * s;
+  T* dst = slab + (int64_t(b) * c.max_blocks + (pos >> 8)) * c.slab_block_stride + int64_t(g) * c.slab_head_stride +
+           2 * s;
   for (int f = threadIdx.x; f < c.n_fc; f += 64) {
     const int fi = fc_idx[g * c.n_fc + f];
     *reinterpret_cast<P*>(dst + int64_t(f) * kSlabFcStride) =

@@ -11,12 +11,32 @@
 // each token then costs 2F fused multiply-adds on 2F cache elements.
 //
 // Mapping (gfx950, wave64): one workgroup = 4 waves = 4 cache blocks of one
-// (b, g); lane l of a wave owns tokens 4l..4l+3 of its block.  Reading the slab,
-// FC f of the block is one contiguous 1 KB (bf16) run and each lane issues one
-// 16-byte load per FC -- F independent loads in flight per lane, no cross-lane
-// traffic, and the folded query is a wave-uniform LDS broadcast.  Scores leave
-// as one 16-byte store per lane.  The kernel is a pure HBM stream
-// (2 flops per 2-byte element), so there is nothing for MFMA to do.
+// (b, g) = one 1024-token chunk; lane l of a wave owns tokens 4l..4l+3 of its
+// block.  Reading the slab, FC f of the block is one contiguous 1 KB (bf16) run
+// and each lane issues one 16-byte load per FC -- F independent loads in flight
+// per lane, no cross-lane traffic, and the folded query is a wave-uniform LDS
+// broadcast.  The slab is indexed by (sequence, logical block), so its
+// addresses need nothing but the workgroup's coordinates: the slab loads go
+// out at kernel entry, beside the query and length loads.  Scores leave as one
+// 16-byte store per lane.  The kernel is a pure HBM stream (2 flops per 2-byte
+// element), so there is nothing for MFMA to do.
+//
+// Three epilogues (MODE):
+//   kTipScores: scores only (fasa_tip);
+//   kTipHist:   also the unit's coarse key histogram for the filter launch of
+//               the three-launch select (global atomics);
+//   kTipEmit:   also this chunk's candidates for the exact select that the
+//               FAC launch finishes: every candidate key of the chunk at or
+//               above tau, the lower edge of the coarse bin (key bits 31..21)
+//               that holds the chunk's k-th largest key (k from the unit's
+//               budget and length), written as (key, token) pairs in index
+//               order, with the chunk's count, tau, and whether any candidate
+//               of the chunk was left out.  Keys left out are all below tau,
+//               which is what lets the FAC launch prove that the union of the
+//               chunks' lists holds the unit's top-B (or fall back to the
+//               whole scores row).  (An exact k-th largest found by ballot
+//               binary searches, 32 dependent rounds per wave, measured 10 us
+//               slower per launch than this LDS histogram.)
 #include "fasa_device.hpp"
 #include "fasa_internal.hpp"
 
@@ -31,67 +51,65 @@ struct TipArgs {
   const int32_t* seq_lens;
   const int32_t* fc_idx;
   float* scores;
-  uint32_t* hist;       // [units][kHistBins] coarse key histogram (HIST only)
+  uint32_t* hist;       // [units][kHistBins] coarse key histogram (kTipHist)
+  uint2* slots;         // [units][emit chunks][kEmitChunk] (key, token) pairs (kTipEmit)
+  uint2* meta;          // [units][emit chunks] chunk summary: (emit_word, tau) (kTipEmit)
 };
 
 // FT > 0: compile-time F (all loads of a block issued back to back); FT == 0: runtime F.
-// HIST: also add this workgroup's candidate scores to the unit's coarse histogram
-// of key bits 31..21 (the first radix digit of the top-B select), while the
-// scores are still in registers.
-template <typename T, int FT, bool FROM_SLAB, bool HIST>
+template <typename T, int FT, bool FROM_SLAB, int MODE>
 __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
+  constexpr bool HIST = MODE == kTipHist, EMIT = MODE == kTipEmit, LDS_HIST = HIST || EMIT;
   const Common& c = a.c;
   const WgCoord wg = xcd_grouped();
   const int b = wg.z, g = wg.y;
   const int F = FT > 0 ? FT : c.n_fc;
-  // The wave index is made explicitly uniform so the block-table entry is a
-  // scalar load, issued at once and waited on its own counter.
+  // The wave index is made explicitly uniform so the block-table entry (row
+  // gather only) is a scalar load, issued at once and waited on its own counter.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int blk = wg.x * 4 + wave;
+  const int64_t unit = int64_t(b) * c.n_kv_heads + g;
 
-  // Dependency chain kept to two memory round trips: (sequence length, block
-  // table entry, FC index) are independent loads; then the slab loads and the
-  // query loads go out together.
+  // Independent loads: (sequence length, FC index, the slab), then the query
+  // loads, which depend on the FC index only; the fold waits for the query
+  // values while the slab stream is in flight.  The row-gather path also needs
+  // the block-table entry before its key loads.
   const int e = threadIdx.x;
   const int ec = e < 2 * F ? e : 0;
   const int f_q = ec >> 1, comp = ec & 1;
   const int t_raw = a.seq_lens[b];
-  const int64_t phys_raw = a.block_table[int64_t(b) * c.max_blocks + min(blk, c.max_blocks - 1)];
   const int fi = a.fc_idx[g * F + f_q];          // < 0: unused slot (a head with fewer FCs)
   const int col = 2 * (fi < 0 ? 0 : fi) + comp;
+  const int blk_c = min(blk, c.max_blocks - 1);
+  Raw8<T> x[FROM_SLAB && FT > 0 ? FT : 1];
+  const T* sbase = static_cast<const T*>(a.src) + (int64_t(b) * c.max_blocks + blk_c) * c.slab_block_stride +
+                   int64_t(g) * c.slab_head_stride + lane * 8;
+  if constexpr (FROM_SLAB && FT > 0) {
+    // Unconditional (a block past the sequence's end is within the slab and
+    // its values are not used), so nothing waits for the length first.
+#pragma unroll
+    for (int f = 0; f < FT; ++f) x[f].load_nt(sbase + f * kSlabFcStride);
+  }
+  const int64_t phys_raw = FROM_SLAB ? 0 : a.block_table[int64_t(b) * c.max_blocks + blk_c];
   const int t = clamp_len(t_raw, c.max_t, c.max_blocks);
   // A workgroup whose four blocks all lie past the end of a short sequence has
   // nothing to do (the whole workgroup leaves together, before any barrier).
-  // The slab loads need the length and the block-table entry anyway, so this
-  // adds no wait for the others.
   if (wg.x * 4 * kBlock >= t) return;
 
   __shared__ float qf[kHeadDim];   // folded query, [f][2]
   __shared__ int cols[kHeadDim / 2];
-  __shared__ uint32_t hist_s[HIST ? kHistBins : 1];
-  if constexpr (HIST) {
+  __shared__ uint32_t hist_s[LDS_HIST ? kHistBins : 1];
+  if constexpr (LDS_HIST) {
     for (int i = threadIdx.x; i < kHistBins; i += 256) hist_s[i] = 0u;
   }
   const bool live = blk * kBlock < t;          // wave-uniform
   const int64_t phys = live ? phys_raw : 0;
 
-  // Query loads first (unconditional, head index clamped), then this block's slab
-  // loads; the fold only waits for the query values.
   const T* qh = static_cast<const T*>(a.q) +
                 (int64_t(b) * c.n_q_heads + int64_t(g) * c.group) * kHeadDim + col;
   T qv[16];
 #pragma unroll
   for (int h = 0; h < 16; ++h) qv[h] = qh[min(h, c.group - 1) * kHeadDim];
-
-  Raw8<T> x[FROM_SLAB && FT > 0 ? FT : 1];
-  const T* sbase = static_cast<const T*>(a.src) + phys * c.slab_block_stride +
-                   int64_t(g) * c.slab_head_stride + lane * 8;
-  if constexpr (FROM_SLAB && FT > 0) {
-    if (live) {
-#pragma unroll
-      for (int f = 0; f < FT; ++f) x[f].load_nt(sbase + f * kSlabFcStride);
-    }
-  }
   {
     // Folded query: thread e < 2F sums column 2 I_g[f] + comp over the group's
     // heads in head order (terms past the group are masked to +0).
@@ -104,7 +122,7 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
     }
   }
   __syncthreads();
-  if (!HIST && !live) return;                  // with HIST every wave reaches the second barrier
+  if (!LDS_HIST && !live) return;              // otherwise every wave reaches the later barriers
 
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   if (live) {
@@ -148,9 +166,16 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
 
   const int j0 = blk * kBlock + lane * 4;
   if (live) {
-    float* dst = a.scores + (int64_t(b) * c.n_kv_heads + g) * c.score_stride + j0;
+    float* dst = a.scores + unit * c.score_stride + j0;
     if (j0 + 3 < t && (c.score_stride & 3) == 0) {
-      *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      if constexpr (EMIT) {
+        // Only the select's fallback reads these scores back: streaming
+        // stores, which leave no dirty lines for the kernel's end to write back.
+        typedef float f4v __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(f4v{acc[0], acc[1], acc[2], acc[3]}, reinterpret_cast<f4v*>(dst));
+      } else {
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      }
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -175,42 +200,129 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
     }
     if (run_cnt != 0u) atomicAdd(&hist_s[run_bin], run_cnt);
     __syncthreads();
-    uint32_t* hg = a.hist + (int64_t(b) * c.n_kv_heads + g) * kHistBins;
+    uint32_t* hg = a.hist + unit * kHistBins;
     for (int i = threadIdx.x; i < kHistBins; i += 256) {
       const uint32_t v = hist_s[i];
       if (v != 0u) atomicAdd(&hg[i], v);
     }
   }
+  if constexpr (EMIT) {
+    // This chunk's candidates [max(c_lo, k0), min(c_hi, k0 + 1024)) and the
+    // unit's target (the same in every chunk of the unit).
+    const int c_lo = min(c.n_sink, t);
+    const int c_hi = max(c_lo, t - c.n_recent);
+    const int k0 = wg.x * kEmitChunk;
+    const int n_in = max(0, min(c_hi, k0 + kEmitChunk) - max(c_lo, k0));
+    const int nC = c_hi - c_lo;
+    const uint32_t want = uint32_t(emit_target(min(c.budget, nC), nC));
+    uint32_t key[4];
+    bool act[4];
+    uint32_t run_bin = 0u, run_cnt = 0u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = j0 + r;
+      act[r] = live && j >= c_lo && j < c_hi;
+      key[r] = score_key(acc[r]);
+      const uint32_t bin = key[r] >> kHistShift;
+      const bool brk = act[r] && bin != run_bin;
+      if (brk && run_cnt != 0u) atomicAdd(&hist_s[run_bin], run_cnt);
+      run_cnt = brk ? 1u : run_cnt + (act[r] ? 1u : 0u);
+      run_bin = brk ? bin : run_bin;
+    }
+    if (run_cnt != 0u) atomicAdd(&hist_s[run_bin], run_cnt);
+    __syncthreads();
+    // The bin where the count from the top first reaches `want`: thread e owns
+    // bins 2047 - 8e down to 2040 - 8e; an exclusive scan over threads counts
+    // the keys above them.  With want >= n_in every candidate is written (bin 0).
+    // (Each wave finding the bin itself from the whole histogram, one barrier
+    // instead of two, measured 0.4 us slower.)
+    __shared__ uint32_t s_w[4], s_w2[4];
+    __shared__ uint32_t s_bin;
+    const uint4 hlo = *reinterpret_cast<const uint4*>(hist_s + kHistBins - 8 - 8 * e);
+    const uint4 hhi = *reinterpret_cast<const uint4*>(hist_s + kHistBins - 4 - 8 * e);
+    const uint32_t h[8] = {hhi.w, hhi.z, hhi.y, hhi.x, hlo.w, hlo.z, hlo.y, hlo.x};   // descending bins
+    uint32_t hs = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hs += h[i];
+    const uint32_t incl = wave_inclusive_scan(hs);
+    if (lane == 63) s_w[wave] = incl;
+    if (e == 0) s_bin = 0u;
+    __syncthreads();
+    uint32_t above = incl - hs;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) above += (w < wave) ? s_w[w] : 0u;
+    if (want < uint32_t(n_in) && above < want && want <= above + hs) {
+      uint32_t cum = above;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (cum < want && want <= cum + h[i]) s_bin = uint32_t(kHistBins - 1 - 8 * e - i);
+        cum += h[i];
+      }
+    }
+    __syncthreads();
+    const uint32_t tau = s_bin << kHistShift;
+    // Every candidate key at or above the bin's lower edge tau, in index order
+    // (lanes in order, then slots).
+    bool keep[4];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      keep[r] = act[r] && key[r] >= tau;
+      cnt += keep[r] ? 1u : 0u;
+    }
+    const uint32_t pin = wave_inclusive_scan(cnt);
+    if (lane == 63) s_w2[wave] = pin;
+    __syncthreads();
+    uint32_t pos = pin - cnt, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t v = s_w2[w];
+      pos += (w < wave) ? v : 0u;
+      tot += v;
+    }
+    uint2* out = a.slots + (unit * emit_chunks(c) + wg.x) * int64_t(kEmitChunk);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (keep[r]) out[pos] = make_uint2(key[r], uint32_t(j0 + r));
+      pos += keep[r] ? 1u : 0u;
+    }
+    if (e == 0) a.meta[unit * emit_chunks(c) + wg.x] = make_uint2(emit_word(tot, tot < uint32_t(n_in)), tau);
+  }
 }
 
-template <typename T, bool FROM_SLAB, bool HIST>
+template <typename T, bool FROM_SLAB, int MODE>
 hipError_t launch_t(const TipArgs& a, dim3 grid, hipStream_t s) {
   switch (a.c.n_fc) {
-    case 8: hipLaunchKernelGGL((tip_kernel<T, 8, FROM_SLAB, HIST>), grid, dim3(256), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((tip_kernel<T, 16, FROM_SLAB, HIST>), grid, dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((tip_kernel<T, 32, FROM_SLAB, HIST>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((tip_kernel<T, 0, FROM_SLAB, HIST>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((tip_kernel<T, 8, FROM_SLAB, MODE>), grid, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((tip_kernel<T, 16, FROM_SLAB, MODE>), grid, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((tip_kernel<T, 32, FROM_SLAB, MODE>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((tip_kernel<T, 0, FROM_SLAB, MODE>), grid, dim3(256), 0, s, a); break;
   }
   return hipGetLastError();
 }
 
-template <typename T, bool HIST>
+template <typename T, int MODE>
 hipError_t launch_src(const TipArgs& a, dim3 grid, bool slab, hipStream_t s) {
-  return slab ? launch_t<T, true, HIST>(a, grid, s) : launch_t<T, false, HIST>(a, grid, s);
+  return slab ? launch_t<T, true, MODE>(a, grid, s) : launch_t<T, false, MODE>(a, grid, s);
+}
+
+template <typename T>
+hipError_t launch_mode(const TipArgs& a, dim3 grid, bool slab, int mode, hipStream_t s) {
+  if (mode == kTipHist) return launch_src<T, kTipHist>(a, grid, slab, s);
+  if (mode == kTipEmit) return launch_src<T, kTipEmit>(a, grid, slab, s);
+  return launch_src<T, kTipScores>(a, grid, slab, s);
 }
 
 }  // namespace
 
 hipError_t launch_tip(const Common& c, const void* q, const void* slab, const void* k_pool,
                       const int32_t* block_table, const int32_t* seq_lens, const int32_t* fc_idx,
-                      float* scores, uint32_t* hist, hipStream_t s) {
-  TipArgs a{c, q, slab ? slab : k_pool, block_table, seq_lens, fc_idx, scores, hist};
+                      float* scores, const TipOutputs& o, hipStream_t s) {
+  TipArgs a{c, q, slab ? slab : k_pool, block_table, seq_lens, fc_idx, scores, o.hist, o.slots, o.meta};
   const int nblk = (c.max_t + kBlock - 1) / kBlock;
   const dim3 grid((nblk + 3) / 4, c.n_kv_heads, c.batch);
   const bool sl = slab != nullptr;
-  if (c.bf16)
-    return hist ? launch_src<uint16_t, true>(a, grid, sl, s) : launch_src<uint16_t, false>(a, grid, sl, s);
-  return hist ? launch_src<float, true>(a, grid, sl, s) : launch_src<float, false>(a, grid, sl, s);
+  return c.bf16 ? launch_mode<uint16_t>(a, grid, sl, o.mode, s) : launch_mode<float>(a, grid, sl, o.mode, s);
 }
 
 }  // namespace fasa

@@ -181,11 +181,15 @@ __global__ __launch_bounds__(FNT) void filter_kernel(TopkArgs a) {
 #pragma unroll
   for (int w = 0; w < FNT / 64; ++w) above += (w < wave) ? s_w[w] : 0u;
   const uint32_t bc = uint32_t(Bc);
+  // A consistent histogram has one crossing.  One that is not (stale counts,
+  // whose 32-bit sums may wrap) can have several: the largest crossing bin wins,
+  // so every chunk of the unit -- all reading the same histogram -- keeps from
+  // the same b1, the one chunk 0 publishes.
   if (above < bc && bc <= above + hs) {
     uint32_t cum = above;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (cum < bc && bc <= cum + h[i]) s_b1 = uint32_t(HB - 1 - 8 * tid - i);
+      if (cum < bc && bc <= cum + h[i]) atomicMax(&s_b1, uint32_t(HB - 1 - 8 * tid - i));
       cum += h[i];
     }
   }
@@ -292,7 +296,10 @@ size_t slots_bytes(const Common& c) {
   return (size_t(c.batch) * c.n_kv_heads * filter_chunks(c) * FCH * sizeof(uint2) + 255) & ~size_t(255);
 }
 size_t counts_bytes(const Common& c) {
-  return (size_t(c.batch) * c.n_kv_heads * filter_chunks(c) * sizeof(int32_t) + 255) & ~size_t(255);
+  // Per-chunk counts of the filter (4 bytes per 2048-token chunk) or the
+  // summaries of TIP's emitted lists (8 bytes per 1024-token chunk).
+  const size_t fb = size_t(filter_chunks(c)) * sizeof(int32_t), eb = size_t(emit_chunks(c)) * sizeof(uint2);
+  return (size_t(c.batch) * c.n_kv_heads * (eb > fb ? eb : fb) + 255) & ~size_t(255);
 }
 
 hipError_t launch_filter(const Common& c, const float* scores, const int32_t* seq_lens, const SelectBuffers& w,

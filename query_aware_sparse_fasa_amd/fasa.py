@@ -115,7 +115,7 @@ def make_shape(batch: int, n_q_heads: int, n_kv_heads: int, n_fc: int, budget: i
                kv_head_stride: Optional[int] = None, slab_block_stride: Optional[int] = None,
                slab_head_stride: Optional[int] = None) -> fasa_shape:
     """A shape for a paged pool [n_blocks][H_kv][256][128] and a slab
-    [n_blocks][H_kv][F][256][2] unless other strides are given."""
+    [batch][max_blocks_per_seq][H_kv][F][256][2] unless other strides are given."""
     s = fasa_shape()
     s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim = batch, n_q_heads, n_kv_heads, HEAD_DIM
     s.n_fc, s.budget, s.n_sink, s.n_recent = n_fc, budget, n_sink, n_recent
@@ -318,9 +318,12 @@ def fasa_ca_dominant(shape, hits, n_rows, n_tip, fc_idx, stream=None) -> None:
 
 
 # --------------------------------------------------------------------------- buffers
-def alloc_slab(shape: fasa_shape, n_blocks: int, device="cuda") -> torch.Tensor:
+def alloc_slab(shape: fasa_shape, device="cuda") -> torch.Tensor:
+    """The dominant-key cache, indexed by (sequence, logical block):
+    [batch][max_blocks_per_seq][H_kv][F][256][2] in the cache dtype."""
     dt = torch.bfloat16 if shape.kv_dtype == FASA_BF16 else torch.float32
-    return torch.empty(n_blocks, shape.n_kv_heads, shape.n_fc, BLOCK, 2, dtype=dt, device=device)
+    return torch.empty(shape.batch, shape.max_blocks_per_seq, shape.n_kv_heads, shape.n_fc, BLOCK, 2, dtype=dt,
+                       device=device)
 
 
 def alloc_m_host(shape: fasa_shape, n_blocks: int):

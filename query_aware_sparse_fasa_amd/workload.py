@@ -41,7 +41,7 @@ class DeviceLayer:
         self.workspace = fasa.alloc_workspace(self.shape, self.max_t, device=dev)
         self.slab = None
         if with_slab:
-            self.slab = fasa.alloc_slab(self.shape, inp.n_blocks, device=dev)
+            self.slab = fasa.alloc_slab(self.shape, device=dev)
             if build_slab:
                 self.build_slab()
 

@@ -89,7 +89,7 @@ def test_slab_build_bit_exact(name):
             K = synth.unit_rows(inp, b, g, inp.k_pool)             # cast values, no widening
             ref = O.slab_rows(K.float().numpy(), inp.fc_idx[g])   # [F][t][2]
             n = (t + 255) // 256
-            got = slab[torch.as_tensor(inp.block_table[b, :n].astype(np.int64)), g]  # [n][F][256][2]
+            got = slab[b, :n, g]                                  # [n][F][256][2], logical blocks
             got = got.permute(1, 0, 2, 3).reshape(cfg.n_fc, n * 256, 2)[:, :t].float().numpy()
             np.testing.assert_array_equal(got, ref, err_msg=f"{name} b={b} g={g}")
 
@@ -107,15 +107,16 @@ def test_slab_append_writes_one_slot():
     fasa.fasa_slab_append(L2.shape, L2.k_pool, L2.block_table, torch.from_numpy(pos).cuda(),
                           L2.fc_idx, L2.slab)
     torch.cuda.synchronize()
-    a, ref = L2.slab.cpu(), L.slab.cpu()
-    written = np.zeros(a.shape[0] * 256, dtype=bool)
+    a, ref = L2.slab.cpu(), L.slab.cpu()                 # [batch][max_blocks][H][F][256][2]
+    nb = a.shape[1]
+    written = np.zeros(a.shape[0] * nb * 256, dtype=bool)
     for b in range(cfg.batch):
         if pos[b] < 0:
             continue
-        p, s = int(inp.block_table[b, pos[b] // 256]), int(pos[b]) % 256
-        assert torch.equal(a[p, :, :, s], ref[p, :, :, s]), b
-        written[p * 256 + s] = True
-    rest = a.permute(0, 3, 1, 2, 4).reshape(a.shape[0] * 256, -1)[~torch.from_numpy(written)]
+        k, s = int(pos[b]) // 256, int(pos[b]) % 256
+        assert torch.equal(a[b, k, :, :, s], ref[b, k, :, :, s]), b
+        written[(b * nb + k) * 256 + s] = True
+    rest = a.permute(0, 1, 4, 2, 3, 5).reshape(a.shape[0] * nb * 256, -1)[~torch.from_numpy(written)]
     assert torch.isnan(rest.float()).all()
 
 
@@ -619,12 +620,99 @@ def test_graph_capture_replays():
 
 
 # ------------------------------------------------------------------------ full sizes
+# Units the oracle checks at full size: every unit of c1-c4; for the ragged
+# batch every kv head of its shortest, median and longest sequence.
 FULL_SAMPLES = {
-    "c2": None,                                  # every unit
-    "c3": [(0, 0), (5, 3), (15, 7)],
-    "c4": [(0, 0), (1, 2), (3, 3)],
     "c5": "extremes",
 }
+
+
+def test_decode_duplicate_keys_tie_to_lower_index():
+    """Exact score ties through the whole decode step: in every unit, 30 copies
+    of the key of the token the oracle ranks B - 10 are written at other
+    positions (in its own 1024-token chunk and in others, before and after it),
+    so the B-th score is shared by many tokens.  TIP gives identical rows
+    bit-identical scores, and the select must keep the lowest indices among
+    them, exactly as the oracle's (-S, j) order does."""
+    cfg = C["c2"].replace(batch=2, n_q_heads=8, n_kv_heads=2, t=None, t_range=(6000, 9000), budget=200)
+    say("[decode duplicate keys]")
+    inp = synth.make_inputs(cfg, seed=41)
+    rng = np.random.default_rng(41)
+    G = cfg.group
+    dup = {}
+    for b in range(cfg.batch):
+        t = int(inp.seq_lens[b])
+        for g in range(cfg.n_kv_heads):
+            q = inp.q[b, g * G:(g + 1) * G].double().numpy()
+            K = unit_rows(inp, b, g, inp.k_pool).double().numpy()
+            S = O.tip_scores(q, K, inp.fc_idx[g])
+            order = np.lexsort((np.arange(t), -S))
+            src = int(order[cfg.budget - 10])
+            near = rng.choice(np.arange(max(0, src - 900), min(t, src + 900)), size=10, replace=False)
+            far = rng.choice(t, size=20, replace=False)
+            pos = np.setdiff1d(np.concatenate([near, far]), order[:cfg.budget - 10])
+            pos = pos[pos != src]
+            row = inp.k_pool[int(inp.block_table[b, src // 256]), g, src % 256].clone()
+            for j in pos:
+                inp.k_pool[int(inp.block_table[b, j // 256]), g, int(j) % 256] = row
+            dup[(b, g)] = np.sort(np.append(pos, src))
+    L = DeviceLayer(inp)
+    L.out.fill_(float("nan"))
+    L.decode()
+    units = oracle_units(inp)
+    _check_decode(inp, L, units, "duplicate keys")
+    for (b, g), grp in dup.items():
+        got = np.intersect1d(L.selection(b, g), grp)
+        want = np.intersect1d(units[(b, g)][3]["sel"], grp)
+        assert 0 < len(want) < len(grp), (b, g, len(want), len(grp))   # the B-th score is shared
+        np.testing.assert_array_equal(got, want, err_msg=f"b={b} g={g}: tied copies kept")
+
+
+def test_decode_clustered_top_scores():
+    """Every unit's top-B inside one 1024-token chunk (keys there pushed along
+    the folded dominant query): a chunk's candidate list then cannot cover the
+    top-B, and the select must notice and still return the exact set."""
+    cfg = C["c2"].replace(batch=2, n_q_heads=8, n_kv_heads=2, t=None, t_range=(8000, 12000), budget=256)
+    say("[decode clustered]")
+    inp = synth.make_inputs(cfg, seed=43)
+    G = cfg.group
+    for b in range(cfg.batch):
+        for g in range(cfg.n_kv_heads):
+            qf = inp.q[b, g * G:(g + 1) * G].float().sum(0)
+            u = torch.zeros(128)
+            for i in inp.fc_idx[g]:
+                u[2 * i:2 * i + 2] = qf[2 * i:2 * i + 2]
+            u = u / u.norm()
+            for j in range(3072 + 64 * g, 4096):
+                p, s_ = int(inp.block_table[b, j // 256]), j % 256
+                k = inp.k_pool[p, g, s_].float() + (40.0 + 0.01 * j) * u
+                inp.k_pool[p, g, s_] = k.to(inp.k_pool.dtype)
+    L = DeviceLayer(inp)
+    L.out.fill_(float("nan"))
+    L.decode()
+    units = oracle_units(inp)
+    _check_decode(inp, L, units, "clustered")
+    for (b, g), (_, _, _, r) in units.items():
+        assert ((r["sel"] >= 3072) & (r["sel"] < 4096)).all(), "the construction failed to cluster the top-B"
+
+
+@pytest.mark.parametrize("budget", [512, 1500])
+def test_decode_ragged_many_chunks(budget):
+    """Nine sequences x 8 kv heads, max_t 65536, lengths at chunk edges, 0 and
+    at most n_sink + n_recent, every unit against the oracle.  B = 512 takes
+    the two-launch step (TIP's candidate lists); B = 1500 the filter launch,
+    whose grid (32 x 8 x 9 workgroups) reads each sequence's length before its
+    scores, then the select launch and the split FAC."""
+    cfg = C["c5"].replace(batch=9, budget=budget)
+    say(f"[decode ragged many chunks] B={budget}")
+    lens = [65536, 100, 2047, 2048, 2049, 30000, 1023, 0, 65000]
+    inp = synth.make_inputs(cfg, seed=47, seq_lens=lens)
+    L = DeviceLayer(inp)
+    L.out.fill_(float("nan"))
+    L.decode()
+    torch.cuda.synchronize()
+    assert (L.out[7] == 0).all() and (L.sel_count[7] == 0).all()
+    _check_decode(inp, L, {k: v for k, v in oracle_units(inp).items() if k[0] != 7}, f"ragged B={budget}")
 
 
 @pytest.mark.parametrize("name", ["c2-ragged", "fp32-gqa4", "c5-ragged", "c3-shape"])
@@ -708,11 +796,15 @@ def test_full_size_configs(key):
     pick = FULL_SAMPLES.get(key)
     if pick == "extremes":
         order = np.argsort(inp.seq_lens)
-        pick = [(int(order[0]), 0), (int(order[-1]), 7), (int(order[len(order) // 2]), 3)]
+        seqs = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+        pick = [(b, g) for b in seqs for g in range(cfg.n_kv_heads)]
     units = oracle_units(inp, set(pick) if pick else None)
     _check_decode(inp, L, units, key)
     say(f"[full dense] {key}")
     L.dense()
-    _check_dense(inp, L, list(units), key + " dense")
+    dense_units = sorted(units)
+    if len(dense_units) > 24:
+        dense_units = dense_units[::len(dense_units) // 24]
+    _check_dense(inp, L, dense_units, key + " dense")
     del L, inp
     torch.cuda.empty_cache()
