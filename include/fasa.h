@@ -80,7 +80,8 @@ typedef enum fasa_status {
   FASA_ERR_INVALID_ARG = 1,  /* null pointer, size or stride out of range */
   FASA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head_dim != 128, ...) */
   FASA_ERR_WORKSPACE = 3,    /* workspace too small or misaligned */
-  FASA_ERR_HIP = 4           /* a kernel launch failed */
+  FASA_ERR_HIP = 4,          /* a kernel launch failed */
+  FASA_ERR_SCRATCH = 5       /* fasa_decode_scratch: the call needs more than its fixed scratch */
 } fasa_status;
 
 typedef enum fasa_dtype { FASA_F32 = 0, FASA_BF16 = 1 } fasa_dtype;
@@ -293,6 +294,23 @@ fasa_status fasa_dense_decode(const fasa_shape* shape, const void* q, const void
                               const void* v_pool, const int32_t* block_table,
                               const int32_t* seq_lens, int32_t max_t, float* out,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- Allocation-free decode, for callers that cannot allocate memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid it).
+ * fasa_decode_scratch is fasa_decode with the workspace taken from a fixed
+ * device array that the library owns: fasa_scratch_capacity() bytes (64 MiB)
+ * on every device the library runs on, held until the process ends.  The
+ * caller passes inputs and outputs only; nothing is allocated or freed.  A call
+ * whose fasa_workspace_size exceeds the capacity returns FASA_ERR_SCRATCH
+ * before anything is enqueued.  The stream must belong to the current device
+ * (FASA_ERR_INVALID_ARG otherwise).  All calls on one device share its array:
+ * calls that may overlap (unordered streams) race and must not be issued;
+ * calls ordered on one stream are safe.  Results equal fasa_decode's. */
+size_t fasa_scratch_capacity(void);
+fasa_status fasa_decode_scratch(const fasa_shape* shape, const void* q, const void* k_pool,
+                                const void* v_pool, const void* slab, const int32_t* block_table,
+                                const int32_t* seq_lens, int32_t max_t, const int32_t* fc_idx,
+                                float* out, int32_t* sel_idx, int32_t* sel_count, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -216,6 +216,8 @@ const char* fasa_status_str(fasa_status s) {
     case FASA_ERR_UNSUPPORTED: return "FASA_ERR_UNSUPPORTED: shape not implemented (head_dim must be 128, block_size 256, group <= 16)";
     case FASA_ERR_WORKSPACE: return "FASA_ERR_WORKSPACE: workspace missing, too small or not 256-byte aligned";
     case FASA_ERR_HIP: return "FASA_ERR_HIP: a kernel launch failed";
+    case FASA_ERR_SCRATCH:
+      return "FASA_ERR_SCRATCH: the call needs more workspace than fasa_decode_scratch's fixed 64 MiB per device";
   }
   return "FASA: unknown status";
 }

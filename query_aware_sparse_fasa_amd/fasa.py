@@ -18,7 +18,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfasa.so")
 
-FASA_OK, FASA_ERR_INVALID_ARG, FASA_ERR_UNSUPPORTED, FASA_ERR_WORKSPACE, FASA_ERR_HIP = range(5)
+FASA_OK, FASA_ERR_INVALID_ARG, FASA_ERR_UNSUPPORTED, FASA_ERR_WORKSPACE, FASA_ERR_HIP, FASA_ERR_SCRATCH = range(6)
 FASA_F32, FASA_BF16 = 0, 1
 HEAD_DIM = 128
 BLOCK = 256
@@ -27,7 +27,8 @@ EXPORTS = ["fasa_status_str", "fasa_validate_shape", "fasa_selection_capacity",
            "fasa_workspace_size", "fasa_check_fc_idx", "fasa_slab_build", "fasa_slab_append",
            "fasa_tip", "fasa_topk", "fasa_fac", "fasa_decode", "fasa_dense_workspace_size",
            "fasa_dense_decode", "fasa_m_host_sizes", "fasa_m_offload", "fasa_m_workspace_size",
-           "fasa_m_decode", "fasa_ca_workspace_size", "fasa_ca_hits", "fasa_ca_dominant"]
+           "fasa_m_decode", "fasa_ca_workspace_size", "fasa_ca_hits", "fasa_ca_dominant",
+           "fasa_scratch_capacity", "fasa_decode_scratch"]
 
 
 class fasa_shape(ctypes.Structure):
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
         "fasa_ca_workspace_size": (ctypes.c_int, [_S, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
         "fasa_ca_hits": (ctypes.c_int, [_S, _P, _P, _P, _P, _I32, _I32, _P, _P, ctypes.c_size_t, _P]),
         "fasa_ca_dominant": (ctypes.c_int, [_S, _P, _I32, _I32, _P, _P]),
+        "fasa_scratch_capacity": (ctypes.c_size_t, []),
+        "fasa_decode_scratch": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -227,6 +230,21 @@ def fasa_decode(shape, q, k_pool, v_pool, slab, block_table, seq_lens, max_t, fc
                              _ptr(block_table), _ptr(seq_lens), max_t, _ptr(fc_idx), _ptr(out),
                              _ptr(sel_idx), _ptr(sel_count), _ptr(workspace), nbytes, _stream(stream)),
            "fasa_decode")
+
+
+def fasa_scratch_capacity() -> int:
+    return int(lib().fasa_scratch_capacity())
+
+
+def fasa_decode_scratch(shape, q, k_pool, v_pool, slab, block_table, seq_lens, max_t, fc_idx, out, sel_idx,
+                        sel_count, stream=None) -> None:
+    """fasa_decode with the library's own fixed device scratch as workspace."""
+    _need(out, torch.float32, "out")
+    _need(sel_idx, torch.int32, "sel_idx")
+    _need(sel_count, torch.int32, "sel_count")
+    _check(lib().fasa_decode_scratch(ctypes.byref(shape), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(slab),
+                                     _ptr(block_table), _ptr(seq_lens), max_t, _ptr(fc_idx), _ptr(out),
+                                     _ptr(sel_idx), _ptr(sel_count), _stream(stream)), "fasa_decode_scratch")
 
 
 def fasa_dense_workspace_size(shape: fasa_shape, max_t: int) -> int:

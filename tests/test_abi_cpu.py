@@ -17,13 +17,13 @@ FAKE = 0x10000   # never dereferenced: validation fails before any launch
 
 def header_functions():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+char\*|fasa_status)\s+(fasa_\w+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\*|fasa_status|size_t)\s+(fasa_\w+)\s*\(", src, re.M)))
 
 
 def test_exports_every_declared_symbol():
     L = fasa.lib()
     names = header_functions()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(fasa.EXPORTS) == names
@@ -36,7 +36,7 @@ def test_struct_layout_matches_header():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert fasa.status_str(s).startswith("FASA_")
     assert "unknown" in fasa.status_str(99)
 
@@ -229,3 +229,19 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(4)
     with pytest.raises(ValueError):
         fasa.fasa_tip(s, x, x, None, x, x, x, x, 4)
+
+
+def test_scratch_entry_rejects_calls_beyond_its_capacity():
+    """fasa_decode_scratch: a workspace need above the fixed 64 MiB is refused on
+    the host, before the device is touched; so is a bad shape."""
+    assert fasa.fasa_scratch_capacity() == 64 << 20
+    big = good(batch=64, max_blocks_per_seq=256)                 # 64 x 8 units x 65536 tokens
+    assert fasa.fasa_workspace_size(big, 65536) > fasa.fasa_scratch_capacity()
+    with pytest.raises(fasa.FasaError) as e:
+        fasa.fasa_decode_scratch(big, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 65536, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == fasa.FASA_ERR_SCRATCH
+    assert "64 MiB" in fasa.status_str(fasa.FASA_ERR_SCRATCH)
+    with pytest.raises(fasa.FasaError) as e:
+        fasa.fasa_decode_scratch(good(budget=0), FAKE, FAKE, FAKE,
+                                 FAKE, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == fasa.FASA_ERR_INVALID_ARG
