@@ -256,16 +256,19 @@ fasa_status fasa_ca_workspace_size(const fasa_shape* shape, int32_t max_t, int32
 /* hits[b][g][i] (int32, [batch][n_kv_heads][64]) = the size of the
  * intersection of TopK-I(alpha, K) and TopK-I(alpha^(i), K), where alpha_j is
  * the full q.k_j score and alpha^(i)_j the score of FC i alone, over tokens
- * j < t_b; CA of FC i is hits / k_top.  TopK-I takes the largest values, the
- * lower index on ties, and every token when t_b < k_top.  The scores are
- * float32 in one fixed order without fused multiply-adds (the group's heads
- * summed in head order; each FC as fl(fl(q x k) + fl(q x k)); alpha as the 64
- * FC terms added in FC order), so the sets are reproducible bit for bit.
- * fc_idx, budget, n_sink and n_recent are not used. */
+ * j < t_b; CA of FC i is hits / k_top (section 3.4, the CA metric, Eq. 4).
+ * TopK-I takes the largest values, the lower index on ties, and every token
+ * when t_b < k_top.  The scores are float32 in one fixed order without fused
+ * multiply-adds (the group's heads summed in head order; each FC as
+ * fl(fl(q x k) + fl(q x k)); alpha as the 64 FC terms added in FC order), so
+ * the sets are reproducible bit for bit.  topk (nullable, int32,
+ * [batch][n_kv_heads][65][min(k_top, max_t)]) receives the lists behind the
+ * counts: row 0 is TopK-I(alpha), row 1 + i TopK-I(alpha^(i)), each ascending
+ * and padded with -1.  fc_idx, budget, n_sink and n_recent are not used. */
 fasa_status fasa_ca_hits(const fasa_shape* shape, const void* q, const void* k_pool,
                          const int32_t* block_table, const int32_t* seq_lens, int32_t max_t,
-                         int32_t k_top, int32_t* hits, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream);
+                         int32_t k_top, int32_t* hits, int32_t* topk, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /* The dominant FCs from n_rows calibration rows of hits ([n_rows][n_kv_heads][64]):
  * per kv head, the n_tip FCs with the largest total hits (the largest mean

@@ -30,7 +30,8 @@ notation, in plain NumPy float64, one (sequence b, kv head g) unit at a time:
 
 Pinned against: closed forms of RoPE scores, the exact FC decomposition of the
 full dot product, full sorts on small inputs, a library scaled-dot-product
-attention, and special cases (see tests/test_oracle_pins.py).
+attention (per unit, and for a whole paged multi-head step), exact integer
+arithmetic on small inputs, and special cases (see tests/oracle_pins.py).
 """
 from __future__ import annotations
 
@@ -196,31 +197,22 @@ def decode(q, k_pool, v_pool, block_table, seq_lens, fc_idx, budget,
 # ---------------------------------------------------------------------------
 def ca_score_vectors(q_group: np.ndarray, K: np.ndarray) -> np.ndarray:
     """The full-head score vector alpha and the 64 single-FC vectors alpha^(i)
-    of one unit, [1 + d/2][t] float32 (review section 3.4, the CA metric: raw
-    pre-softmax dot products of the query with every past key, over all of
-    q.k and over FC i's pair of columns).
+    of one unit, [1 + d/2][t] in float64 (review section 3.4, the CA metric:
+    raw pre-softmax dot products of the query with every past key, over all of
+    q.k for alpha and over FC i's pair of columns for alpha^(i)).
 
     Grouped-query attention: one vector per kv head, from the group's queries
-    summed per column (as TIP scores them).  Because the top-K of these
-    vectors decides integer results, the arithmetic is fixed in float32 and in
-    this order, exactly as the kernel does it: q~ = sum of the group's heads in
-    head order; alpha^(i)_j = fl(fl(q~_2i k_2i) + fl(q~_2i+1 k_2i+1));
-    alpha_j = alpha^(0)_j + alpha^(1)_j + ... added in FC order.
+    summed per column -- by linearity, the sum of the heads' own scores, which
+    is the score TIP ranks by.
     """
-    qf = np.zeros(np.asarray(q_group).shape[1], dtype=np.float32)
-    for h in range(np.asarray(q_group).shape[0]):
-        qf = (qf + np.asarray(q_group[h], dtype=np.float32)).astype(np.float32)
-    K32 = np.asarray(K, dtype=np.float32)
-    d = K32.shape[1]
-    t = K32.shape[0]
-    out = np.empty((1 + d // 2, t), dtype=np.float32)
-    full = np.zeros(t, dtype=np.float32)
+    q_group = np.asarray(q_group, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    qs = q_group.sum(axis=0)
+    d = K.shape[1]
+    out = np.empty((1 + d // 2, K.shape[0]), dtype=np.float64)
+    out[0] = K @ qs
     for i in range(d // 2):
-        a = (qf[2 * i] * K32[:, 2 * i]).astype(np.float32)
-        b = (qf[2 * i + 1] * K32[:, 2 * i + 1]).astype(np.float32)
-        out[1 + i] = (a + b).astype(np.float32)
-        full = (full + out[1 + i]).astype(np.float32)
-    out[0] = full
+        out[1 + i] = qs[2 * i] * K[:, 2 * i] + qs[2 * i + 1] * K[:, 2 * i + 1]
     return out
 
 
@@ -229,11 +221,11 @@ def contextual_agreement(q_group: np.ndarray, K: np.ndarray, k_top: int) -> np.n
     (review section 3.4, the CA equation).  TopK-I is top_b (largest first,
     lower index on ties); with fewer than K tokens it keeps them all."""
     vec = ca_score_vectors(q_group, K)
-    full, _ = top_b(vec[0].astype(np.float64), k_top)
+    full, _ = top_b(vec[0], k_top)
     full = set(full.tolist())
     ca = np.empty(vec.shape[0] - 1)
     for i in range(vec.shape[0] - 1):
-        fc_set, _ = top_b(vec[1 + i].astype(np.float64), k_top)
+        fc_set, _ = top_b(vec[1 + i], k_top)
         ca[i] = len(full & set(fc_set.tolist())) / float(k_top)
     return ca
 

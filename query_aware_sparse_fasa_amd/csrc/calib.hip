@@ -39,6 +39,7 @@ struct CaArgs {
   const int32_t* sel_idx;  // [b][H_kv * 65][cap]
   const int32_t* sel_count;
   int32_t* hits;           // [b][H_kv][64]
+  int32_t* topk;           // nullable: [b][H_kv][65][cap] copies of the lists, -1 padded
 };
 
 // Grid (ceil(max_t / 256), H_kv, batch), one thread per token.
@@ -107,6 +108,14 @@ __global__ __launch_bounds__(256) void ca_hits_kernel(CaArgs a) {
     h += (lo < nf && full[lo] == x) ? 1u : 0u;
   }
   atomicAdd(&cnt[i], h);
+  if (a.topk != nullptr) {
+    // The 65 lists behind the counts, each padded with -1 to cap entries.
+    for (int r = 0; r < kCaRows; ++r) {
+      const int64_t ur = u0 + r;
+      const int n = min(max(a.sel_count[ur], 0), c.cap);
+      for (int e = threadIdx.x; e < c.cap; e += 256) a.topk[ur * c.cap + e] = e < n ? a.sel_idx[ur * c.cap + e] : -1;
+    }
+  }
   __syncthreads();
   if (threadIdx.x < kFcAll) a.hits[(int64_t(b) * c.n_kv_heads + g) * kFcAll + threadIdx.x] = int32_t(cnt[threadIdx.x]);
 }
@@ -134,7 +143,7 @@ __global__ __launch_bounds__(64) void ca_dominant_kernel(const int32_t* hits, in
 
 hipError_t launch_ca_scores(const Common& c, const void* q, const void* k_pool, const int32_t* block_table,
                             const int32_t* seq_lens, float* scores, hipStream_t s) {
-  CaArgs a{c, q, k_pool, block_table, seq_lens, scores, nullptr, nullptr, nullptr};
+  CaArgs a{c, q, k_pool, block_table, seq_lens, scores, nullptr, nullptr, nullptr, nullptr};
   const dim3 grid((c.max_t + kBlock - 1) / kBlock, c.n_kv_heads, c.batch);
   if (c.bf16) hipLaunchKernelGGL(ca_scores_kernel<uint16_t>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(ca_scores_kernel<float>, grid, dim3(256), 0, s, a);
@@ -142,8 +151,8 @@ hipError_t launch_ca_scores(const Common& c, const void* q, const void* k_pool, 
 }
 
 hipError_t launch_ca_hits(const Common& c, const int32_t* sel_idx, const int32_t* sel_count, int32_t* hits,
-                          hipStream_t s) {
-  CaArgs a{c, nullptr, nullptr, nullptr, nullptr, nullptr, sel_idx, sel_count, hits};
+                          int32_t* topk, hipStream_t s) {
+  CaArgs a{c, nullptr, nullptr, nullptr, nullptr, nullptr, sel_idx, sel_count, hits, topk};
   hipLaunchKernelGGL(ca_hits_kernel, dim3(c.n_kv_heads, c.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }

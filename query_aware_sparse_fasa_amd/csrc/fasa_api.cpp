@@ -488,8 +488,8 @@ fasa_status fasa_ca_workspace_size(const fasa_shape* shape, int32_t max_t, int32
 }
 
 fasa_status fasa_ca_hits(const fasa_shape* shape, const void* q, const void* k_pool, const int32_t* block_table,
-                         const int32_t* seq_lens, int32_t max_t, int32_t k_top, int32_t* hits, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
+                         const int32_t* seq_lens, int32_t max_t, int32_t k_top, int32_t* hits, int32_t* topk,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
   fasa_status st = check_shape(shape);
   if (st != FASA_OK) return st;
   if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
@@ -518,7 +518,7 @@ fasa_status fasa_ca_hits(const fasa_shape* shape, const void* q, const void* k_p
     return st;
   Common ch = cs;
   ch.n_kv_heads = shape->n_kv_heads;
-  return hip_status(fasa::launch_ca_hits(ch, sel_idx, sel_count, hits, stream));
+  return hip_status(fasa::launch_ca_hits(ch, sel_idx, sel_count, hits, topk, stream));
 }
 
 fasa_status fasa_ca_dominant(const fasa_shape* shape, const int32_t* hits, int32_t n_rows, int32_t n_tip,

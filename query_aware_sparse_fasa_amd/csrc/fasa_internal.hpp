@@ -172,7 +172,7 @@ hipError_t launch_ca_scores(const Common& c, const void* q, const void* k_pool, 
 // hits[b][g][i] from the top-K lists of the 65 rows of each unit; c is the
 // selection's Common (cap = the lists' row length; c.n_kv_heads = H_kv).
 hipError_t launch_ca_hits(const Common& c, const int32_t* sel_idx, const int32_t* sel_count, int32_t* hits,
-                          hipStream_t s);
+                          int32_t* topk, hipStream_t s);
 hipError_t launch_ca_dominant(const int32_t* hits, int n_rows, int n_kv, int n_tip, int32_t* fc_idx, hipStream_t s);
 
 // Whether a decode step may use launch_fac_select (small budget, block-table

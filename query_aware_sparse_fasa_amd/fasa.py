@@ -89,7 +89,7 @@ def lib() -> ctypes.CDLL:
         "fasa_m_decode": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                                          ctypes.c_size_t, _P]),
         "fasa_ca_workspace_size": (ctypes.c_int, [_S, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
-        "fasa_ca_hits": (ctypes.c_int, [_S, _P, _P, _P, _P, _I32, _I32, _P, _P, ctypes.c_size_t, _P]),
+        "fasa_ca_hits": (ctypes.c_int, [_S, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P]),
         "fasa_ca_dominant": (ctypes.c_int, [_S, _P, _I32, _I32, _P, _P]),
         "fasa_scratch_capacity": (ctypes.c_size_t, []),
         "fasa_decode_scratch": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P]),
@@ -319,13 +319,17 @@ def fasa_ca_workspace_size(shape: fasa_shape, max_t: int, k_top: int) -> int:
     return n.value
 
 
-def fasa_ca_hits(shape, q, k_pool, block_table, seq_lens, max_t, k_top, hits, workspace, stream=None) -> None:
+def fasa_ca_hits(shape, q, k_pool, block_table, seq_lens, max_t, k_top, hits, workspace, stream=None,
+                 topk=None) -> None:
+    """topk (optional, int32 [batch][H_kv][65][min(k_top, max_t)]): the top-K lists behind the counts."""
     _need(hits, torch.int32, "hits")
     _need(block_table, torch.int32, "block_table")
     _need(seq_lens, torch.int32, "seq_lens")
+    _need(topk, torch.int32, "topk")
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().fasa_ca_hits(ctypes.byref(shape), _ptr(q), _ptr(k_pool), _ptr(block_table), _ptr(seq_lens), max_t,
-                              k_top, _ptr(hits), _ptr(workspace), nbytes, _stream(stream)), "fasa_ca_hits")
+                              k_top, _ptr(hits), _ptr(topk), _ptr(workspace), nbytes, _stream(stream)),
+           "fasa_ca_hits")
 
 
 def fasa_ca_dominant(shape, hits, n_rows, n_tip, fc_idx, stream=None) -> None:

@@ -293,6 +293,75 @@ def pin_dense_is_library_attention(O):
         np.testing.assert_allclose(res[(b, g)], ref, rtol=1e-12, atol=1e-12)
 
 
+def pin_decode_is_library_attention(O):
+    """The whole step over a paged, multi-head cache (permuted block table,
+    ragged lengths, three kv heads of two query heads each): with every FC
+    dominant and B >= t it is torch's scaled_dot_product_attention in fp64 on
+    the logical rows, for each group's own query heads."""
+    rng = np.random.default_rng(22)
+    lens = [5, 300, 260]
+    H, G = 3, 2
+    nblk = [(t + 255) // 256 for t in lens]
+    perm = rng.permutation(sum(nblk))
+    kp = np.full((sum(nblk) + 1, H, 256, D), np.nan)
+    vp = np.full_like(kp, np.nan)
+    table = np.full((len(lens), max(nblk)), sum(nblk), dtype=np.int32)
+    q = rng.standard_normal((len(lens), H * G, D))
+    rows = {}
+    o = 0
+    for b, t in enumerate(lens):
+        table[b, :nblk[b]] = perm[o:o + nblk[b]]
+        o += nblk[b]
+        for g in range(H):
+            K = rng.standard_normal((t, D))
+            V = rng.standard_normal((t, D))
+            rows[(b, g)] = (K, V)
+            for j in range(t):
+                kp[table[b, j // 256], g, j % 256] = K[j]
+                vp[table[b, j // 256], g, j % 256] = V[j]
+    fc = np.tile(np.arange(D // 2), (H, 1))
+    res = O.decode(q, kp, vp, table, np.array(lens), fc, budget=1000)
+    for (b, g), (K, V) in rows.items():
+        t = lens[b]
+        r = res[(b, g)]
+        assert list(r["sel"]) == list(range(t))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[b, g * G:(g + 1) * G])[None, :, None, :],
+            torch.from_numpy(K)[None, None].expand(1, G, t, D),
+            torch.from_numpy(V)[None, None].expand(1, G, t, D))[0, :, 0, :].numpy()
+        np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_decode_per_head_fc_rows(O):
+    """Each kv head ranks by its own row of dominant FCs: head g keeps only FC
+    a_g, every head's keys carry a planted set of large values in the columns
+    of every a_h, a different set per (g, h), and the query weights only the
+    first column of each FC -- so head g must select exactly its set (g, g)."""
+    rng = np.random.default_rng(23)
+    H, G, t, B = 3, 2, 300, 12
+    a = [5, 17, 40]
+    kp = np.zeros((2, H, 256, D))
+    vp = rng.standard_normal((2, H, 256, D))
+    table = np.array([[1, 0]], dtype=np.int32)
+    q = np.zeros((1, H * G, D))
+    for h in range(H):
+        q[0, :, 2 * a[h]] = 1.0
+    planted = {}
+    perm = rng.permutation(t)
+    for g in range(H):
+        K = rng.uniform(-0.5, 0.5, (t, D))
+        for h in range(H):
+            P = perm[(g * H + h) * B:(g * H + h + 1) * B]
+            planted[(g, h)] = np.sort(P)
+            K[P, 2 * a[h]] = 10.0 + rng.uniform(0, 1, B)
+        for j in range(t):
+            kp[table[0, j // 256], g, j % 256] = K[j]
+    fc = np.array([[a[g], -1] for g in range(H)], dtype=np.int32)
+    res = O.decode(q, kp, vp, table, np.array([t]), fc, budget=B)
+    for g in range(H):
+        assert list(res[(0, g)]["sel"]) == list(planted[(g, g)]), g
+
+
 def pin_fasa_m_split(O):
     """FASA-M's split of the keys: every column appears exactly once, either in
     the dominant-key cache (slab) or among the non-dominant columns, which keep
@@ -338,6 +407,19 @@ def pin_ca_exact_small(O):
             fc = [qs[2 * i] * int(K[j, 2 * i]) + qs[2 * i + 1] * int(K[j, 2 * i + 1]) for j in range(t)]
             assert vec[1 + i].tolist() == fc
             assert ca[i] == len(top_full & _exact_topk(fc, k)) / k
+
+
+def pin_ca_fc_sum_is_full(O):
+    """The 64 single-FC vectors add up to the full-head vector (the FC
+    decomposition of the dot product is exact, section 3.4), on random
+    inputs with several query heads."""
+    rng = np.random.default_rng(24)
+    q = rng.standard_normal((3, D)) * 2
+    K = rng.standard_normal((40, D)) * 2
+    vec = O.ca_score_vectors(q, K)
+    assert vec.shape == (1 + D // 2, 40)
+    np.testing.assert_allclose(vec[1:].sum(axis=0), vec[0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(vec[0], K @ q.sum(axis=0), rtol=1e-12, atol=1e-12)
 
 
 def pin_ca_single_fc_query(O):
@@ -401,8 +483,9 @@ ALL_PINS = [pin_tip_closed_form, pin_tip_relative_form, pin_tip_all_fc_is_full_d
             pin_tip_reads_only_dominant, pin_topb_full_sort, pin_topb_exhaustive,
             pin_topb_signed_and_zero, pin_forced_union, pin_fac_is_library_attention,
             pin_fac_special_cases, pin_fac_duplicate_keys_tie, pin_paged_rows, pin_slab,
-            pin_dense_is_library_attention, pin_fasa_m_split, pin_ca_exact_small, pin_ca_single_fc_query,
-            pin_dominant_fcs, pin_per_head_fc_padding]
+            pin_dense_is_library_attention, pin_decode_is_library_attention, pin_decode_per_head_fc_rows, pin_fasa_m_split,
+            pin_ca_exact_small, pin_ca_fc_sum_is_full, pin_ca_single_fc_query, pin_dominant_fcs,
+            pin_per_head_fc_padding]
 
 
 def golden():

@@ -9,7 +9,13 @@ Tolerances (stated once, used by every GPU test):
 * TIP scores: |S_gpu - S| <= (2F + G + 2) * 2^-24 * sum_c (sum_h |q_h,c|) |k_c|,
   the forward error bound of the fp32 evaluation order (the group's query
   heads summed per column, then 2F fused multiply-adds);
-* slab, top-B on given scores: bit-exact.
+* slab, top-B on given scores: bit-exact;
+* CA top-K lists: each of the 65 lists of a unit equals the oracle's fp64
+  TopK-I except in tokens whose fp64 score lies within 1e-5 relative of the
+  K-th score plus the fp32 forward error bound of both scores (the group's
+  heads summed per column, then per FC two products and one add, then the 64
+  FC terms added for alpha); the hit counts then equal, bit for bit, the
+  intersections of the validated lists.
 """
 from __future__ import annotations
 
@@ -63,3 +69,45 @@ def check_output(gpu_out: np.ndarray, q_group, K, V, gpu_sel, ref: dict, same_se
     err = np.abs(gpu_out - expect).max(initial=0.0)
     assert err <= OUT_ATOL[dtype], f"{where}: max |out - oracle| = {err:.3e} > {OUT_ATOL[dtype]}"
     return err
+
+
+def _ca_bounds(q_group: np.ndarray, K: np.ndarray) -> np.ndarray:
+    """Forward error bounds of the fp32 CA scores, [1 + d/2][t]."""
+    G, d = q_group.shape
+    prod = np.abs(K) * np.abs(q_group).sum(axis=0)[None, :]
+    out = np.empty((1 + d // 2, K.shape[0]))
+    out[0] = (G + 66) * U32 * prod.sum(axis=1)
+    out[1:] = (G + 2) * U32 * (prod[:, 0::2] + prod[:, 1::2]).T
+    return out + 1e-30
+
+
+def check_ca_lists(gpu_lists: np.ndarray, q_group: np.ndarray, K: np.ndarray, k_top: int,
+                   where: str = "") -> tuple[np.ndarray, int]:
+    """Validate one unit's 65 GPU top-K lists ([65][cap], -1 padded) against
+    the fp64 CA vectors.  Returns the hit counts those lists give and the number
+    of lists that differ from the oracle's inside the band."""
+    vec = O.ca_score_vectors(q_group, K)
+    bnd = _ca_bounds(q_group, K)
+    t = K.shape[0]
+    n = min(k_top, t)
+    sets = []
+    differ = 0
+    for r in range(vec.shape[0]):
+        row = gpu_lists[r]
+        got = row[:n]
+        assert (row[n:] == -1).all(), f"{where} row {r}: padding"
+        assert np.all(np.diff(got) > 0), f"{where} row {r}: list not strictly ascending"
+        assert n == 0 or (got[0] >= 0 and got[-1] < t), f"{where} row {r}: index out of range"
+        want, s_k = O.top_b(vec[r], k_top)
+        if not np.array_equal(got, want):
+            differ += 1
+            v = vec[r]
+            order = np.lexsort((np.arange(t), -v))
+            jk = order[n - 1]
+            diff = np.setxor1d(got, want)
+            band = np.abs(v[diff] - s_k) <= TIE_RTOL * abs(s_k) + bnd[r, diff] + bnd[r, jk]
+            assert band.all(), (f"{where} row {r}: lists differ outside the band: {diff[~band][:10]} "
+                                f"scores {v[diff[~band]][:10]} vs s_K {s_k}")
+        sets.append(set(got.tolist()))
+    hits = np.array([len(sets[0] & sets[1 + i]) for i in range(vec.shape[0] - 1)], dtype=np.int32)
+    return hits, differ

@@ -213,10 +213,10 @@ def test_ca_sizes_and_rejections():
     n = ctypes.c_size_t()
     for k in (0, 4097):
         assert raw("fasa_ca_workspace_size", sp, 4096, k, ctypes.byref(n)) == E
-        assert raw("fasa_ca_hits", sp, FAKE, FAKE, FAKE, FAKE, 4096, k, FAKE, FAKE, a, None) == E
-    assert raw("fasa_ca_hits", sp, None, FAKE, FAKE, FAKE, 4096, 256, FAKE, FAKE, a, None) == E
-    assert raw("fasa_ca_hits", sp, FAKE, FAKE, FAKE, FAKE, 4096, 256, None, FAKE, a, None) == E
-    assert raw("fasa_ca_hits", sp, FAKE, FAKE, FAKE, FAKE, 4096, 256, FAKE, FAKE, a - 1, None) == \
+        assert raw("fasa_ca_hits", sp, FAKE, FAKE, FAKE, FAKE, 4096, k, FAKE, None, FAKE, a, None) == E
+    assert raw("fasa_ca_hits", sp, None, FAKE, FAKE, FAKE, 4096, 256, FAKE, None, FAKE, a, None) == E
+    assert raw("fasa_ca_hits", sp, FAKE, FAKE, FAKE, FAKE, 4096, 256, None, None, FAKE, a, None) == E
+    assert raw("fasa_ca_hits", sp, FAKE, FAKE, FAKE, FAKE, 4096, 256, FAKE, None, FAKE, a - 1, None) == \
         fasa.FASA_ERR_WORKSPACE
     for n_tip in (0, 65):
         assert raw("fasa_ca_dominant", sp, FAKE, 4, n_tip, FAKE, None) == E

@@ -213,11 +213,16 @@ def test_topk_exact_on_given_scores(case):
     sc = torch.from_numpy(scores).to(dev)
     lens_t = torch.tensor(lens, dtype=torch.int32, device=dev)
     ws = fasa.alloc_workspace(shape, max_t)
-    # First call on a workspace full of garbage (the select must fall back to its
-    # full-row path and still be exact), then two calls on the workspace the
-    # select left behind (the fast path).
+    # First call on a workspace full of one garbage byte (the select must fall back
+    # to its full-row path and still be exact), then a call on the workspace the
+    # select left behind (the fast path), then one on seeded random bytes (counts
+    # and thresholds that look plausible but are wrong), then the fast path again.
     ws.fill_(0xA5)
-    for attempt in range(3):
+    noise = torch.randint(0, 256, ws.shape, dtype=torch.uint8,
+                          generator=torch.Generator().manual_seed(max_t + budget)).to(dev)
+    for attempt in range(4):
+        if attempt == 2:
+            ws.copy_(noise)
         sel = torch.full((batch, H, max(cap, 1)), -7, dtype=torch.int32, device=dev)
         cnt = torch.full((batch, H), -7, dtype=torch.int32, device=dev)
         fasa.fasa_topk(shape, sc, lens_t, max_t, sel, cnt, ws)
@@ -344,22 +349,29 @@ def test_decode_end_to_end(name):
     _check_decode(inp, L, oracle_units(inp), name)
 
 
-def test_decode_with_garbage_workspace_is_identical():
+@pytest.mark.parametrize("name", ["c4-ragged", "c3-shape", "wide-g4"])
+def test_decode_with_garbage_workspace_is_identical(name):
     """The workspace carries a histogram between calls; garbage there may only
-    cost speed, never change a result."""
-    name = "c4-ragged"
+    cost speed, never change a result (the two-launch path with per-chunk
+    candidates, the split path of large budgets, and the three-launch path)."""
     say(f"[decode garbage ws] {name}")
     inp, L = layer_for(name)
     L.decode()
     a = (L.out.clone(), L.sel_idx.clone(), L.sel_count.clone())
-    L.workspace.fill_(0x5A)
-    L.decode()
-    b = (L.out.clone(), L.sel_idx.clone(), L.sel_count.clone())
-    L.decode()
-    torch.cuda.synchronize()
-    for x, y in zip(a, b):
-        assert torch.equal(x, y)
-    assert torch.equal(a[0], L.out) and torch.equal(a[1], L.sel_idx)
+    noise = torch.randint(0, 256, L.workspace.shape, dtype=torch.uint8,
+                          generator=torch.Generator().manual_seed(17)).to(L.workspace.device)
+    for fill in ("byte", "random"):
+        if fill == "byte":
+            L.workspace.fill_(0x5A)
+        else:
+            L.workspace.copy_(noise)
+        L.decode()
+        b = (L.out.clone(), L.sel_idx.clone(), L.sel_count.clone())
+        L.decode()
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x, y), fill
+        assert torch.equal(a[0], L.out) and torch.equal(a[1], L.sel_idx), fill
 
 
 def test_decode_without_slab_is_identical():
@@ -525,40 +537,53 @@ CA_CASES = ["c1", "c2-ragged", "c5-ragged", "fp32-gqa4", "g16-f5"]
 
 
 def _ca_hits(L, k_top):
+    """The kernel's hit counts and the 65 top-K lists of every unit behind them."""
     cfg = L.cfg
     ws = torch.zeros(fasa.fasa_ca_workspace_size(L.shape, L.max_t, k_top), dtype=torch.uint8, device="cuda")
     hits = torch.full((cfg.batch, cfg.n_kv_heads, 64), -1, dtype=torch.int32, device="cuda")
-    fasa.fasa_ca_hits(L.shape, L.q, L.k_pool, L.block_table, L.seq_lens, L.max_t, k_top, hits, ws)
+    cap = min(k_top, L.max_t)
+    lists = torch.full((cfg.batch, cfg.n_kv_heads, 65, cap), -7, dtype=torch.int32, device="cuda")
+    fasa.fasa_ca_hits(L.shape, L.q, L.k_pool, L.block_table, L.seq_lens, L.max_t, k_top, hits, ws, topk=lists)
     torch.cuda.synchronize()
-    return hits
+    return hits, lists.cpu().numpy()
 
 
-def _ca_expect(inp, b, g, k_top):
+def _ca_check_unit(inp, lists, hits, b, g, k_top, where):
+    """The unit's lists validated against the fp64 oracle, then its hits against
+    the intersections of those lists.  Returns the number of lists in the band."""
     G = inp.cfg.group
-    q = inp.q[b, g * G:(g + 1) * G].float().cpu().numpy()
-    K = unit_rows(inp, b, g, inp.k_pool).float().cpu().numpy()
-    return np.rint(O.contextual_agreement(q, K, k_top) * k_top).astype(np.int32)
+    q = inp.q[b, g * G:(g + 1) * G].double().cpu().numpy()
+    K = unit_rows(inp, b, g, inp.k_pool).double().cpu().numpy()
+    expect, differ = PR.check_ca_lists(lists[b, g], q, K, k_top, where)
+    np.testing.assert_array_equal(hits[b, g], expect, err_msg=where)
+    if differ == 0:
+        np.testing.assert_array_equal(hits[b, g], np.rint(O.contextual_agreement(q, K, k_top) * k_top),
+                                      err_msg=where)
+    return differ
 
 
 @pytest.mark.parametrize("k_top", [64, 256])
 @pytest.mark.parametrize("name", CA_CASES)
 def test_ca_hits_exact(name, k_top):
-    """The top-K overlaps of every FC with its head, bit-exact against the oracle."""
+    """The 65 top-K lists of every sampled unit against the fp64 oracle (tie
+    band), and the hit counts bit-exact against those lists."""
     say(f"[ca hits] {name} K={k_top}")
     inp, L = layer_for(name)
-    h = _ca_hits(L, k_top).cpu().numpy()
+    h, lists = _ca_hits(L, k_top)
+    h = h.cpu().numpy()
     cfg = inp.cfg
     units = [(b, g) for b in range(cfg.batch) for g in range(cfg.n_kv_heads)]
     if len(units) > 12:
         units = units[::len(units) // 12]
-    for b, g in units:
-        np.testing.assert_array_equal(h[b, g], _ca_expect(inp, b, g, k_top), err_msg=f"{name} b={b} g={g}")
+    differ = sum(_ca_check_unit(inp, lists, h, b, g, k_top, f"{name} b={b} g={g}") for b, g in units)
+    say(f"  {len(units)} units, {differ} of {65 * len(units)} lists differ inside the band")
 
 
 def test_ca_calibration_sample_steps():
     """Eight steps of one calibration sample (block tables sharing one
-    sequence's blocks, lengths 1990..1997), K = 256, then the dominant FCs of
-    the summed hits against the oracle's choice from its own CA."""
+    sequence's blocks, lengths 1990..1997), K = 256: every unit's lists and hits
+    validated, then the dominant FCs of the summed hits against the oracle's
+    ranking of the mean CA."""
     cfg = C["c2"].replace(batch=8, t=2000)
     say("[ca sample steps]")
     inp = synth.make_inputs(cfg, seed=13)
@@ -566,17 +591,17 @@ def test_ca_calibration_sample_steps():
     inp.seq_lens[:] = 1990 + np.arange(8, dtype=np.int32)
     L = DeviceLayer(inp, with_slab=False)
     k_top = 256
-    hits = _ca_hits(L, k_top)
+    hits, lists = _ca_hits(L, k_top)
     h = hits.cpu().numpy()
-    expect = np.stack([np.stack([_ca_expect(inp, b, g, k_top) for g in range(cfg.n_kv_heads)])
-                       for b in range(cfg.batch)])
-    np.testing.assert_array_equal(h, expect)
+    for b in range(cfg.batch):
+        for g in range(cfg.n_kv_heads):
+            _ca_check_unit(inp, lists, h, b, g, k_top, f"sample b={b} g={g}")
     fc = torch.full((cfg.n_kv_heads, 16), -1, dtype=torch.int32, device="cuda")
     fasa.fasa_ca_dominant(L.shape, hits, cfg.batch, 16, fc)
     torch.cuda.synchronize()
     got = fc.cpu().numpy()
     for g in range(cfg.n_kv_heads):
-        mean = expect[:, g, :].sum(axis=0) / float(cfg.batch * k_top)
+        mean = h[:, g, :].sum(axis=0) / float(cfg.batch * k_top)
         assert list(got[g]) == list(O.dominant_fcs(mean, 16)), g
     fasa.fasa_check_fc_idx(L.shape, got)     # a valid fc_idx for the decode path
 

@@ -74,11 +74,20 @@ MUTANTS = [
      "        dominant.add(2 * int(i))\n",
      "        dominant.add(int(i))\n"),
     ("ca_pair_wrong_column",
-     "b = (qf[2 * i + 1] * K32[:, 2 * i + 1]).astype(np.float32)",
-     "b = (qf[2 * i + 1] * K32[:, 2 * i]).astype(np.float32)"),
+     "out[1 + i] = qs[2 * i] * K[:, 2 * i] + qs[2 * i + 1] * K[:, 2 * i + 1]",
+     "out[1 + i] = qs[2 * i] * K[:, 2 * i] + qs[2 * i + 1] * K[:, 2 * i]"),
     ("ca_first_head_only",
-     "    for h in range(np.asarray(q_group).shape[0]):\n        qf = (qf +",
-     "    for h in range(1):\n        qf = (qf +"),
+     "qs = q_group.sum(axis=0)",
+     "qs = q_group[0]"),
+    ("ca_full_drops_first_fc",
+     "out[0] = K @ qs",
+     "out[0] = K[:, 2:] @ qs[2:]"),
+    ("decode_wrong_group_slice",
+     "res[(b, g)] = decode_unit(q[b, g * G:(g + 1) * G], K, V, fc_idx[g], budget,",
+     "res[(b, g)] = decode_unit(q[b, g:g + G], K, V, fc_idx[g], budget,"),
+    ("decode_wrong_fc_row",
+     "res[(b, g)] = decode_unit(q[b, g * G:(g + 1) * G], K, V, fc_idx[g], budget,",
+     "res[(b, g)] = decode_unit(q[b, g * G:(g + 1) * G], K, V, fc_idx[0], budget,"),
     ("ca_divides_by_set_size",
      "ca[i] = len(full & set(fc_set.tolist())) / float(k_top)",
      "ca[i] = len(full & set(fc_set.tolist())) / float(max(len(full), 1))"),
