@@ -65,19 +65,23 @@ def time_graph(torch, stream, graphs, reps):
     return start.elapsed_time(end) / 1e3
 
 
-COUNTERS = os.path.join(ROOT, "profiles", "tip_kernel_llama3-8b-t32768_hbm_counters.txt")
 TIP_SOURCES = ("tip.hip", "fasa_device.hpp", "fasa_internal.hpp")
 
 
-def measured_traffic(cfg_key: str, use_slab: bool):
-    """HBM bytes per TIP launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE, each scaled by a 1 GiB reference copy), or None
-    when the summary is for another workload or the TIP sources changed since."""
+def counters_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"tip_kernel_{workload}_hbm_counters.txt")
+
+
+def measured_traffic(workload: str, use_slab: bool):
+    """HBM bytes per launch of the step's TIP from the committed rocprofv3 counter
+    summary of this workload (FETCH_SIZE + WRITE_SIZE, each scaled by a 1 GiB
+    reference copy), or None when there is none or the TIP sources changed since."""
     import hashlib
-    if cfg_key != "c2" or not use_slab or not os.path.exists(COUNTERS):
+    path = counters_file(workload)
+    if not use_slab or not os.path.exists(path):
         return None
     kv = {}
-    for line in open(COUNTERS):
+    for line in open(path):
         if line.startswith("#") or ":" not in line:
             continue
         k, v = line.split(":", 1)
@@ -91,32 +95,72 @@ def measured_traffic(cfg_key: str, use_slab: bool):
     return int(kv["traffic_bytes_per_launch"])
 
 
-def cpu_oracle_baseline(layer, cfg, seconds: float):
-    """The fp64 oracle (as it stands) on the host: one step = every unit of the layer.
-    Runs single-threaded (BLAS limited to 1 thread); returns steps/s and what was sampled."""
+# The sampled units of the CPU baseline, shared with the worker processes
+# (forked before this process touches the GPU).
+_CPU = {}
+
+
+def _oracle_loop(offset: int, seconds: float):
+    """Decode the sampled units round-robin from `offset` for `seconds` on one
+    thread; returns (units decoded, elapsed seconds)."""
     from threadpoolctl import threadpool_limits
 
     from oracle import fasa_oracle as O
-    units = [(b, g) for b in range(cfg.batch) for g in range(cfg.n_kv_heads)]
-    # Bound the host copy: at most 32 units (the step rate is scaled by units per step).
-    rng = np.random.default_rng(0)
-    sample = units if len(units) <= 32 else [units[i] for i in sorted(rng.choice(len(units), 32, replace=False))]
-    data = [(u, layer.unit_host(*u)) for u in sample]
+    data, fc, budget, ns, nr = _CPU["data"], _CPU["fc"], _CPU["budget"], _CPU["ns"], _CPU["nr"]
     done = 0
     t0 = time.perf_counter()
     with threadpool_limits(1):
         while True:
-            for (b, g), (q, K, V) in data:
-                O.decode_unit(q, K, V, layer.inp.fc_idx[g], cfg.budget, cfg.n_sink, cfg.n_recent)
-                done += 1
+            g, q, K, V = data[(offset + done) % len(data)]
+            O.decode_unit(q, K, V, fc[g], budget, ns, nr)
+            done += 1
             if time.perf_counter() - t0 >= seconds:
                 break
-    el = time.perf_counter() - t0
-    steps_per_s = done / len(units) / el
-    return {"value": steps_per_s, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} (sequence, kv head) unit evaluations of the fp64 NumPy oracle "
-                      f"({len(sample)} distinct units of {len(units)} per step) in {el:.1f} s on the host; "
-                      f"steps/s = units/s / units per step"}
+    return done, time.perf_counter() - t0
+
+
+def cpu_oracle_baseline(cfg, seconds: float):
+    """The fp64 oracle (as it stands) on the host cores, before the GPU is used:
+    one step = every unit of the layer.  Inputs are the workload's, drawn on the
+    host with the same seeds (the generator streams differ from the GPU's, the
+    shapes and distributions do not).  Two legs over a sample of at most 16
+    units: one process with BLAS held to one thread, then one such process per
+    core of the host's CPU share (at most 16), all running at once."""
+    import multiprocessing as mp
+
+    from query_aware_sparse_fasa_amd import synth
+    from query_aware_sparse_fasa_amd.synth import unit_rows
+    inp = synth.make_inputs(cfg, seed=0, device="cpu")
+    units = [(b, g) for b in range(cfg.batch) for g in range(cfg.n_kv_heads)]
+    rng = np.random.default_rng(0)
+    sample = units if len(units) <= 16 else [units[i] for i in sorted(rng.choice(len(units), 16, replace=False))]
+    G = cfg.group
+    data = []
+    for b, g in sample:
+        q = inp.q[b, g * G:(g + 1) * G].double().numpy()
+        data.append((g, q, unit_rows(inp, b, g, inp.k_pool).double().numpy(),
+                     unit_rows(inp, b, g, inp.v_pool).double().numpy()))
+    _CPU.update(data=data, fc=np.asarray(inp.fc_idx), budget=cfg.budget, ns=cfg.n_sink, nr=cfg.n_recent)
+    del inp
+    host_cores = len(os.sched_getaffinity(0))
+    procs = max(1, min(16, host_cores))
+    one_done, one_el = _oracle_loop(0, seconds / 2)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(procs) as pool:
+        res = pool.starmap(_oracle_loop, [(k, seconds / 2) for k in range(procs)])
+    _CPU.clear()
+    n_units = len(units)
+    all_rate = sum(d / e for d, e in res) / n_units
+    all_done = sum(d for d, _ in res)
+    one_rate = one_done / one_el / n_units
+    desc = (f"{len(sample)} distinct units of the {n_units} per step (sequence, kv head), decoded round-robin "
+            f"by the fp64 NumPy oracle; steps/s = units/s / units per step")
+    return {"value": all_rate, "unit": "steps/s", "cores": procs, "kind": "oracle",
+            "sample": f"{all_done} unit evaluations in {procs} processes of one thread each, "
+                      f"about {seconds / 2:.0f} s; " + desc,
+            "host_cores": host_cores, "os_cpu_count": os.cpu_count(),
+            "single_core": {"value": one_rate, "unit": "steps/s", "cores": 1,
+                            "sample": f"{one_done} unit evaluations in {one_el:.1f} s on one thread; " + desc}}
 
 
 def main():
@@ -132,9 +176,9 @@ def main():
     ap.add_argument("--no-fasa-m", action="store_true", help="skip the FASA-M (host-offloaded) timing")
     ap.add_argument("--no-calib", action="store_true", help="skip the CA calibration timing")
     ap.add_argument("--mode", choices=["step", "tip", "decode", "dense"], default="step",
-                    help="step: the benchmark; tip / decode / dense: only --steps TIP launches, "
-                         "whole decode steps or dense decodes, then one 1 GiB reference copy "
-                         "(for hardware-counter runs)")
+                    help="step: the benchmark; tip / decode / dense: only --steps launches of the "
+                         "step's TIP (fasa_decode_tip), whole decode steps or dense decodes, then one "
+                         "1 GiB reference copy (for hardware-counter runs)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -143,12 +187,21 @@ def main():
               f"(--gpus {args.gpus}, WORLD_SIZE {world} requested). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    from query_aware_sparse_fasa_amd import synth
+    cfg = synth.CONFIGS[args.config]
+    cpu = None
+    if args.mode == "step" and not args.no_cpu_baseline:
+        # Before anything touches the GPU: the worker processes are forked.
+        log(f"[bench] timing the fp64 oracle on the host for ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_oracle_baseline(cfg, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['value']:.3f} steps/s on {cpu['cores']} cores "
+            f"({cpu['single_core']['value']:.3f} on one)")
+
     import torch
 
-    from query_aware_sparse_fasa_amd import costmodel, fasa, synth
+    from query_aware_sparse_fasa_amd import costmodel, fasa
     from query_aware_sparse_fasa_amd.workload import DeviceLayer
 
-    cfg = synth.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fasa.lib()
@@ -189,7 +242,7 @@ def main():
             for i in range(args.steps):
                 lay = layers[i % L]
                 if args.mode == "tip":
-                    lay.tip(use_slab=use_slab)
+                    lay.decode_tip(use_slab=use_slab)
                 elif args.mode == "decode":
                     lay.decode(use_slab=use_slab)
                 else:
@@ -208,6 +261,8 @@ def main():
     with torch.cuda.stream(stream):
         for lay in layers:          # eager warm-up of every entry point
             lay.decode(use_slab=use_slab)
+            lay.decode_tip(use_slab=use_slab)
+            lay.decode_rest()
             lay.tip(use_slab=use_slab)
             lay.topk()
             lay.fac()
@@ -218,7 +273,7 @@ def main():
     g_full = graph_of(torch, stream, [lambda l=l: l.decode(use_slab=use_slab) for l in layers])
     rem = args.steps % L
     g_rem = graph_of(torch, stream, [lambda l=l: l.decode(use_slab=use_slab) for l in layers[:rem]]) if rem else None
-    g_tip = graph_of(torch, stream, [lambda l=l: l.tip(use_slab=use_slab) for l in layers])
+    g_tip = graph_of(torch, stream, [lambda l=l: l.decode_tip(use_slab=use_slab) for l in layers])
     g_topk = graph_of(torch, stream, [lambda l=l: l.topk() for l in layers])
     g_fac = graph_of(torch, stream, [lambda l=l: l.fac() for l in layers])
     g_dense = graph_of(torch, stream, [lambda l=l: l.dense() for l in layers])
@@ -248,6 +303,8 @@ def main():
         raise RuntimeError(f"event time {el:.4f} s disagrees with the host clock {wall:.4f} s")
 
     # Per-kernel-group times (each group alone, same rotation over the L layers).
+    # TIP alone is the step's own first launch (fasa_decode_tip: the same
+    # kernel variant, grid and outputs as inside fasa_decode).
     reps = max(1, min(50, 2000 // L))
     t_tip = time_graph(torch, stream, [g_tip], reps) / (reps * L)
     t_topk = time_graph(torch, stream, [g_topk], reps) / (reps * L)
@@ -352,11 +409,6 @@ def main():
     tip_gbps = tip_bytes / t_tip / 1e9
     step_gbps = per_layer_touch * steps_per_s / 1e9
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        log(f"[bench] timing the fp64 oracle on the host for ~{args.cpu_seconds:.0f} s")
-        cpu = cpu_oracle_baseline(base, cfg, args.cpu_seconds)
-
     res = {
         "metric": METRIC,
         "value": steps_per_s,
@@ -386,11 +438,14 @@ def main():
                          "decode_step": el / args.steps * 1e6},
         "roofline": {"kernel": "tip_kernel", "bound": "hbm", "achieved": tip_gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": tip_gbps / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(args.config, use_slab),
+                     "traffic": measured_traffic(cfg.name, use_slab),
                      "algorithmic_bytes_per_launch": int(tip_bytes),
                      "avg_launch_us": t_tip * 1e6,
-                     "variant": "fasa_tip launches (scores only); inside fasa_decode the same kernel also "
-                                "builds the select's coarse histogram, which the kernel trace times separately"},
+                     "variant": "the step's own TIP launch (fasa_decode_tip): slab read, scores written, "
+                                "plus the per-chunk candidate lists or the unit histograms the step's select reads",
+                     "step": {"bound": "hbm", "achieved": step_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                              "frac": step_gbps / HBM_PEAK_GBPS, "algorithmic_bytes": int(per_layer_touch),
+                              "us": el / args.steps * 1e6}},
         "measured_references": {"copy_1GiB_GBps": copy_gbps, "sum_1GiB_GBps": read_gbps,
                                 "tip_frac_of_copy": tip_gbps / copy_gbps, "tip_frac_of_sum": tip_gbps / read_gbps,
                                 "step_frac_of_sum": step_gbps / read_gbps,

@@ -156,8 +156,11 @@ fasa_status fasa_slab_append(const fasa_shape* shape, const void* k_pool,
                              const int32_t* block_table, const int32_t* positions,
                              const int32_t* fc_idx, void* slab, hipStream_t stream);
 
-/* TIP: scores[b][g][j] for j < t_b (columns past t_b are left untouched).
- * Reads the slab when slab != NULL; with slab == NULL it gathers the dominant
+/* TIP (section 3.4, "Online Stage 1: Token Importance Predictor (TIP)", the
+ * score equation: the importance of every cached token from the dominant FCs
+ * only; FC i is the pair (2i, 2i+1), section 3.4 "RoPE from a Frequency-Chunk
+ * Perspective"): scores[b][g][j] for j < t_b (columns past t_b are left
+ * untouched).  Reads the slab when slab != NULL; with slab == NULL it gathers the dominant
  * columns straight from k_pool (same arithmetic, same bits, more bytes).
  * Scores accumulate in fp32: the query heads of the group are first summed per
  * dominant column (fp32), then each token's 2*n_fc products are added in FC
@@ -167,7 +170,9 @@ fasa_status fasa_tip(const fasa_shape* shape, const void* q, const void* slab,
                      const int32_t* seq_lens, const int32_t* fc_idx, float* scores,
                      int32_t max_t, hipStream_t stream);
 
-/* TOP-B over given scores: sel_idx / sel_count as described above.  Exact:
+/* TOP-B over given scores (section 3.4, the token-selection equation
+ * T_t = TopK-I(S_t, N_fac): the indices of the N_fac largest scores, with the
+ * forced tokens kept on top): sel_idx / sel_count as described above.  Exact:
  * the selection is a function of the fp32 score bits only.  The workspace is
  * sized by fasa_workspace_size. */
 fasa_status fasa_topk(const fasa_shape* shape, const float* scores,
@@ -175,8 +180,10 @@ fasa_status fasa_topk(const fasa_shape* shape, const float* scores,
                       int32_t* sel_count, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
-/* FAC over a given selection (sel_idx / sel_count laid out for max_t).
- * bf16 caches compute in fp32; fp32 caches compute logits, softmax and the
+/* FAC over a given selection (section 3.4, "Online Stage 2: Focused Attention
+ * Computation (FAC)", the gather and attention equations: softmax(q K_T^T *
+ * scale) V_T over the selected rows, which keep their positions), with
+ * sel_idx / sel_count laid out for max_t.  bf16 caches compute in fp32; fp32 caches compute logits, softmax and the
  * weighted sum in fp64 and round the result to fp32 once.  sel_count is
  * clamped into [0, cap]; entries of sel_idx[0..sel_count) below 0 or at or past
  * max_blocks_per_seq * block_size contribute nothing, and a head whose
@@ -188,14 +195,37 @@ fasa_status fasa_fac(const fasa_shape* shape, const void* q, const void* k_pool,
                      float* out, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
-/* The whole step: TIP -> TOP-B -> FAC, enqueued on one stream.  slab == NULL
- * makes TIP read the dominant columns from k_pool.  sel_idx and sel_count are
- * outputs (the selection used). */
+/* The whole step of section 3.4 (TIP, then the token selection T_t =
+ * TopK-I(S_t, N_fac), then FAC over T_t; the online stages 1 and 2), enqueued
+ * on one stream: the same results as fasa_tip -> fasa_topk -> fasa_fac.  slab
+ * == NULL makes TIP read the dominant columns from k_pool.  sel_idx and
+ * sel_count are outputs (the selection used). */
 fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_pool,
                         const void* v_pool, const void* slab, const int32_t* block_table,
                         const int32_t* seq_lens, int32_t max_t, const int32_t* fc_idx,
                         float* out, int32_t* sel_idx, int32_t* sel_count,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* fasa_decode in its two stages, for callers that time or schedule them apart
+ * (section 3.4's online stage 1, TIP, and stage 2, the selection and FAC).
+ * fasa_decode_tip enqueues the step's first launch only: TIP over every unit,
+ * leaving in the workspace what the rest of the step reads (per-chunk
+ * candidate lists or per-unit score histograms, chosen from shape and max_t as
+ * fasa_decode chooses).  fasa_decode_rest enqueues the rest: the exact top-B
+ * from those, then FAC; sel_idx, sel_count and out as in fasa_decode.  The two
+ * calls, in order on one stream with the same shape, max_t, inputs and
+ * workspace, and nothing else using that workspace between them, give exactly
+ * fasa_decode's results.  Arguments and errors as in fasa_decode (the
+ * arguments a stage does not read are left out). */
+fasa_status fasa_decode_tip(const fasa_shape* shape, const void* q, const void* k_pool,
+                            const void* slab, const int32_t* block_table, const int32_t* seq_lens,
+                            int32_t max_t, const int32_t* fc_idx, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+fasa_status fasa_decode_rest(const fasa_shape* shape, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* block_table,
+                             const int32_t* seq_lens, int32_t max_t, float* out, int32_t* sel_idx,
+                             int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /* ---- FASA-M: the memory-optimised placement (section 3.4, "Hardware-Aware
  * Variants", FASA-M and Equation 10).  The GPU keeps only the dominant-key

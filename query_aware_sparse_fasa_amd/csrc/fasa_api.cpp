@@ -341,49 +341,57 @@ fasa_status fasa_fac(const fasa_shape* shape, const void* q, const void* k_pool,
                                      static_cast<char*>(workspace) + l.fac, nullptr, stream));
 }
 
-fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_pool, const void* v_pool,
-                        const void* slab, const int32_t* block_table, const int32_t* seq_lens,
-                        int32_t max_t, const int32_t* fc_idx, float* out, int32_t* sel_idx,
-                        int32_t* sel_count, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream) {
-  fasa_status st = check_shape(shape);
-  if (st != FASA_OK) return st;
-  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
-  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !fc_idx || !out || !sel_count)
-    return FASA_ERR_INVALID_ARG;
-  if (!sel_idx && capacity(shape, max_t) > 0) return FASA_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16)) return FASA_ERR_INVALID_ARG;
-  if (slab && !aligned(slab, 16)) return FASA_ERR_INVALID_ARG;
-  Common c = make_common(shape, max_t);
-  c.score_stride = (max_t + 3) & ~3;   // the workspace's scores rows: 16-byte loads throughout
-  const FacPlan p = fasa::fac_plan(c);
-  const Layout l = layout(c, p);
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < l.total) return FASA_ERR_WORKSPACE;
-  // Small budgets and rows whose candidate lists fit on chip: TIP (+ each
-  // chunk's candidates) -> FAC that finishes the exact select from them and
-  // writes out directly; two launches.  Otherwise TIP (+ unit histograms) ->
-  // filter (+ FAC counters zeroed) -> the same FAC over the filter's kept keys
-  // (small budgets), or for large budgets the exact select as a launch of its
-  // own, followed by a split-K FAC merged in its last workgroups.
+namespace {
+
+// The per-call plan of a decode step, shared by its two stages: the layout of
+// the workspace and whether TIP emits per-chunk candidates (two launches) or
+// builds the unit histograms for a filter launch.
+struct DecodePlan {
+  Common c;
+  FacPlan p;
+  Layout l;
+  bool emits;
+};
+
+fasa_status decode_plan(const fasa_shape* shape, int32_t max_t, const void* workspace, size_t workspace_bytes,
+                        DecodePlan& d) {
+  d.c = make_common(shape, max_t);
+  d.c.score_stride = (max_t + 3) & ~3;   // the workspace's scores rows: 16-byte loads throughout
+  d.p = fasa::fac_plan(d.c);
+  d.l = layout(d.c, d.p);
+  d.emits = max_t > 0 && fasa::decode_emits(d.c, d.p);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < d.l.total) return FASA_ERR_WORKSPACE;
+  return FASA_OK;
+}
+
+// Stage 1: TIP, with the outputs stage 2 reads (candidate lists or histograms).
+fasa_status decode_tip_stage(const DecodePlan& d, const void* q, const void* k_pool, const void* slab,
+                             const int32_t* block_table, const int32_t* seq_lens, const int32_t* fc_idx,
+                             void* workspace, hipStream_t stream) {
+  if (d.c.max_t <= 0) return FASA_OK;
   char* w = static_cast<char*>(workspace);
-  const fasa::SelectBuffers sb = select_buffers(workspace, l);
-  float* scores = reinterpret_cast<float*>(w + l.scores);
-  uint32_t* fac_arrive = reinterpret_cast<uint32_t*>(w + l.fac_arrive);
-  if (max_t > 0 && fasa::decode_emits(c, p)) {
-    const fasa::TipOutputs to{fasa::kTipEmit, nullptr, static_cast<uint2*>(sb.slots),
-                              reinterpret_cast<uint2*>(sb.counts)};
-    if ((st = hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores, to,
-                                          stream))) != FASA_OK)
-      return st;
+  const fasa::SelectBuffers sb = select_buffers(workspace, d.l);
+  float* scores = reinterpret_cast<float*>(w + d.l.scores);
+  const fasa::TipOutputs to = d.emits ? fasa::TipOutputs{fasa::kTipEmit, nullptr, static_cast<uint2*>(sb.slots),
+                                                         reinterpret_cast<uint2*>(sb.counts)}
+                                      : fasa::TipOutputs{fasa::kTipHist, sb.hist, nullptr, nullptr};
+  return hip_status(fasa::launch_tip(d.c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores, to, stream));
+}
+
+// Stage 2: the exact top-B from stage 1's outputs, then FAC.
+fasa_status decode_rest_stage(const DecodePlan& d, const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, const int32_t* seq_lens, float* out, int32_t* sel_idx,
+                              int32_t* sel_count, void* workspace, hipStream_t stream) {
+  const Common& c = d.c;
+  const FacPlan& p = d.p;
+  char* w = static_cast<char*>(workspace);
+  const fasa::SelectBuffers sb = select_buffers(workspace, d.l);
+  float* scores = reinterpret_cast<float*>(w + d.l.scores);
+  uint32_t* fac_arrive = reinterpret_cast<uint32_t*>(w + d.l.fac_arrive);
+  if (d.emits)
     return hip_status(fasa::launch_fac_select(c, p, q, k_pool, v_pool, block_table, scores, seq_lens, sb, true,
                                               sel_idx, sel_count, out, stream));
-  }
-  if (max_t > 0) {
-    if ((st = hip_status(fasa::launch_tip(c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores,
-                                          fasa::TipOutputs{fasa::kTipHist, sb.hist, nullptr, nullptr}, stream))) !=
-        FASA_OK)
-      return st;
-  }
+  fasa_status st;
   if ((st = hip_status(fasa::launch_filter(c, scores, seq_lens, sb, true, fac_arrive, p.head_chunks, stream))) !=
       FASA_OK)
     return st;
@@ -394,7 +402,73 @@ fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_po
                                            stream))) != FASA_OK)
     return st;
   return hip_status(fasa::launch_fac(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out,
-                                     w + l.fac, fac_arrive, stream));
+                                     w + d.l.fac, fac_arrive, stream));
+}
+
+fasa_status check_decode_inputs(const fasa_shape* shape, int32_t max_t, const void* q, const void* k_pool,
+                                const void* slab, const int32_t* block_table, const int32_t* seq_lens) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
+  if (!q || !k_pool || !block_table || !seq_lens) return FASA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_pool, 16)) return FASA_ERR_INVALID_ARG;
+  if (slab && !aligned(slab, 16)) return FASA_ERR_INVALID_ARG;
+  return FASA_OK;
+}
+
+fasa_status check_decode_outputs(const fasa_shape* shape, int32_t max_t, const void* v_pool, const float* out,
+                                 const int32_t* sel_idx, const int32_t* sel_count) {
+  if (!v_pool || !out || !sel_count) return FASA_ERR_INVALID_ARG;
+  if (!sel_idx && capacity(shape, max_t) > 0) return FASA_ERR_INVALID_ARG;
+  if (!aligned(v_pool, 16)) return FASA_ERR_INVALID_ARG;
+  return FASA_OK;
+}
+
+}  // namespace
+
+fasa_status fasa_decode(const fasa_shape* shape, const void* q, const void* k_pool, const void* v_pool,
+                        const void* slab, const int32_t* block_table, const int32_t* seq_lens,
+                        int32_t max_t, const int32_t* fc_idx, float* out, int32_t* sel_idx,
+                        int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  // Small budgets and rows whose candidate lists fit on chip: TIP (+ each
+  // chunk's candidates) -> FAC that finishes the exact select from them and
+  // writes out directly; two launches.  Otherwise TIP (+ unit histograms) ->
+  // filter (+ FAC counters zeroed) -> the same FAC over the filter's kept keys
+  // (small budgets), or for large budgets the exact select as a launch of its
+  // own, followed by a split-K FAC merged in its last workgroups.
+  fasa_status st = check_decode_inputs(shape, max_t, q, k_pool, slab, block_table, seq_lens);
+  if (st != FASA_OK) return st;
+  if (!fc_idx) return FASA_ERR_INVALID_ARG;
+  if ((st = check_decode_outputs(shape, max_t, v_pool, out, sel_idx, sel_count)) != FASA_OK) return st;
+  DecodePlan d;
+  if ((st = decode_plan(shape, max_t, workspace, workspace_bytes, d)) != FASA_OK) return st;
+  if ((st = decode_tip_stage(d, q, k_pool, slab, block_table, seq_lens, fc_idx, workspace, stream)) != FASA_OK)
+    return st;
+  return decode_rest_stage(d, q, k_pool, v_pool, block_table, seq_lens, out, sel_idx, sel_count, workspace, stream);
+}
+
+fasa_status fasa_decode_tip(const fasa_shape* shape, const void* q, const void* k_pool, const void* slab,
+                            const int32_t* block_table, const int32_t* seq_lens, int32_t max_t,
+                            const int32_t* fc_idx, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  fasa_status st = check_decode_inputs(shape, max_t, q, k_pool, slab, block_table, seq_lens);
+  if (st != FASA_OK) return st;
+  if (!fc_idx) return FASA_ERR_INVALID_ARG;
+  DecodePlan d;
+  if ((st = decode_plan(shape, max_t, workspace, workspace_bytes, d)) != FASA_OK) return st;
+  return decode_tip_stage(d, q, k_pool, slab, block_table, seq_lens, fc_idx, workspace, stream);
+}
+
+fasa_status fasa_decode_rest(const fasa_shape* shape, const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, const int32_t* seq_lens, int32_t max_t, float* out,
+                             int32_t* sel_idx, int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  fasa_status st = check_decode_inputs(shape, max_t, q, k_pool, nullptr, block_table, seq_lens);
+  if (st != FASA_OK) return st;
+  if ((st = check_decode_outputs(shape, max_t, v_pool, out, sel_idx, sel_count)) != FASA_OK) return st;
+  DecodePlan d;
+  if ((st = decode_plan(shape, max_t, workspace, workspace_bytes, d)) != FASA_OK) return st;
+  return decode_rest_stage(d, q, k_pool, v_pool, block_table, seq_lens, out, sel_idx, sel_count, workspace, stream);
 }
 
 fasa_status fasa_m_host_sizes(const fasa_shape* shape, int64_t n_blocks, size_t* k_nd_bytes, size_t* v_bytes) {

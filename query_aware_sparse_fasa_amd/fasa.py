@@ -25,7 +25,8 @@ BLOCK = 256
 
 EXPORTS = ["fasa_status_str", "fasa_validate_shape", "fasa_selection_capacity",
            "fasa_workspace_size", "fasa_check_fc_idx", "fasa_slab_build", "fasa_slab_append",
-           "fasa_tip", "fasa_topk", "fasa_fac", "fasa_decode", "fasa_dense_workspace_size",
+           "fasa_tip", "fasa_topk", "fasa_fac", "fasa_decode", "fasa_decode_tip", "fasa_decode_rest",
+           "fasa_dense_workspace_size",
            "fasa_dense_decode", "fasa_m_host_sizes", "fasa_m_offload", "fasa_m_workspace_size",
            "fasa_m_decode", "fasa_ca_workspace_size", "fasa_ca_hits", "fasa_ca_dominant",
            "fasa_scratch_capacity", "fasa_decode_scratch"]
@@ -80,6 +81,9 @@ def lib() -> ctypes.CDLL:
         "fasa_fac": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
         "fasa_decode": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _P]),
+        "fasa_decode_tip": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
+        "fasa_decode_rest": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, ctypes.c_size_t,
+                                            _P]),
         "fasa_dense_workspace_size": (ctypes.c_int, [_S, _I32, ctypes.POINTER(ctypes.c_size_t)]),
         "fasa_dense_decode": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
         "fasa_m_host_sizes": (ctypes.c_int, [_S, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t),
@@ -230,6 +234,26 @@ def fasa_decode(shape, q, k_pool, v_pool, slab, block_table, seq_lens, max_t, fc
                              _ptr(block_table), _ptr(seq_lens), max_t, _ptr(fc_idx), _ptr(out),
                              _ptr(sel_idx), _ptr(sel_count), _ptr(workspace), nbytes, _stream(stream)),
            "fasa_decode")
+
+
+def fasa_decode_tip(shape, q, k_pool, slab, block_table, seq_lens, max_t, fc_idx, workspace, stream=None) -> None:
+    """The first launch of fasa_decode (TIP with what the rest of the step reads)."""
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fasa_decode_tip(ctypes.byref(shape), _ptr(q), _ptr(k_pool), _ptr(slab), _ptr(block_table),
+                                 _ptr(seq_lens), max_t, _ptr(fc_idx), _ptr(workspace), nbytes, _stream(stream)),
+           "fasa_decode_tip")
+
+
+def fasa_decode_rest(shape, q, k_pool, v_pool, block_table, seq_lens, max_t, out, sel_idx, sel_count, workspace,
+                     stream=None) -> None:
+    """The rest of fasa_decode after fasa_decode_tip (top-B and FAC)."""
+    _need(out, torch.float32, "out")
+    _need(sel_idx, torch.int32, "sel_idx")
+    _need(sel_count, torch.int32, "sel_count")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fasa_decode_rest(ctypes.byref(shape), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                  _ptr(seq_lens), max_t, _ptr(out), _ptr(sel_idx), _ptr(sel_count),
+                                  _ptr(workspace), nbytes, _stream(stream)), "fasa_decode_rest")
 
 
 def fasa_scratch_capacity() -> int:

@@ -67,6 +67,15 @@ class DeviceLayer:
                          self.block_table, self.seq_lens, self.max_t, self.fc_idx, self.out,
                          self.sel_idx, self.sel_count, self.workspace, stream)
 
+    def decode_tip(self, use_slab=True, stream=None):
+        """fasa_decode's first launch only (TIP as the step runs it)."""
+        fasa.fasa_decode_tip(self.shape, self.q, self.k_pool, self.slab if use_slab else None, self.block_table,
+                             self.seq_lens, self.max_t, self.fc_idx, self.workspace, stream)
+
+    def decode_rest(self, stream=None):
+        fasa.fasa_decode_rest(self.shape, self.q, self.k_pool, self.v_pool, self.block_table, self.seq_lens,
+                              self.max_t, self.out, self.sel_idx, self.sel_count, self.workspace, stream)
+
     def dense(self, out=None, stream=None):
         """Full attention over every cached token (into out, default self.dense_out)."""
         if getattr(self, "dense_ws", None) is None:

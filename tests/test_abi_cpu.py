@@ -23,7 +23,7 @@ def header_functions():
 def test_exports_every_declared_symbol():
     L = fasa.lib()
     names = header_functions()
-    assert len(names) == 22, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(fasa.EXPORTS) == names
@@ -141,6 +141,21 @@ def test_entry_points_reject_before_launch():
     assert raw("fasa_decode", *args, FAKE, ws - 1, None) == W
     assert raw("fasa_decode", *args, FAKE + 16, ws, None) == W
     assert raw("fasa_fac", sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, 1024, None) == W
+    # the two stages of the step: what each reads is checked, then the workspace
+    tip_args = (sp, FAKE, FAKE, None, FAKE, FAKE, 4096)
+    assert raw("fasa_decode_tip", *tip_args, None, FAKE, ws, None) == E          # fc_idx
+    assert raw("fasa_decode_tip", sp, FAKE, None, None, FAKE, FAKE, 4096, FAKE, FAKE, ws, None) == E
+    assert raw("fasa_decode_tip", sp, FAKE, FAKE, FAKE + 2, FAKE, FAKE, 4096, FAKE, FAKE, ws, None) == E
+    assert raw("fasa_decode_tip", *tip_args, FAKE, FAKE, ws - 1, None) == W
+    assert raw("fasa_decode_tip", *tip_args, FAKE, None, ws, None) == W
+    rest = (sp, FAKE, FAKE, FAKE, FAKE, FAKE, 4096)
+    assert raw("fasa_decode_rest", *rest, None, FAKE, FAKE, FAKE, ws, None) == E     # out
+    assert raw("fasa_decode_rest", *rest, FAKE, None, FAKE, FAKE, ws, None) == E     # sel_idx, cap > 0
+    assert raw("fasa_decode_rest", sp, FAKE, FAKE, None, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, ws,
+               None) == E                                                            # v_pool
+    assert raw("fasa_decode_rest", *rest, FAKE, FAKE, FAKE, FAKE + 16, ws, None) == W
+    assert raw("fasa_decode_rest", sp, FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, ws,
+               None) == E                                                            # max_t
     # dense decode: null pointers, max_t, workspace
     dws = fasa.fasa_dense_workspace_size(s, 4096)
     assert raw("fasa_dense_decode", sp, FAKE, FAKE, FAKE, FAKE, None, 4096, FAKE, FAKE, dws, None) == E

@@ -374,6 +374,29 @@ def test_decode_with_garbage_workspace_is_identical(name):
         assert torch.equal(a[0], L.out) and torch.equal(a[1], L.sel_idx), fill
 
 
+@pytest.mark.parametrize("name", ["c2-ragged", "c3-shape", "wide-g4", "fp32-gqa4"])
+def test_decode_in_two_stages_is_identical(name):
+    """fasa_decode_tip then fasa_decode_rest give fasa_decode's results bit for
+    bit (the per-chunk-candidate path, the split path of large budgets, the
+    three-launch path, an fp32 cache); so does a second TIP stage issued before
+    the rest, as a loop timing the TIP stage alone leaves the workspace."""
+    say(f"[two stages] {name}")
+    inp, L = layer_for(name)
+    L.decode()
+    torch.cuda.synchronize()
+    ref = (L.out.clone(), L.sel_idx.clone(), L.sel_count.clone())
+    for tips in (1, 2):
+        L.out.fill_(float("nan"))
+        L.sel_idx.fill_(-7)
+        L.sel_count.fill_(-7)
+        for _ in range(tips):
+            L.decode_tip()
+        L.decode_rest()
+        torch.cuda.synchronize()
+        for x, y in zip(ref, (L.out, L.sel_idx, L.sel_count)):
+            assert torch.equal(x, y), (name, tips)
+
+
 def test_decode_without_slab_is_identical():
     name = "c2-ragged"
     say(f"[decode no-slab] {name}")
@@ -617,6 +640,22 @@ def test_empty_and_tiny_sequences():
     assert (L.out[0] == 0).all()
     assert (L.sel_count[0] == 0).all()
     _check_decode(inp, L, {k: v for k, v in oracle_units(inp).items() if k[0] > 0}, "edge")
+
+
+def test_decode_long_rows_ragged():
+    """The Qwen2.5-7B-shaped layer (groups of 7, B = 1024) on the filter path
+    (rows too long for TIP's per-chunk lists), with one-head selecting
+    workgroups over 1024-row lists: a 90000-token row, a short one just past
+    the budget, an empty sequence and a one-token one."""
+    cfg = C["c4"].replace(batch=4)
+    say("[long rows] c4 shape, lengths 90000 1500 0 1")
+    inp = synth.make_inputs(cfg, seed=21, seq_lens=[90000, 1500, 0, 1])
+    L = DeviceLayer(inp)
+    L.out.fill_(float("nan"))
+    L.decode()
+    torch.cuda.synchronize()
+    assert (L.out[2] == 0).all() and (L.sel_count[2] == 0).all()
+    _check_decode(inp, L, {k: v for k, v in oracle_units(inp).items() if k[0] != 2}, "long rows")
 
 
 def test_graph_capture_replays():
