@@ -163,6 +163,82 @@ def cpu_oracle_baseline(cfg, seconds: float):
                             "sample": f"{one_done} unit evaluations in {one_el:.1f} s on one thread; " + desc}}
 
 
+def time_m_reuse(torch, synth, stream, m_layers, nd: int, e: int, n_q: int = 8, rho: float = 0.9):
+    """FASA-M over n_q consecutive steps per layer whose query drifts (each rho
+    times the last plus fresh noise), three ways, each captured in a graph over
+    the same queries: the sequential step (fasa_m_decode: every selected row over
+    the host link after the select); the previous step's rows kept in the
+    layer's workspace (resident: only rows new to the step cross the link); and
+    the previous step's rows brought back from the host by fasa_m_prefetch on a
+    second stream while the step selects (prefetch, as with a workspace shared
+    by several layers)."""
+    side = torch.cuda.Stream()
+    row_bytes = (nd + 128) * e
+    plan = []
+    for lay in m_layers:
+        qs = synth.drifting_queries(lay.q, n_q, rho=rho, seed=7)
+        sels = [(torch.full_like(lay.m_sel_idx, -7), torch.full_like(lay.m_sel_count, 0)) for _ in range(2)]
+        plan.append((lay, qs, sels))
+
+    def seq_steps():
+        for lay, qs, _ in plan:
+            for q in qs:
+                lay.q.copy_(q)
+                lay.m_decode()
+
+    def reuse_steps(prefetch, hits=None):
+        for lay, qs, sels in plan:
+            for n, q in enumerate(qs):
+                par = n % 2
+                cur, prev = sels[par], sels[1 - par]
+                if prefetch:
+                    fork = torch.cuda.Event()
+                    fork.record(stream)
+                    side.wait_event(fork)
+                    lay.m_prefetch(prev[0], prev[1], par, stream=side)
+                lay.m_select(q=q, sel_idx=cur[0], sel_count=cur[1], stream=stream)
+                if prefetch:
+                    join = torch.cuda.Event()
+                    join.record(side)
+                    stream.wait_event(join)
+                lay.m_finish(prev[0], prev[1], par, q=q, sel_idx=cur[0], sel_count=cur[1], hits=hits, stream=stream)
+
+    with torch.cuda.stream(stream):
+        reuse_steps(True)          # fills both selection buffers and both row areas
+        hits = torch.zeros_like(m_layers[0].m_sel_count)
+        reuse_steps(False, hits)
+    torch.cuda.synchronize()
+    # rows per sweep: every step's selection size (the same queries each sweep)
+    rows = 0
+    with torch.cuda.stream(stream):
+        for lay, qs, sels in plan:
+            for n, q in enumerate(qs):
+                lay.m_select(q=q, sel_idx=sels[n % 2][0], sel_count=sels[n % 2][1], stream=stream)
+                rows += int(sels[n % 2][1].sum().item())
+    torch.cuda.synchronize()
+    n_hits = int(hits.sum().item())
+    g_seq = graph_of(torch, stream, [seq_steps])
+    g_res = graph_of(torch, stream, [lambda: reuse_steps(False)])
+    g_pf = graph_of(torch, stream, [lambda: reuse_steps(True)])
+    steps = len(plan) * n_q
+    reps = max(1, 200 // steps)
+    t_seq = time_graph(torch, stream, [g_seq], reps) / (reps * steps)
+    t_res = time_graph(torch, stream, [g_res], reps) / (reps * steps)
+    t_pf = time_graph(torch, stream, [g_pf], reps) / (reps * steps)
+    for lay, qs, _ in plan:
+        lay.q.copy_(qs[0])
+    log(f"[bench] FASA-M over {n_q} drifting queries: sequential {t_seq * 1e6:.2f} us, resident rows "
+        f"{t_res * 1e6:.2f} us, host prefetch {t_pf * 1e6:.2f} us per step; {n_hits} of {rows} rows reused")
+    return {"queries_per_layer": n_q, "query_drift_rho": rho,
+            "sequential_us_per_step": t_seq * 1e6, "resident_us_per_step": t_res * 1e6,
+            "prefetch_us_per_step": t_pf * 1e6,
+            "rows_per_step": rows / steps, "rows_reused_frac": n_hits / max(rows, 1),
+            "host_bytes_sequential_per_step": int(rows * row_bytes / steps),
+            "host_bytes_resident_per_step": int((rows - n_hits) * row_bytes / steps),
+            "host_bytes_saved_resident_per_step": int(n_hits * row_bytes / steps),
+            "host_bytes_prefetch_per_step": int((2 * rows - n_hits) * row_bytes / steps)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,12 +445,14 @@ def main():
         sel_rows = sb["rows"] // (2 * 128 * e)
         host_bytes = sel_rows * (nd + 128) * e
         t_all = int(inp.seq_lens.sum())
-        gpu_m = t_all * cfg.n_kv_heads * 2 * cfg.n_fc * e + sel_rows * 2 * 128 * e   # slab + staged rows
+        # slab + the two row areas (the step's staged rows and the previous step's)
+        gpu_m = t_all * cfg.n_kv_heads * 2 * cfg.n_fc * e + 2 * sel_rows * 2 * 128 * e
         gpu_fkv = t_all * cfg.n_kv_heads * 2 * 128 * e
         fasa_m = {"us_per_step": t_m * 1e6, "host_bytes_per_step": int(host_bytes),
                   "host_GBps": host_bytes / t_m / 1e9, "gpu_cache_bytes": int(gpu_m),
                   "fkv_cache_bytes": int(gpu_fkv), "gpu_memory_reduction": gpu_fkv / gpu_m,
                   "layers_rotated": len(m_layers)}
+        fasa_m["reuse"] = time_m_reuse(torch, synth, stream, m_layers, nd, e)
         log(f"[bench] FASA-M step {t_m * 1e6:.2f} us ({host_bytes / 1e6:.2f} MB from host, "
             f"{host_bytes / t_m / 1e9:.1f} GB/s); GPU cache {gpu_m / 1e6:.1f} MB vs {gpu_fkv / 1e6:.1f} MB full "
             f"({gpu_fkv / gpu_m:.2f}x less)")

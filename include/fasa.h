@@ -254,8 +254,9 @@ fasa_status fasa_m_offload(const fasa_shape* shape, const void* k_pool, const vo
                            const int32_t* fc_idx, void* k_nd_host, void* v_host,
                            hipStream_t stream);
 
-/* Workspace of fasa_m_decode: fasa_workspace_size's layout plus two staging
- * arrays of batch * n_kv_heads * cap rows of 128 elements (K and V). */
+/* Workspace of fasa_m_decode and its stages: fasa_workspace_size's layout plus
+ * two row areas, each two staging arrays of batch * n_kv_heads * cap rows of
+ * 128 elements (K and V). */
 fasa_status fasa_m_workspace_size(const fasa_shape* shape, int32_t max_t, size_t* bytes);
 
 /* One FASA-M decode step: TIP on the slab, the exact top-B (sel_idx and
@@ -270,6 +271,52 @@ fasa_status fasa_m_decode(const fasa_shape* shape, const void* q, const void* sl
                           const int32_t* seq_lens, int32_t max_t, const int32_t* fc_idx,
                           float* out, int32_t* sel_idx, int32_t* sel_count, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
+
+/* FASA-M with the previous query's rows loaded in advance (section 3.4,
+ * "Hardware-Aware Variants", the mitigation of FASA-M's CPU-GPU transfer
+ * latency: the keys and values that the previous query needed are loaded
+ * asynchronously, in advance, so that TIP overlaps the transfer).
+ * fasa_m_decode in two stages around a pair of row areas in the workspace; a
+ * step of parity p (0 or 1; consecutive steps alternate) stages its selected
+ * rows in area p and takes every row whose token the previous selection also
+ * holds from area 1 - p, so that only the others cross the host link:
+ *   fasa_m_decode_select: TIP, then the exact top-B into sel_idx / sel_count;
+ *   fasa_m_decode_finish: after it, the selected rows into area `parity` --
+ *     from area 1 - parity where the token is in prev_sel_idx, from the host
+ *     otherwise -- then FAC into out.  prev_sel_idx / prev_sel_count (laid out
+ *     as sel_idx / sel_count) must be the selection whose rows area 1 - parity
+ *     holds; pass NULL for both to take every row from the host (hits must
+ *     then be NULL).  hits (nullable, int32 [batch][n_kv_heads]) is
+ *     incremented by the rows taken from area 1 - parity.  Rows are reused
+ *     only when cap <= 8192; above that every row comes from the host.
+ *   Area 1 - parity holds the previous selection's rows when the previous
+ *   step ran fasa_m_decode_finish with parity 1 - parity on this workspace
+ *   (a workspace kept per layer: nothing crosses the link for those rows), or
+ *   after fasa_m_prefetch:
+ *   fasa_m_prefetch: the rows of prev_sel_idx / prev_sel_count rebuilt from
+ *     the host arrays and the slab into area 1 - parity, for a step of parity
+ *     `parity` (a workspace shared by several layers).  It touches nothing else
+ *     of the workspace, so it may run on a second stream concurrently with
+ *     fasa_m_decode_select on the same workspace.
+ * The results (sel_idx, sel_count, out) equal fasa_m_decode's bit for bit,
+ * whatever the previous selection was.  Order: fasa_m_prefetch and
+ * fasa_m_decode_select after the previous step's finish; the finish after
+ * both.  fasa_m_decode itself stages in area 0. */
+fasa_status fasa_m_decode_select(const fasa_shape* shape, const void* q, const void* slab,
+                                 const int32_t* block_table, const int32_t* seq_lens, int32_t max_t,
+                                 const int32_t* fc_idx, int32_t* sel_idx, int32_t* sel_count,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+fasa_status fasa_m_prefetch(const fasa_shape* shape, const void* slab, const void* k_nd_host,
+                            const void* v_host, const int32_t* block_table, int32_t max_t,
+                            const int32_t* fc_idx, const int32_t* prev_sel_idx,
+                            const int32_t* prev_sel_count, int32_t parity, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+fasa_status fasa_m_decode_finish(const fasa_shape* shape, const void* q, const void* slab,
+                                 const void* k_nd_host, const void* v_host, const int32_t* block_table,
+                                 int32_t max_t, const int32_t* fc_idx, const int32_t* prev_sel_idx,
+                                 const int32_t* prev_sel_count, const int32_t* sel_idx,
+                                 const int32_t* sel_count, int32_t parity, float* out, int32_t* hits,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---- Offline calibration: Contextual Agreement (section 3.4, the CA metric
  * and the offline calibration).  A calibration row is one decode query

@@ -161,18 +161,24 @@ CaLayout ca_layout(const Common& cs) {
 
 // FASA-M: the decode workspace followed by the two staging arrays
 // [b][H_kv][cap][128] (K, then V).
+// Two row areas (K and V staging each): a step of parity p stages its rows in
+// area p and finds the previous step's rows in area 1 - p.
 struct MLayout {
   Layout d;
-  size_t stage_k, stage_v, total;
+  size_t rows_k[2], rows_v[2], total;
 };
 MLayout m_layout(const Common& c, const FacPlan& p) {
   MLayout m;
   m.d = layout(c, p);
   const size_t e = c.bf16 ? 2 : 4;
   const size_t st = align256(size_t(c.batch) * c.n_kv_heads * size_t(c.cap) * fasa::kHeadDim * e);
-  m.stage_k = m.d.total;
-  m.stage_v = m.stage_k + st;
-  m.total = m.stage_v + st;
+  size_t o = m.d.total;
+  for (int a = 0; a < 2; ++a) {
+    m.rows_k[a] = o;
+    m.rows_v[a] = o + st;
+    o += 2 * st;
+  }
+  m.total = o;
   return m;
 }
 
@@ -507,13 +513,79 @@ fasa_status fasa_m_workspace_size(const fasa_shape* shape, int32_t max_t, size_t
   return FASA_OK;
 }
 
+namespace {
+
+// Shared checks and plan of the FASA-M entry points.
+struct MPlan {
+  Common c;
+  FacPlan p;
+  MLayout m;
+};
+
+fasa_status m_plan(const fasa_shape* shape, int32_t max_t, const void* workspace, size_t workspace_bytes,
+                   MPlan& mp) {
+  mp.c = make_common(shape, max_t);
+  mp.c.score_stride = (max_t + 3) & ~3;
+  mp.p = fasa::fac_plan(mp.c);
+  mp.m = m_layout(mp.c, mp.p);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < mp.m.total) return FASA_ERR_WORKSPACE;
+  return FASA_OK;
+}
+
+fasa_status m_check(const fasa_shape* shape, int32_t max_t) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  return check_max_t(shape, max_t);
+}
+
+// TIP on the slab -> filter -> exact select (the list is needed to gather).
+fasa_status m_select_stage(const MPlan& mp, const void* q, const void* slab, const int32_t* block_table,
+                           const int32_t* seq_lens, const int32_t* fc_idx, int32_t* sel_idx, int32_t* sel_count,
+                           void* workspace, hipStream_t stream) {
+  const Common& c = mp.c;
+  char* w = static_cast<char*>(workspace);
+  const fasa::SelectBuffers sb = select_buffers(workspace, mp.m.d);
+  float* scores = reinterpret_cast<float*>(w + mp.m.d.scores);
+  uint32_t* fac_arrive = reinterpret_cast<uint32_t*>(w + mp.m.d.fac_arrive);
+  fasa_status st;
+  if (c.max_t > 0) {
+    if ((st = hip_status(fasa::launch_tip(c, q, slab, nullptr, block_table, seq_lens, fc_idx, scores,
+                                          fasa::TipOutputs{fasa::kTipHist, sb.hist, nullptr, nullptr}, stream))) !=
+        FASA_OK)
+      return st;
+  }
+  if ((st = hip_status(fasa::launch_filter(c, scores, seq_lens, sb, true, fac_arrive, mp.p.head_chunks, stream))) !=
+      FASA_OK)
+    return st;
+  return hip_status(fasa::launch_finish(c, scores, seq_lens, sel_idx, sel_count, sb, fac_arrive, mp.p.head_chunks,
+                                        stream));
+}
+
+// Rows from the host (and, with reuse, the other row area) into row area
+// `area` -> FAC.
+fasa_status m_finish_stage(const MPlan& mp, const void* q, const void* slab, const void* knd, const void* vh,
+                           const int32_t* block_table, const int32_t* fc_idx, const int32_t* sel_idx,
+                           const int32_t* sel_count, const fasa::MReuse& reuse, int area, float* out,
+                           void* workspace, hipStream_t stream) {
+  char* w = static_cast<char*>(workspace);
+  uint32_t* fac_arrive = reinterpret_cast<uint32_t*>(w + mp.m.d.fac_arrive);
+  fasa_status st;
+  if ((st = hip_status(fasa::launch_m_gather(mp.c, knd, vh, slab, block_table, fc_idx, sel_idx, sel_count,
+                                             w + mp.m.rows_k[area], w + mp.m.rows_v[area], reuse, stream))) !=
+      FASA_OK)
+    return st;
+  return hip_status(fasa::launch_fac_staged(mp.c, mp.p, q, w + mp.m.rows_k[area], w + mp.m.rows_v[area], sel_count,
+                                            out, w + mp.m.d.fac, fac_arrive, stream));
+}
+
+}  // namespace
+
 fasa_status fasa_m_decode(const fasa_shape* shape, const void* q, const void* slab, const void* k_nd_host,
                           const void* v_host, const int32_t* block_table, const int32_t* seq_lens, int32_t max_t,
                           const int32_t* fc_idx, float* out, int32_t* sel_idx, int32_t* sel_count, void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {
-  fasa_status st = check_shape(shape);
+  fasa_status st = m_check(shape, max_t);
   if (st != FASA_OK) return st;
-  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
   if (!q || !slab || !k_nd_host || !v_host || !block_table || !seq_lens || !fc_idx || !out || !sel_count)
     return FASA_ERR_INVALID_ARG;
   if (!sel_idx && capacity(shape, max_t) > 0) return FASA_ERR_INVALID_ARG;
@@ -522,34 +594,82 @@ fasa_status fasa_m_decode(const fasa_shape* shape, const void* q, const void* sl
   const void* knd = host_alias(k_nd_host);
   const void* vh = host_alias(v_host);
   if (!knd || !vh) return FASA_ERR_INVALID_ARG;
-  Common c = make_common(shape, max_t);
-  c.score_stride = (max_t + 3) & ~3;
-  const FacPlan p = fasa::fac_plan(c);
-  const MLayout m = m_layout(c, p);
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < m.total) return FASA_ERR_WORKSPACE;
-  // TIP on the slab -> filter -> exact select (the list is needed to gather)
-  // -> rows from the host into staging -> FAC over the staged rows.
-  char* w = static_cast<char*>(workspace);
-  const fasa::SelectBuffers sb = select_buffers(workspace, m.d);
-  float* scores = reinterpret_cast<float*>(w + m.d.scores);
-  uint32_t* fac_arrive = reinterpret_cast<uint32_t*>(w + m.d.fac_arrive);
-  if (max_t > 0) {
-    if ((st = hip_status(fasa::launch_tip(c, q, slab, nullptr, block_table, seq_lens, fc_idx, scores,
-                                          fasa::TipOutputs{fasa::kTipHist, sb.hist, nullptr, nullptr}, stream))) !=
-        FASA_OK)
-      return st;
-  }
-  if ((st = hip_status(fasa::launch_filter(c, scores, seq_lens, sb, true, fac_arrive, p.head_chunks, stream))) !=
+  MPlan mp;
+  if ((st = m_plan(shape, max_t, workspace, workspace_bytes, mp)) != FASA_OK) return st;
+  if ((st = m_select_stage(mp, q, slab, block_table, seq_lens, fc_idx, sel_idx, sel_count, workspace, stream)) !=
       FASA_OK)
     return st;
-  if ((st = hip_status(fasa::launch_finish(c, scores, seq_lens, sel_idx, sel_count, sb, fac_arrive, p.head_chunks,
-                                           stream))) != FASA_OK)
-    return st;
-  if ((st = hip_status(fasa::launch_m_gather(c, knd, vh, slab, block_table, fc_idx, sel_idx, sel_count,
-                                             w + m.stage_k, w + m.stage_v, stream))) != FASA_OK)
-    return st;
-  return hip_status(fasa::launch_fac_staged(c, p, q, w + m.stage_k, w + m.stage_v, sel_count, out, w + m.d.fac,
-                                            fac_arrive, stream));
+  return m_finish_stage(mp, q, slab, knd, vh, block_table, fc_idx, sel_idx, sel_count, fasa::MReuse{}, 0, out,
+                        workspace, stream);
+}
+
+fasa_status fasa_m_decode_select(const fasa_shape* shape, const void* q, const void* slab,
+                                 const int32_t* block_table, const int32_t* seq_lens, int32_t max_t,
+                                 const int32_t* fc_idx, int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  fasa_status st = m_check(shape, max_t);
+  if (st != FASA_OK) return st;
+  if (!q || !slab || !block_table || !seq_lens || !fc_idx || !sel_count) return FASA_ERR_INVALID_ARG;
+  if (!sel_idx && capacity(shape, max_t) > 0) return FASA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(slab, 16)) return FASA_ERR_INVALID_ARG;
+  MPlan mp;
+  if ((st = m_plan(shape, max_t, workspace, workspace_bytes, mp)) != FASA_OK) return st;
+  return m_select_stage(mp, q, slab, block_table, seq_lens, fc_idx, sel_idx, sel_count, workspace, stream);
+}
+
+fasa_status fasa_m_prefetch(const fasa_shape* shape, const void* slab, const void* k_nd_host, const void* v_host,
+                            const int32_t* block_table, int32_t max_t, const int32_t* fc_idx,
+                            const int32_t* prev_sel_idx, const int32_t* prev_sel_count, int32_t parity,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  fasa_status st = m_check(shape, max_t);
+  if (st != FASA_OK) return st;
+  if (parity != 0 && parity != 1) return FASA_ERR_INVALID_ARG;
+  if (!slab || !k_nd_host || !v_host || !block_table || !fc_idx || !prev_sel_count) return FASA_ERR_INVALID_ARG;
+  if (!prev_sel_idx && capacity(shape, max_t) > 0) return FASA_ERR_INVALID_ARG;
+  if (!aligned(slab, 16) || !aligned(k_nd_host, 16) || !aligned(v_host, 16)) return FASA_ERR_INVALID_ARG;
+  const void* knd = host_alias(k_nd_host);
+  const void* vh = host_alias(v_host);
+  if (!knd || !vh) return FASA_ERR_INVALID_ARG;
+  MPlan mp;
+  if ((st = m_plan(shape, max_t, workspace, workspace_bytes, mp)) != FASA_OK) return st;
+  char* w = static_cast<char*>(workspace);
+  return hip_status(fasa::launch_m_gather(mp.c, knd, vh, slab, block_table, fc_idx, prev_sel_idx, prev_sel_count,
+                                          w + mp.m.rows_k[1 - parity], w + mp.m.rows_v[1 - parity],
+                                          fasa::MReuse{}, stream));
+}
+
+fasa_status fasa_m_decode_finish(const fasa_shape* shape, const void* q, const void* slab, const void* k_nd_host,
+                                 const void* v_host, const int32_t* block_table, int32_t max_t,
+                                 const int32_t* fc_idx, const int32_t* prev_sel_idx,
+                                 const int32_t* prev_sel_count, const int32_t* sel_idx, const int32_t* sel_count,
+                                 int32_t parity, float* out, int32_t* hits, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  fasa_status st = m_check(shape, max_t);
+  if (st != FASA_OK) return st;
+  if (parity != 0 && parity != 1) return FASA_ERR_INVALID_ARG;
+  if (!q || !slab || !k_nd_host || !v_host || !block_table || !fc_idx || !out || !sel_count)
+    return FASA_ERR_INVALID_ARG;
+  if (!sel_idx && capacity(shape, max_t) > 0) return FASA_ERR_INVALID_ARG;
+  if ((prev_sel_idx == nullptr) != (prev_sel_count == nullptr)) return FASA_ERR_INVALID_ARG;
+  if (!prev_sel_idx && hits) return FASA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(slab, 16) || !aligned(k_nd_host, 16) || !aligned(v_host, 16))
+    return FASA_ERR_INVALID_ARG;
+  const void* knd = host_alias(k_nd_host);
+  const void* vh = host_alias(v_host);
+  if (!knd || !vh) return FASA_ERR_INVALID_ARG;
+  MPlan mp;
+  if ((st = m_plan(shape, max_t, workspace, workspace_bytes, mp)) != FASA_OK) return st;
+  char* w = static_cast<char*>(workspace);
+  fasa::MReuse reuse;
+  if (prev_sel_idx) {
+    reuse.prev_idx = prev_sel_idx;
+    reuse.prev_count = prev_sel_count;
+    reuse.pf_k = w + mp.m.rows_k[1 - parity];
+    reuse.pf_v = w + mp.m.rows_v[1 - parity];
+    reuse.hits = hits;
+  }
+  return m_finish_stage(mp, q, slab, knd, vh, block_table, fc_idx, sel_idx, sel_count, reuse, parity, out, workspace,
+                        stream);
 }
 
 fasa_status fasa_ca_workspace_size(const fasa_shape* shape, int32_t max_t, int32_t k_top, size_t* bytes) {

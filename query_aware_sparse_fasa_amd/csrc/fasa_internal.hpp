@@ -157,11 +157,27 @@ int m_nd_stride(const Common& c);
 hipError_t launch_m_offload(const Common& c, const void* k_pool, const void* v_pool, const int32_t* block_table,
                             const int32_t* seq_lens, const int32_t* fc_idx, void* k_nd, void* v_host,
                             hipStream_t s);
+// Reuse of the previous step's rows by the gather: its selection (ascending,
+// [b][H_kv][cap]) and its rows in the prefetch area ([b][H_kv][cap][128], K and
+// V); hits (nullable) counts per unit the rows taken from there.  prev_idx ==
+// nullptr: no reuse.
+struct MReuse {
+  const int32_t* prev_idx = nullptr;
+  const int32_t* prev_count = nullptr;
+  const void* pf_k = nullptr;
+  const void* pf_v = nullptr;
+  int32_t* hits = nullptr;
+};
+// Whether the gather can search the previous selection on chip (cap <= 8192);
+// otherwise every row comes from the host.
+bool m_reuses(const Common& c);
 // Rebuild the selected rows (non-dominant columns and values from the host,
-// dominant pairs from the slab) into the staging arrays [b][H_kv][cap][128].
+// dominant pairs from the slab; with reuse, the rows the previous step selected
+// from the prefetch area) into the staging arrays [b][H_kv][cap][128].
 hipError_t launch_m_gather(const Common& c, const void* k_nd, const void* v_host, const void* slab,
                            const int32_t* block_table, const int32_t* fc_idx, const int32_t* sel_idx,
-                           const int32_t* sel_count, void* stage_k, void* stage_v, hipStream_t s);
+                           const int32_t* sel_count, void* stage_k, void* stage_v, const MReuse& reuse,
+                           hipStream_t s);
 
 // Offline calibration (calib.hip).  kCaMaxK: largest calibration window K.
 constexpr int kCaMaxK = 4096;

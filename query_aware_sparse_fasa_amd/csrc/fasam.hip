@@ -16,6 +16,14 @@
 //   v    [block][H_kv][256][128]: the value rows.
 // Staging (device workspace): [b][H_kv][cap][128] for K and for V; row r of a
 // unit is its r-th selected token.
+//
+// Prefetch (the latency mitigation of the same section: while TIP runs, the
+// keys and values that the previous query needed are loaded in advance): the
+// previous step's selection is gathered, the same way, into a second pair of
+// staging arrays (the prefetch area) on another stream, concurrently with
+// TIP and the select; the step's own gather then takes every selected row that
+// the previous step also selected from the prefetch area (device memory) and
+// only the others from the host.
 #include "fasa_device.hpp"
 #include "fasa_internal.hpp"
 
@@ -37,6 +45,12 @@ struct MArgs {
   void* stage_k;            // gather: device staging
   void* stage_v;
   int nd_stride;            // elements per k_nd row
+  // Gather with reuse: the previous selection and its rows in the prefetch area.
+  const int32_t* prev_idx;  // [b][H_kv][cap], ascending
+  const int32_t* prev_count;
+  const void* pf_k;         // [b][H_kv][cap][128], row p = token prev_idx[p]
+  const void* pf_v;
+  int32_t* hits;            // nullable: rows taken from the prefetch area, added per unit
 };
 
 // Raw element of the cache type.
@@ -124,7 +138,11 @@ __global__ __launch_bounds__(256) void fasam_offload_kernel(MArgs a) {
 // channels straight into registers (16-byte pieces too: host reads are not
 // cached, so every piece is one transfer), its dominant pairs from the slab;
 // the full key row is then written in channel order.
-template <typename T>
+// REUSE: the gather with reuse (see the head of the file): the previous
+// selection (at most kPrevLds entries) is staged in LDS and searched for each
+// row's token; a row found there is copied from the prefetch area.
+constexpr int kPrevLds = 8192;
+template <typename T, bool REUSE>
 __global__ __launch_bounds__(256) void fasam_gather_kernel(MArgs a) {
   typedef typename Bits<T>::type E;
   constexpr int EPL = 8;                                   // channels per lane
@@ -137,6 +155,7 @@ __global__ __launch_bounds__(256) void fasam_gather_kernel(MArgs a) {
   __shared__ int dom_f[64];
   __shared__ int nd_pos[kHeadDim];
   __shared__ __align__(16) E nd[16 * kHeadDim];
+  __shared__ int prev_s[REUSE ? kPrevLds : 1];
   column_map(c, a.fc_idx, g, dom_f, nd_pos);
 
   int count = a.sel_count[unit];
@@ -148,20 +167,55 @@ __global__ __launch_bounds__(256) void fasam_gather_kernel(MArgs a) {
   const int s = j & (kBlock - 1);
   const int64_t hrow = (pb * c.n_kv_heads + g) * kBlock + s;
 
+  // REUSE: where the row's token sits in the previous selection, or -1.
+  int hit = -1;
+  if constexpr (REUSE) {
+    int np = a.prev_count[unit];
+    np = np < 0 ? 0 : (np > c.cap ? c.cap : np);
+    for (int k = threadIdx.x; k < np; k += 256) prev_s[k] = a.prev_idx[unit * c.cap + k];
+    __syncthreads();                                        // the list (and the column map)
+    int lo = 0, hi = np;                                    // first position with prev_s[pos] >= j
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (prev_s[mid] < j) lo = mid + 1;
+      else hi = mid;
+    }
+    hit = (live && lo < np && prev_s[lo] == j) ? lo : -1;
+    if (a.hits != nullptr) {
+      const uint64_t m = __ballot(hit >= 0 && lane == 0);
+      if ((threadIdx.x & 63) == 0 && m != 0u) atomicAdd(&a.hits[unit], int32_t(__popcll(m)));
+    }
+  }
+  const bool from_host = live && hit < 0;
+
   // Host reads: this row's non-dominant pieces (lane l takes pieces l, l + 16)
-  // and the lane's value channels.
+  // and the lane's value channels.  A row found in the prefetch area reads its
+  // whole key and value rows from there instead.
   const int nd_pieces = a.nd_stride * int(sizeof(E)) / 16;
   const uint4* knd = reinterpret_cast<const uint4*>(static_cast<const E*>(a.k_nd) + hrow * a.nd_stride);
   const uint4* vh = reinterpret_cast<const uint4*>(static_cast<const E*>(a.v_host) + hrow * kHeadDim + EPL * lane);
-  uint4 piece[LP], vx[LP];
+  uint4 piece[LP], vx[LP], pk[LP];
 #pragma unroll
   for (int k = 0; k < LP; ++k) {
     const int pc = lane + 16 * k;
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    piece[k] = (live && pc < nd_pieces) ? knd[pc] : z;
-    vx[k] = live ? vh[k] : z;
+    piece[k] = (from_host && pc < nd_pieces) ? knd[pc] : z;
+    vx[k] = from_host ? vh[k] : z;
+    pk[k] = z;
   }
-  __syncthreads();                                          // the column map
+  if constexpr (REUSE) {
+    if (hit >= 0) {
+      const int64_t prow = (unit * c.cap + hit) * int64_t(kHeadDim) + EPL * lane;
+      const uint4* fk = reinterpret_cast<const uint4*>(static_cast<const E*>(a.pf_k) + prow);
+      const uint4* fv = reinterpret_cast<const uint4*>(static_cast<const E*>(a.pf_v) + prow);
+#pragma unroll
+      for (int k = 0; k < LP; ++k) {
+        pk[k] = fk[k];
+        vx[k] = fv[k];
+      }
+    }
+  }
+  if constexpr (!REUSE) __syncthreads();                    // the column map
   // Dominant pairs of the lane's 4 FC pairs, from the slab (device; indexed by
   // the sequence and the logical block).
   const E* sl = static_cast<const E*>(a.slab) + (int64_t(b) * c.max_blocks + (j >> 8)) * c.slab_block_stride +
@@ -170,7 +224,7 @@ __global__ __launch_bounds__(256) void fasam_gather_kernel(MArgs a) {
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     const int f = dom_f[(EPL * lane + e) >> 1];
-    dv[e] = (live && f >= 0) ? sl[int64_t(f) * kSlabFcStride + (e & 1)] : E(0);
+    dv[e] = (from_host && f >= 0) ? sl[int64_t(f) * kSlabFcStride + (e & 1)] : E(0);
   }
 #pragma unroll
   for (int k = 0; k < LP; ++k) {
@@ -185,6 +239,10 @@ __global__ __launch_bounds__(256) void fasam_gather_kernel(MArgs a) {
   for (int e = 0; e < EPL; ++e) {
     const int ch = EPL * lane + e;
     ke[e] = dom_f[ch >> 1] >= 0 ? dv[e] : nd[i * kHeadDim + nd_pos[ch]];
+  }
+  if (hit >= 0) {
+#pragma unroll
+    for (int k = 0; k < LP; ++k) kx[k] = pk[k];
   }
   const int64_t row = (unit * c.cap + r) * int64_t(kHeadDim) + EPL * lane;
   uint4* sk = reinterpret_cast<uint4*>(static_cast<E*>(a.stage_k) + row);
@@ -217,14 +275,24 @@ hipError_t launch_m_offload(const Common& c, const void* k_pool, const void* v_p
 
 hipError_t launch_m_gather(const Common& c, const void* k_nd, const void* v_host, const void* slab,
                            const int32_t* block_table, const int32_t* fc_idx, const int32_t* sel_idx,
-                           const int32_t* sel_count, void* stage_k, void* stage_v, hipStream_t s) {
+                           const int32_t* sel_count, void* stage_k, void* stage_v, const MReuse& reuse,
+                           hipStream_t s) {
   if (c.cap == 0) return hipSuccess;
   MArgs a{c, nullptr, nullptr, block_table, nullptr, fc_idx, const_cast<void*>(k_nd), const_cast<void*>(v_host),
-          slab, sel_idx, sel_count, stage_k, stage_v, m_nd_stride(c)};
+          slab, sel_idx, sel_count, stage_k, stage_v, m_nd_stride(c),
+          reuse.prev_idx, reuse.prev_count, reuse.pf_k, reuse.pf_v, reuse.hits};
   const dim3 grid((c.cap + 15) / 16, c.n_kv_heads, c.batch);
-  if (c.bf16) hipLaunchKernelGGL(fasam_gather_kernel<uint16_t>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(fasam_gather_kernel<float>, grid, dim3(256), 0, s, a);
+  const bool re = reuse.prev_idx != nullptr && m_reuses(c);
+  if (c.bf16) {
+    if (re) hipLaunchKernelGGL((fasam_gather_kernel<uint16_t, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((fasam_gather_kernel<uint16_t, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (re) hipLaunchKernelGGL((fasam_gather_kernel<float, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((fasam_gather_kernel<float, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
+
+bool m_reuses(const Common& c) { return c.cap <= kPrevLds; }
 
 }  // namespace fasa

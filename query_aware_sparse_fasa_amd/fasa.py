@@ -28,7 +28,8 @@ EXPORTS = ["fasa_status_str", "fasa_validate_shape", "fasa_selection_capacity",
            "fasa_tip", "fasa_topk", "fasa_fac", "fasa_decode", "fasa_decode_tip", "fasa_decode_rest",
            "fasa_dense_workspace_size",
            "fasa_dense_decode", "fasa_m_host_sizes", "fasa_m_offload", "fasa_m_workspace_size",
-           "fasa_m_decode", "fasa_ca_workspace_size", "fasa_ca_hits", "fasa_ca_dominant",
+           "fasa_m_decode", "fasa_m_decode_select", "fasa_m_prefetch", "fasa_m_decode_finish",
+           "fasa_ca_workspace_size", "fasa_ca_hits", "fasa_ca_dominant",
            "fasa_scratch_capacity", "fasa_decode_scratch"]
 
 
@@ -93,6 +94,10 @@ def lib() -> ctypes.CDLL:
         "fasa_m_decode": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                                          ctypes.c_size_t, _P]),
         "fasa_ca_workspace_size": (ctypes.c_int, [_S, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+        "fasa_m_decode_select": (ctypes.c_int, [_S, _P, _P, _P, _P, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+        "fasa_m_prefetch": (ctypes.c_int, [_S, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _P, ctypes.c_size_t, _P]),
+        "fasa_m_decode_finish": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _P, _P, _P,
+                                                ctypes.c_size_t, _P]),
         "fasa_ca_hits": (ctypes.c_int, [_S, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P]),
         "fasa_ca_dominant": (ctypes.c_int, [_S, _P, _I32, _I32, _P, _P]),
         "fasa_scratch_capacity": (ctypes.c_size_t, []),
@@ -334,6 +339,44 @@ def fasa_m_decode(shape, q, slab, k_nd_host, v_host, block_table, seq_lens, max_
     _check(lib().fasa_m_decode(ctypes.byref(shape), _ptr(q), _ptr(slab), _host_ptr(k_nd_host), _host_ptr(v_host),
                                _ptr(block_table), _ptr(seq_lens), max_t, _ptr(fc_idx), _ptr(out), _ptr(sel_idx),
                                _ptr(sel_count), _ptr(workspace), nbytes, _stream(stream)), "fasa_m_decode")
+
+
+def fasa_m_decode_select(shape, q, slab, block_table, seq_lens, max_t, fc_idx, sel_idx, sel_count, workspace,
+                         stream=None) -> None:
+    """FASA-M stage 1: TIP on the slab and the exact top-B."""
+    _need(sel_idx, torch.int32, "sel_idx")
+    _need(sel_count, torch.int32, "sel_count")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fasa_m_decode_select(ctypes.byref(shape), _ptr(q), _ptr(slab), _ptr(block_table), _ptr(seq_lens),
+                                      max_t, _ptr(fc_idx), _ptr(sel_idx), _ptr(sel_count), _ptr(workspace), nbytes,
+                                      _stream(stream)), "fasa_m_decode_select")
+
+
+def fasa_m_prefetch(shape, slab, k_nd_host, v_host, block_table, max_t, fc_idx, prev_sel_idx, prev_sel_count,
+                    parity, workspace, stream=None) -> None:
+    """The rows of a previous selection into row area 1 - parity, for a step of that parity."""
+    _need(prev_sel_idx, torch.int32, "prev_sel_idx")
+    _need(prev_sel_count, torch.int32, "prev_sel_count")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fasa_m_prefetch(ctypes.byref(shape), _ptr(slab), _host_ptr(k_nd_host), _host_ptr(v_host),
+                                 _ptr(block_table), max_t, _ptr(fc_idx), _ptr(prev_sel_idx), _ptr(prev_sel_count),
+                                 parity, _ptr(workspace), nbytes, _stream(stream)), "fasa_m_prefetch")
+
+
+def fasa_m_decode_finish(shape, q, slab, k_nd_host, v_host, block_table, max_t, fc_idx, prev_sel_idx,
+                         prev_sel_count, sel_idx, sel_count, parity, out, workspace, hits=None, stream=None) -> None:
+    """FASA-M stage 2: rows into row area `parity` (the previous selection's from the other area), then FAC."""
+    _need(out, torch.float32, "out")
+    _need(sel_idx, torch.int32, "sel_idx")
+    _need(sel_count, torch.int32, "sel_count")
+    _need(prev_sel_idx, torch.int32, "prev_sel_idx")
+    _need(prev_sel_count, torch.int32, "prev_sel_count")
+    _need(hits, torch.int32, "hits")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fasa_m_decode_finish(ctypes.byref(shape), _ptr(q), _ptr(slab), _host_ptr(k_nd_host),
+                                      _host_ptr(v_host), _ptr(block_table), max_t, _ptr(fc_idx), _ptr(prev_sel_idx),
+                                      _ptr(prev_sel_count), _ptr(sel_idx), _ptr(sel_count), parity, _ptr(out),
+                                      _ptr(hits), _ptr(workspace), nbytes, _stream(stream)), "fasa_m_decode_finish")
 
 
 def fasa_ca_workspace_size(shape: fasa_shape, max_t: int, k_top: int) -> int:

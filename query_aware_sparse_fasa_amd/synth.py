@@ -239,6 +239,23 @@ def make_inputs(cfg: Config, seed: int = 0, device="cpu", seq_lens=None,
                   v_pool=v_pool)
 
 
+def drifting_queries(q: torch.Tensor, n_steps: int, rho: float = 0.9, seed: int = 0) -> list:
+    """Queries of n_steps consecutive decode steps that change every step:
+    q_0 = q, q_{n+1} = rho q_n + sqrt(1 - rho^2) z_n, where z_n is Gaussian noise
+    with the per-channel standard deviation of q (over sequences and heads),
+    drawn from a seeded generator on q's device; rounded to q's dtype.  rho
+    sets how much consecutive selections overlap."""
+    gen = torch.Generator(device=q.device).manual_seed(0x5EED + seed)
+    sd = q.float().std(dim=(0, 1), keepdim=True)
+    out = [q.clone()]
+    cur = q.float()
+    for _ in range(n_steps - 1):
+        z = torch.randn(q.shape, generator=gen, device=q.device, dtype=torch.float32) * sd
+        cur = rho * cur + math.sqrt(1.0 - rho * rho) * z
+        out.append(cur.to(q.dtype))
+    return out
+
+
 def random_scores(n_units: int, max_t: int, kind: str, seed: int = 0) -> np.ndarray:
     """Seeded fp32 score rows [n_units][max_t] for exercising the top-B select alone.
 

@@ -100,6 +100,23 @@ class DeviceLayer:
         fasa.fasa_m_decode(self.shape, self.q, self.slab, self.m_knd, self.m_v, self.block_table, self.seq_lens,
                            self.max_t, self.fc_idx, self.m_out, self.m_sel_idx, self.m_sel_count, self.m_ws, stream)
 
+    def m_select(self, q=None, sel_idx=None, sel_count=None, stream=None):
+        fasa.fasa_m_decode_select(self.shape, self.q if q is None else q, self.slab, self.block_table, self.seq_lens,
+                                  self.max_t, self.fc_idx, self.m_sel_idx if sel_idx is None else sel_idx,
+                                  self.m_sel_count if sel_count is None else sel_count, self.m_ws, stream)
+
+    def m_prefetch(self, prev_sel_idx, prev_sel_count, parity, stream=None):
+        fasa.fasa_m_prefetch(self.shape, self.slab, self.m_knd, self.m_v, self.block_table, self.max_t, self.fc_idx,
+                             prev_sel_idx, prev_sel_count, parity, self.m_ws, stream)
+
+    def m_finish(self, prev_sel_idx, prev_sel_count, parity, q=None, sel_idx=None, sel_count=None, hits=None,
+                 stream=None):
+        fasa.fasa_m_decode_finish(self.shape, self.q if q is None else q, self.slab, self.m_knd, self.m_v,
+                                  self.block_table, self.max_t, self.fc_idx, prev_sel_idx, prev_sel_count,
+                                  self.m_sel_idx if sel_idx is None else sel_idx,
+                                  self.m_sel_count if sel_count is None else sel_count, parity, self.m_out,
+                                  self.m_ws, hits, stream)
+
     # -- host copies ----------------------------------------------------------------
     def selection(self, b: int, g: int) -> np.ndarray:
         n = int(self.sel_count[b, g].item())

@@ -23,7 +23,7 @@ def header_functions():
 def test_exports_every_declared_symbol():
     L = fasa.lib()
     names = header_functions()
-    assert len(names) == 24, names
+    assert len(names) == 27, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(fasa.EXPORTS) == names
@@ -216,6 +216,23 @@ def test_fasa_m_sizes_and_rejections():
     bad = list(args)
     bad[3] = FAKE + 4                           # misaligned host array
     assert raw("fasa_m_decode", *bad) == E
+    # the stages of the prefetching step
+    W = fasa.FASA_ERR_WORKSPACE
+    sel = [sp, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, mws, None]
+    assert raw("fasa_m_decode_select", *sel[:1], None, *sel[2:]) == E           # q
+    assert raw("fasa_m_decode_select", *sel[:5], -1, *sel[6:]) == E              # max_t
+    assert raw("fasa_m_decode_select", *sel[:10], mws - 1, None) == W
+    pf = [sp, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, 1, FAKE, mws, None]
+    assert raw("fasa_m_prefetch", *pf[:2], None, *pf[3:]) == E                  # k_nd
+    assert raw("fasa_m_prefetch", *pf[:8], None, *pf[9:]) == E                  # prev_sel_count
+    assert raw("fasa_m_prefetch", *pf[:2], FAKE + 4, *pf[3:]) == E              # misaligned host array
+    assert raw("fasa_m_prefetch", *pf[:9], 2, *pf[10:]) == E                    # parity
+    fin = [sp, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, mws, None]
+    assert raw("fasa_m_decode_finish", *fin[:9], None, *fin[10:]) == E          # prev count without list
+    assert raw("fasa_m_decode_finish", *fin[:8], None, None, *fin[10:]) == E    # hits without a previous list
+    assert raw("fasa_m_decode_finish", *fin[:13], None, *fin[14:]) == E         # out
+    assert raw("fasa_m_decode_finish", *fin[:6], -1, *fin[7:]) == E             # max_t
+    assert raw("fasa_m_decode_finish", *fin[:12], -1, *fin[13:]) == E           # parity
 
 
 def test_ca_sizes_and_rejections():

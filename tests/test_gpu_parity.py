@@ -322,11 +322,14 @@ def test_fac_skips_entries_outside_the_cache(dtype):
 # ------------------------------------------------------------------------ whole step
 def _check_decode(inp, L, units, label, m=False):
     """Selections and outputs of the last fasa_decode (m: fasa_m_decode) on L."""
-    cfg = inp.cfg
     torch.cuda.synchronize()
-    out = (L.m_out if m else L.out).cpu().numpy()
-    sel = (L.m_sel_idx if m else L.sel_idx).cpu().numpy()
-    cnt = (L.m_sel_count if m else L.sel_count).cpu().numpy()
+    return _check_arrays(inp, L, L.m_out if m else L.out, L.m_sel_idx if m else L.sel_idx,
+                         L.m_sel_count if m else L.sel_count, units, label)
+
+
+def _check_arrays(inp, L, out, sel, cnt, units, label):
+    cfg = inp.cfg
+    out, sel, cnt = out.cpu().numpy(), sel.cpu().numpy(), cnt.cpu().numpy()
     G = cfg.group
     same = 0
     for (b, g), (q, K, V, r) in units.items():
@@ -540,6 +543,75 @@ def test_m_decode(name):
     cap = L.cap
     assert torch.equal(L.m_sel_idx[..., :cap], L.sel_idx[..., :cap])
     _check_decode(inp, L, oracle_units(inp), name + " fasa-m", m=True)
+
+
+@pytest.mark.parametrize("mode", ["resident", "prefetch"])
+@pytest.mark.parametrize("name", ["c2-ragged", "c5-ragged", "fp32-gqa4", "g2-f1-sink"])
+def test_m_reuse_consecutive_steps(name, mode):
+    """FASA-M over four consecutive steps whose query changes every step (each
+    query 0.9 times the last plus fresh noise), the rows of the previous
+    selection reused: left in the workspace by the previous step (resident), or
+    -- with the whole workspace overwritten before every step -- brought back by
+    fasa_m_prefetch on a second stream while the step selects (prefetch).
+    Every step against the oracle, bit for bit against fasa_m_decode of the
+    same query (on a workspace of its own), and the reused rows equal to the
+    overlap of consecutive selections."""
+    import dataclasses
+    cfg = SMALL[name]
+    say(f"[fasa-m reuse] {name} {mode}")
+    inp = synth.make_inputs(cfg, seed=3, device="cuda")
+    L = DeviceLayer(inp)
+    L.m_setup()
+    ref_ws = torch.zeros_like(L.m_ws)
+    ref = (torch.zeros_like(L.m_out), torch.zeros_like(L.m_sel_idx), torch.zeros_like(L.m_sel_count))
+    qs = synth.drifting_queries(L.q.clone(), 4, rho=0.9, seed=1)
+    sels = [(torch.full_like(L.m_sel_idx, -7), torch.full_like(L.m_sel_count, -7)) for _ in range(2)]
+    hits = torch.zeros_like(L.m_sel_count)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    total_hits = total_rows = 0
+    for n, q in enumerate(qs):
+        par = n % 2
+        cur = sels[par]
+        prev = sels[1 - par] if n > 0 else None
+        hits.zero_()
+        L.m_out.fill_(float("nan"))
+        if mode == "prefetch":
+            L.m_ws.fill_(0xFF)
+        fork = torch.cuda.Event()
+        fork.record(main)
+        side.wait_event(fork)
+        if prev is not None and mode == "prefetch":
+            L.m_prefetch(prev[0], prev[1], par, stream=side)
+        L.m_select(q=q, sel_idx=cur[0], sel_count=cur[1], stream=main)
+        join = torch.cuda.Event()
+        join.record(side)
+        main.wait_event(join)
+        if prev is not None:
+            L.m_finish(prev[0], prev[1], par, q=q, sel_idx=cur[0], sel_count=cur[1], hits=hits, stream=main)
+        else:
+            L.m_finish(None, None, par, q=q, sel_idx=cur[0], sel_count=cur[1], stream=main)
+        torch.cuda.synchronize()
+        got = (L.m_out.clone(), cur[0].clone(), cur[1].clone())
+        inp_n = dataclasses.replace(inp, q=q)
+        _check_arrays(inp_n, L, *got, oracle_units(inp_n), f"{name} {mode} step {n}")
+        fasa.fasa_m_decode(L.shape, q, L.slab, L.m_knd, L.m_v, L.block_table, L.seq_lens, L.max_t, L.fc_idx,
+                           ref[0], ref[1], ref[2], ref_ws)
+        torch.cuda.synchronize()
+        assert torch.equal(ref[0], got[0]) and torch.equal(ref[2], got[2]), (name, mode, n)
+        assert torch.equal(ref[1][..., :L.cap], got[1][..., :L.cap]), (name, mode, n)
+        if prev is not None:
+            h = hits.cpu().numpy()
+            c_sel, c_cnt = got[1].cpu().numpy(), got[2].cpu().numpy()
+            p_sel, p_cnt = prev[0].cpu().numpy(), prev[1].cpu().numpy()
+            for b in range(cfg.batch):
+                for g in range(cfg.n_kv_heads):
+                    both = np.intersect1d(c_sel[b, g, :c_cnt[b, g]], p_sel[b, g, :p_cnt[b, g]])
+                    assert h[b, g] == len(both), (name, n, b, g, h[b, g], len(both))
+            total_hits += int(h.sum())
+            total_rows += int(got[2].sum().item())
+    say(f"  {total_hits} of {total_rows} rows of steps 1-3 reused")
+    assert total_hits > 0
 
 
 def test_m_decode_full_size_8b_layer():
