@@ -7,8 +7,11 @@
 // I_dom; keys are cached after RoPE, so each alpha^(i) entry is the FC-i dot
 // product of the post-RoPE vectors, section 3.4 "RoPE from a Frequency-Chunk
 // Perspective").  The score is linear in q, so the G query heads of the group
-// are first summed per dominant column (the "folded" query, 2F fp32 values);
-// each token then costs 2F fused multiply-adds on 2F cache elements.
+// are first summed per dominant column (the "folded" query, 2F fp32 values, a
+// wave reduction in wave 0: a few heads per lane, then butterfly shuffles
+// across the lanes of a column -- measured level with a per-thread serial sum
+// over all heads at 1-8 sequences and 1.3 us faster at 64); each token then
+// costs 2F fused multiply-adds on 2F cache elements.
 //
 // Mapping (gfx950, wave64): one workgroup = 4 waves = 4 cache blocks of one
 // (b, g) = one 1024-token chunk; lane l of a wave owns tokens 4l..4l+3 of its
@@ -56,6 +59,13 @@ struct TipArgs {
   uint2* meta;          // [units][emit chunks] chunk summary: (emit_word, tau) (kTipEmit)
 };
 
+// Column slots of the query fold for F dominant FCs: 2F rounded up to a power of two.
+__host__ __device__ constexpr int fold_slots(int F) {
+  int p = 2;
+  while (p < 2 * F) p <<= 1;
+  return p;
+}
+
 // FT > 0: compile-time F (all loads of a block issued back to back); FT == 0: runtime F.
 template <typename T, int FT, bool FROM_SLAB, int MODE>
 __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
@@ -70,16 +80,17 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
   const int blk = wg.x * 4 + wave;
   const int64_t unit = int64_t(b) * c.n_kv_heads + g;
 
-  // Independent loads: (sequence length, FC index, the slab), then the query
-  // loads, which depend on the FC index only; the fold waits for the query
-  // values while the slab stream is in flight.  The row-gather path also needs
-  // the block-table entry before its key loads.
+  // Independent loads: (sequence length, the slab), then (wave 0) the FC
+  // indices and the query values the fold needs; the fold waits for them while
+  // the slab stream is in flight.  The row-gather path also needs the
+  // block-table entry before its key loads.
   const int e = threadIdx.x;
-  const int ec = e < 2 * F ? e : 0;
-  const int f_q = ec >> 1, comp = ec & 1;
   const int t_raw = a.seq_lens[b];
-  const int fi = a.fc_idx[g * F + f_q];          // < 0: unused slot (a head with fewer FCs)
-  const int col = 2 * (fi < 0 ? 0 : fi) + comp;
+  // The fold's column slots (used by wave 0; see below): P = 2F rounded up to
+  // a power of two; a lane's first slot and its FC index.
+  const int P = fold_slots(F);
+  const int sl0 = P <= 64 ? (lane & (P - 1)) : lane;
+  const int fi0 = sl0 < 2 * F ? a.fc_idx[g * F + (sl0 >> 1)] : -1;
   const int blk_c = min(blk, c.max_blocks - 1);
   Raw8<T> x[FROM_SLAB && FT > 0 ? FT : 1];
   const T* sbase = static_cast<const T*>(a.src) + (int64_t(b) * c.max_blocks + blk_c) * c.slab_block_stride +
@@ -105,20 +116,36 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
   const bool live = blk * kBlock < t;          // wave-uniform
   const int64_t phys = live ? phys_raw : 0;
 
-  const T* qh = static_cast<const T*>(a.q) +
-                (int64_t(b) * c.n_q_heads + int64_t(g) * c.group) * kHeadDim + col;
-  T qv[16];
+  if (wave == 0) {
+    // Folded query, summed over the group's query heads by a wave reduction:
+    // column slot sl = 2f + comp (column 2 I_g[f] + comp) of P slots, P = 2F
+    // rounded up to a power of two.  With P <= 64, lane l takes slot l % P and
+    // heads l / P, l / P + 64 / P, ...; the 64 / P lanes of a slot then add
+    // their sums with butterfly shuffles.  With P = 128 (F > 32) a lane takes
+    // slots l and l + 64 and all the heads.  Slots past 2F, and unused FC
+    // slots (index < 0, a head with fewer FCs), contribute nothing.
+    const T* qg = static_cast<const T*>(a.q) + (int64_t(b) * c.n_q_heads + int64_t(g) * c.group) * kHeadDim;
+    // Heads per lane: at most NH (known when F is), loads clamped to the group
+    // and issued together, terms past the group masked to +0.
+    constexpr int NH = FT > 0 ? (16 + 64 / fold_slots(FT) - 1) / (64 / fold_slots(FT)) : 16;
+    const int hs = P <= 64 ? 64 / P : 1;
+    const int per = P <= 64 ? 1 : 2;
+    for (int k = 0; k < per; ++k) {
+      const int sl = k == 0 ? sl0 : lane + 64;
+      const int fi = k == 0 ? fi0 : (sl < 2 * F ? a.fc_idx[g * F + (sl >> 1)] : -1);
+      const int col = 2 * (fi < 0 ? 0 : fi) + (sl & 1);
+      const int h0 = P <= 64 ? lane / P : 0;
+      T qv[NH];
 #pragma unroll
-  for (int h = 0; h < 16; ++h) qv[h] = qh[min(h, c.group - 1) * kHeadDim];
-  {
-    // Folded query: thread e < 2F sums column 2 I_g[f] + comp over the group's
-    // heads in head order (terms past the group are masked to +0).
-    float s = 0.f;
+      for (int u = 0; u < NH; ++u) qv[u] = qg[min(h0 + u * hs, c.group - 1) * kHeadDim + col];
+      float s = 0.f;
 #pragma unroll
-    for (int h = 0; h < 16; ++h) s += (h < c.group) ? to_f32(qv[h]) : 0.f;
-    if (e < 2 * F) {
-      qf[e] = fi < 0 ? 0.f : s;                  // an unused slot scores nothing
-      if (comp == 0) cols[f_q] = col;
+      for (int u = 0; u < NH; ++u) s += (h0 + u * hs < c.group) ? to_f32(qv[u]) : 0.f;
+      for (int o = P; o < 64; o <<= 1) s += __shfl_xor(s, o, 64);
+      if ((P <= 64 ? lane : sl) < 2 * F && (P > 64 || lane < P)) {
+        qf[sl] = fi < 0 ? 0.f : s;
+        if ((sl & 1) == 0) cols[sl >> 1] = col;
+      }
     }
   }
   __syncthreads();
