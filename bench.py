@@ -445,12 +445,15 @@ def main():
         sel_rows = sb["rows"] // (2 * 128 * e)
         host_bytes = sel_rows * (nd + 128) * e
         t_all = int(inp.seq_lens.sum())
-        # slab + the two row areas (the step's staged rows and the previous step's)
-        gpu_m = t_all * cfg.n_kv_heads * 2 * cfg.n_fc * e + 2 * sel_rows * 2 * 128 * e
+        # slab + the step's staged rows; keeping the previous step's rows adds one more row area
+        gpu_m = t_all * cfg.n_kv_heads * 2 * cfg.n_fc * e + sel_rows * 2 * 128 * e
+        gpu_m_resident = gpu_m + sel_rows * 2 * 128 * e
         gpu_fkv = t_all * cfg.n_kv_heads * 2 * 128 * e
         fasa_m = {"us_per_step": t_m * 1e6, "host_bytes_per_step": int(host_bytes),
                   "host_GBps": host_bytes / t_m / 1e9, "gpu_cache_bytes": int(gpu_m),
                   "fkv_cache_bytes": int(gpu_fkv), "gpu_memory_reduction": gpu_fkv / gpu_m,
+                  "gpu_cache_bytes_resident_rows": int(gpu_m_resident),
+                  "gpu_memory_reduction_resident_rows": gpu_fkv / gpu_m_resident,
                   "layers_rotated": len(m_layers)}
         fasa_m["reuse"] = time_m_reuse(torch, synth, stream, m_layers, nd, e)
         log(f"[bench] FASA-M step {t_m * 1e6:.2f} us ({host_bytes / 1e6:.2f} MB from host, "
