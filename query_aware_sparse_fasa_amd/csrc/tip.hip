@@ -40,6 +40,11 @@
 //               whole scores row).  (An exact k-th largest found by ballot
 //               binary searches, 32 dependent rounds per wave, measured 10 us
 //               slower per launch than this LDS histogram.)
+// One chunk per workgroup: workgroups that walked 2-8 chunks of a unit, with
+// the next chunk's slab loads in flight during the current one's arithmetic and
+// one histogram flush at the end (91-178 VGPRs), streamed slower than these
+// light workgroups (56 VGPRs, many resident per CU): TIP 51.8 -> 54.0 us at
+// batch 16, 15.1 -> 15.4 us at 128K tokens, 224 -> 260 us on the ragged batch.
 #include "fasa_device.hpp"
 #include "fasa_internal.hpp"
 
@@ -64,6 +69,63 @@ __host__ __device__ constexpr int fold_slots(int F) {
   int p = 2;
   while (p < 2 * F) p <<= 1;
   return p;
+}
+
+// Folded query of unit (b, g) into qf[0..2F) and cols[0..F), summed over the
+// group's query heads by a wave reduction (run by wave 0): column slot
+// sl = 2f + comp (column 2 I_g[f] + comp) of P slots, P = 2F rounded up to a
+// power of two.  With P <= 64, lane l takes slot l % P and heads l / P,
+// l / P + 64 / P, ...; the 64 / P lanes of a slot then add their sums with
+// butterfly shuffles.  With P = 128 (F > 32) a lane takes slots l and l + 64 and
+// all the heads.  Slots past 2F, and unused FC slots (index < 0, a head with
+// fewer FCs), contribute nothing.  sl0 / fi0: the lane's first slot and its FC
+// index, loaded by the caller at kernel entry.
+template <typename T, int FT>
+__device__ __forceinline__ void fold_query(const TipArgs& a, int b, int g, int F, int P, int sl0, int fi0,
+                                           float* qf, int* cols) {
+  const Common& c = a.c;
+  const int lane = threadIdx.x & 63;
+  const T* qg = static_cast<const T*>(a.q) + (int64_t(b) * c.n_q_heads + int64_t(g) * c.group) * kHeadDim;
+  // Heads per lane: at most NH (known when F is), loads clamped to the group
+  // and issued together, terms past the group masked to +0.
+  constexpr int NH = FT > 0 ? (16 + 64 / fold_slots(FT) - 1) / (64 / fold_slots(FT)) : 16;
+  const int hs = P <= 64 ? 64 / P : 1;
+  const int per = P <= 64 ? 1 : 2;
+  for (int k = 0; k < per; ++k) {
+    const int sl = k == 0 ? sl0 : lane + 64;
+    const int fi = k == 0 ? fi0 : (sl < 2 * F ? a.fc_idx[g * F + (sl >> 1)] : -1);
+    const int col = 2 * (fi < 0 ? 0 : fi) + (sl & 1);
+    const int h0 = P <= 64 ? lane / P : 0;
+    T qv[NH];
+#pragma unroll
+    for (int u = 0; u < NH; ++u) qv[u] = qg[min(h0 + u * hs, c.group - 1) * kHeadDim + col];
+    float s = 0.f;
+#pragma unroll
+    for (int u = 0; u < NH; ++u) s += (h0 + u * hs < c.group) ? to_f32(qv[u]) : 0.f;
+    for (int o = P; o < 64; o <<= 1) s += __shfl_xor(s, o, 64);
+    if ((P <= 64 ? lane : sl) < 2 * F && (P > 64 || lane < P)) {
+      qf[sl] = fi < 0 ? 0.f : s;
+      if ((sl & 1) == 0) cols[sl >> 1] = col;
+    }
+  }
+}
+
+// Adds a lane's 4 consecutive tokens j0 .. j0+3 (candidates in [c_lo, c_hi)
+// only) to the LDS histogram of coarse key bins; equal bins are merged first.
+__device__ __forceinline__ void hist_add4(uint32_t* hist_s, const float (&acc)[4], int j0, bool live, int c_lo,
+                                          int c_hi) {
+  uint32_t run_bin = 0u, run_cnt = 0u;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int j = j0 + r;
+    const bool act = live && j >= c_lo && j < c_hi;
+    const uint32_t bin = score_key(acc[r]) >> kHistShift;
+    const bool brk = act && bin != run_bin;
+    if (brk && run_cnt != 0u) atomicAdd(&hist_s[run_bin], run_cnt);
+    run_cnt = brk ? 1u : run_cnt + (act ? 1u : 0u);
+    run_bin = brk ? bin : run_bin;
+  }
+  if (run_cnt != 0u) atomicAdd(&hist_s[run_bin], run_cnt);
 }
 
 // FT > 0: compile-time F (all loads of a block issued back to back); FT == 0: runtime F.
@@ -116,38 +178,7 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
   const bool live = blk * kBlock < t;          // wave-uniform
   const int64_t phys = live ? phys_raw : 0;
 
-  if (wave == 0) {
-    // Folded query, summed over the group's query heads by a wave reduction:
-    // column slot sl = 2f + comp (column 2 I_g[f] + comp) of P slots, P = 2F
-    // rounded up to a power of two.  With P <= 64, lane l takes slot l % P and
-    // heads l / P, l / P + 64 / P, ...; the 64 / P lanes of a slot then add
-    // their sums with butterfly shuffles.  With P = 128 (F > 32) a lane takes
-    // slots l and l + 64 and all the heads.  Slots past 2F, and unused FC
-    // slots (index < 0, a head with fewer FCs), contribute nothing.
-    const T* qg = static_cast<const T*>(a.q) + (int64_t(b) * c.n_q_heads + int64_t(g) * c.group) * kHeadDim;
-    // Heads per lane: at most NH (known when F is), loads clamped to the group
-    // and issued together, terms past the group masked to +0.
-    constexpr int NH = FT > 0 ? (16 + 64 / fold_slots(FT) - 1) / (64 / fold_slots(FT)) : 16;
-    const int hs = P <= 64 ? 64 / P : 1;
-    const int per = P <= 64 ? 1 : 2;
-    for (int k = 0; k < per; ++k) {
-      const int sl = k == 0 ? sl0 : lane + 64;
-      const int fi = k == 0 ? fi0 : (sl < 2 * F ? a.fc_idx[g * F + (sl >> 1)] : -1);
-      const int col = 2 * (fi < 0 ? 0 : fi) + (sl & 1);
-      const int h0 = P <= 64 ? lane / P : 0;
-      T qv[NH];
-#pragma unroll
-      for (int u = 0; u < NH; ++u) qv[u] = qg[min(h0 + u * hs, c.group - 1) * kHeadDim + col];
-      float s = 0.f;
-#pragma unroll
-      for (int u = 0; u < NH; ++u) s += (h0 + u * hs < c.group) ? to_f32(qv[u]) : 0.f;
-      for (int o = P; o < 64; o <<= 1) s += __shfl_xor(s, o, 64);
-      if ((P <= 64 ? lane : sl) < 2 * F && (P > 64 || lane < P)) {
-        qf[sl] = fi < 0 ? 0.f : s;
-        if ((sl & 1) == 0) cols[sl >> 1] = col;
-      }
-    }
-  }
+  if (wave == 0) fold_query<T, FT>(a, b, g, F, P, sl0, fi0, qf, cols);
   __syncthreads();
   if (!LDS_HIST && !live) return;              // otherwise every wave reaches the later barriers
 
@@ -210,22 +241,10 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
     }
   }
   if constexpr (HIST) {
-    // Candidates exclude the forced tokens [0, c_lo) and [c_hi, t).  A lane's 4
-    // tokens are consecutive: equal bins are merged before the LDS add.
+    // Candidates exclude the forced tokens [0, c_lo) and [c_hi, t).
     const int c_lo = min(c.n_sink, t);
     const int c_hi = max(c_lo, t - c.n_recent);
-    uint32_t run_bin = 0u, run_cnt = 0u;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = j0 + r;
-      const bool act = live && j >= c_lo && j < c_hi;
-      const uint32_t bin = score_key(acc[r]) >> kHistShift;
-      const bool brk = act && bin != run_bin;
-      if (brk && run_cnt != 0u) atomicAdd(&hist_s[run_bin], run_cnt);
-      run_cnt = brk ? 1u : run_cnt + (act ? 1u : 0u);
-      run_bin = brk ? bin : run_bin;
-    }
-    if (run_cnt != 0u) atomicAdd(&hist_s[run_bin], run_cnt);
+    hist_add4(hist_s, acc, j0, live, c_lo, c_hi);
     __syncthreads();
     uint32_t* hg = a.hist + unit * kHistBins;
     for (int i = threadIdx.x; i < kHistBins; i += 256) {

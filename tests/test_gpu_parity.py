@@ -730,6 +730,51 @@ def test_decode_long_rows_ragged():
     _check_decode(inp, L, {k: v for k, v in oracle_units(inp).items() if k[0] != 2}, "long rows")
 
 
+def _score_bins(S: np.ndarray) -> np.ndarray:
+    """Coarse bins (top 11 bits) of the order-preserving 32-bit images of fp32
+    scores, -0.0 taken as +0.0 -- the histogram's definition."""
+    u = np.ascontiguousarray(S, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = np.where(u == 0x80000000, 0, u)
+    key = np.where(u & 0x80000000, (~u) & 0xFFFFFFFF, u | 0x80000000)
+    return (key >> 21).astype(np.int64)
+
+
+def test_decode_tip_histograms_ragged():
+    """A ragged batch of 64 sequences x 8 kv heads (512 units, rows up to 16384
+    tokens, B = 512 plus 4 + 64 forced: the three-launch step, TIP building the
+    unit histograms).  Lengths at chunk edges, odd chunk counts, 0 and 1.  The
+    histograms only steer the select's speed, so a wrong one would pass every
+    parity test: the per-unit histograms TIP leaves in a zeroed workspace must
+    equal the bin counts of the same TIP scores.  Then every unit's step against
+    the oracle."""
+    lens = [16384, 0, 1, 1023, 1024, 1025, 5 * 1024, 5 * 1024 + 1, 7 * 1024 - 1, 9000, 12345, 16000, 67, 68, 69]
+    rng = np.random.default_rng(31)
+    lens += [int(x) for x in rng.integers(100, 16385, size=64 - len(lens))]
+    cfg = C["c5"].replace(batch=64)
+    say("[tip histograms] ragged 64 x 8, t <= 16384")
+    inp = synth.make_inputs(cfg, seed=31, seq_lens=lens, device="cuda")
+    L = DeviceLayer(inp)
+    L.workspace.zero_()
+    L.decode_tip()
+    L.tip()
+    torch.cuda.synchronize()
+    units = cfg.batch * cfg.n_kv_heads
+    hist = L.workspace[:units * 2048 * 4].view(torch.int32).reshape(cfg.batch, cfg.n_kv_heads, 2048).cpu().numpy()
+    S = L.scores.cpu().numpy()
+    for b in range(cfg.batch):
+        t = int(inp.seq_lens[b])
+        c_lo = min(cfg.n_sink, t)
+        c_hi = max(c_lo, t - cfg.n_recent)
+        for g in range(cfg.n_kv_heads):
+            want = np.bincount(_score_bins(S[b, g, c_lo:c_hi]), minlength=2048)
+            np.testing.assert_array_equal(hist[b, g], want, err_msg=f"b={b} g={g} t={t}")
+    L.out.fill_(float("nan"))
+    L.decode()
+    torch.cuda.synchronize()
+    assert (L.out[1] == 0).all() and (L.sel_count[1] == 0).all()
+    _check_decode(inp, L, {k: v for k, v in oracle_units(inp).items() if k[0] != 1}, "tip histograms")
+
+
 def test_graph_capture_replays():
     name = "c2-ragged"
     say(f"[graph] {name}")
