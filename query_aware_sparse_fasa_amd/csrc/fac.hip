@@ -259,6 +259,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
 constexpr int kSelThreads = 512;            // workgroup of the selecting launch
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelWideUnits = 256;          // units from which a workgroup covers several heads
+constexpr int kB1Early = 0;                 // list pieces read before the lengths are known (per thread)
 
 // The selecting launch of a decode step (budgets up to kSmallBudget).  One
 // workgroup per (sequence, query head chunk): it first makes its unit's exact
@@ -294,9 +295,13 @@ struct FacSelShared {
 // more than 16 filter chunks, or more than 32 emitted chunks): the first kept
 // pairs of up to 64 chunks are prefetched at kernel start instead of 16 (32).
 // EMIT: the candidates are the lists TIP emitted per 1024-token chunk (the
-// two-launch step, no filter launch); otherwise the filter's kept pairs.
-template <typename T, typename Acc, int HG, bool DEEP = false, bool EMIT = false>
+// two-launch step, no filter launch); otherwise the filter's kept pairs.  B1
+// (with EMIT): only the list keys in bins >= the unit histogram's bin of the
+// B-th key, each thread holding a slice of one list; the unit's last
+// workgroup to read the histogram clears it.
+template <typename T, typename Acc, int HG, bool DEEP = false, bool EMIT = false, bool B1 = false>
 __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
+  static_assert(!B1 || (EMIT && HG == 1), "the histogram filter reads TIP's lists, one head per workgroup");
   const Common& c = a.c;
   const WgCoord wg = xcd_grouped();
   const int b = wg.z, g = wg.y, hc = wg.x;
@@ -316,12 +321,24 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   // slices, the block-table row and the length.
   constexpr int PRE = (DEEP ? 64 : (EMIT ? 32 : 16)) / kSelWaves;
   uint2 pre[PRE];
-  if constexpr (EMIT) sel::prefetch_kept<kSelThreads, PRE, 1, kEmitChunk>(unit_slots, nfa, pre);
-  else sel::prefetch_kept<kSelThreads, PRE>(unit_slots, nfa, pre);
   int cnt[sel::CPT];
   uint2 meta[sel::CPT];
-  if constexpr (EMIT) sel::load_meta(reinterpret_cast<const uint2*>(a.w.counts) + unit * nfa, nfa, meta);
-  else sel::load_counts(a.w.counts + unit * nfa, nfa, cnt);
+  uint4 hv = make_uint4(0u, 0u, 0u, 0u);
+  uint2 m1 = make_uint2(0u, 0u);
+  sel::B1Slice<kSelThreads, kB1Early> sl;
+  if constexpr (B1) {
+    // The unit histogram (bins 4 t .. 4 t + 3) and the summary of the chunk
+    // whose list slice this thread takes; the slice itself once the length is known.
+    static_assert(kSelThreads * 4 == sel::HB, "one uint4 of bins per thread");
+    hv = reinterpret_cast<const uint4*>(a.w.hist + unit * sel::HB)[tid];
+    m1 = reinterpret_cast<const uint2*>(a.w.counts)[unit * nfa + min(tid / sel::B1Slice<kSelThreads>::TPC, nfa - 1)];
+    sl.early(unit_slots, nfa);
+  } else {
+    if constexpr (EMIT) sel::prefetch_kept<kSelThreads, PRE, 1, kEmitChunk>(unit_slots, nfa, pre);
+    else sel::prefetch_kept<kSelThreads, PRE>(unit_slots, nfa, pre);
+    if constexpr (EMIT) sel::load_meta(reinterpret_cast<const uint2*>(a.w.counts) + unit * nfa, nfa, meta);
+    else sel::load_counts(a.w.counts + unit * nfa, nfa, cnt);
+  }
   const int b1 = EMIT ? -1 : a.w.b1[unit];
   const int64_t head0 = int64_t(b) * c.n_q_heads + g * c.group + h0;
   // bf16 caches with 4 or more heads per workgroup run the FAC on the matrix
@@ -347,8 +364,15 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   const int count = (t - nC) + Bc;          // forced + chosen, <= cap
   const bool keep_all = Bc == nC;
 
+  if constexpr (B1) {
+    if (!keep_all) sl.late(unit_slots, emit_chunks_of(t), m1);
+    reinterpret_cast<uint4*>(sm.u.s.st.hist)[tid] = hv;   // consumed in every workgroup
+  }
   if (!keep_all) {
-    if constexpr (EMIT)
+    if constexpr (B1)
+      sel::select_from_lists_b1<kSelThreads, true, kB1Early>(sm.u.s.st, sm.u.s.key, sm.u.s.idx, kSmallCand, sl, m1, row, lim,
+                                                   c.max_t, emit_chunks_of(t), c_lo, c_hi, Bc, sm.chosen);
+    else if constexpr (EMIT)
       sel::select_from_emitted<kSelThreads, PRE, true>(sm.u.s.st, sm.u.s.chunk_off, sm.u.s.key, sm.u.s.idx,
                                                        kSmallCand, unit_slots, row, lim, c.max_t,
                                                        emit_chunks_of(t), meta, pre, c_lo, c_hi, Bc, sm.chosen);
@@ -361,6 +385,20 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   for (int k = 0; k < kBtabLds / kSelThreads; ++k)
     if (tid + kSelThreads * k < c.max_blocks) sm.btab[tid + kSelThreads * k] = bt[k];
   __syncthreads();                          // the list and the block table are in LDS; the select area is free
+  if constexpr (B1) {
+    // Every wave of this workgroup has stored its histogram bins (its reads are
+    // done); the unit's last workgroup to get here leaves the histogram zero for
+    // the next step's TIP.  The counter was zeroed by TIP.
+    if (wave == 0) {
+      uint32_t old = 0;
+      if (tid == 0) old = atomicAdd(&a.arrive[unit], 1u);
+      old = uint32_t(__shfl(int(old), 0, 64));
+      if (old == gridDim.x - 1) {
+        uint4* hg = reinterpret_cast<uint4*>(a.w.hist + unit * sel::HB);
+        for (int i = tid; i < sel::HB / 4; i += 64) hg[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
 
   // Row r of the list: the forced prefix, the chosen, then the forced suffix.
   std::conditional_t<kMfma, FacWaveMfma<HG>, FacWave<T, Acc, HG>> w;
@@ -574,14 +612,19 @@ int select_heads(const Common& c) {
 }
 
 template <typename T, typename Acc>
-hipError_t launch_fac_select_t(const FacArgs& a, bool emitted, hipStream_t s) {
+hipError_t launch_fac_select_t(const FacArgs& a, int lists, hipStream_t s) {
   const int hg = select_heads(a.c);
   const dim3 grid((a.c.group + hg - 1) / hg, a.c.n_kv_heads, a.c.batch);
+  const bool emitted = lists != kFromFilter;
+  if (lists == kFromListsB1) {
+    hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, true>), grid, dim3(kSelThreads), 0, s, a);
+    return hipGetLastError();
+  }
   // One head per workgroup has the registers for a deeper prefetch; it pays only
   // when the rows span more than 16 filter chunks (measured: 128K-token rows
   // gain 0.7 us, 32K-token rows lose 0.4 us to the redundant loads), or more
   // than 32 emitted chunks.  TIP's lists are only used with one head per
-  // workgroup (decode_emits).
+  // workgroup (decode_lists).
   if (emitted) {
     if (emit_chunks(a.c) > 32)
       hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, true, true>), grid, dim3(kSelThreads), 0, s, a);
@@ -620,17 +663,21 @@ bool fac_selects(const Common& c, const FacPlan& p) {
   return c.max_t > 0 && c.budget <= kSmallBudget && c.max_blocks <= kBtabLds && (c.score_stride & 3) == 0;
 }
 
-bool decode_emits(const Common& c, const FacPlan& p) {
+int decode_lists(const Common& c, const FacPlan& p) {
   // Few units (one-head selecting workgroups): there the filter launch and its
   // launch gap are a large part of the step.  Many units keep the filter
   // launch, whose cost they share, and whose global threshold does not depend
   // on how the top keys cluster along the row.
-  if (!fac_selects(c, p) || select_heads(c) != 1 || emit_chunks(c) > 64 * sel::CPT) return false;
+  if (c.max_t <= 0 || !fac_selects(c, p) || select_heads(c) != 1 || emit_chunks(c) > 64 * sel::CPT)
+    return kFromFilter;
   // Every chunk writes emit_target() keys (more only with ties): at the longest
   // row about 2 Bc + 18 per chunk; a quarter more for ties and short rows.
+  // Lists expected to overflow the selecting launch's LDS are cut down to the
+  // filter's kept set with the unit histogram.
   const int64_t bc = c.budget < c.max_t ? c.budget : c.max_t;
   const int64_t expect = 5 * (2 * bc + 18 * int64_t(emit_chunks(c))) / 4;
-  return expect <= kSmallCand;
+  if (expect <= kSmallCand) return kFromLists;
+  return emit_chunks(c) <= sel::B1_LISTS ? kFromListsB1 : kFromFilter;
 }
 
 FacPlan fac_plan(const Common& c) {
@@ -715,14 +762,14 @@ hipError_t launch_dense(const Common& c, const FacPlan& p, const void* q, const 
 
 hipError_t launch_fac_select(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
                              const void* v_pool, const int32_t* block_table, const float* scores,
-                             const int32_t* seq_lens, const SelectBuffers& sb, bool emitted, int32_t* sel_idx,
-                             int32_t* sel_count, float* out, hipStream_t s) {
-  FacArgs a = make_args(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out, nullptr, nullptr);
+                             const int32_t* seq_lens, const SelectBuffers& sb, int lists, uint32_t* arrive,
+                             int32_t* sel_idx, int32_t* sel_count, float* out, hipStream_t s) {
+  FacArgs a = make_args(c, p, q, k_pool, v_pool, block_table, sel_idx, sel_count, out, nullptr, arrive);
   a.scores = scores;
   a.seq_lens = seq_lens;
   a.w = sb;
-  if (c.bf16) return launch_fac_select_t<uint16_t, float>(a, emitted, s);
-  return launch_fac_select_t<float, double>(a, emitted, s);
+  if (c.bf16) return launch_fac_select_t<uint16_t, float>(a, lists, s);
+  return launch_fac_select_t<float, double>(a, lists, s);
 }
 
 }  // namespace fasa

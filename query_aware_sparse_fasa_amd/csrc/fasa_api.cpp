@@ -356,7 +356,7 @@ struct DecodePlan {
   Common c;
   FacPlan p;
   Layout l;
-  bool emits;
+  int lists;        // where the select's candidates come from (fasa::kFrom*)
 };
 
 fasa_status decode_plan(const fasa_shape* shape, int32_t max_t, const void* workspace, size_t workspace_bytes,
@@ -365,7 +365,7 @@ fasa_status decode_plan(const fasa_shape* shape, int32_t max_t, const void* work
   d.c.score_stride = (max_t + 3) & ~3;   // the workspace's scores rows: 16-byte loads throughout
   d.p = fasa::fac_plan(d.c);
   d.l = layout(d.c, d.p);
-  d.emits = max_t > 0 && fasa::decode_emits(d.c, d.p);
+  d.lists = fasa::decode_lists(d.c, d.p);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < d.l.total) return FASA_ERR_WORKSPACE;
   return FASA_OK;
 }
@@ -378,9 +378,11 @@ fasa_status decode_tip_stage(const DecodePlan& d, const void* q, const void* k_p
   char* w = static_cast<char*>(workspace);
   const fasa::SelectBuffers sb = select_buffers(workspace, d.l);
   float* scores = reinterpret_cast<float*>(w + d.l.scores);
-  const fasa::TipOutputs to = d.emits ? fasa::TipOutputs{fasa::kTipEmit, nullptr, static_cast<uint2*>(sb.slots),
-                                                         reinterpret_cast<uint2*>(sb.counts)}
-                                      : fasa::TipOutputs{fasa::kTipHist, sb.hist, nullptr, nullptr};
+  uint32_t* fac_arrive = reinterpret_cast<uint32_t*>(w + d.l.fac_arrive);
+  const int mode = d.lists == fasa::kFromLists ? fasa::kTipEmit
+                   : (d.lists == fasa::kFromListsB1 ? fasa::kTipEmitHist : fasa::kTipHist);
+  const fasa::TipOutputs to{mode, sb.hist, static_cast<uint2*>(sb.slots), reinterpret_cast<uint2*>(sb.counts),
+                            fac_arrive};
   return hip_status(fasa::launch_tip(d.c, q, slab, k_pool, block_table, seq_lens, fc_idx, scores, to, stream));
 }
 
@@ -394,16 +396,16 @@ fasa_status decode_rest_stage(const DecodePlan& d, const void* q, const void* k_
   const fasa::SelectBuffers sb = select_buffers(workspace, d.l);
   float* scores = reinterpret_cast<float*>(w + d.l.scores);
   uint32_t* fac_arrive = reinterpret_cast<uint32_t*>(w + d.l.fac_arrive);
-  if (d.emits)
-    return hip_status(fasa::launch_fac_select(c, p, q, k_pool, v_pool, block_table, scores, seq_lens, sb, true,
-                                              sel_idx, sel_count, out, stream));
+  if (d.lists != fasa::kFromFilter)
+    return hip_status(fasa::launch_fac_select(c, p, q, k_pool, v_pool, block_table, scores, seq_lens, sb, d.lists,
+                                              fac_arrive, sel_idx, sel_count, out, stream));
   fasa_status st;
   if ((st = hip_status(fasa::launch_filter(c, scores, seq_lens, sb, true, fac_arrive, p.head_chunks, stream))) !=
       FASA_OK)
     return st;
   if (fasa::fac_selects(c, p))
-    return hip_status(fasa::launch_fac_select(c, p, q, k_pool, v_pool, block_table, scores, seq_lens, sb, false,
-                                              sel_idx, sel_count, out, stream));
+    return hip_status(fasa::launch_fac_select(c, p, q, k_pool, v_pool, block_table, scores, seq_lens, sb,
+                                              fasa::kFromFilter, nullptr, sel_idx, sel_count, out, stream));
   if ((st = hip_status(fasa::launch_finish(c, scores, seq_lens, sel_idx, sel_count, sb, fac_arrive, p.head_chunks,
                                            stream))) != FASA_OK)
     return st;

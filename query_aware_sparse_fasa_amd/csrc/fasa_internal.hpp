@@ -111,13 +111,16 @@ struct SelectBuffers {
 
 // TIP epilogues: scores only; + the unit's coarse histogram (global atomics,
 // for the filter launch); + this chunk's candidate list for the select that
-// the FAC launch finishes (no filter launch).
-enum { kTipScores = 0, kTipHist = 1, kTipEmit = 2 };
+// the FAC launch finishes (no filter launch); + both the list and the unit
+// histogram (the FAC launch keeps only the list keys in bins >= the
+// histogram's bin of the B-th largest key).
+enum { kTipScores = 0, kTipHist = 1, kTipEmit = 2, kTipEmitHist = 3 };
 struct TipOutputs {
   int mode;
-  uint32_t* hist;   // kTipHist: [units][kHistBins], holding the counts of nothing else
-  uint2* slots;     // kTipEmit: [units][emit_chunks][kEmitChunk] (key, token) pairs
-  uint2* meta;      // kTipEmit: [units][emit_chunks] (emit_word, tau)
+  uint32_t* hist;   // kTipHist, kTipEmitHist: [units][kHistBins], holding the counts of nothing else
+  uint2* slots;     // kTipEmit, kTipEmitHist: [units][emit_chunks][kEmitChunk] (key, token) pairs
+  uint2* meta;      // kTipEmit, kTipEmitHist: [units][emit_chunks] (emit_word, tau)
+  uint32_t* arrive = nullptr;   // kTipEmitHist: [units] counters, zeroed (by chunk 0's workgroup)
 };
 hipError_t launch_tip(const Common& c, const void* q, const void* slab, const void* k_pool,
                       const int32_t* block_table, const int32_t* seq_lens,
@@ -194,18 +197,24 @@ hipError_t launch_ca_dominant(const int32_t* hits, int n_rows, int n_kv, int n_t
 // Whether a decode step may use launch_fac_select (small budget, block-table
 // rows that fit in LDS).
 bool fac_selects(const Common& c, const FacPlan& p);
-// Top-B stage 3 and FAC in one launch, after launch_filter: writes the
-// selection lists and counts, zeroes the histograms, and computes out (one
-// workgroup per query head, no merge).
-// emitted: the candidates are TIP's per-chunk lists (TIP ran with kTipEmit;
-// sb.slots / sb.counts hold its pairs and summaries); otherwise the filter's.
+// Top-B stage 3 and FAC in one launch: writes the selection lists and counts,
+// leaves the unit histograms zero, and computes out (one workgroup per query
+// head, no merge).  lists: where the candidates come from --
+//   kFromFilter: the filter's kept pairs (after launch_filter);
+//   kFromLists:  TIP's per-chunk lists (TIP ran with kTipEmit; sb.slots /
+//                sb.counts hold its pairs and summaries);
+//   kFromListsB1: the same lists, keeping the keys in bins >= the unit
+//                histogram's bin of the B-th largest key (TIP ran with
+//                kTipEmitHist; arrive holds its per-unit counters).
+enum { kFromFilter = 0, kFromLists = 1, kFromListsB1 = 2 };
 hipError_t launch_fac_select(const Common& c, const FacPlan& p, const void* q, const void* k_pool,
                              const void* v_pool, const int32_t* block_table, const float* scores,
-                             const int32_t* seq_lens, const SelectBuffers& sb, bool emitted, int32_t* sel_idx,
-                             int32_t* sel_count, float* out, hipStream_t s);
-// Whether a decode step takes two launches (TIP emitting candidates, then the
-// selecting FAC launch): fac_selects() and candidate lists that are expected
-// to fit the selecting launch's LDS.
-bool decode_emits(const Common& c, const FacPlan& p);
+                             const int32_t* seq_lens, const SelectBuffers& sb, int lists, uint32_t* arrive,
+                             int32_t* sel_idx, int32_t* sel_count, float* out, hipStream_t s);
+// Where a decode step's candidates come from (kFrom*): TIP's lists (two
+// launches) when fac_selects() and few units; with the unit histogram's filter
+// when the plain lists are not expected to fit the selecting launch's LDS; the
+// filter launch otherwise.
+int decode_lists(const Common& c, const FacPlan& p);
 
 }  // namespace fasa

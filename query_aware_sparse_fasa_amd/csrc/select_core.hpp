@@ -495,6 +495,116 @@ __device__ __forceinline__ int gather_emitted(SelState<NTH>& s, int32_t* chunk_o
   return int(N);
 }
 
+// Lists of at most B1_LISTS chunks, each read up to B1_LIST pairs, by the
+// histogram-filtered gather below.
+constexpr int B1_LISTS = 128;
+constexpr int B1_LIST = 128;
+
+// The pairs of TIP's lists that thread t holds: list (chunk) t / TPC, and of
+// it, with j = t mod TPC, the uint4 (two pairs) TPC i + j for i < VPT -- the
+// TPC threads of a chunk read adjacent 16-byte pieces, so one load instruction
+// of a wave covers whole 64-byte runs of 64 / TPC lists.  Steps i < EARLY are
+// read before the list's length is known (early, for nfa chunks); the others
+// (late) only below the list's length n, taken from the chunk's summary m (0
+// past the unit's nfc chunks).
+template <int NTH, int EARLY = 0>
+struct B1Slice {
+  static constexpr int TPC = NTH / B1_LISTS;         // threads per chunk
+  static constexpr int VPT = B1_LIST / (2 * TPC);    // uint4 per thread
+  static_assert(TPC * B1_LISTS == NTH && VPT * 2 * TPC == B1_LIST && VPT <= 16 && EARLY <= VPT,
+                "whole chunks per block; a kept mask fits 32 bits");
+  uint4 pr[VPT];
+  int n = 0;                                         // the list's length
+  __device__ __forceinline__ int j() const { return int(threadIdx.x) % TPC; }
+  __device__ __forceinline__ const uint4* src(const uint2* slots, int nch) const {
+    return reinterpret_cast<const uint4*>(slots + int64_t(min(int(threadIdx.x) / TPC, nch - 1)) * kEmitChunk) + j();
+  }
+  // Position of the h-th pair of step i in the list.
+  __device__ __forceinline__ int pos(int i, int h) const { return 2 * (TPC * i + j()) + h; }
+  __device__ __forceinline__ void early(const uint2* slots, int nfa) {
+    const uint4* p = src(slots, nfa);
+#pragma unroll
+    for (int i = 0; i < EARLY; ++i) pr[i] = p[TPC * i];
+  }
+  __device__ __forceinline__ void late(const uint2* slots, int nfc, uint2 m) {
+    const int ch = int(threadIdx.x) / TPC;
+    n = ch < nfc ? int(emit_count(m.x)) : 0;
+    const uint4* p = src(slots, nfc);
+#pragma unroll
+    for (int i = EARLY; i < VPT; ++i) pr[i] = pos(i, 0) < n ? p[TPC * i] : make_uint4(0u, 0u, 0u, 0u);
+  }
+};
+
+// Gather from TIP's per-chunk lists only the keys in coarse bins >= b1 (the
+// unit histogram's bin of the Bc-th largest key), in index order, into LDS: the
+// filter's kept set without a filter launch.  Each thread holds its pieces of
+// one list (sl, with the summary m of that chunk); the kept pairs of a list
+// are placed from the masks of its TPC threads (which pieces each keeps), the
+// lists one after another by a block scan of their kept counts, so the keys
+// land in index order (chunk by chunk, each list ascending).  Builds the
+// second-digit histogram (bits 20..10) of the keys in bin b1 in s.hist (zeroed
+// by the caller) and counts the keys above b1.  The lists hold every key of bin
+// >= b1 when no chunk that left candidates out has its threshold tau above b1's
+// lower edge (a chunk leaves out only keys below its tau).  Returns the number
+// of pairs, or -1 (nothing gathered) when that does not hold, a list is longer
+// than B1_LIST, or the kept keys exceed cap_lds.
+template <int NTH, int EARLY>
+__device__ __forceinline__ int gather_lists_b1(SelState<NTH>& s, const B1Slice<NTH, EARLY>& sl, uint2 m, int nfc,
+                                               int cap_lds, uint32_t* key, int32_t* idx, uint32_t b1, uint32_t& above) {
+  using S = B1Slice<NTH, EARLY>;
+  constexpr int TPC = S::TPC, VPT = S::VPT;
+  const int lane = int(threadIdx.x) & 63, j = sl.j();
+  const int ch = int(threadIdx.x) / TPC;
+  const bool unusable = sl.n > B1_LIST || (ch < nfc && emit_cut(m.x) && m.y > (b1 << kHistShift));
+  // Bit 2 i + h: the h-th pair of step i is kept.
+  uint32_t mask = 0, n_above = 0;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t bin = (h == 0 ? sl.pr[i].x : sl.pr[i].z) >> kHistShift;
+      const bool ok = sl.pos(i, h) < sl.n;
+      mask |= (ok && bin >= b1) ? (1u << (2 * i + h)) : 0u;
+      n_above += (ok && bin > b1) ? 1u : 0u;
+    }
+  }
+  uint32_t mg[TPC], list_kept = 0;
+#pragma unroll
+  for (int q = 0; q < TPC; ++q) {
+    mg[q] = uint32_t(__shfl(int(mask), (lane & ~(TPC - 1)) + q, 64));
+    list_kept += uint32_t(__popc(mg[q]));
+  }
+  // The list's count rides on its last thread; a flag on any thread adds more
+  // than any block could keep.
+  const uint32_t v = (j == TPC - 1 ? list_kept : 0u) + (unusable ? uint32_t(cap_lds) + 1u : 0u);
+  uint32_t tot;
+  uint32_t run = block_excl_scan(s, v, tot);
+  (void)block_excl_scan<1>(s, n_above, above);   // right after the previous scan: the other buffer
+  if (tot > uint32_t(cap_lds)) return -1;   // uniform
+  auto put = [&](uint32_t at, uint32_t k, uint32_t t) {
+    key[at] = k;
+    idx[at] = int32_t(t);
+    if ((k >> kHistShift) == b1) atomicAdd(&s.hist[(k >> 10) & 2047u], 1u);
+  };
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int q = 0; q < TPC; ++q) {
+      const uint32_t c = uint32_t(__popc((mg[q] >> (2 * i)) & 3u));
+      before += q < j ? c : 0u;
+      all += c;
+    }
+    const uint32_t at = run + before;
+    const uint32_t mine = mask >> (2 * i);
+    if (mine & 1u) put(at, sl.pr[i].x, sl.pr[i].y);
+    if (mine & 2u) put(at + (mine & 1u), sl.pr[i].z, sl.pr[i].w);
+    run += all;
+  }
+  __syncthreads();                          // the pairs and the histogram
+  return int(tot);
+}
+
 // Exact select of the Bc largest of the N (>= Bc) emitted keys in LDS, whose
 // first-digit histogram gather_emitted built, into out[0..Bc) ascending.
 // The emitted lists are the whole story only if no chunk left out a key that
@@ -672,6 +782,33 @@ __device__ __forceinline__ void load_counts(const int32_t* unit_counts, int nfa,
 // (nfc chunks, counts cnt and first pairs pre already loaded), into out[0..Bc)
 // -- global or LDS.  b1: the coarse bin the filter kept keys from.  Falls back
 // to the whole score row when the kept pairs are fewer than Bc or do not fit.
+// The exact select from TIP's lists filtered by the unit histogram (see
+// gather_lists_b1): s.hist holds the unit's histogram (stored by the caller,
+// not yet published), whose bin of the Bc-th largest key is b1; sl holds the
+// thread's slice of the lists, m its chunk's summary.  Falls back to the whole
+// scores row when the lists cannot be used.
+template <int NTH, bool VEC, int EARLY>
+__device__ void select_from_lists_b1(SelState<NTH>& s, uint32_t* key, int32_t* idx, int cap_lds,
+                                     const B1Slice<NTH, EARLY>& sl, uint2 m, const float* row, int lim, int max_t, int nfc,
+                                     int c_lo, int c_hi, int Bc, int32_t* out) {
+  if (threadIdx.x == 0) {
+    s.digit = 0u;                            // fewer than Bc keys counted: keep every candidate
+    s.rem = uint32_t(Bc);
+    s.full = 0u;
+  }
+  __syncthreads();
+  find_digit<NTH, HB>(s, uint32_t(Bc));      // ends with a barrier: s.hist is free again
+  const uint32_t b1 = s.digit;
+  zero_bins<NTH, HB>(s);                     // the second-digit histogram; published by the gather's first barrier
+  uint32_t above = 0;
+  const int N = gather_lists_b1<NTH, EARLY>(s, sl, m, nfc, cap_lds, key, idx, b1, above);
+  if (N >= Bc) {
+    lds_select<NTH>(s, key, idx, N, Bc, int(b1), above, out);
+    return;
+  }
+  row_select<NTH, VEC>(s, row, lim, max_t, c_lo, c_hi, Bc, out);
+}
+
 template <int NTH, int PRE, bool VEC, int D = 1>
 __device__ void select_from_kept(SelState<NTH>& s, int32_t* chunk_off, uint32_t* key, int32_t* idx, int cap_lds,
                                  const uint2* unit_slots, const float* row, int lim, int max_t, int nfc,

@@ -24,7 +24,7 @@
 // 16-byte store per lane.  The kernel is a pure HBM stream (2 flops per 2-byte
 // element), so there is nothing for MFMA to do.
 //
-// Three epilogues (MODE):
+// Four epilogues (MODE):
 //   kTipScores: scores only (fasa_tip);
 //   kTipHist:   also the unit's coarse key histogram for the filter launch of
 //               the three-launch select (global atomics);
@@ -40,6 +40,10 @@
 //               whole scores row).  (An exact k-th largest found by ballot
 //               binary searches, 32 dependent rounds per wave, measured 10 us
 //               slower per launch than this LDS histogram.)
+//   kTipEmitHist: the list and the unit histogram both (the chunk's LDS
+//               histogram added to the unit's); the FAC launch keeps only the
+//               list keys in bins at or above the unit histogram's bin of the
+//               B-th key.
 // One chunk per workgroup: workgroups that walked 2-8 chunks of a unit, with
 // the next chunk's slab loads in flight during the current one's arithmetic and
 // one histogram flush at the end (91-178 VGPRs), streamed slower than these
@@ -62,6 +66,7 @@ struct TipArgs {
   uint32_t* hist;       // [units][kHistBins] coarse key histogram (kTipHist)
   uint2* slots;         // [units][emit chunks][kEmitChunk] (key, token) pairs (kTipEmit)
   uint2* meta;          // [units][emit chunks] chunk summary: (emit_word, tau) (kTipEmit)
+  uint32_t* arrive;     // [units] counters of the FAC launch, zeroed by chunk 0 (kTipEmitHist)
 };
 
 // Column slots of the query fold for F dominant FCs: 2F rounded up to a power of two.
@@ -110,6 +115,14 @@ __device__ __forceinline__ void fold_query(const TipArgs& a, int b, int g, int F
   }
 }
 
+// Adds the chunk's histogram to the unit's.
+__device__ __forceinline__ void hist_flush(const uint32_t* hist_s, uint32_t* hg) {
+  for (int i = threadIdx.x; i < kHistBins; i += 256) {
+    const uint32_t v = hist_s[i];
+    if (v != 0u) atomicAdd(&hg[i], v);
+  }
+}
+
 // Adds a lane's 4 consecutive tokens j0 .. j0+3 (candidates in [c_lo, c_hi)
 // only) to the LDS histogram of coarse key bins; equal bins are merged first.
 __device__ __forceinline__ void hist_add4(uint32_t* hist_s, const float (&acc)[4], int j0, bool live, int c_lo,
@@ -131,7 +144,7 @@ __device__ __forceinline__ void hist_add4(uint32_t* hist_s, const float (&acc)[4
 // FT > 0: compile-time F (all loads of a block issued back to back); FT == 0: runtime F.
 template <typename T, int FT, bool FROM_SLAB, int MODE>
 __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
-  constexpr bool HIST = MODE == kTipHist, EMIT = MODE == kTipEmit, LDS_HIST = HIST || EMIT;
+  constexpr bool HIST = MODE == kTipHist, EMIT = MODE == kTipEmit || MODE == kTipEmitHist, LDS_HIST = HIST || EMIT;
   const Common& c = a.c;
   const WgCoord wg = xcd_grouped();
   const int b = wg.z, g = wg.y;
@@ -171,7 +184,7 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
 
   __shared__ float qf[kHeadDim];   // folded query, [f][2]
   __shared__ int cols[kHeadDim / 2];
-  __shared__ uint32_t hist_s[LDS_HIST ? kHistBins : 1];
+  __shared__ __align__(16) uint32_t hist_s[LDS_HIST ? kHistBins : 1];
   if constexpr (LDS_HIST) {
     for (int i = threadIdx.x; i < kHistBins; i += 256) hist_s[i] = 0u;
   }
@@ -246,11 +259,7 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
     const int c_hi = max(c_lo, t - c.n_recent);
     hist_add4(hist_s, acc, j0, live, c_lo, c_hi);
     __syncthreads();
-    uint32_t* hg = a.hist + unit * kHistBins;
-    for (int i = threadIdx.x; i < kHistBins; i += 256) {
-      const uint32_t v = hist_s[i];
-      if (v != 0u) atomicAdd(&hg[i], v);
-    }
+    hist_flush(hist_s, a.hist + unit * kHistBins);
   }
   if constexpr (EMIT) {
     // This chunk's candidates [max(c_lo, k0), min(c_hi, k0 + 1024)) and the
@@ -333,6 +342,12 @@ __global__ __launch_bounds__(256) void tip_kernel(TipArgs a) {
       pos += keep[r] ? 1u : 0u;
     }
     if (e == 0) a.meta[unit * emit_chunks(c) + wg.x] = make_uint2(emit_word(tot, tot < uint32_t(n_in)), tau);
+    if constexpr (MODE == kTipEmitHist) {
+      // The chunk's histogram (still intact: the bin search only read it) into
+      // the unit's, for the FAC launch's global threshold.
+      hist_flush(hist_s, a.hist + unit * kHistBins);
+      if (wg.x == 0 && e == 0) a.arrive[unit] = 0u;
+    }
   }
 }
 
@@ -356,6 +371,7 @@ template <typename T>
 hipError_t launch_mode(const TipArgs& a, dim3 grid, bool slab, int mode, hipStream_t s) {
   if (mode == kTipHist) return launch_src<T, kTipHist>(a, grid, slab, s);
   if (mode == kTipEmit) return launch_src<T, kTipEmit>(a, grid, slab, s);
+  if (mode == kTipEmitHist) return launch_src<T, kTipEmitHist>(a, grid, slab, s);
   return launch_src<T, kTipScores>(a, grid, slab, s);
 }
 
@@ -364,7 +380,7 @@ hipError_t launch_mode(const TipArgs& a, dim3 grid, bool slab, int mode, hipStre
 hipError_t launch_tip(const Common& c, const void* q, const void* slab, const void* k_pool,
                       const int32_t* block_table, const int32_t* seq_lens, const int32_t* fc_idx,
                       float* scores, const TipOutputs& o, hipStream_t s) {
-  TipArgs a{c, q, slab ? slab : k_pool, block_table, seq_lens, fc_idx, scores, o.hist, o.slots, o.meta};
+  TipArgs a{c, q, slab ? slab : k_pool, block_table, seq_lens, fc_idx, scores, o.hist, o.slots, o.meta, o.arrive};
   const int nblk = (c.max_t + kBlock - 1) / kBlock;
   const dim3 grid((nblk + 3) / 4, c.n_kv_heads, c.batch);
   const bool sl = slab != nullptr;

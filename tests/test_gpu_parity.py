@@ -715,10 +715,11 @@ def test_empty_and_tiny_sequences():
 
 
 def test_decode_long_rows_ragged():
-    """The Qwen2.5-7B-shaped layer (groups of 7, B = 1024) on the filter path
-    (rows too long for TIP's per-chunk lists), with one-head selecting
-    workgroups over 1024-row lists: a 90000-token row, a short one just past
-    the budget, an empty sequence and a one-token one."""
+    """The Qwen2.5-7B-shaped layer (groups of 7, B = 1024) on the
+    histogram-filtered list path (TIP's per-chunk lists together too long for
+    the selecting workgroup, cut down with the unit histogram), with one-head
+    selecting workgroups over 1024-row lists: a 90000-token row, a short one
+    just past the budget, an empty sequence and a one-token one."""
     cfg = C["c4"].replace(batch=4)
     say("[long rows] c4 shape, lengths 90000 1500 0 1")
     inp = synth.make_inputs(cfg, seed=21, seq_lens=[90000, 1500, 0, 1])
@@ -737,6 +738,70 @@ def _score_bins(S: np.ndarray) -> np.ndarray:
     u = np.where(u == 0x80000000, 0, u)
     key = np.where(u & 0x80000000, (~u) & 0xFFFFFFFF, u | 0x80000000)
     return (key >> 21).astype(np.int64)
+
+
+def test_decode_filtered_lists_fallbacks():
+    """The histogram-filtered list path at 128 chunks per row (Qwen2.5-7B
+    layer, B = 1024, rows of 131072 and 70001 tokens), with both ways a unit's
+    lists can fail it planted: in unit (0, 0) chunk 5 holds 200 copies of one
+    high key (its list outgrows what the selecting workgroup reads of a list),
+    in unit (1, 1) the top-B sits in one chunk (a chunk that left keys out has
+    its threshold above the B-th key's bin).  TIP's unit histograms (the
+    filter's threshold) must equal the bin counts of its scores; every unit
+    must match the oracle; a workspace of random bytes (a wrong histogram and
+    arrival counters) must give the same result."""
+    cfg = C["c4"].replace(batch=2)
+    say("[filtered lists] c4 shape, lengths 131072 70001, long list + clustered")
+    inp = synth.make_inputs(cfg, seed=53, seq_lens=[131072, 70001])
+    G = cfg.group
+    # Unit (0, 0): 200 copies of chunk 5's best key inside chunk 5.
+    q = inp.q[0, 0:G].double().numpy()
+    K = unit_rows(inp, 0, 0, inp.k_pool).double().numpy()
+    S = O.tip_scores(q, K, inp.fc_idx[0])
+    src = 5 * 1024 + int(np.argmax(S[5 * 1024:6 * 1024]))
+    row = inp.k_pool[int(inp.block_table[0, src // 256]), 0, src % 256].clone()
+    pos = [j for j in range(5 * 1024, 6 * 1024, 5) if j != src][:200]
+    for j in pos:
+        inp.k_pool[int(inp.block_table[0, j // 256]), 0, j % 256] = row
+    # Unit (1, 1): keys of 40000 .. 41023 pushed along the folded dominant query.
+    qf = inp.q[1, G:2 * G].float().sum(0)
+    u = torch.zeros(128)
+    for i in inp.fc_idx[1]:
+        u[2 * i:2 * i + 2] = qf[2 * i:2 * i + 2]
+    u = u / u.norm()
+    for j in range(40000, 41024):
+        p, s_ = int(inp.block_table[1, j // 256]), j % 256
+        inp.k_pool[p, 1, s_] = (inp.k_pool[p, 1, s_].float() + (40.0 + 0.01 * j) * u).to(inp.k_pool.dtype)
+    L = DeviceLayer(inp)
+    L.workspace.zero_()
+    L.decode_tip()
+    L.tip()
+    torch.cuda.synchronize()
+    units = cfg.batch * cfg.n_kv_heads
+    hist = L.workspace[:units * 2048 * 4].view(torch.int32).reshape(cfg.batch, cfg.n_kv_heads, 2048).cpu().numpy()
+    Sg = L.scores.cpu().numpy()
+    for b in range(cfg.batch):
+        t = int(inp.seq_lens[b])
+        c_lo = min(cfg.n_sink, t)
+        c_hi = max(c_lo, t - cfg.n_recent)
+        for g in range(cfg.n_kv_heads):
+            want = np.bincount(_score_bins(Sg[b, g, c_lo:c_hi]), minlength=2048)
+            np.testing.assert_array_equal(hist[b, g], want, err_msg=f"b={b} g={g}")
+    L.out.fill_(float("nan"))
+    L.decode()
+    torch.cuda.synchronize()
+    units_o = oracle_units(inp)
+    _check_decode(inp, L, units_o, "filtered lists")
+    sel = units_o[(1, 1)][3]["sel"]
+    assert ((sel >= 40000) & (sel < 41024)).all(), "the construction failed to cluster the top-B"
+    a = (L.out.clone(), L.sel_idx.clone(), L.sel_count.clone())
+    L.workspace.copy_(torch.randint(0, 256, L.workspace.shape, dtype=torch.uint8,
+                                    generator=torch.Generator().manual_seed(53)).to(L.workspace.device))
+    for _ in range(2):
+        L.decode()
+        torch.cuda.synchronize()
+        for x, y in zip(a, (L.out, L.sel_idx, L.sel_count)):
+            assert torch.equal(x, y), "random workspace"
 
 
 def test_decode_tip_histograms_ragged():
