@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
     w.fold_row_groups();
     __syncthreads();                        // the fold area below overlaps the other waves' tiles
   } else {
-    w.template run<U>(r0, r1, lane_offset, kbase, vbase);
+    w.template run<U, false, B1>(r0, r1, lane_offset, kbase, vbase);
     w.fold_row_groups();
   }
 
@@ -673,11 +673,15 @@ int decode_lists(const Common& c, const FacPlan& p) {
   // Every chunk writes emit_target() keys (more only with ties): at the longest
   // row about 2 Bc + 18 per chunk; a quarter more for ties and short rows.
   // Lists expected to overflow the selecting launch's LDS are cut down to the
-  // filter's kept set with the unit histogram.
+  // filter's kept set with the unit histogram, when a list's target leaves
+  // room for ties within what the gather reads of a list (a longer list sends
+  // its unit to the scores row: measured 20 -> 32 us at a 4096-token row whose
+  // chunks target 144 keys each).
   const int64_t bc = c.budget < c.max_t ? c.budget : c.max_t;
   const int64_t expect = 5 * (2 * bc + 18 * int64_t(emit_chunks(c))) / 4;
   if (expect <= kSmallCand) return kFromLists;
-  return emit_chunks(c) <= sel::B1_LISTS ? kFromListsB1 : kFromFilter;
+  if (emit_chunks(c) <= sel::B1_LISTS && 2 * emit_target(int(bc), c.max_t) <= sel::B1_LIST) return kFromListsB1;
+  return kFromFilter;
 }
 
 FacPlan fac_plan(const Common& c) {

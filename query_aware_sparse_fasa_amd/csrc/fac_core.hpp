@@ -164,7 +164,10 @@ struct FacWave {
   // all U quads first, then one rescale of each head's state to the new
   // maximum, then the U weighted rows added.
   // NT: non-temporal row loads, for rows that no other workgroup reads.
-  template <int U = 2, bool NT = false, typename LaneOffset>
+  // FAST: batches whose rows all exist and are valid take an unmasked copy of
+  // the batch (measured 0.7 us faster over 1024-row lists, 0.1 us slower over
+  // 256-row lists, where each wave sees one batch and fetches both copies).
+  template <int U = 2, bool NT = false, bool FAST = false, typename LaneOffset>
   __device__ __forceinline__ void run(int r0, int r1, LaneOffset lane_offset, const T* kbase,
                                       const T* vbase) {
     const int lane = threadIdx.x & 63, rg = lane >> 4, sub = lane & 15;
@@ -178,6 +181,26 @@ struct FacWave {
       const int nrows = min(64, r1 - base);
       for (int q4 = 0; q4 < nrows; q4 += 4 * U) {
         Raw8<T> kr[U], vr[U];
+        // A batch whose 4 U rows all exist and are valid skips every mask.
+        static_assert(4 * U < 64, "a batch within one 64-row window");
+        const bool full = FAST && q4 + 4 * U <= nrows &&
+                          ((ok >> q4) & ((uint64_t(1) << (4 * U)) - 1)) == ((uint64_t(1) << (4 * U)) - 1);
+        if constexpr (FAST) if (full) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int64_t o = __shfl(my_off, q4 + 4 * u + rg, 64);
+            if constexpr (NT) {
+              kr[u].load_nt(kbase + o);
+              vr[u].load_nt(vbase + o);
+            } else {
+              kr[u].load(kbase + o);
+              vr[u].load(vbase + o);
+            }
+          }
+          const bool all[U] = {};
+          absorb<U, false>(kr, vr, all);
+          continue;
+        }
         bool valid[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -201,8 +224,10 @@ struct FacWave {
   // Fold U row quads already loaded (kr, vr: this row group's row of each
   // quad; valid[u] false drops quad u's row) into the online softmax: the
   // logits of all U quads first, then one rescale of each head's state to the
-  // new maximum, then the U weighted rows added.
-  template <int U>
+  // new maximum, then the U weighted rows added.  MASKED false: every row is
+  // valid (valid is not read), so no logit is -inf and the batch's maximum is
+  // finite.
+  template <int U, bool MASKED = true>
   __device__ __forceinline__ void absorb(const Raw8<T> (&kr)[U], const Raw8<T> (&vr)[U], const bool (&valid)[U]) {
     Acc z[U][HG], mn[HG];
 #pragma unroll
@@ -222,7 +247,7 @@ struct FacWave {
           for (int e = 0; e < 8; ++e) sdot = fma(qv[hh][e], Acc(kx[e]), sdot);
         }
         const Acc zz = row_sum(sdot) * zscale;
-        z[u][hh] = valid[u] ? zz : neg_inf<Acc>();
+        z[u][hh] = (!MASKED || valid[u]) ? zz : neg_inf<Acc>();
         mn[hh] = fmax(mn[hh], z[u][hh]);
       }
     }
@@ -242,7 +267,7 @@ struct FacWave {
       vr[u].unpack(vx);
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh) {
-        const Acc pz = merge_weight(z[u][hh], mn[hh]);
+        const Acc pz = MASKED ? merge_weight(z[u][hh], mn[hh]) : fexp<Acc>(z[u][hh] - mn[hh]);
         l[hh] += pz;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[hh][e] = fma(pz, Acc(vx[e]), acc[hh][e]);

@@ -556,22 +556,32 @@ __device__ __forceinline__ int gather_lists_b1(SelState<NTH>& s, const B1Slice<N
   const int lane = int(threadIdx.x) & 63, j = sl.j();
   const int ch = int(threadIdx.x) / TPC;
   const bool unusable = sl.n > B1_LIST || (ch < nfc && emit_cut(m.x) && m.y > (b1 << kHistShift));
+  // Steps that hold a pair of some list of this wave (the longest list decides).
+  int longest = sl.n;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) longest = max(longest, __shfl_xor(longest, o, 64));
+  const int steps = __builtin_amdgcn_readfirstlane((min(longest, B1_LIST) + 2 * TPC - 1) / (2 * TPC));
   // Bit 2 i + h: the h-th pair of step i is kept.
   uint32_t mask = 0, n_above = 0;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
+    if (i < steps) {                        // uniform; no break, so pr keeps static indices
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t bin = (h == 0 ? sl.pr[i].x : sl.pr[i].z) >> kHistShift;
-      const bool ok = sl.pos(i, h) < sl.n;
-      mask |= (ok && bin >= b1) ? (1u << (2 * i + h)) : 0u;
-      n_above += (ok && bin > b1) ? 1u : 0u;
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t bin = (h == 0 ? sl.pr[i].x : sl.pr[i].z) >> kHistShift;
+        const bool ok = sl.pos(i, h) < sl.n;
+        mask |= (ok && bin >= b1) ? (1u << (2 * i + h)) : 0u;
+        n_above += (ok && bin > b1) ? 1u : 0u;
+      }
     }
   }
-  uint32_t mg[TPC], list_kept = 0;
+  // The masks of the list's TPC threads; below[q]: thread q's mask if it comes
+  // before this thread in the list's order within a step, else 0.
+  uint32_t mg[TPC], below[TPC], list_kept = 0;
 #pragma unroll
   for (int q = 0; q < TPC; ++q) {
     mg[q] = uint32_t(__shfl(int(mask), (lane & ~(TPC - 1)) + q, 64));
+    below[q] = q < j ? mg[q] : 0u;
     list_kept += uint32_t(__popc(mg[q]));
   }
   // The list's count rides on its last thread; a flag on any thread adds more
@@ -588,18 +598,17 @@ __device__ __forceinline__ int gather_lists_b1(SelState<NTH>& s, const B1Slice<N
   };
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
-    uint32_t before = 0, all = 0;
+    if (i < steps) {                        // uniform
+      const uint32_t step = 3u << (2 * i);
+      uint32_t at = run;                    // the list's kept pairs before this thread's in step i
 #pragma unroll
-    for (int q = 0; q < TPC; ++q) {
-      const uint32_t c = uint32_t(__popc((mg[q] >> (2 * i)) & 3u));
-      before += q < j ? c : 0u;
-      all += c;
+      for (int q = 0; q < TPC; ++q) at += uint32_t(__popc(below[q] & step));
+#pragma unroll
+      for (int q = 0; q < TPC; ++q) run += uint32_t(__popc(mg[q] & step));
+      const uint32_t mine = mask >> (2 * i);
+      if (mine & 1u) put(at, sl.pr[i].x, sl.pr[i].y);
+      if (mine & 2u) put(at + (mine & 1u), sl.pr[i].z, sl.pr[i].w);
     }
-    const uint32_t at = run + before;
-    const uint32_t mine = mask >> (2 * i);
-    if (mine & 1u) put(at, sl.pr[i].x, sl.pr[i].y);
-    if (mine & 2u) put(at + (mine & 1u), sl.pr[i].z, sl.pr[i].w);
-    run += all;
   }
   __syncthreads();                          // the pairs and the histogram
   return int(tot);
