@@ -322,8 +322,8 @@ struct FacWave {
 //     B[4 g + j][n], j < 4).  B = P: lane l's own four logits' weights.  A = V^T:
 //     lane l needs channel 16 dt + n of block rows 4 g .. 4 g + 3, a transposed
 //     access, so each wave first writes its 16 V rows into its own LDS tile
-//     (rows padded to 264 bytes: the four row groups of a read land in
-//     different banks) and reads them back 16 bits at a time.  P enters as a
+//     (rows padded to 264 bytes) and reads each 16-channel tile back with one
+//     transposing LDS read (ds_read_b64_tr_b16).  P enters as a
 //     bf16 high part and a bf16 low part (the rounding error of a single bf16
 //     P, about 2^-9 of |v|, would exceed the 2e-3 bound on outputs with large
 //     channels); the two products add up to P within about 2^-17.  D: lane l
@@ -521,11 +521,16 @@ struct FacWaveMfma {
     }
     lrun = lrun * corr + psum;
     __builtin_amdgcn_wave_barrier();
+    // V^T operand of channel tile dt: lane (g, n) needs rows 4 g .. 4 g + 3 of
+    // channel 16 dt + n.  The transposing LDS read gives it in one instruction:
+    // within each 16-lane group, lane 4 r + q supplies 4 channels (4 q .. 4 q + 3
+    // of the tile) of row 4 g + r, and lane n receives channel n of the four rows.
+    const uint16_t* vsrc = tile + (4 * g + (n >> 2)) * kMfmaTilePitch + 4 * (n & 3);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      s16x4 vt;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vt[j] = short(tile[(4 * g + j) * kMfmaTilePitch + 16 * dt + n]);
+      typedef short s16x4_lds __attribute__((ext_vector_type(4)));
+      const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (s16x4_lds __attribute__((address_space(3)))*)(vsrc + 16 * dt));
       o[dt] = o[dt] * corr;
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi, o[dt], 0, 0, 0);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo, o[dt], 0, 0, 0);
