@@ -707,7 +707,10 @@ fasa_status fasa_ca_hits(const fasa_shape* shape, const void* q, const void* k_p
     if ((st = hip_status(fasa::launch_ca_scores(c, q, k_pool, block_table, seq_lens, scores, stream))) != FASA_OK)
       return st;
   }
-  if ((st = hip_status(fasa::launch_filter(cs, scores, seq_lens, sb, false, nullptr, 0, stream))) != FASA_OK)
+  // One calibration sequence normally fills its rows to max_t: the filter
+  // then loads its scores without waiting for the length.
+  if ((st = hip_status(fasa::launch_filter(cs, scores, seq_lens, sb, false, nullptr, 0, stream,
+                                           shape->batch == 1))) != FASA_OK)
     return st;
   if ((st = hip_status(fasa::launch_finish(cs, scores, seq_lens, sel_idx, sel_count, sb, nullptr, 0, stream))) !=
       FASA_OK)

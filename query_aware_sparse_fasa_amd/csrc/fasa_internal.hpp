@@ -128,9 +128,11 @@ hipError_t launch_tip(const Common& c, const void* q, const void* slab, const vo
 // Top-B stages 1-2: the unit histograms (unless have_hist: TIP filled them) and
 // the filter's kept pairs, counts and b1.  Nothing when max_t == 0.
 // fac_arrive (nullable): FAC arrival counters, [units][head_chunks], zeroed here
-// for the FAC launch that follows.
+// for the FAC launch that follows.  rows_full: the caller expects every row to
+// run to max_t (a speed hint; any lengths stay correct).
 hipError_t launch_filter(const Common& c, const float* scores, const int32_t* seq_lens, const SelectBuffers& w,
-                         bool have_hist, uint32_t* fac_arrive, int head_chunks, hipStream_t s);
+                         bool have_hist, uint32_t* fac_arrive, int head_chunks, hipStream_t s,
+                         bool rows_full = false);
 // Top-B stage 3 as its own launch: the selection lists and counts; zeroes the
 // histograms (and fac_arrive when given).
 hipError_t launch_finish(const Common& c, const float* scores, const int32_t* seq_lens, int32_t* sel_idx,
