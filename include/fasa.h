@@ -227,6 +227,29 @@ fasa_status fasa_decode_rest(const fasa_shape* shape, const void* q, const void*
                              int32_t* sel_count, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* The launch structure fasa_decode (and its two stages) uses for a shape and
+ * max_t, written to *path (host memory); the results never depend on it.  It
+ * is reported for tests and tuning:
+ *   FASA_PATH_NONE            max_t == 0: nothing is launched;
+ *   FASA_PATH_LISTS           TIP writes per-chunk candidate lists, and one
+ *                             selecting FAC launch finishes the top-B from them;
+ *   FASA_PATH_FILTERED_LISTS  the same, TIP also building the unit histograms,
+ *                             whose threshold cuts the lists down;
+ *   FASA_PATH_FILTER          TIP's unit histograms, a filter launch, then the
+ *                             selecting FAC launch;
+ *   FASA_PATH_SPLIT           large budgets: filter, finish, and the split FAC
+ *                             with its merge.
+ * No device work.  Errors: as fasa_workspace_size (FASA_ERR_INVALID_ARG for a
+ * NULL path). */
+enum {
+  FASA_PATH_NONE = 0,
+  FASA_PATH_LISTS = 1,
+  FASA_PATH_FILTERED_LISTS = 2,
+  FASA_PATH_FILTER = 3,
+  FASA_PATH_SPLIT = 4
+};
+fasa_status fasa_decode_path(const fasa_shape* shape, int32_t max_t, int32_t* path);
+
 /* ---- FASA-M: the memory-optimised placement (section 3.4, "Hardware-Aware
  * Variants", FASA-M and Equation 10).  The GPU keeps only the dominant-key
  * cache (the slab) and per-step buffers; the non-dominant key columns and all

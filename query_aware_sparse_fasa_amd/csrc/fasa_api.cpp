@@ -249,6 +249,23 @@ fasa_status fasa_workspace_size(const fasa_shape* shape, int32_t max_t, size_t* 
   return FASA_OK;
 }
 
+fasa_status fasa_decode_path(const fasa_shape* shape, int32_t max_t, int32_t* path) {
+  fasa_status st = check_shape(shape);
+  if (st != FASA_OK) return st;
+  if ((st = check_max_t(shape, max_t)) != FASA_OK) return st;
+  if (!path) return FASA_ERR_INVALID_ARG;
+  Common c = make_common(shape, max_t);
+  c.score_stride = (max_t + 3) & ~3;   // as the decode step lays out its workspace
+  const FacPlan p = fasa::fac_plan(c);
+  const int lists = fasa::decode_lists(c, p);
+  if (max_t <= 0) *path = FASA_PATH_NONE;
+  else if (lists == fasa::kFromLists) *path = FASA_PATH_LISTS;
+  else if (lists == fasa::kFromListsB1) *path = FASA_PATH_FILTERED_LISTS;
+  else if (fasa::fac_selects(c, p)) *path = FASA_PATH_FILTER;
+  else *path = FASA_PATH_SPLIT;
+  return FASA_OK;
+}
+
 fasa_status fasa_check_fc_idx(const fasa_shape* shape, const int32_t* fc_idx_host) {
   fasa_status st = check_shape(shape);
   if (st != FASA_OK) return st;

@@ -26,6 +26,7 @@ BLOCK = 256
 EXPORTS = ["fasa_status_str", "fasa_validate_shape", "fasa_selection_capacity",
            "fasa_workspace_size", "fasa_check_fc_idx", "fasa_slab_build", "fasa_slab_append",
            "fasa_tip", "fasa_topk", "fasa_fac", "fasa_decode", "fasa_decode_tip", "fasa_decode_rest",
+           "fasa_decode_path",
            "fasa_dense_workspace_size",
            "fasa_dense_decode", "fasa_m_host_sizes", "fasa_m_offload", "fasa_m_workspace_size",
            "fasa_m_decode", "fasa_m_decode_select", "fasa_m_prefetch", "fasa_m_decode_finish",
@@ -85,6 +86,7 @@ def lib() -> ctypes.CDLL:
         "fasa_decode_tip": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
         "fasa_decode_rest": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, ctypes.c_size_t,
                                             _P]),
+        "fasa_decode_path": (ctypes.c_int, [_S, _I32, ctypes.POINTER(ctypes.c_int32)]),
         "fasa_dense_workspace_size": (ctypes.c_int, [_S, _I32, ctypes.POINTER(ctypes.c_size_t)]),
         "fasa_dense_decode": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
         "fasa_m_host_sizes": (ctypes.c_int, [_S, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t),
@@ -184,6 +186,16 @@ def fasa_workspace_size(shape: fasa_shape, max_t: int) -> int:
     n = ctypes.c_size_t()
     _check(lib().fasa_workspace_size(ctypes.byref(shape), max_t, ctypes.byref(n)), "fasa_workspace_size")
     return n.value
+
+
+# Launch structures reported by fasa_decode_path (the header's FASA_PATH_* values).
+PATH_NONE, PATH_LISTS, PATH_FILTERED_LISTS, PATH_FILTER, PATH_SPLIT = 0, 1, 2, 3, 4
+
+
+def fasa_decode_path(shape: fasa_shape, max_t: int) -> int:
+    v = ctypes.c_int32()
+    _check(lib().fasa_decode_path(ctypes.byref(shape), max_t, ctypes.byref(v)), "fasa_decode_path")
+    return v.value
 
 
 def fasa_check_fc_idx(shape: fasa_shape, fc_idx_host) -> None:

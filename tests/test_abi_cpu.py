@@ -23,7 +23,7 @@ def header_functions():
 def test_exports_every_declared_symbol():
     L = fasa.lib()
     names = header_functions()
-    assert len(names) == 27, names
+    assert len(names) == 28, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(fasa.EXPORTS) == names
@@ -46,6 +46,31 @@ def good(**kw):
                 kv_dtype=torch.bfloat16)
     base.update(kw)
     return fasa.make_shape(**base)
+
+
+@pytest.mark.parametrize("key,max_t,path", [
+    ("c1", 4096, fasa.PATH_LISTS), ("c2", 32768, fasa.PATH_LISTS), ("c3", 32768, fasa.PATH_SPLIT),
+    ("c4", 131072, fasa.PATH_FILTERED_LISTS), ("c5", 65536, fasa.PATH_FILTER)])
+def test_decode_path_of_each_workload(key, max_t, path):
+    """The launch structure chosen for each workload at its full size (host
+    logic only): lists at the single head and the 8B layer, filtered lists at
+    the Qwen shape, the filter launch for the 512-unit ragged batch, the split
+    FAC for the large budget."""
+    from query_aware_sparse_fasa_amd import synth
+    cfg = synth.CONFIGS[key]
+    s = fasa.make_shape(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.n_fc, cfg.budget, (max_t + 255) // 256,
+                        cfg.torch_dtype, cfg.n_sink, cfg.n_recent)
+    assert fasa.fasa_decode_path(s, max_t) == path
+    assert fasa.fasa_decode_path(s, 0) == fasa.PATH_NONE
+
+
+def test_decode_path_rejects_bad_arguments():
+    s = good()
+    assert fasa.lib().fasa_decode_path(ctypes.byref(s), 4096, None) == fasa.FASA_ERR_INVALID_ARG
+    bad = good(n_fc=0)
+    v = ctypes.c_int32()
+    assert fasa.lib().fasa_decode_path(ctypes.byref(bad), 4096, ctypes.byref(v)) != 0
+    assert fasa.lib().fasa_decode_path(ctypes.byref(s), 16 * 256 + 1, ctypes.byref(v)) != 0
 
 
 def test_valid_shape_and_sizes():

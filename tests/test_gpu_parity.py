@@ -724,6 +724,7 @@ def test_decode_long_rows_ragged():
     say("[long rows] c4 shape, lengths 90000 1500 0 1")
     inp = synth.make_inputs(cfg, seed=21, seq_lens=[90000, 1500, 0, 1])
     L = DeviceLayer(inp)
+    assert fasa.fasa_decode_path(L.shape, L.max_t) == fasa.PATH_FILTERED_LISTS
     L.out.fill_(float("nan"))
     L.decode()
     torch.cuda.synchronize()
@@ -773,6 +774,7 @@ def test_decode_filtered_lists_fallbacks():
         p, s_ = int(inp.block_table[1, j // 256]), j % 256
         inp.k_pool[p, 1, s_] = (inp.k_pool[p, 1, s_].float() + (40.0 + 0.01 * j) * u).to(inp.k_pool.dtype)
     L = DeviceLayer(inp)
+    assert fasa.fasa_decode_path(L.shape, L.max_t) == fasa.PATH_FILTERED_LISTS
     L.workspace.zero_()
     L.decode_tip()
     L.tip()
@@ -802,6 +804,22 @@ def test_decode_filtered_lists_fallbacks():
         torch.cuda.synchronize()
         for x, y in zip(a, (L.out, L.sel_idx, L.sel_count)):
             assert torch.equal(x, y), "random workspace"
+
+
+def test_decode_filtered_lists_fp32_forced():
+    """The histogram-filtered list path with fp32 caches (fp64 softmax and
+    weighted sum, the unmasked row batches included) and forced sink and
+    recent tokens: the Qwen2.5-7B layer shape at rows of 131072 and 77777
+    tokens, B = 1024 plus 4 + 64 forced; every unit against the oracle."""
+    cfg = C["c4"].replace(dtype="fp32", batch=2, n_sink=4, n_recent=64)
+    say("[filtered lists fp32] c4 shape fp32, lengths 131072 77777, 4 + 64 forced")
+    inp = synth.make_inputs(cfg, seed=57, seq_lens=[131072, 77777])
+    L = DeviceLayer(inp)
+    assert fasa.fasa_decode_path(L.shape, L.max_t) == fasa.PATH_FILTERED_LISTS
+    L.out.fill_(float("nan"))
+    L.decode()
+    torch.cuda.synchronize()
+    _check_decode(inp, L, oracle_units(inp), "filtered lists fp32")
 
 
 def test_decode_tip_histograms_ragged():
