@@ -34,6 +34,7 @@ __host__ __device__ __forceinline__ int filter_chunks(const Common& c) {
 template <int NTH>
 struct SelState {
   alignas(16) uint32_t hist[HB];
+  alignas(16) uint32_t hist2[HB];   // the exact select's passes alternate between hist2 and hist
   uint32_t wave_sum[2][NTH / 64];   // two buffers: back-to-back scans alternate
   uint32_t digit, rem, full;
   uint32_t cut;                     // emitted lists: largest threshold of a chunk that left a candidate out, or 0
@@ -85,21 +86,23 @@ __device__ __forceinline__ uint32_t wave_base(SelState<NTH>& s, uint32_t wave_va
 // owns the BPT bins below NB - BPT t (read as 16-byte vectors when BPT >= 4);
 // an exclusive scan over threads counts the keys above them, and the thread
 // whose bins hold the crossing walks them in registers.  Leaves s.digit
-// untouched when there are fewer than rem keys in total.
+// untouched when there are fewer than rem keys in total.  hist: the histogram
+// (s.hist unless given).
 template <int NTH, int NB>
-__device__ __forceinline__ void find_digit(SelState<NTH>& s, uint32_t rem) {
+__device__ __forceinline__ void find_digit(SelState<NTH>& s, uint32_t rem, const uint32_t* hist = nullptr) {
   constexpr int BPT = NB > NTH ? NB / NTH : 1;
+  const uint32_t* hb = hist ? hist : s.hist;
   const int lo = NB - BPT * (int(threadIdx.x) + 1);     // lowest owned bin
   uint32_t h[BPT];
   if constexpr (BPT >= 4) {
 #pragma unroll
     for (int v = 0; v < BPT / 4; ++v) {
-      const uint4 x = reinterpret_cast<const uint4*>(s.hist + lo)[v];
+      const uint4 x = reinterpret_cast<const uint4*>(hb + lo)[v];
       h[4 * v + 0] = x.x; h[4 * v + 1] = x.y; h[4 * v + 2] = x.z; h[4 * v + 3] = x.w;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) h[i] = lo + i >= 0 ? s.hist[lo + i] : 0u;
+    for (int i = 0; i < BPT; ++i) h[i] = lo + i >= 0 ? hb[lo + i] : 0u;
   }
   uint32_t sum = 0;
 #pragma unroll
@@ -124,6 +127,12 @@ __device__ __forceinline__ void find_digit(SelState<NTH>& s, uint32_t rem) {
 template <int NTH, int NB>
 __device__ __forceinline__ void zero_bins(SelState<NTH>& s) {
   for (int i = threadIdx.x; i < NB / 4; i += NTH) reinterpret_cast<uint4*>(s.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+// The exact select's first buffer, zeroed by every gather that precedes it
+// (published by the gather's barriers).
+template <int NTH>
+__device__ __forceinline__ void zero_hist2(SelState<NTH>& s) {
+  for (int i = threadIdx.x; i < HB / 4; i += NTH) reinterpret_cast<uint4*>(s.hist2)[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // Run-length histogram of one lane's slots: consecutive active slots in the same
@@ -348,7 +357,10 @@ __device__ __forceinline__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off,
 // all_eq: every key equal to the prefix is taken (skip to one scan).  Thread t
 // owns a contiguous run of the keys.
 // Returns the determined digits of the Bc-th largest key with the others zero
-// (a lower bound of that key).
+// (a lower bound of that key).  The passes alternate histogram buffers: the
+// first pass counts into s.hist2, which the caller's gather zeroed, and each
+// pass zeroes the next one's buffer (free since the previous digit search
+// ended) while it counts, so no pass waits on its own zeroing.
 template <int NTH>
 __device__ __forceinline__ uint32_t lds_select_from(SelState<NTH>& s, const uint32_t* key, const int32_t* idx,
                                                     int N, int Bc, uint32_t prefix, uint32_t pmask, uint32_t rem,
@@ -356,27 +368,33 @@ __device__ __forceinline__ uint32_t lds_select_from(SelState<NTH>& s, const uint
   const int tid = threadIdx.x;
   const int per = (N + NTH - 1) / NTH;
   const int i0 = min(N, tid * per), i1 = min(N, i0 + per);
+  uint32_t* cur = s.hist2;
+  uint32_t* nxt = s.hist;
 #pragma unroll 1
   for (; !all_eq && pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const uint32_t dmask = pass == 2 ? 1023u : 2047u;
-    if (pass == 2) zero_bins<NTH, 1024>(s);
-    else zero_bins<NTH, 2048>(s);
-    __syncthreads();
+    if (pass < 2) {
+      for (int i = tid; i < (pass == 1 ? 1024 : 2048) / 4; i += NTH)
+        reinterpret_cast<uint4*>(nxt)[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
     RunHist rh;
     for (int i = i0; i < i1; ++i) {
       const uint32_t k = key[i];
-      rh.add(s.hist, (k & pmask) == prefix, (k >> shift) & dmask);
+      rh.add(cur, (k & pmask) == prefix, (k >> shift) & dmask);
     }
-    rh.flush(s.hist);
-    __syncthreads();
-    if (pass == 2) find_digit<NTH, 1024>(s, rem);
-    else find_digit<NTH, 2048>(s, rem);
+    rh.flush(cur);
+    __syncthreads();                        // the counts, and the next buffer's zeros
+    if (pass == 2) find_digit<NTH, 1024>(s, rem, cur);
+    else find_digit<NTH, 2048>(s, rem, cur);
     const uint32_t d = s.digit, full = s.full;
     rem = s.rem;
     prefix |= d << shift;
     pmask |= dmask << shift;
     all_eq = full != 0u;
+    uint32_t* t = cur;
+    cur = nxt;
+    nxt = t;
   }
   if (all_eq) {
     // Every key at or above the prefix is taken: one scan places them.
@@ -809,6 +827,7 @@ __device__ void select_from_lists_b1(SelState<NTH>& s, uint32_t* key, int32_t* i
   find_digit<NTH, HB>(s, uint32_t(Bc));      // ends with a barrier: s.hist is free again
   const uint32_t b1 = s.digit;
   zero_bins<NTH, HB>(s);                     // the second-digit histogram; published by the gather's first barrier
+  zero_hist2<NTH>(s);
   uint32_t above = 0;
   const int N = gather_lists_b1<NTH, EARLY>(s, sl, m, nfc, cap_lds, key, idx, b1, above);
   if (N >= Bc) {
@@ -824,6 +843,7 @@ __device__ void select_from_kept(SelState<NTH>& s, int32_t* chunk_off, uint32_t*
                                  const int (&cnt)[CPT],
                                  const uint2 (&pre)[PRE * D], int c_lo, int c_hi, int Bc, int b1, int32_t* out) {
   zero_bins<NTH, HB>(s);               // the gather's second-digit histogram; published by its first barrier
+  zero_hist2<NTH>(s);
   uint32_t above = 0;
   const int N = gather_kept<NTH, PRE, D>(s, chunk_off, unit_slots, nfc, cap_lds, cnt, pre, key, idx, b1, above);
   if (N >= Bc) lds_select<NTH>(s, key, idx, N, Bc, b1, above, out);
@@ -841,6 +861,7 @@ __device__ void select_from_emitted(SelState<NTH>& s, int32_t* chunk_off, uint32
                                     const uint2 (&meta)[CPT], const uint2 (&pre)[PRE * D], int c_lo, int c_hi, int Bc,
                                     int32_t* out) {
   zero_bins<NTH, HB>(s);               // the gather's first-digit histogram; published by its first barrier
+  zero_hist2<NTH>(s);
   const int N = gather_emitted<NTH, PRE, D>(s, chunk_off, unit_slots, nfc, cap_lds, meta, pre, key, idx);
   if (N >= Bc && select_emitted<NTH>(s, key, idx, N, Bc, out)) return;
   row_select<NTH, VEC>(s, row, lim, max_t, c_lo, c_hi, Bc, out);
