@@ -36,6 +36,10 @@ def _scratch_decode(L):
     (("c2", dict(batch=3, t=None, t_range=(9000, 20000)), 3), ("c5", dict(batch=2, t_range=(700, 3000)), 5)),
     # Large budget (filter launch, separate select, split FAC), then the tiny fp32 workload.
     (("c3", dict(batch=2, t=None, t_range=(7000, 9000)), 7), ("c1", dict(), 1)),
+    # The Qwen-shaped layer on the histogram-filtered lists (TIP's unit
+    # histogram and arrival counters in the scratch), a 131072-token row, then
+    # a shorter one.
+    (("c4", dict(batch=1), 11), ("c4", dict(batch=1, t=None, t_range=(85000, 100000)), 13)),
 ])
 def test_scratch_decode_matches_workspace_decode(cases):
     for k, (key, repl, seed) in enumerate(cases):
@@ -44,6 +48,8 @@ def test_scratch_decode_matches_workspace_decode(cases):
         inp = synth.make_inputs(cfg, seed=seed)
         L = DeviceLayer(inp)
         assert fasa.fasa_workspace_size(L.shape, L.max_t) <= fasa.fasa_scratch_capacity()
+        if key == "c4":
+            assert fasa.fasa_decode_path(L.shape, L.max_t) == fasa.PATH_FILTERED_LISTS
         got = _scratch_decode(L)
         L.out.fill_(float("nan"))
         L.decode()
