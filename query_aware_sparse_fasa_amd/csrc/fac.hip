@@ -667,7 +667,9 @@ int decode_lists(const Common& c, const FacPlan& p) {
   // Few units (one-head selecting workgroups): there the filter launch and its
   // launch gap are a large part of the step.  Many units keep the filter
   // launch, whose cost they share, and whose global threshold does not depend
-  // on how the top keys cluster along the row.
+  // on how the top keys cluster along the row (measured: the ragged batch of
+  // 64 sequences x 8 kv heads on TIP's lists, four heads per workgroup, took
+  // 350 us against 292 us).
   if (c.max_t <= 0 || !fac_selects(c, p) || select_heads(c) != 1 || emit_chunks(c) > 64 * sel::CPT)
     return kFromFilter;
   // Every chunk writes emit_target() keys (more only with ties): at the longest
