@@ -383,6 +383,12 @@ def main():
     # kernel variant, grid and outputs as inside fasa_decode).
     reps = max(1, min(50, 2000 // L))
     t_tip = time_graph(torch, stream, [g_tip], reps) / (reps * L)
+    # TIP alone, repeated with nothing consuming what it leaves, can leave unit
+    # histograms that only steer a later select to its slow path: clear the
+    # workspaces before timing the other stages.
+    for lay in layers:
+        lay.workspace.zero_()
+    torch.cuda.synchronize()
     t_topk = time_graph(torch, stream, [g_topk], reps) / (reps * L)
     t_fac = time_graph(torch, stream, [g_fac], reps) / (reps * L)
     log(f"[bench] alone: tip {t_tip * 1e6:.2f} us, topk {t_topk * 1e6:.2f} us, fac {t_fac * 1e6:.2f} us")
