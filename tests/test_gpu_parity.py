@@ -822,6 +822,38 @@ def test_decode_filtered_lists_fp32_forced():
     _check_decode(inp, L, oracle_units(inp), "filtered lists fp32")
 
 
+def test_decode_filtered_lists_in_two_stages():
+    """The histogram-filtered list path (Qwen2.5-7B layer, B = 1024, a ragged
+    batch of three rows up to 131072 tokens) split into fasa_decode_tip and
+    fasa_decode_rest gives fasa_decode's results bit for bit; so does a second
+    TIP stage before the rest, which leaves every unit histogram at twice its
+    counts (a threshold bin that keeps fewer than B keys, so the select takes
+    its slower route), and a decode that follows it on the same workspace."""
+    cfg = C["c4"].replace(batch=3, t=None, t_range=(40000, 131072))
+    say("[filtered lists two stages] c4 shape, 3 ragged rows")
+    inp = synth.make_inputs(cfg, seed=61)
+    L = DeviceLayer(inp)
+    assert fasa.fasa_decode_path(L.shape, L.max_t) == fasa.PATH_FILTERED_LISTS
+    L.decode()
+    torch.cuda.synchronize()
+    ref = (L.out.clone(), L.sel_idx.clone(), L.sel_count.clone())
+    assert not torch.isnan(ref[0]).any()
+    for tips in (1, 2, 1):
+        L.out.fill_(float("nan"))
+        L.sel_idx.fill_(-7)
+        L.sel_count.fill_(-7)
+        for _ in range(tips):
+            L.decode_tip()
+        L.decode_rest()
+        torch.cuda.synchronize()
+        for x, y in zip(ref, (L.out, L.sel_idx, L.sel_count)):
+            assert torch.equal(x, y), tips
+    L.decode()
+    torch.cuda.synchronize()
+    for x, y in zip(ref, (L.out, L.sel_idx, L.sel_count)):
+        assert torch.equal(x, y), "decode after the stages"
+
+
 def test_decode_tip_histograms_ragged():
     """A ragged batch of 64 sequences x 8 kv heads (512 units, rows up to 16384
     tokens, B = 512 plus 4 + 64 forced: the three-launch step, TIP building the
