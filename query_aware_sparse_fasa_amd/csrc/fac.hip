@@ -347,10 +347,13 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   // the matrix tiles mostly idle, and its 32 rows per wave in one round trip
   // against two 16-row blocks); fp32 caches always take the vector path.
   constexpr bool kMfma = sizeof(T) == 2 && HG >= 4;
-  Raw8<T> qraw[kMfma ? 1 : HG];
+  // The filtered lists' 1024-row lists run 8 lanes per row (FacWaveOct).
+  constexpr bool kOct = B1 && sizeof(T) == 2;
+  using VecWave = std::conditional_t<kOct, FacWaveOct<HG>, FacWave<T, Acc, HG>>;
+  typename VecWave::QRaw qraw[kMfma ? 1 : HG];
   uint4 qm[kMfma ? 4 : 1];
   if constexpr (kMfma) FacWaveMfma<HG>::load_q(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, qm);
-  else FacWave<T, Acc, HG>::load_q(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, qraw);
+  else VecWave::load_q(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, qraw);
   // The sequence's block-table row (at most kBtabLds entries), held in
   // registers through the select and moved to LDS after it.
   const int32_t* btab = a.block_table + int64_t(b) * c.max_blocks;
@@ -401,7 +404,7 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   }
 
   // Row r of the list: the forced prefix, the chosen, then the forced suffix.
-  std::conditional_t<kMfma, FacWaveMfma<HG>, FacWave<T, Acc, HG>> w;
+  std::conditional_t<kMfma, FacWaveMfma<HG>, VecWave> w;
   if constexpr (kMfma) w.init_raw(qm, nh, c.scale, sm.u.tiles[wave]);
   else w.init_raw(qraw, nh, c.scale);
   auto token = [&](int r) -> int {
@@ -421,7 +424,7 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   const T* vbase = static_cast<const T*>(a.v_pool) + int64_t(g) * c.kv_head_stride;
   // Row quads in flight per wave: 8 (a whole 32-row share of a 256-row list in
   // one round trip) for one head; fewer as the per-head state grows.
-  constexpr int U = HG == 1 ? 8 : (HG <= 4 && sizeof(Acc) == 4 ? 4 : 2);
+  constexpr int U = kOct ? 4 : (HG == 1 ? 8 : (HG <= 4 && sizeof(Acc) == 4 ? 4 : 2));
   if constexpr (kMfma) {
     w.template run<false>(r0, r1, lane_offset, kbase, vbase);
     w.fold_row_groups();
@@ -433,12 +436,13 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
 
   // Fold the waves through LDS and write the heads' outputs.
   WaveFold<Acc, HG, kSelWaves>& f = sm.u.fold;
-  const int lane = tid & 63, sub = lane & 15;
-  if (lane < 16) {
+  constexpr int kLpr = kMfma ? 16 : VecWave::kLanesPerRow, kCh = kHeadDim / kLpr;
+  const int lane = tid & 63, sub = lane & (kLpr - 1);
+  if (lane < kLpr) {
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f.acc[wave][hh][8 * sub + e] = w.acc[hh][e];
+      for (int e = 0; e < kCh; ++e) f.acc[wave][hh][kMfma ? kCh * sub + e : VecWave::channel(sub, e)] = w.acc[hh][e];
       if (sub == 0) {
         f.m[wave][hh] = w.m[hh];
         f.l[wave][hh] = w.l[hh];

@@ -110,6 +110,10 @@ __device__ __forceinline__ float dot8(const uint4& q, const Raw8<uint16_t>& k) {
 template <typename T, typename Acc, int HG>
 struct FacWave {
   static constexpr bool kBf16 = sizeof(T) == 2;
+  static constexpr int kLanesPerRow = 16;   // lanes per row; each holds kCh channels
+  static constexpr int kCh = 8;
+  using QRaw = Raw8<T>;
+  static __device__ __forceinline__ int channel(int sub, int e) { return 8 * sub + e; }
   // Query slices: raw bf16 pairs (logits scaled afterwards by zscale), or
   // pre-scaled fp64 values for fp32 caches.
   uint4 q2[kBf16 ? HG : 1];
@@ -299,6 +303,217 @@ struct FacWave {
     }
   }
   __device__ __forceinline__ void fold_row_groups() {
+    fold_pairs<16>();
+    fold_pairs<32>();
+  }
+};
+
+// DPP patterns inside each 8-lane half of a 16-lane row.
+constexpr int kDppHalfMirror = 0x141;   // lane i reads lane 7 - i of its half row
+constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2, 3, 0, 1]: lane i reads lane i ^ 2
+constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1, 0, 3, 2]: lane i reads lane i ^ 1
+constexpr int kDppRowRor8 = 0x128;      // lane i reads lane i ^ 8 of its 16-lane row
+
+// Sum over the 8 lanes of a half row, the same value in all 8: the pair sums
+// v_i + v_(7-i), then pairs of those, then the two halves of the quad (every
+// lane adds the same two pair-of-pair sums, so the results agree bit for bit).
+__device__ __forceinline__ float oct_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppHalfMirror, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppQuadSwap2, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppQuadSwap1, 0xF, 0xF, false));
+  return v;
+}
+
+// 16 bf16 values of a row: channels c .. c+7 and 64+c .. 64+c+7 (from p = row + c),
+// so that the 8 lanes of a row read its first 128 bytes with one instruction
+// and the other 128 with the next.
+struct Raw16 {
+  uint4 a, b;
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    a = *reinterpret_cast<const uint4*>(p);
+    b = *reinterpret_cast<const uint4*>(p + 64);
+  }
+  __device__ __forceinline__ void unpack(float (&x)[16]) const {
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[2 * i] = bf16_lo(w[i]);
+      x[2 * i + 1] = bf16_hi(w[i]);
+    }
+  }
+};
+
+// The same online softmax as FacWave for bf16 caches, with 8 lanes per row and
+// 16 channels per lane: a wave takes eight rows per step.  Per row that halves
+// the lanes running the logit reduction, the exponentials and the row
+// addresses, and takes one DPP step less for the sum; the V unpack and FMAs stay
+// one per channel.  exp2 is the hardware instruction: arguments below -126 (a
+// weight under 2^-126 of the running maximum's) give 0 instead of a denormal.
+template <int HG>
+struct FacWaveOct {
+  static constexpr int kLanesPerRow = 8;
+  static constexpr int kCh = 16;
+  using QRaw = Raw16;
+  // Channel of a lane's value e (sub = lane % 8).
+  static __device__ __forceinline__ int channel(int sub, int e) { return (e < 8 ? 0 : 64) + 8 * sub + (e & 7); }
+  uint4 q2[HG][2];
+  float zscale;
+  float m[HG], l[HG], acc[HG][16];
+
+  static __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+  static __device__ __forceinline__ float weight(float mi, float M) {
+    return mi == -INFINITY ? 0.f : ex2(mi - M);
+  }
+
+  static __device__ __forceinline__ void load_q(const uint16_t* q_head0, int nh, Raw16 (&qr)[HG]) {
+    const int sub = threadIdx.x & 7;
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) qr[hh].load(q_head0 + int64_t(min(hh, nh - 1)) * kHeadDim + 8 * sub);
+  }
+
+  __device__ __forceinline__ void init_raw(const Raw16 (&qr)[HG], int nh, float scale) {
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      m[hh] = -INFINITY;
+      l[hh] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[hh][e] = 0.f;
+      q2[hh][0] = hh < nh ? qr[hh].a : z4;
+      q2[hh][1] = hh < nh ? qr[hh].b : z4;
+    }
+    zscale = scale * 1.4426950408889634f;
+  }
+
+  // Rows r0 .. r1-1, as FacWave::run; U: rows per lane in flight (8 U per wave).
+  template <int U = 4, bool NT = false, bool FAST = false, typename LaneOffset>
+  __device__ __forceinline__ void run(int r0, int r1, LaneOffset lane_offset, const uint16_t* kbase,
+                                      const uint16_t* vbase) {
+    static_assert(!NT, "ordinary row loads");
+    const int lane = threadIdx.x & 63, rg = lane >> 3, sub = lane & 7;
+    kbase += 8 * sub;
+    vbase += 8 * sub;
+    for (int base = r0; base < r1; base += 64) {   // wave-uniform
+      const int64_t my_off = lane_offset(base + lane);
+      const uint64_t ok = __ballot(my_off >= 0);
+      if (ok == 0) continue;
+      const int64_t dummy = __shfl(my_off, __ffsll((unsigned long long)ok) - 1, 64);
+      const int nrows = min(64, r1 - base);
+      for (int q8 = 0; q8 < nrows; q8 += 8 * U) {
+        Raw16 kr[U], vr[U];
+        static_assert(8 * U < 64, "a batch within one 64-row window");
+        constexpr uint64_t kAll = (uint64_t(1) << (8 * U)) - 1;
+        const bool full = FAST && q8 + 8 * U <= nrows && ((ok >> q8) & kAll) == kAll;
+        if constexpr (FAST) if (full) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int64_t o = __shfl(my_off, q8 + 8 * u + rg, 64);
+            kr[u].load(kbase + o);
+            vr[u].load(vbase + o);
+          }
+          const bool all[U] = {};
+          absorb<U, false>(kr, vr, all);
+          continue;
+        }
+        bool valid[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int src = q8 + 8 * u + rg;
+          const int64_t off = __shfl(my_off, src < 64 ? src : 0, 64);
+          valid[u] = (src < nrows) && off >= 0;
+          const int64_t o = valid[u] ? off : dummy;
+          kr[u].load(kbase + o);
+          vr[u].load(vbase + o);
+        }
+        absorb<U>(kr, vr, valid);
+      }
+    }
+  }
+
+  template <int U, bool MASKED = true>
+  __device__ __forceinline__ void absorb(const Raw16 (&kr)[U], const Raw16 (&vr)[U], const bool (&valid)[U]) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    auto h = [](uint32_t x) { return __builtin_bit_cast(bf16x2, x); };
+    float z[U][HG], mn[HG];
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) mn[hh] = m[hh];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        const uint4 &qa = q2[hh][0], &qb = q2[hh][1];
+        float s0 = __builtin_amdgcn_fdot2_f32_bf16(h(kr[u].a.x), h(qa.x), 0.f, false);
+        float s1 = __builtin_amdgcn_fdot2_f32_bf16(h(kr[u].a.y), h(qa.y), 0.f, false);
+        s0 = __builtin_amdgcn_fdot2_f32_bf16(h(kr[u].a.z), h(qa.z), s0, false);
+        s1 = __builtin_amdgcn_fdot2_f32_bf16(h(kr[u].a.w), h(qa.w), s1, false);
+        s0 = __builtin_amdgcn_fdot2_f32_bf16(h(kr[u].b.x), h(qb.x), s0, false);
+        s1 = __builtin_amdgcn_fdot2_f32_bf16(h(kr[u].b.y), h(qb.y), s1, false);
+        s0 = __builtin_amdgcn_fdot2_f32_bf16(h(kr[u].b.z), h(qb.z), s0, false);
+        s1 = __builtin_amdgcn_fdot2_f32_bf16(h(kr[u].b.w), h(qb.w), s1, false);
+        const float zz = oct_sum(s0 + s1) * zscale;
+        z[u][hh] = (!MASKED || valid[u]) ? zz : -INFINITY;
+        mn[hh] = fmaxf(mn[hh], z[u][hh]);
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      const float corr = weight(m[hh], mn[hh]);
+      l[hh] *= corr;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[hh][e] *= corr;
+      m[hh] = mn[hh];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vx[16];
+      vr[u].unpack(vx);
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        const float pz = MASKED ? weight(z[u][hh], mn[hh]) : ex2(z[u][hh] - mn[hh]);
+        l[hh] += pz;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[hh][e] = fmaf(pz, vx[e], acc[hh][e]);
+      }
+    }
+  }
+
+  // The pair of row groups that differ in lane bit 3 (PAIR 8, a DPP rotation by
+  // 8 inside the 16-lane row), bit 4 or bit 5, merged by the log-sum-exp rule in
+  // (lower, upper) order in both lanes of the pair.
+  template <int PAIR>
+  static __device__ __forceinline__ void pair_of(float v, float& lo, float& hi) {
+    if constexpr (PAIR == 8) {
+      const float o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowRor8, 0xF, 0xF, false));
+      const bool upper = threadIdx.x & 8;
+      lo = upper ? o : v;
+      hi = upper ? v : o;
+    } else {
+      lane_pair<PAIR>(v, lo, hi);
+    }
+  }
+  template <int PAIR>
+  __device__ __forceinline__ void fold_pairs() {
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      float ma, mb, la, lb;
+      pair_of<PAIR>(m[hh], ma, mb);
+      pair_of<PAIR>(l[hh], la, lb);
+      const float mn = fmaxf(ma, mb);
+      const float wa = weight(ma, mn), wb = weight(mb, mn);
+      l[hh] = la * wa + lb * wb;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float aa, ab;
+        pair_of<PAIR>(acc[hh][e], aa, ab);
+        acc[hh][e] = aa * wa + ab * wb;
+      }
+      m[hh] = mn;
+    }
+  }
+  // Afterwards lanes 0 .. 7 (and every other half row) hold the wave's state
+  // for their 16 channels.
+  __device__ __forceinline__ void fold_row_groups() {
+    fold_pairs<8>();
     fold_pairs<16>();
     fold_pairs<32>();
   }
