@@ -822,6 +822,23 @@ def test_decode_filtered_lists_fp32_forced():
     _check_decode(inp, L, oracle_units(inp), "filtered lists fp32")
 
 
+def test_decode_filtered_lists_bf16_forced():
+    """The histogram-filtered list path with bf16 caches and forced tokens
+    (3 sink, 37 recent): lists of B + 40 rows end in a part batch, and a
+    900-token row keeps every token (a list of 900 rows), so the 8-lanes-per-row
+    FAC runs its masked batches as well as the unmasked ones.  Qwen2.5-7B layer
+    shape, rows of 131072, 77777 and 900 tokens; every unit against the oracle."""
+    cfg = C["c4"].replace(batch=3, n_sink=3, n_recent=37)
+    say("[filtered lists bf16] c4 shape, lengths 131072 77777 900, 3 + 37 forced")
+    inp = synth.make_inputs(cfg, seed=59, seq_lens=[131072, 77777, 900])
+    L = DeviceLayer(inp)
+    assert fasa.fasa_decode_path(L.shape, L.max_t) == fasa.PATH_FILTERED_LISTS
+    L.out.fill_(float("nan"))
+    L.decode()
+    torch.cuda.synchronize()
+    _check_decode(inp, L, oracle_units(inp), "filtered lists bf16 forced")
+
+
 def test_decode_filtered_lists_in_two_stages():
     """The histogram-filtered list path (Qwen2.5-7B layer, B = 1024, a ragged
     batch of three rows up to 131072 tokens) split into fasa_decode_tip and
