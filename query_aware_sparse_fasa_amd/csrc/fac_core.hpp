@@ -7,6 +7,9 @@
 // row, 8 channels per lane.  Every K/V row is loaded once and serves all HG
 // heads.  The state per head is (running max m, running sum l, acc[8 channels])
 // in each of the four 16-lane row groups; fold_row_groups() combines them.
+// FacWaveOct (bf16, long one-head lists) takes eight rows per step with 8 lanes
+// of 16 channels per row; FacWaveMfma (bf16, several heads) runs the same
+// softmax on the matrix cores.
 //
 // Precision: bf16 caches accumulate in fp32 (logits pre-scaled by log2(e),
 // exponentiated with exp2); fp32 caches run logits, softmax and the weighted sum
