@@ -305,7 +305,11 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   const Common& c = a.c;
   const WgCoord wg = xcd_grouped();
   const int b = wg.z, g = wg.y, hc = wg.x;
-  const int h0 = hc * HG, nh = min(HG, c.group - h0);
+  // The filtered lists' FAC (bf16) runs two workgroups per head, each over half
+  // of the V channels (FacWaveOct's VH): x = 2 head + half.
+  constexpr bool kVh = B1 && sizeof(T) == 2;
+  const int vpart = kVh ? (hc & 1) : 0;
+  const int h0 = (kVh ? hc >> 1 : hc) * HG, nh = min(HG, c.group - h0);
   const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t unit = int64_t(b) * c.n_kv_heads + g;
   constexpr int CHUNK = EMIT ? kEmitChunk : sel::FCH;
@@ -349,7 +353,7 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   constexpr bool kMfma = sizeof(T) == 2 && HG >= 4;
   // The filtered lists' 1024-row lists run 8 lanes per row (FacWaveOct).
   constexpr bool kOct = B1 && sizeof(T) == 2;
-  using VecWave = std::conditional_t<kOct, FacWaveOct<HG>, FacWave<T, Acc, HG>>;
+  using VecWave = std::conditional_t<kOct, FacWaveOct<HG, kVh>, FacWave<T, Acc, HG>>;
   typename VecWave::QRaw qraw[kMfma ? 1 : HG];
   uint4 qm[kMfma ? 4 : 1];
   if constexpr (kMfma) FacWaveMfma<HG>::load_q(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, qm);
@@ -406,6 +410,7 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   // Row r of the list: the forced prefix, the chosen, then the forced suffix.
   std::conditional_t<kMfma, FacWaveMfma<HG>, VecWave> w;
   if constexpr (kMfma) w.init_raw(qm, nh, c.scale, sm.u.tiles[wave]);
+  else if constexpr (kOct) w.init_raw(qraw, nh, c.scale, vpart);
   else w.init_raw(qraw, nh, c.scale);
   auto token = [&](int r) -> int {
     const int ch = sm.chosen[min(max(r - c_lo, 0), kSmallBudget - 1)];
@@ -436,13 +441,13 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
 
   // Fold the waves through LDS and write the heads' outputs.
   WaveFold<Acc, HG, kSelWaves>& f = sm.u.fold;
-  constexpr int kLpr = kMfma ? 16 : VecWave::kLanesPerRow, kCh = kHeadDim / kLpr;
+  constexpr int kLpr = kMfma ? 16 : VecWave::kLanesPerRow, kCh = kMfma ? kHeadDim / 16 : VecWave::kCh;
   const int lane = tid & 63, sub = lane & (kLpr - 1);
   if (lane < kLpr) {
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
 #pragma unroll
-      for (int e = 0; e < kCh; ++e) f.acc[wave][hh][kMfma ? kCh * sub + e : VecWave::channel(sub, e)] = w.acc[hh][e];
+      for (int e = 0; e < kCh; ++e) f.acc[wave][hh][w.chan(sub, e)] = w.acc[hh][e];
       if (sub == 0) {
         f.m[wave][hh] = w.m[hh];
         f.l[wave][hh] = w.l[hh];
@@ -450,8 +455,9 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < nh * kHeadDim; idx += kSelThreads) {
-    const int hh = idx / kHeadDim, ch = idx % kHeadDim;
+  constexpr int kOutCh = kVh ? kHeadDim / 2 : kHeadDim;   // this workgroup's output channels
+  for (int idx = tid; idx < nh * kOutCh; idx += kSelThreads) {
+    const int hh = idx / kOutCh, ch = kOutCh * vpart + idx % kOutCh;
     Acc M = neg_inf<Acc>();
 #pragma unroll
     for (int v = 0; v < kSelWaves; ++v) M = fmax(M, f.m[v][hh]);
@@ -621,7 +627,9 @@ hipError_t launch_fac_select_t(const FacArgs& a, int lists, hipStream_t s) {
   const dim3 grid((a.c.group + hg - 1) / hg, a.c.n_kv_heads, a.c.batch);
   const bool emitted = lists != kFromFilter;
   if (lists == kFromListsB1) {
-    hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, true>), grid, dim3(kSelThreads), 0, s, a);
+    // bf16: two workgroups per head, one per half of the V channels.
+    const dim3 g2(sizeof(T) == 2 ? 2 * grid.x : grid.x, grid.y, grid.z);
+    hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, true>), g2, dim3(kSelThreads), 0, s, a);
     return hipGetLastError();
   }
   // One head per workgroup has the registers for a deeper prefetch; it pays only

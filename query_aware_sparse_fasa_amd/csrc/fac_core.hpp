@@ -19,6 +19,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "fasa_device.hpp"
 #include "fasa_internal.hpp"
 
@@ -116,7 +118,7 @@ struct FacWave {
   static constexpr int kLanesPerRow = 16;   // lanes per row; each holds kCh channels
   static constexpr int kCh = 8;
   using QRaw = Raw8<T>;
-  static __device__ __forceinline__ int channel(int sub, int e) { return 8 * sub + e; }
+  __device__ __forceinline__ int chan(int sub, int e) const { return 8 * sub + e; }
   // Query slices: raw bf16 pairs (logits scaled afterwards by zscale), or
   // pre-scaled fp64 values for fp32 caches.
   uint4 q2[kBf16 ? HG : 1];
@@ -352,16 +354,25 @@ struct Raw16 {
 // addresses, and takes one DPP step less for the sum; the V unpack and FMAs stay
 // one per channel.  exp2 is the hardware instruction: arguments below -126 (a
 // weight under 2^-126 of the running maximum's) give 0 instead of a denormal.
-template <int HG>
+template <int HG, bool VH = false>
 struct FacWaveOct {
+  // VH: this wave's workgroup takes only half of each V row (channels
+  // 64 vpart .. 64 vpart + 63; the logits still use all of K), so one
+  // instruction per 8 rows brings its V instead of two; each lane then holds
+  // 8 accumulated channels instead of 16.
   static constexpr int kLanesPerRow = 8;
-  static constexpr int kCh = 16;
+  static constexpr int kCh = VH ? 8 : 16;
   using QRaw = Raw16;
-  // Channel of a lane's value e (sub = lane % 8).
-  static __device__ __forceinline__ int channel(int sub, int e) { return (e < 8 ? 0 : 64) + 8 * sub + (e & 7); }
+  using VRaw = std::conditional_t<VH, Raw8<uint16_t>, Raw16>;
   uint4 q2[HG][2];
   float zscale;
-  float m[HG], l[HG], acc[HG][16];
+  float m[HG], l[HG], acc[HG][kCh];
+  int vofs;                                 // VH: 64 vpart, the first channel of the half
+
+  // Channel of a lane's value e (sub = lane % 8).
+  __device__ __forceinline__ int chan(int sub, int e) const {
+    return VH ? vofs + 8 * sub + e : (e < 8 ? 0 : 64) + 8 * sub + (e & 7);
+  }
 
   static __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
   static __device__ __forceinline__ float weight(float mi, float M) {
@@ -374,18 +385,19 @@ struct FacWaveOct {
     for (int hh = 0; hh < HG; ++hh) qr[hh].load(q_head0 + int64_t(min(hh, nh - 1)) * kHeadDim + 8 * sub);
   }
 
-  __device__ __forceinline__ void init_raw(const Raw16 (&qr)[HG], int nh, float scale) {
+  __device__ __forceinline__ void init_raw(const Raw16 (&qr)[HG], int nh, float scale, int vpart = 0) {
     const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
       m[hh] = -INFINITY;
       l[hh] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[hh][e] = 0.f;
+      for (int e = 0; e < kCh; ++e) acc[hh][e] = 0.f;
       q2[hh][0] = hh < nh ? qr[hh].a : z4;
       q2[hh][1] = hh < nh ? qr[hh].b : z4;
     }
     zscale = scale * 1.4426950408889634f;
+    vofs = VH ? 64 * vpart : 0;
   }
 
   // Rows r0 .. r1-1, as FacWave::run; U: rows per lane in flight (8 U per wave).
@@ -395,7 +407,7 @@ struct FacWaveOct {
     static_assert(!NT, "ordinary row loads");
     const int lane = threadIdx.x & 63, rg = lane >> 3, sub = lane & 7;
     kbase += 8 * sub;
-    vbase += 8 * sub;
+    vbase += 8 * sub + vofs;
     for (int base = r0; base < r1; base += 64) {   // wave-uniform
       const int64_t my_off = lane_offset(base + lane);
       const uint64_t ok = __ballot(my_off >= 0);
@@ -403,7 +415,8 @@ struct FacWaveOct {
       const int64_t dummy = __shfl(my_off, __ffsll((unsigned long long)ok) - 1, 64);
       const int nrows = min(64, r1 - base);
       for (int q8 = 0; q8 < nrows; q8 += 8 * U) {
-        Raw16 kr[U], vr[U];
+        Raw16 kr[U];
+        VRaw vr[U];
         static_assert(8 * U < 64, "a batch within one 64-row window");
         constexpr uint64_t kAll = (uint64_t(1) << (8 * U)) - 1;
         const bool full = FAST && q8 + 8 * U <= nrows && ((ok >> q8) & kAll) == kAll;
@@ -434,7 +447,7 @@ struct FacWaveOct {
   }
 
   template <int U, bool MASKED = true>
-  __device__ __forceinline__ void absorb(const Raw16 (&kr)[U], const Raw16 (&vr)[U], const bool (&valid)[U]) {
+  __device__ __forceinline__ void absorb(const Raw16 (&kr)[U], const VRaw (&vr)[U], const bool (&valid)[U]) {
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
     auto h = [](uint32_t x) { return __builtin_bit_cast(bf16x2, x); };
     float z[U][HG], mn[HG];
@@ -463,19 +476,19 @@ struct FacWaveOct {
       const float corr = weight(m[hh], mn[hh]);
       l[hh] *= corr;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[hh][e] *= corr;
+      for (int e = 0; e < kCh; ++e) acc[hh][e] *= corr;
       m[hh] = mn[hh];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float vx[16];
+      float vx[kCh];
       vr[u].unpack(vx);
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh) {
         const float pz = MASKED ? weight(z[u][hh], mn[hh]) : ex2(z[u][hh] - mn[hh]);
         l[hh] += pz;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[hh][e] = fmaf(pz, vx[e], acc[hh][e]);
+        for (int e = 0; e < kCh; ++e) acc[hh][e] = fmaf(pz, vx[e], acc[hh][e]);
       }
     }
   }
@@ -505,7 +518,7 @@ struct FacWaveOct {
       const float wa = weight(ma, mn), wb = weight(mb, mn);
       l[hh] = la * wa + lb * wb;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < kCh; ++e) {
         float aa, ab;
         pair_of<PAIR>(acc[hh][e], aa, ab);
         acc[hh][e] = aa * wa + ab * wb;
@@ -556,6 +569,8 @@ constexpr int kMfmaTileElems = 16 * kMfmaTilePitch;  // one wave's tile
 
 template <int HG>
 struct FacWaveMfma {
+  // Channel of a lane's value e after fold_row_groups (lanes 0 .. 15 hold 8 each).
+  __device__ __forceinline__ int chan(int sub, int e) const { return 8 * sub + e; }
   typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
   typedef __attribute__((ext_vector_type(4))) short s16x4;
   typedef __attribute__((ext_vector_type(4))) float f32x4;
