@@ -305,9 +305,9 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   const Common& c = a.c;
   const WgCoord wg = xcd_grouped();
   const int b = wg.z, g = wg.y, hc = wg.x;
-  // The filtered lists' FAC (bf16) runs two workgroups per head, each over half
-  // of the V channels (FacWaveOct's VH): x = 2 head + half.
-  constexpr bool kVh = B1 && sizeof(T) == 2;
+  // The FAC over TIP's lists (bf16, one head per workgroup) runs two workgroups
+  // per head, each over half of the V channels (FacWaveOct's VH): x = 2 head + half.
+  constexpr bool kVh = EMIT && HG == 1 && sizeof(T) == 2;
   const int vpart = kVh ? (hc & 1) : 0;
   const int h0 = (kVh ? hc >> 1 : hc) * HG, nh = min(HG, c.group - h0);
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -351,8 +351,8 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   // the matrix tiles mostly idle, and its 32 rows per wave in one round trip
   // against two 16-row blocks); fp32 caches always take the vector path.
   constexpr bool kMfma = sizeof(T) == 2 && HG >= 4;
-  // The filtered lists' 1024-row lists run 8 lanes per row (FacWaveOct).
-  constexpr bool kOct = B1 && sizeof(T) == 2;
+  // One head over TIP's lists: 8 lanes per row (FacWaveOct).
+  constexpr bool kOct = EMIT && HG == 1 && sizeof(T) == 2;
   using VecWave = std::conditional_t<kOct, FacWaveOct<HG, kVh>, FacWave<T, Acc, HG>>;
   typename VecWave::QRaw qraw[kMfma ? 1 : HG];
   uint4 qm[kMfma ? 4 : 1];
@@ -638,10 +638,11 @@ hipError_t launch_fac_select_t(const FacArgs& a, int lists, hipStream_t s) {
   // than 32 emitted chunks.  TIP's lists are only used with one head per
   // workgroup (decode_lists).
   if (emitted) {
+    const dim3 g2(sizeof(T) == 2 ? 2 * grid.x : grid.x, grid.y, grid.z);
     if (emit_chunks(a.c) > 32)
-      hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, true, true>), grid, dim3(kSelThreads), 0, s, a);
+      hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, true, true>), g2, dim3(kSelThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true>), grid, dim3(kSelThreads), 0, s, a);
+      hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true>), g2, dim3(kSelThreads), 0, s, a);
     return hipGetLastError();
   }
   const bool deep = sel::filter_chunks(a.c) > 16;
