@@ -439,7 +439,7 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
     w.fold_row_groups();
     __syncthreads();                        // the fold area below overlaps the other waves' tiles
   } else {
-    w.template run<U, false, B1>(r0, r1, lane_offset, kbase, vbase);
+    w.template run<U, false, B1 || kOct>(r0, r1, lane_offset, kbase, vbase);
     w.fold_row_groups();
   }
 

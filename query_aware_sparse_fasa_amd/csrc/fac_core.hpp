@@ -175,7 +175,8 @@ struct FacWave {
   // NT: non-temporal row loads, for rows that no other workgroup reads.
   // FAST: batches whose rows all exist and are valid take an unmasked copy of
   // the batch (measured 0.7 us faster over 1024-row lists, 0.1 us slower over
-  // 256-row lists, where each wave sees one batch and fetches both copies).
+  // 256-row lists, where each wave sees one batch and fetches both copies; the
+  // 8-lane FacWaveOct gains over both).
   template <int U = 2, bool NT = false, bool FAST = false, typename LaneOffset>
   __device__ __forceinline__ void run(int r0, int r1, LaneOffset lane_offset, const T* kbase,
                                       const T* vbase) {
