@@ -259,6 +259,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
 constexpr int kSelThreads = 512;            // workgroup of the selecting launch
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelWideUnits = 256;          // units from which a workgroup covers several heads
+constexpr int64_t kCus = 256;               // compute units of the chip
 constexpr int kB1Early = 0;                 // list pieces read before the lengths are known (per thread)
 
 // The selecting launch of a decode step (budgets up to kSmallBudget).  One
@@ -303,17 +304,17 @@ struct FacSelShared {
 // (with EMIT): only the list keys in bins >= the unit histogram's bin of the
 // B-th key, each thread holding a slice of one list; the unit's last
 // workgroup to read the histogram clears it.
-template <typename T, typename Acc, int HG, bool DEEP = false, bool EMIT = false, bool B1 = false>
+template <typename T, typename Acc, int HG, bool DEEP = false, bool EMIT = false, bool B1 = false, int VS = 1>
 __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   static_assert(!B1 || (EMIT && HG == 1), "the histogram filter reads TIP's lists, one head per workgroup");
+  static_assert(VS == 1 || (EMIT && HG == 1 && sizeof(T) == 2), "V is split over bf16 one-head list workgroups");
   const Common& c = a.c;
   const WgCoord wg = xcd_grouped();
   const int b = wg.z, g = wg.y, hc = wg.x;
-  // The FAC over TIP's lists (bf16, one head per workgroup) runs two workgroups
-  // per head, each over half of the V channels (FacWaveOct's VH): x = 2 head + half.
-  constexpr bool kVh = EMIT && HG == 1 && sizeof(T) == 2;
-  const int vpart = kVh ? (hc & 1) : 0;
-  const int h0 = (kVh ? hc >> 1 : hc) * HG, nh = min(HG, c.group - h0);
+  // VS > 1 (TIP's lists, bf16, one head per workgroup): VS workgroups per
+  // head, each over 1/VS of the V channels (FacWaveOct): x = VS head + part.
+  const int vpart = VS > 1 ? hc % VS : 0;
+  const int h0 = (hc / VS) * HG, nh = min(HG, c.group - h0);
   const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t unit = int64_t(b) * c.n_kv_heads + g;
   constexpr int CHUNK = EMIT ? kEmitChunk : sel::FCH;
@@ -355,9 +356,9 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   // the matrix tiles mostly idle, and its 32 rows per wave in one round trip
   // against two 16-row blocks); fp32 caches always take the vector path.
   constexpr bool kMfma = sizeof(T) == 2 && HG >= 4;
-  // One head over TIP's lists: 8 lanes per row (FacWaveOct).
-  constexpr bool kOct = EMIT && HG == 1 && sizeof(T) == 2;
-  using VecWave = std::conditional_t<kOct, FacWaveOct<HG, kVh>, FacWave<T, Acc, HG>>;
+  // One head over TIP's lists with V split: 8 lanes per row (FacWaveOct).
+  constexpr bool kOct = VS > 1;
+  using VecWave = std::conditional_t<kOct, FacWaveOct<HG, VS>, FacWave<T, Acc, HG>>;
   typename VecWave::QRaw qraw[kMfma ? 1 : HG];
   uint4 qm[kMfma ? 4 : 1];
   if constexpr (kMfma) FacWaveMfma<HG>::load_q(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, qm);
@@ -459,7 +460,7 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
     }
   }
   __syncthreads();
-  constexpr int kOutCh = kVh ? kHeadDim / 2 : kHeadDim;   // this workgroup's output channels
+  constexpr int kOutCh = kHeadDim / VS;    // this workgroup's output channels
   for (int idx = tid; idx < nh * kOutCh; idx += kSelThreads) {
     const int hh = idx / kOutCh, ch = kOutCh * vpart + idx % kOutCh;
     Acc M = neg_inf<Acc>();
@@ -630,10 +631,21 @@ hipError_t launch_fac_select_t(const FacArgs& a, int lists, hipStream_t s) {
   const int hg = select_heads(a.c);
   const dim3 grid((a.c.group + hg - 1) / hg, a.c.n_kv_heads, a.c.batch);
   const bool emitted = lists != kFromFilter;
+  // One-head workgroups over TIP's lists with bf16 caches split V over VS
+  // workgroups per head, as many as keep one workgroup per CU (measured at the
+  // 8B layer: halves 17.54 -> 17.41 us, quarters 16.8 us, eighths no better;
+  // the Qwen shape's 224 half workgroups 34.1 -> 33.0 us, 448 quarters 36.3 us).
+  const int64_t heads = int64_t(a.c.batch) * a.c.n_kv_heads * a.c.group;
+  const int vs = sizeof(T) != 2 || hg != 1 || !emitted ? 1 : (heads * 4 <= kCus ? 4 : (heads * 2 <= kCus ? 2 : 1));
+  const dim3 gv(grid.x * vs, grid.y, grid.z);
   if (lists == kFromListsB1) {
-    // bf16: two workgroups per head, one per half of the V channels.
-    const dim3 g2(sizeof(T) == 2 ? 2 * grid.x : grid.x, grid.y, grid.z);
-    hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, true>), g2, dim3(kSelThreads), 0, s, a);
+    if constexpr (sizeof(T) == 2) {
+      if (vs == 4) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, true, 4>), gv, dim3(kSelThreads), 0, s, a);
+      else if (vs == 2) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, true, 2>), gv, dim3(kSelThreads), 0, s, a);
+      else hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, true>), gv, dim3(kSelThreads), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, true>), gv, dim3(kSelThreads), 0, s, a);
+    }
     return hipGetLastError();
   }
   // One head per workgroup has the registers for a deeper prefetch; it pays only
@@ -642,11 +654,21 @@ hipError_t launch_fac_select_t(const FacArgs& a, int lists, hipStream_t s) {
   // than 32 emitted chunks.  TIP's lists are only used with one head per
   // workgroup (decode_lists).
   if (emitted) {
-    const dim3 g2(sizeof(T) == 2 ? 2 * grid.x : grid.x, grid.y, grid.z);
-    if (emit_chunks(a.c) > 32)
-      hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, true, true>), g2, dim3(kSelThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true>), g2, dim3(kSelThreads), 0, s, a);
+    const bool deep = emit_chunks(a.c) > 32;
+    if constexpr (sizeof(T) == 2) {
+      if (vs == 4) {
+        if (deep) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, true, true, false, 4>), gv, dim3(kSelThreads), 0, s, a);
+        else hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, false, 4>), gv, dim3(kSelThreads), 0, s, a);
+        return hipGetLastError();
+      }
+      if (vs == 2) {
+        if (deep) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, true, true, false, 2>), gv, dim3(kSelThreads), 0, s, a);
+        else hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, false, 2>), gv, dim3(kSelThreads), 0, s, a);
+        return hipGetLastError();
+      }
+    }
+    if (deep) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, true, true>), gv, dim3(kSelThreads), 0, s, a);
+    else hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true>), gv, dim3(kSelThreads), 0, s, a);
     return hipGetLastError();
   }
   const bool deep = sel::filter_chunks(a.c) > 16;

@@ -355,24 +355,35 @@ struct Raw16 {
 // addresses, and takes one DPP step less for the sum; the V unpack and FMAs stay
 // one per channel.  exp2 is the hardware instruction: arguments below -126 (a
 // weight under 2^-126 of the running maximum's) give 0 instead of a denormal.
-template <int HG, bool VH = false>
+// 4 bf16 values (8 bytes) of a row.
+struct Raw4 {
+  uint2 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void unpack(float (&x)[4]) const {
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  }
+};
+
+template <int HG, int VS = 1>
 struct FacWaveOct {
-  // VH: this wave's workgroup takes only half of each V row (channels
-  // 64 vpart .. 64 vpart + 63; the logits still use all of K), so one
-  // instruction per 8 rows brings its V instead of two; each lane then holds
-  // 8 accumulated channels instead of 16.
+  // VS > 1: this wave's workgroup takes only 1/VS of each V row (channels
+  // (128/VS) vpart onwards; the logits still use all of K), so V costs one
+  // load instruction per 8 rows (of 16 or 8 bytes a lane) instead of two, and
+  // VS workgroups per head share the rows; each lane then holds 16/VS channels.
+  static_assert(VS == 1 || VS == 2 || VS == 4, "whole, half or quarter V rows");
   static constexpr int kLanesPerRow = 8;
-  static constexpr int kCh = VH ? 8 : 16;
+  static constexpr int kCh = 16 / VS;
   using QRaw = Raw16;
-  using VRaw = std::conditional_t<VH, Raw8<uint16_t>, Raw16>;
+  using VRaw = std::conditional_t<VS == 1, Raw16, std::conditional_t<VS == 2, Raw8<uint16_t>, Raw4>>;
   uint4 q2[HG][2];
   float zscale;
   float m[HG], l[HG], acc[HG][kCh];
-  int vofs;                                 // VH: 64 vpart, the first channel of the half
+  int vofs;                                 // VS > 1: the first channel of this workgroup's part
 
   // Channel of a lane's value e (sub = lane % 8).
   __device__ __forceinline__ int chan(int sub, int e) const {
-    return VH ? vofs + 8 * sub + e : (e < 8 ? 0 : 64) + 8 * sub + (e & 7);
+    return VS > 1 ? vofs + kCh * sub + e : (e < 8 ? 0 : 64) + 8 * sub + (e & 7);
   }
 
   static __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -398,7 +409,7 @@ struct FacWaveOct {
       q2[hh][1] = hh < nh ? qr[hh].b : z4;
     }
     zscale = scale * 1.4426950408889634f;
-    vofs = VH ? 64 * vpart : 0;
+    vofs = VS > 1 ? (kHeadDim / VS) * vpart : 0;
   }
 
   // Rows r0 .. r1-1, as FacWave::run; U: rows per lane in flight (8 U per wave).
@@ -408,7 +419,7 @@ struct FacWaveOct {
     static_assert(!NT, "ordinary row loads");
     const int lane = threadIdx.x & 63, rg = lane >> 3, sub = lane & 7;
     kbase += 8 * sub;
-    vbase += 8 * sub + vofs;
+    vbase += (VS > 1 ? kCh * sub : 8 * sub) + vofs;
     for (int base = r0; base < r1; base += 64) {   // wave-uniform
       const int64_t my_off = lane_offset(base + lane);
       const uint64_t ok = __ballot(my_off >= 0);
