@@ -839,6 +839,30 @@ def test_decode_filtered_lists_bf16_forced():
     _check_decode(inp, L, oracle_units(inp), "filtered lists bf16 forced")
 
 
+@pytest.mark.parametrize("kind", ["lists", "filtered"])
+def test_decode_lists_whole_v_rows(kind):
+    """TIP's lists with more query heads than CUs to split V over (bf16, one
+    head per workgroup, 2 x heads > 256 CUs): each head keeps one workgroup
+    over whole V rows.  The 8B-layer shape at batch 20 (640 heads, rows of
+    1500-3000 tokens: whole lists) and the Qwen2.5-7B shape at batch 10 (280
+    heads, rows of 90000-100000 tokens: filtered lists); every unit against
+    the oracle."""
+    if kind == "lists":
+        cfg = C["c2"].replace(batch=20, t=None, t_range=(1500, 3000))
+        want = fasa.PATH_LISTS
+    else:
+        cfg = C["c4"].replace(batch=10, t=None, t_range=(90000, 100000))
+        want = fasa.PATH_FILTERED_LISTS
+    say(f"[lists whole V] {kind}: {cfg.name} batch {cfg.batch}")
+    inp = synth.make_inputs(cfg, seed=67)
+    L = DeviceLayer(inp)
+    assert fasa.fasa_decode_path(L.shape, L.max_t) == want
+    L.out.fill_(float("nan"))
+    L.decode()
+    torch.cuda.synchronize()
+    _check_decode(inp, L, oracle_units(inp), f"lists whole V {kind}")
+
+
 def test_decode_filtered_lists_in_two_stages():
     """The histogram-filtered list path (Qwen2.5-7B layer, B = 1024, a ragged
     batch of three rows up to 131072 tokens) split into fasa_decode_tip and
