@@ -271,13 +271,13 @@ constexpr int kB1Early = 0;                 // list pieces read before the lengt
 // partials and no merge.  With one head per workgroup (few units) the G
 // workgroups of a unit read the same K/V rows; the XCD-aware order puts them on
 // one XCD, so after the first they mostly come from its L2.  Over TIP's lists
-// with bf16 caches each head takes two workgroups, one per half of the V
-// channels: each computes every logit from all of K but loads, weighs and
-// writes only its half of V, so a CU issues a quarter fewer row loads and twice
-// as many CUs share the rows, still with nothing to merge.  Workgroup 0 of each
-// unit also publishes the list and its count and clears the unit's histogram
-// for the next step.
-// Grid (head chunks, or 2 x heads for the bf16 lists, kv heads, batch).
+// with bf16 caches each head takes VS = 4 or 2 workgroups (as many as keep one
+// workgroup per CU), one per part of the V channels: each computes every logit
+// from all of K but loads, weighs and writes only its part of V, so a CU
+// issues fewer row loads and more CUs share the rows, still with nothing to
+// merge.  Workgroup 0 of each unit also publishes the list and its count and
+// clears the unit's histogram for the next step.
+// Grid (head chunks, or VS x heads for the bf16 lists, kv heads, batch).
 template <typename Acc, int HG>
 struct FacSelShared {
   union {
