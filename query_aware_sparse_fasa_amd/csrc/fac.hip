@@ -33,6 +33,8 @@
 // move a fp32 output by more than 1e-5).
 #include <math.h>
 
+#include <atomic>
+
 #include "fac_core.hpp"
 #include "fasa_device.hpp"
 #include "fasa_internal.hpp"
@@ -259,7 +261,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
 constexpr int kSelThreads = 512;            // workgroup of the selecting launch
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelWideUnits = 256;          // units from which a workgroup covers several heads
-constexpr int64_t kCus = 256;               // compute units of the chip
 constexpr int kB1Early = 0;                 // list pieces read before the lengths are known (per thread)
 
 // The selecting launch of a decode step (budgets up to kSmallBudget).  One
@@ -626,6 +627,26 @@ int select_heads(const Common& c) {
   return hg;
 }
 
+// Compute units of the current device, asked once per device (256, the whole
+// chip, if the query fails).
+int64_t device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <typename T, typename Acc>
 hipError_t launch_fac_select_t(const FacArgs& a, int lists, hipStream_t s) {
   const int hg = select_heads(a.c);
@@ -636,7 +657,8 @@ hipError_t launch_fac_select_t(const FacArgs& a, int lists, hipStream_t s) {
   // 8B layer: halves 17.54 -> 17.41 us, quarters 16.8 us, eighths no better;
   // the Qwen shape's 224 half workgroups 34.1 -> 33.0 us, 448 quarters 36.3 us).
   const int64_t heads = int64_t(a.c.batch) * a.c.n_kv_heads * a.c.group;
-  const int vs = sizeof(T) != 2 || hg != 1 || !emitted ? 1 : (heads * 4 <= kCus ? 4 : (heads * 2 <= kCus ? 2 : 1));
+  const int64_t cus = sizeof(T) == 2 && hg == 1 && emitted ? device_cus() : 0;
+  const int vs = cus == 0 ? 1 : (heads * 4 <= cus ? 4 : (heads * 2 <= cus ? 2 : 1));
   const dim3 gv(grid.x * vs, grid.y, grid.z);
   if (lists == kFromListsB1) {
     if constexpr (sizeof(T) == 2) {
