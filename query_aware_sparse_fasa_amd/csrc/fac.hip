@@ -308,12 +308,12 @@ struct FacSelShared {
 template <typename T, typename Acc, int HG, bool DEEP = false, bool EMIT = false, bool B1 = false, int VS = 1>
 __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   static_assert(!B1 || (EMIT && HG == 1), "the histogram filter reads TIP's lists, one head per workgroup");
-  static_assert(VS == 1 || (EMIT && HG == 1 && sizeof(T) == 2), "V is split over bf16 one-head list workgroups");
+  static_assert(VS == 1 || (EMIT && HG == 1), "V is split over one-head list workgroups");
   const Common& c = a.c;
   const WgCoord wg = xcd_grouped();
   const int b = wg.z, g = wg.y, hc = wg.x;
-  // VS > 1 (TIP's lists, bf16, one head per workgroup): VS workgroups per
-  // head, each over 1/VS of the V channels (FacWaveOct): x = VS head + part.
+  // VS > 1 (TIP's lists, one head per workgroup): VS workgroups per head,
+  // each over 1/VS of the V channels: x = VS head + part.
   const int vpart = VS > 1 ? hc % VS : 0;
   const int h0 = (hc / VS) * HG, nh = min(HG, c.group - h0);
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -357,9 +357,10 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   // the matrix tiles mostly idle, and its 32 rows per wave in one round trip
   // against two 16-row blocks); fp32 caches always take the vector path.
   constexpr bool kMfma = sizeof(T) == 2 && HG >= 4;
-  // One head over TIP's lists with V split: 8 lanes per row (FacWaveOct).
-  constexpr bool kOct = VS > 1;
-  using VecWave = std::conditional_t<kOct, FacWaveOct<HG, VS>, FacWave<T, Acc, HG>>;
+  // One head over TIP's lists with V split: 8 lanes per row (FacWaveOct) for
+  // bf16 caches, 16 for fp32 ones.
+  constexpr bool kOct = VS > 1 && sizeof(T) == 2;
+  using VecWave = std::conditional_t<kOct, FacWaveOct<HG, VS>, FacWave<T, Acc, HG, VS>>;
   typename VecWave::QRaw qraw[kMfma ? 1 : HG];
   uint4 qm[kMfma ? 4 : 1];
   if constexpr (kMfma) FacWaveMfma<HG>::load_q(static_cast<const T*>(a.q) + head0 * kHeadDim, nh, qm);
@@ -416,8 +417,7 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   // Row r of the list: the forced prefix, the chosen, then the forced suffix.
   std::conditional_t<kMfma, FacWaveMfma<HG>, VecWave> w;
   if constexpr (kMfma) w.init_raw(qm, nh, c.scale, sm.u.tiles[wave]);
-  else if constexpr (kOct) w.init_raw(qraw, nh, c.scale, vpart);
-  else w.init_raw(qraw, nh, c.scale);
+  else w.init_raw(qraw, nh, c.scale, vpart);
   auto token = [&](int r) -> int {
     const int ch = sm.chosen[min(max(r - c_lo, 0), kSmallBudget - 1)];
     return (keep_all || r < c_lo) ? r : (r < c_lo + Bc ? ch : c_hi + (r - c_lo - Bc));
@@ -657,17 +657,13 @@ hipError_t launch_fac_select_t(const FacArgs& a, int lists, hipStream_t s) {
   // 8B layer: halves 17.54 -> 17.41 us, quarters 16.8 us, eighths no better;
   // the Qwen shape's 224 half workgroups 34.1 -> 33.0 us, 448 quarters 36.3 us).
   const int64_t heads = int64_t(a.c.batch) * a.c.n_kv_heads * a.c.group;
-  const int64_t cus = sizeof(T) == 2 && hg == 1 && emitted ? device_cus() : 0;
+  const int64_t cus = hg == 1 && emitted ? device_cus() : 0;
   const int vs = cus == 0 ? 1 : (heads * 4 <= cus ? 4 : (heads * 2 <= cus ? 2 : 1));
   const dim3 gv(grid.x * vs, grid.y, grid.z);
   if (lists == kFromListsB1) {
-    if constexpr (sizeof(T) == 2) {
-      if (vs == 4) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, true, 4>), gv, dim3(kSelThreads), 0, s, a);
-      else if (vs == 2) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, true, 2>), gv, dim3(kSelThreads), 0, s, a);
-      else hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, true>), gv, dim3(kSelThreads), 0, s, a);
-    } else {
-      hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, true>), gv, dim3(kSelThreads), 0, s, a);
-    }
+    if (vs == 4) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, true, 4>), gv, dim3(kSelThreads), 0, s, a);
+    else if (vs == 2) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, true, 2>), gv, dim3(kSelThreads), 0, s, a);
+    else hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, true>), gv, dim3(kSelThreads), 0, s, a);
     return hipGetLastError();
   }
   // One head per workgroup has the registers for a deeper prefetch; it pays only
@@ -677,17 +673,15 @@ hipError_t launch_fac_select_t(const FacArgs& a, int lists, hipStream_t s) {
   // workgroup (decode_lists).
   if (emitted) {
     const bool deep = emit_chunks(a.c) > 32;
-    if constexpr (sizeof(T) == 2) {
-      if (vs == 4) {
-        if (deep) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, true, true, false, 4>), gv, dim3(kSelThreads), 0, s, a);
-        else hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, false, 4>), gv, dim3(kSelThreads), 0, s, a);
-        return hipGetLastError();
-      }
-      if (vs == 2) {
-        if (deep) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, true, true, false, 2>), gv, dim3(kSelThreads), 0, s, a);
-        else hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, false, 2>), gv, dim3(kSelThreads), 0, s, a);
-        return hipGetLastError();
-      }
+    if (vs == 4) {
+      if (deep) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, true, true, false, 4>), gv, dim3(kSelThreads), 0, s, a);
+      else hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, false, 4>), gv, dim3(kSelThreads), 0, s, a);
+      return hipGetLastError();
+    }
+    if (vs == 2) {
+      if (deep) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, true, true, false, 2>), gv, dim3(kSelThreads), 0, s, a);
+      else hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true, false, 2>), gv, dim3(kSelThreads), 0, s, a);
+      return hipGetLastError();
     }
     if (deep) hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, true, true>), gv, dim3(kSelThreads), 0, s, a);
     else hipLaunchKernelGGL((fac_select_kernel<T, Acc, 1, false, true>), gv, dim3(kSelThreads), 0, s, a);

@@ -112,19 +112,38 @@ __device__ __forceinline__ float dot8(const uint4& q, const Raw8<uint16_t>& k) {
   return c + d;
 }
 
-template <typename T, typename Acc, int HG>
+// N consecutive fp32 values of a row.
+template <int N>
+struct RawF {
+  typedef float fv __attribute__((ext_vector_type(N)));
+  fv v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const fv*>(p); }
+  __device__ __forceinline__ void unpack(float (&x)[N]) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = v[i];
+  }
+};
+
+// VS > 1 (fp32 caches, one head over TIP's lists): the workgroup takes 1/VS of
+// each V row (channels (128/VS) vpart onwards; the logits still use all of K),
+// one 16- or 8-byte load a lane per row instead of two 16-byte ones; each lane
+// then holds 8/VS channels.
+template <typename T, typename Acc, int HG, int VS = 1>
 struct FacWave {
+  static_assert(VS == 1 || (sizeof(T) == 4 && (VS == 2 || VS == 4)), "fp32 caches split V in halves or quarters");
   static constexpr bool kBf16 = sizeof(T) == 2;
   static constexpr int kLanesPerRow = 16;   // lanes per row; each holds kCh channels
-  static constexpr int kCh = 8;
+  static constexpr int kCh = 8 / VS;
   using QRaw = Raw8<T>;
-  __device__ __forceinline__ int chan(int sub, int e) const { return 8 * sub + e; }
+  using VRaw = std::conditional_t<VS == 1, Raw8<T>, RawF<8 / VS>>;
+  int vofs = 0;                             // VS > 1: the first channel of this workgroup's part
+  __device__ __forceinline__ int chan(int sub, int e) const { return vofs + kCh * sub + e; }
   // Query slices: raw bf16 pairs (logits scaled afterwards by zscale), or
   // pre-scaled fp64 values for fp32 caches.
   uint4 q2[kBf16 ? HG : 1];
   Acc qv[kBf16 ? 1 : HG][8];
   Acc zscale;
-  Acc m[HG], l[HG], acc[HG][8];
+  Acc m[HG], l[HG], acc[HG][kCh];
 
   // This lane's raw query slices of heads 0 .. nh-1 from q_head0 (rows of q,
   // each kHeadDim long); loads are unconditional (slots past nh repeat the last).
@@ -142,14 +161,15 @@ struct FacWave {
     load_q(q_head0, nh, qr);
     init_raw(qr, nh, scale);
   }
-  __device__ __forceinline__ void init_raw(const Raw8<T> (&qr)[HG], int nh, float scale) {
+  __device__ __forceinline__ void init_raw(const Raw8<T> (&qr)[HG], int nh, float scale, int vpart = 0) {
+    vofs = VS > 1 ? (kHeadDim / VS) * vpart : 0;
     const Acc qscale = sizeof(Acc) == 4 ? Acc(scale) * Acc(1.4426950408889634) : Acc(scale);
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
       m[hh] = neg_inf<Acc>();
       l[hh] = Acc(0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] = Acc(0);
+      for (int e = 0; e < kCh; ++e) acc[hh][e] = Acc(0);
       if constexpr (kBf16) {
         const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
         q2[hh] = (hh < nh) ? reinterpret_cast<const uint4&>(qr[hh]) : z4;
@@ -182,7 +202,7 @@ struct FacWave {
                                       const T* vbase) {
     const int lane = threadIdx.x & 63, rg = lane >> 4, sub = lane & 15;
     kbase += 8 * sub;
-    vbase += 8 * sub;
+    vbase += kCh * sub + vofs;
     for (int base = r0; base < r1; base += 64) {   // wave-uniform
       const int64_t my_off = lane_offset(base + lane);
       const uint64_t ok = __ballot(my_off >= 0);
@@ -190,7 +210,8 @@ struct FacWave {
       const int64_t dummy = __shfl(my_off, __ffsll((unsigned long long)ok) - 1, 64);
       const int nrows = min(64, r1 - base);
       for (int q4 = 0; q4 < nrows; q4 += 4 * U) {
-        Raw8<T> kr[U], vr[U];
+        Raw8<T> kr[U];
+        VRaw vr[U];
         // A batch whose 4 U rows all exist and are valid skips every mask.
         static_assert(4 * U < 64, "a batch within one 64-row window");
         const bool full = FAST && q4 + 4 * U <= nrows &&
@@ -238,7 +259,7 @@ struct FacWave {
   // valid (valid is not read), so no logit is -inf and the batch's maximum is
   // finite.
   template <int U, bool MASKED = true>
-  __device__ __forceinline__ void absorb(const Raw8<T> (&kr)[U], const Raw8<T> (&vr)[U], const bool (&valid)[U]) {
+  __device__ __forceinline__ void absorb(const Raw8<T> (&kr)[U], const VRaw (&vr)[U], const bool (&valid)[U]) {
     Acc z[U][HG], mn[HG];
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) mn[hh] = m[hh];
@@ -267,20 +288,20 @@ struct FacWave {
       const Acc corr = merge_weight(m[hh], mn[hh]);
       l[hh] *= corr;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] *= corr;
+      for (int e = 0; e < kCh; ++e) acc[hh][e] *= corr;
       m[hh] = mn[hh];
     }
     // Add the weighted rows.
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float vx[8];
+      float vx[kCh];
       vr[u].unpack(vx);
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh) {
         const Acc pz = MASKED ? merge_weight(z[u][hh], mn[hh]) : fexp<Acc>(z[u][hh] - mn[hh]);
         l[hh] += pz;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] = fma(pz, Acc(vx[e]), acc[hh][e]);
+        for (int e = 0; e < kCh; ++e) acc[hh][e] = fma(pz, Acc(vx[e]), acc[hh][e]);
       }
     }
   }
@@ -300,7 +321,7 @@ struct FacWave {
       const Acc wb = merge_weight(mb, mn);
       l[hh] = la * wa + lb * wb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < kCh; ++e) {
         Acc aa, ab;
         lane_pair<PAIR>(acc[hh][e], aa, ab);
         acc[hh][e] = aa * wa + ab * wb;
