@@ -177,7 +177,7 @@ __device__ __forceinline__ void fac_split_body(const FacArgs& a) {
   const int g = wg.y / p.head_chunks;
   const int h0 = (wg.y % p.head_chunks) * HG;      // first head of this pass, within the group
   const int nh = min(HG, c.group - h0);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, sub = lane & 15;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t unit = int64_t(b) * c.n_kv_heads + g;
   const int r0 = (wg.x * kFacWaves + wave) * p.rows_per_wave;
   const int32_t* sel = a.sel_idx + unit * c.cap;

@@ -62,6 +62,51 @@ __device__ __forceinline__ uint32_t block_excl_scan(SelState<NTH>& s, uint32_t v
   return base + incl - v;
 }
 
+// block_excl_scan of v, and the block total of w, behind one barrier (the wave
+// totals of v go through buffer 0, those of w through buffer 1).  Both buffers
+// must be free: a barrier has passed since the last scan returned.
+template <int NTH>
+__device__ __forceinline__ uint32_t block_excl_scan_and_sum(SelState<NTH>& s, uint32_t v, uint32_t& total, uint32_t w,
+                                                           uint32_t& w_total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_inclusive_scan(v), incl_w = wave_inclusive_scan(w);
+  if (lane == 63) {
+    s.wave_sum[0][wave] = incl;
+    s.wave_sum[1][wave] = incl_w;
+  }
+  __syncthreads();
+  uint32_t base = 0, tot = 0, tot_w = 0;
+#pragma unroll
+  for (int i = 0; i < NTH / 64; ++i) {
+    const uint32_t x = s.wave_sum[0][i];
+    base += (i < wave) ? x : 0u;
+    tot += x;
+    tot_w += s.wave_sum[1][i];
+  }
+  total = tot;
+  w_total = tot_w;
+  return base + incl - v;
+}
+
+// Largest value over the wave's 64 lanes (all active), as a scalar: rotations
+// by 8, 4, 2 and 1 inside each 16-lane row, then the four rows' results -- no
+// LDS round trips.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), kDppRowRor + 8, 0xF, 0xF, false)));
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), kDppRowRor + 4, 0xF, 0xF, false)));
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), kDppRowRor + 2, 0xF, 0xF, false)));
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), kDppRowRor + 1, 0xF, 0xF, false)));
+  const uint32_t r0 = uint32_t(__builtin_amdgcn_readlane(int(v), 0)), r1 = uint32_t(__builtin_amdgcn_readlane(int(v), 16));
+  const uint32_t r2 = uint32_t(__builtin_amdgcn_readlane(int(v), 32)), r3 = uint32_t(__builtin_amdgcn_readlane(int(v), 48));
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// Lane Q of the lane's quad (DPP quad_perm [Q, Q, Q, Q]).
+template <int Q>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x55 * Q, 0xF, 0xF, false));
+}
+
 // Exclusive prefix over the waves of a per-wave value (the same in every lane
 // of a wave); also returns the block total.
 template <int NTH>
@@ -487,8 +532,7 @@ __device__ __forceinline__ int gather_emitted(SelState<NTH>& s, int32_t* chunk_o
       sum += cnt[k];
       cut = (in && emit_cut(w)) ? max(cut, meta_raw[k].y) : cut;
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) cut = max(cut, uint32_t(__shfl_xor(int(cut), o, 64)));
+    cut = wave_max_u32(cut);
     const uint32_t incl = wave_inclusive_scan(sum);
     uint32_t off = incl - sum;
 #pragma unroll
@@ -571,43 +615,65 @@ __device__ __forceinline__ int gather_lists_b1(SelState<NTH>& s, const B1Slice<N
                                                int cap_lds, uint32_t* key, int32_t* idx, uint32_t b1, uint32_t& above) {
   using S = B1Slice<NTH, EARLY>;
   constexpr int TPC = S::TPC, VPT = S::VPT;
+  static_assert(2 * TPC <= 15, "a step's kept count of a list fits 4 bits");
   const int lane = int(threadIdx.x) & 63, j = sl.j();
   const int ch = int(threadIdx.x) / TPC;
   const bool unusable = sl.n > B1_LIST || (ch < nfc && emit_cut(m.x) && m.y > (b1 << kHistShift));
   // Steps that hold a pair of some list of this wave (the longest list decides).
-  int longest = sl.n;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) longest = max(longest, __shfl_xor(longest, o, 64));
-  const int steps = __builtin_amdgcn_readfirstlane((min(longest, B1_LIST) + 2 * TPC - 1) / (2 * TPC));
-  // Bit 2 i + h: the h-th pair of step i is kept.
-  uint32_t mask = 0, n_above = 0;
+  const int steps = int((min(wave_max_u32(uint32_t(sl.n)), uint32_t(B1_LIST)) + 2 * TPC - 1) / (2 * TPC));
+  // Bit 2 i + h: the h-th pair of step i lies in the list (its position
+  // 2 (TPC i + j) + h is below n): i < ceil((n - 2 j - h) / (2 TPC)).
+  const int r = sl.n - 2 * j;
+  const int a0 = min((max(r, 0) + 2 * TPC - 1) / (2 * TPC), VPT);
+  const int a1 = min((max(r - 1, 0) + 2 * TPC - 1) / (2 * TPC), VPT);
+  const uint32_t valid = (0x55555555u & (a0 >= 16 ? ~0u : (1u << (2 * a0)) - 1u)) |
+                         (0xAAAAAAAAu & (a1 >= 16 ? ~0u : (1u << (2 * a1)) - 1u));
+  // Bit 2 i + h of mask: that pair is kept (bin >= b1); of amask: its bin is above b1.
+  const uint32_t lo_key = b1 << kHistShift, hi_key = lo_key | ((1u << kHistShift) - 1u);
+  uint32_t mask = 0, amask = 0;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     if (i < steps) {                        // uniform; no break, so pr keeps static indices
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint32_t bin = (h == 0 ? sl.pr[i].x : sl.pr[i].z) >> kHistShift;
-        const bool ok = sl.pos(i, h) < sl.n;
-        mask |= (ok && bin >= b1) ? (1u << (2 * i + h)) : 0u;
-        n_above += (ok && bin > b1) ? 1u : 0u;
+        const uint32_t k = h == 0 ? sl.pr[i].x : sl.pr[i].z;
+        mask |= k >= lo_key ? (1u << (2 * i + h)) : 0u;
+        amask |= k > hi_key ? (1u << (2 * i + h)) : 0u;
       }
     }
   }
-  // The masks of the list's TPC threads; below[q]: thread q's mask if it comes
-  // before this thread in the list's order within a step, else 0.
-  uint32_t mg[TPC], below[TPC], list_kept = 0;
+  mask &= valid;
+  const uint32_t n_above = uint32_t(__popc(amask & valid));
+  // The masks of the list's TPC threads, and their kept counts per step, 4 bits
+  // a step: step 2 k in bits 4 k .. 4 k + 3 of *_e, step 2 k + 1 in those of
+  // *_o; tot_* over the list's TPC threads, pre_* over those before this one.
+  uint32_t mg[TPC];
+  if constexpr (TPC == 4) {                 // the list is the lane's quad: quad broadcasts
+    mg[0] = quad_bcast<0>(mask);
+    mg[1] = quad_bcast<1>(mask);
+    mg[2] = quad_bcast<2>(mask);
+    mg[3] = quad_bcast<3>(mask);
+  } else {
+#pragma unroll
+    for (int q = 0; q < TPC; ++q) mg[q] = uint32_t(__shfl(int(mask), (lane & ~(TPC - 1)) + q, 64));
+  }
+  uint32_t list_kept = 0, tot_e = 0, tot_o = 0, pre_e = 0, pre_o = 0;
 #pragma unroll
   for (int q = 0; q < TPC; ++q) {
-    mg[q] = uint32_t(__shfl(int(mask), (lane & ~(TPC - 1)) + q, 64));
-    below[q] = q < j ? mg[q] : 0u;
-    list_kept += uint32_t(__popc(mg[q]));
+    const uint32_t mq = mg[q];
+    list_kept += uint32_t(__popc(mq));
+    const uint32_t c2 = (mq & 0x55555555u) + ((mq >> 1) & 0x55555555u);   // 2 bits a step
+    const uint32_t e = c2 & 0x33333333u, o = (c2 >> 2) & 0x33333333u;
+    tot_e += e;
+    tot_o += o;
+    pre_e += q < j ? e : 0u;
+    pre_o += q < j ? o : 0u;
   }
   // The list's count rides on its last thread; a flag on any thread adds more
   // than any block could keep.
   const uint32_t v = (j == TPC - 1 ? list_kept : 0u) + (unusable ? uint32_t(cap_lds) + 1u : 0u);
   uint32_t tot;
-  uint32_t run = block_excl_scan(s, v, tot);
-  (void)block_excl_scan<1>(s, n_above, above);   // right after the previous scan: the other buffer
+  uint32_t run = block_excl_scan_and_sum(s, v, tot, n_above, above);
   if (tot > uint32_t(cap_lds)) return -1;   // uniform
   auto put = [&](uint32_t at, uint32_t k, uint32_t t) {
     key[at] = k;
@@ -617,12 +683,9 @@ __device__ __forceinline__ int gather_lists_b1(SelState<NTH>& s, const B1Slice<N
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     if (i < steps) {                        // uniform
-      const uint32_t step = 3u << (2 * i);
-      uint32_t at = run;                    // the list's kept pairs before this thread's in step i
-#pragma unroll
-      for (int q = 0; q < TPC; ++q) at += uint32_t(__popc(below[q] & step));
-#pragma unroll
-      for (int q = 0; q < TPC; ++q) run += uint32_t(__popc(mg[q] & step));
+      const int sh = 4 * (i >> 1);
+      const uint32_t at = run + ((((i & 1) ? pre_o : pre_e) >> sh) & 15u);   // the list's kept pairs before this thread's
+      run += (((i & 1) ? tot_o : tot_e) >> sh) & 15u;
       const uint32_t mine = mask >> (2 * i);
       if (mine & 1u) put(at, sl.pr[i].x, sl.pr[i].y);
       if (mine & 2u) put(at + (mine & 1u), sl.pr[i].z, sl.pr[i].w);
