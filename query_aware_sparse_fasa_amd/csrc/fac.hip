@@ -337,10 +337,11 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
   uint2 m1 = make_uint2(0u, 0u);
   sel::B1Slice<kSelThreads, kB1Early> sl;
   if constexpr (B1) {
-    // The unit histogram (bins 4 t .. 4 t + 3) and the summary of the chunk
+    // The unit histogram (thread t: bins HB - 4 (t + 1) .. HB - 4 t - 1, the
+    // order of the digit search) and the summary of the chunk
     // whose list slice this thread takes; the slice itself once the length is known.
     static_assert(kSelThreads * 4 == sel::HB, "one uint4 of bins per thread");
-    hv = reinterpret_cast<const uint4*>(a.w.hist + unit * sel::HB)[tid];
+    hv = reinterpret_cast<const uint4*>(a.w.hist + unit * sel::HB)[kSelThreads - 1 - tid];
     m1 = reinterpret_cast<const uint2*>(a.w.counts)[unit * nfa + min(tid / sel::B1Slice<kSelThreads>::TPC, nfa - 1)];
     sl.early(unit_slots, nfa);
   } else {
@@ -380,11 +381,10 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
 
   if constexpr (B1) {
     if (!keep_all) sl.late(unit_slots, emit_chunks_of(t), m1);
-    reinterpret_cast<uint4*>(sm.u.s.st.hist)[tid] = hv;   // consumed in every workgroup
   }
   if (!keep_all) {
     if constexpr (B1)
-      sel::select_from_lists_b1<kSelThreads, true, kB1Early>(sm.u.s.st, sm.u.s.key, sm.u.s.idx, kSmallCand, sl, m1, row, lim,
+      sel::select_from_lists_b1<kSelThreads, true, kB1Early>(sm.u.s.st, sm.u.s.key, sm.u.s.idx, kSmallCand, sl, m1, hv, row, lim,
                                                    c.max_t, emit_chunks_of(t), c_lo, c_hi, Bc, sm.chosen);
     else if constexpr (EMIT)
       sel::select_from_emitted<kSelThreads, PRE, true>(sm.u.s.st, sm.u.s.chunk_off, sm.u.s.key, sm.u.s.idx,
@@ -400,9 +400,10 @@ __global__ __launch_bounds__(kSelThreads) void fac_select_kernel(FacArgs a) {
     if (tid + kSelThreads * k < c.max_blocks) sm.btab[tid + kSelThreads * k] = bt[k];
   __syncthreads();                          // the list and the block table are in LDS; the select area is free
   if constexpr (B1) {
-    // Every wave of this workgroup has stored its histogram bins (its reads are
-    // done); the unit's last workgroup to get here leaves the histogram zero for
-    // the next step's TIP.  The counter was zeroed by TIP.
+    // Every wave of this workgroup is done with its histogram bins (the digit
+    // search has used them; a keep-all workgroup never uses them); the unit's
+    // last workgroup to get here leaves the histogram zero for the next step's
+    // TIP.  The counter was zeroed by TIP.
     if (wave == 0) {
       uint32_t old = 0;
       if (tid == 0) old = atomicAdd(&a.arrive[unit], 1u);

@@ -133,6 +133,9 @@ __device__ __forceinline__ uint32_t wave_base(SelState<NTH>& s, uint32_t wave_va
 // whose bins hold the crossing walks them in registers.  Leaves s.digit
 // untouched when there are fewer than rem keys in total.  hist: the histogram
 // (s.hist unless given).
+template <int NTH, int NB, int BPT>
+__device__ __forceinline__ void find_digit_held(SelState<NTH>& s, uint32_t rem, const uint32_t (&h)[BPT]);
+
 template <int NTH, int NB>
 __device__ __forceinline__ void find_digit(SelState<NTH>& s, uint32_t rem, const uint32_t* hist = nullptr) {
   constexpr int BPT = NB > NTH ? NB / NTH : 1;
@@ -149,6 +152,15 @@ __device__ __forceinline__ void find_digit(SelState<NTH>& s, uint32_t rem, const
 #pragma unroll
     for (int i = 0; i < BPT; ++i) h[i] = lo + i >= 0 ? hb[lo + i] : 0u;
   }
+  find_digit_held<NTH, NB, BPT>(s, rem, h);
+}
+
+// find_digit over bins the threads already hold: h[i] is bin NB - BPT (t + 1) + i
+// of thread t.  The scan's barrier orders any write to s.digit, s.rem or s.full
+// made before the call ahead of the search's own.
+template <int NTH, int NB, int BPT>
+__device__ __forceinline__ void find_digit_held(SelState<NTH>& s, uint32_t rem, const uint32_t (&h)[BPT]) {
+  const int lo = NB - BPT * (int(threadIdx.x) + 1);     // lowest owned bin
   uint32_t sum = 0;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) sum += h[i];
@@ -460,10 +472,21 @@ __device__ __forceinline__ uint32_t lds_select_from(SelState<NTH>& s, const uint
     n_gt += m > prefix ? 1u : 0u;
     n_eq += m == prefix ? 1u : 0u;
   }
-  uint32_t eq_tot, sel_tot;
-  const uint32_t eq_base = block_excl_scan(s, n_eq, eq_tot);
-  const uint32_t take_eq = (rem > eq_base) ? min(rem - eq_base, n_eq) : 0u;
-  int pos = int(block_excl_scan<1>(s, n_gt + take_eq, sel_tot));   // right after the previous scan: the other buffer
+  // The keys equal to the prefix are taken in index order, the first rem of
+  // them: the threads before this one take min(rem, eq_base) of theirs.
+  uint32_t eq_base, pos0;
+  if (N < 65536) {                          // uniform: both counts fit 16 bits, one scan
+    uint32_t tot;
+    const uint32_t base = block_excl_scan(s, n_gt | (n_eq << 16), tot);
+    eq_base = base >> 16;
+    pos0 = (base & 0xffffu) + min(rem, eq_base);
+  } else {
+    uint32_t eq_tot, sel_tot;
+    eq_base = block_excl_scan(s, n_eq, eq_tot);
+    const uint32_t take_eq = (rem > eq_base) ? min(rem - eq_base, n_eq) : 0u;
+    pos0 = block_excl_scan<1>(s, n_gt + take_eq, sel_tot);   // right after the previous scan: the other buffer
+  }
+  int pos = int(pos0);
   uint32_t eq_seen = eq_base;
   for (int i = i0; i < i1; ++i) {
     const uint32_t m = key[i] & pmask;
@@ -868,26 +891,23 @@ __device__ __forceinline__ void load_counts(const int32_t* unit_counts, int nfa,
   for (int k = 0; k < CPT; ++k) cnt[k] = unit_counts[min(CPT * int(threadIdx.x) + k, nfa - 1)];
 }
 
-// Exact select of one unit that is not keep-all, from the filter's kept pairs
-// (nfc chunks, counts cnt and first pairs pre already loaded), into out[0..Bc)
-// -- global or LDS.  b1: the coarse bin the filter kept keys from.  Falls back
-// to the whole score row when the kept pairs are fewer than Bc or do not fit.
 // The exact select from TIP's lists filtered by the unit histogram (see
-// gather_lists_b1): s.hist holds the unit's histogram (stored by the caller,
-// not yet published), whose bin of the Bc-th largest key is b1; sl holds the
-// thread's slice of the lists, m its chunk's summary.  Falls back to the whole
-// scores row when the lists cannot be used.
+// gather_lists_b1): thread t holds the unit histogram's bins HB - 4 (t + 1) ..
+// HB - 4 t - 1 in hv (the digit search's order), whose bin of the Bc-th largest
+// key is b1; sl holds the thread's slice of the lists, m its chunk's summary.
+// Falls back to the whole scores row when the lists cannot be used.
 template <int NTH, bool VEC, int EARLY>
 __device__ void select_from_lists_b1(SelState<NTH>& s, uint32_t* key, int32_t* idx, int cap_lds,
-                                     const B1Slice<NTH, EARLY>& sl, uint2 m, const float* row, int lim, int max_t, int nfc,
-                                     int c_lo, int c_hi, int Bc, int32_t* out) {
+                                     const B1Slice<NTH, EARLY>& sl, uint2 m, uint4 hv, const float* row, int lim,
+                                     int max_t, int nfc, int c_lo, int c_hi, int Bc, int32_t* out) {
+  static_assert(HB == 4 * NTH, "four bins per thread");
   if (threadIdx.x == 0) {
     s.digit = 0u;                            // fewer than Bc keys counted: keep every candidate
     s.rem = uint32_t(Bc);
     s.full = 0u;
   }
-  __syncthreads();
-  find_digit<NTH, HB>(s, uint32_t(Bc));      // ends with a barrier: s.hist is free again
+  const uint32_t h[4] = {hv.x, hv.y, hv.z, hv.w};
+  find_digit_held<NTH, HB>(s, uint32_t(Bc), h);   // ends with a barrier
   const uint32_t b1 = s.digit;
   zero_bins<NTH, HB>(s);                     // the second-digit histogram; published by the gather's first barrier
   zero_hist2<NTH>(s);
@@ -900,6 +920,10 @@ __device__ void select_from_lists_b1(SelState<NTH>& s, uint32_t* key, int32_t* i
   row_select<NTH, VEC>(s, row, lim, max_t, c_lo, c_hi, Bc, out);
 }
 
+// Exact select of one unit that is not keep-all, from the filter's kept pairs
+// (nfc chunks, counts cnt and first pairs pre already loaded), into out[0..Bc)
+// -- global or LDS.  b1: the coarse bin the filter kept keys from.  Falls back
+// to the whole score row when the kept pairs are fewer than Bc or do not fit.
 template <int NTH, int PRE, bool VEC, int D = 1>
 __device__ void select_from_kept(SelState<NTH>& s, int32_t* chunk_off, uint32_t* key, int32_t* idx, int cap_lds,
                                  const uint2* unit_slots, const float* row, int lim, int max_t, int nfc,
