@@ -409,7 +409,7 @@ __device__ __forceinline__ int gather_kept(SelState<NTH>& s, int32_t* chunk_off,
 // The radix passes of an exact select from pass `pass` on (0: bits 31..21, 1:
 // bits 20..10, 2: bits 9..0), given the digits found so far (prefix under
 // pmask) and the rem keys still to take among those equal to the prefix, then
-// the index-order compaction: the Bc largest of the N keys key[0..N) (index
+// the index-order compaction: the Bc largest of the N <= kCandLds keys key[0..N) (index
 // order, token indices idx) in LDS are written ascending to out[0..Bc).
 // all_eq: every key equal to the prefix is taken (skip to one scan).  Thread t
 // owns a contiguous run of the keys.
@@ -474,19 +474,13 @@ __device__ __forceinline__ uint32_t lds_select_from(SelState<NTH>& s, const uint
   }
   // The keys equal to the prefix are taken in index order, the first rem of
   // them: the threads before this one take min(rem, eq_base) of theirs.
-  uint32_t eq_base, pos0;
-  if (N < 65536) {                          // uniform: both counts fit 16 bits, one scan
-    uint32_t tot;
-    const uint32_t base = block_excl_scan(s, n_gt | (n_eq << 16), tot);
-    eq_base = base >> 16;
-    pos0 = (base & 0xffffu) + min(rem, eq_base);
-  } else {
-    uint32_t eq_tot, sel_tot;
-    eq_base = block_excl_scan(s, n_eq, eq_tot);
-    const uint32_t take_eq = (rem > eq_base) ? min(rem - eq_base, n_eq) : 0u;
-    pos0 = block_excl_scan<1>(s, n_gt + take_eq, sel_tot);   // right after the previous scan: the other buffer
-  }
-  int pos = int(pos0);
+  // Both counts fit 16 bits (N is at most the LDS capacity), so one scan
+  // carries them.
+  static_assert(kCandLds < 65536 && kSmallCand < 65536, "the keys' counts fit 16 bits");
+  uint32_t tot;
+  const uint32_t base = block_excl_scan(s, n_gt | (n_eq << 16), tot);
+  const uint32_t eq_base = base >> 16;
+  int pos = int((base & 0xffffu) + min(rem, eq_base));
   uint32_t eq_seen = eq_base;
   for (int i = i0; i < i1; ++i) {
     const uint32_t m = key[i] & pmask;
