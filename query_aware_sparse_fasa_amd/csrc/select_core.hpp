@@ -126,6 +126,9 @@ __device__ __forceinline__ uint32_t wave_base(SelState<NTH>& s, uint32_t wave_va
   return base;
 }
 
+template <int NTH, int NB, int BPT>
+__device__ __forceinline__ void find_digit_held(SelState<NTH>& s, uint32_t rem, const uint32_t (&h)[BPT]);
+
 // Find the digit d of a histogram with NB bins (1024 or 2048) such that fewer
 // than rem keys lie in bins above d and at least rem in bins >= d.  Thread t
 // owns the BPT bins below NB - BPT t (read as 16-byte vectors when BPT >= 4);
@@ -133,9 +136,6 @@ __device__ __forceinline__ uint32_t wave_base(SelState<NTH>& s, uint32_t wave_va
 // whose bins hold the crossing walks them in registers.  Leaves s.digit
 // untouched when there are fewer than rem keys in total.  hist: the histogram
 // (s.hist unless given).
-template <int NTH, int NB, int BPT>
-__device__ __forceinline__ void find_digit_held(SelState<NTH>& s, uint32_t rem, const uint32_t (&h)[BPT]);
-
 template <int NTH, int NB>
 __device__ __forceinline__ void find_digit(SelState<NTH>& s, uint32_t rem, const uint32_t* hist = nullptr) {
   constexpr int BPT = NB > NTH ? NB / NTH : 1;
