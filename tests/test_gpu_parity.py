@@ -964,15 +964,23 @@ FULL_SAMPLES = {
 }
 
 
-def test_decode_duplicate_keys_tie_to_lower_index():
+@pytest.mark.parametrize("kind", ["lists", "filtered"])
+def test_decode_duplicate_keys_tie_to_lower_index(kind):
     """Exact score ties through the whole decode step: in every unit, 30 copies
     of the key of the token the oracle ranks B - 10 are written at other
     positions (in its own 1024-token chunk and in others, before and after it),
     so the B-th score is shared by many tokens.  TIP gives identical rows
     bit-identical scores, and the select must keep the lowest indices among
-    them, exactly as the oracle's (-S, j) order does."""
-    cfg = C["c2"].replace(batch=2, n_q_heads=8, n_kv_heads=2, t=None, t_range=(6000, 9000), budget=200)
-    say("[decode duplicate keys]")
+    them, exactly as the oracle's (-S, j) order does.  Through TIP's lists (8B
+    layer shape, rows of 6000-9000 tokens) and through the lists filtered by the
+    unit histogram (Qwen2.5-7B layer shape, rows of 90000-100000 tokens)."""
+    if kind == "lists":
+        cfg = C["c2"].replace(batch=2, n_q_heads=8, n_kv_heads=2, t=None, t_range=(6000, 9000), budget=200)
+        want_path = fasa.PATH_LISTS
+    else:
+        cfg = C["c4"].replace(batch=2, t=None, t_range=(90000, 100000))
+        want_path = fasa.PATH_FILTERED_LISTS
+    say(f"[decode duplicate keys] {kind}")
     inp = synth.make_inputs(cfg, seed=41)
     rng = np.random.default_rng(41)
     G = cfg.group
@@ -994,6 +1002,7 @@ def test_decode_duplicate_keys_tie_to_lower_index():
                 inp.k_pool[int(inp.block_table[b, j // 256]), g, int(j) % 256] = row
             dup[(b, g)] = np.sort(np.append(pos, src))
     L = DeviceLayer(inp)
+    assert fasa.fasa_decode_path(L.shape, L.max_t) == want_path
     L.out.fill_(float("nan"))
     L.decode()
     units = oracle_units(inp)
